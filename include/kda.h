@@ -1,0 +1,150 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation is the KDA forward hot path specified on the page
+ * "KDA Chunk Prefill on Ascend A3" (sections "Function and tensor contract"
+ * and "Mathematical definition") and, for single-token decode, on the page
+ * "flashinfer.kda_decode.packed_kda_decode" (section "Parameters").
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; all work is enqueued
+ *     on `stream` (a hipStream_t; NULL selects the null stream).
+ *   - bf16 tensors are arrays of IEEE bfloat16 bit patterns (uint16).
+ *   - Tensors are dense and row-major in the listed axis order (last axis
+ *     contiguous).  Pointers must be 16-byte aligned.
+ *   - Inputs are read-only; only the named outputs (and, for kda_decode,
+ *     the addressed slots of the state pool) are written.
+ *   - Host-side checks cover metadata only (null pointers, sizes,
+ *     alignment).  A failed check returns a nonzero status and enqueues
+ *     nothing.  Device values are not inspected on the host.
+ *   - After enqueueing, a launch error reported by the HIP runtime is
+ *     returned as KDA_ERR_HIP.
+ *   - K and V must both be 128 (the head width the pages' core cases use).
+ *   - Fixed numerics, not parameters: query scale K**-0.5 and L2 epsilon
+ *     1e-6 inside the square root.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,         /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
+  KDA_ERR_UNSUPPORTED = 3,  /* valid request this build does not support (K, V != 128) */
+  KDA_ERR_ALIGN = 4,        /* a pointer or stride is not 16-byte aligned */
+  KDA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} kda_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* kda_status_string(int status);
+
+/*
+ * kda_qk_l2norm -- bit-exact row L2 normalisation of q or k.
+ *
+ * Defined on "KDA Chunk Prefill on Ascend A3", section "Mathematical
+ * definition": per row x of length K, in float32,
+ *     y = bf16( x / sqrt( sum(x*x) + 1e-6 ) ).
+ * The sum is the exact sum of the float32 squares rounded once to float32
+ * (an order-free reading of the page's float32 reduction); the square root
+ * and the division are correctly rounded float32 operations; the quotient
+ * is rounded to bfloat16, nearest-even.  The same routine is fused into
+ * kda_chunk_prefill and kda_decode, so their normalised values are equal
+ * to this export's bit for bit.
+ *
+ *   x     bf16 [rows, K]   input rows (any Q/K tensor viewed as rows)
+ *   y     bf16 [rows, K]   output; may not alias x
+ *   rows  >= 0 (0 enqueues nothing)
+ *   K     must be 128
+ */
+int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream);
+
+/*
+ * kda_chunk_prefill -- KDA chunked prefill forward.
+ *
+ * Defined on "KDA Chunk Prefill on Ascend A3": section "Function and tensor
+ * contract" (forward(q, k, v, g, beta, initial_state) -> (o, final_state),
+ * HV % H == 0, value head h reads Q/K head h // (HV / H)) and section
+ * "Mathematical definition" (Q/K L2 normalisation as kda_qk_l2norm, then
+ * the per-channel gated delta rule, computed chunk by chunk: chunk-local
+ * G, L, A = solve(I+L, diag(beta)), W, U, Qg, Kg and Aqk, then the carry
+ * Vnew = U - W S, O = Qg S + Aqk Vnew, S = exp(G_last) S + Kg^T Vnew).
+ * The last partial chunk of each sequence behaves as if zero-padded, as
+ * the page's golden does; o is written only for real tokens.
+ *
+ *   q, k           bf16 [B, T, H, K]   raw (unnormalised) queries and keys
+ *   v              bf16 [B, T, HV, V]
+ *   g              fp32 [B, T, HV, K]  per-channel log decay (finite, <= 0)
+ *   beta           bf16 [B, T, HV]
+ *   initial_state  fp32 [N, HV, K, V]  or NULL (zeros)
+ *   cu_seqlens     int32 [N + 1] device array of packed sequence offsets, or
+ *                  NULL.  When given, B must be 1 and the N = num_seqs
+ *                  sequences [cu[n], cu[n+1]) of the T axis are independent,
+ *                  each with its own state; offsets must be non-decreasing,
+ *                  start at 0 and end at T (not checked on the host).
+ *                  When NULL, N = B and every batch row is one sequence.
+ *   num_seqs       N when cu_seqlens is given (>= 1); ignored otherwise
+ *   o              bf16 [B, T, HV, V]  output
+ *   final_state    fp32 [N, HV, K, V]  output, always written
+ * Sizes: B, T, H, HV >= 1 (T == 0 is accepted and only writes final_state),
+ * HV % H == 0, K == V == 128.  q, k, v, g, beta, o must not alias.
+ */
+int kda_chunk_prefill(const void* q, const void* k, const void* v,
+                      const float* g, const void* beta,
+                      const float* initial_state,
+                      const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t B, int32_t T, int32_t H, int32_t HV,
+                      int32_t K, int32_t V,
+                      void* o, float* final_state, void* stream);
+
+/*
+ * kda_decode -- one recurrent KDA step per batch row against a bf16 state
+ * pool, updated in place.
+ *
+ * Defined on "flashinfer.kda_decode.packed_kda_decode", section
+ * "Parameters" (caller-owned bf16 pool [N, HV, K, V] with compact inner
+ * dimensions and a free outer slot stride; int32 slot index per row; -1
+ * marks an inactive row that produces zero output and neither reads nor
+ * writes the pool; scale 1/sqrt(128) and L2 epsilon 1e-6), and on "KDA
+ * Chunk Prefill on Ascend A3", section "Mathematical definition" (the
+ * recurrent step and the Q/K normalisation, as kda_qk_l2norm):
+ *     S  = exp(g)[:,None] * pool[idx, hv]        (bf16 widened to fp32)
+ *     r  = v - k^T S
+ *     S' = S + beta k r^T
+ *     o  = K**-0.5 q^T S'                        (from the unrounded S')
+ *     pool[idx, hv] = bf16(S')                   (nearest-even)
+ *
+ *   q, k           bf16 [B, H, K]     (one token per row)
+ *   v              bf16 [B, HV, V]
+ *   g              fp32 [B, HV, K]
+ *   beta           bf16 [B, HV]
+ *   state_pool     bf16, slot s at state_pool + s * slot_stride elements,
+ *                  each slot [HV, K, V] compact; slot_stride >= HV*K*V and a
+ *                  multiple of 8 elements
+ *   num_slots      number of slots in the pool
+ *   state_indices  int32 [B] device array; active indices must be unique.
+ *                  Any index outside [0, num_slots) -- including -1 -- is an
+ *                  inactive row: zero output, no pool access.
+ *   o              bf16 [B, HV, V]  (the [B, 1, HV, V] output)
+ * Sizes: B >= 0 (0 enqueues nothing), H, HV >= 1, HV % H == 0,
+ * K == V == 128.  Rows with the same active index race (undefined result).
+ */
+int kda_decode(const void* q, const void* k, const void* v,
+               const float* g, const void* beta,
+               void* state_pool, int64_t slot_stride, int64_t num_slots,
+               const int32_t* state_indices,
+               int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+               void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,175 @@
+"""MI355X-native Kimi Delta Attention (KDA) forward path -- Python binding.
+
+Thin ctypes binding over ``libkda.so`` (HIP, gfx950), whose C ABI is
+declared in ``include/kda.h``.  The functions here only marshal arguments:
+they check dtypes, shapes, devices and contiguity of torch tensors, allocate
+outputs with torch when the caller does not pass them, and call the library
+on the current torch stream.  Every arithmetic step runs in the library's
+kernels; there is no fallback path -- a missing or unloadable library raises.
+
+Entry points (same names as the C ABI, without the ``kda_`` prefix):
+  qk_l2norm(x)                                    -> y
+  chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
+                                                  -> (o, final_state)
+  decode(q, k, v, g, beta, state_pool, state_indices)   -> o
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill", "kda_decode")
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def load():
+    """Load libkda.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KDAError(f"{LIB_PATH} not found; build it with `python -m kda_gated_delta_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_qk_l2norm.restype = ctypes.c_int
+    lib.kda_qk_l2norm.argtypes = [_vp, _vp, _i64, _i32, _vp]
+    lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                               _i32, _i32, _i32, _i32, _i32, _vp, _vp]
+    _lib = lib
+    return lib
+
+
+def status_string(code):
+    return load().kda_status_string(int(code)).decode()
+
+
+def _check(code, what):
+    if code != 0:
+        raise KDAError(f"{what}: {status_string(code)} (status {code})")
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def qk_l2norm(x, out=None):
+    """Bit-exact row normalisation of a bf16 tensor whose last dim is 128."""
+    lib = load()
+    _need(x, "x", torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, device=x.device)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    K = x.shape[-1]
+    rows = x.numel() // K if K else 0
+    _check(lib.kda_qk_l2norm(_ptr(x), _ptr(out), rows, K, _stream()), "kda_qk_l2norm")
+    return out
+
+
+def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                  out=None, final_state=None):
+    """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
+    fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
+    cu_seqlens int32 [N+1] (with B == 1) or None.  Returns (o, final_state)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    B, T, H, K = q.shape
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    HV, V = v.shape[2], v.shape[3]
+    _need(g, "g", torch.float32, 4, dev)
+    _need(beta, "beta", torch.bfloat16, 3, dev)
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, HV, K) \
+            or beta.shape != (B, T, HV):
+        raise ValueError("inconsistent shapes")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4, dev)
+        if initial_state.shape != (N, HV, K, V):
+            raise ValueError(f"initial_state must be {(N, HV, K, V)}")
+    if out is None:
+        out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+    if final_state is None:
+        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    _need(final_state, "final_state", torch.float32, 4, dev)
+    code = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
+                                 B, T, H, HV, K, V, _ptr(out), _ptr(final_state), _stream())
+    _check(code, "kda_chunk_prefill")
+    return out, final_state
+
+
+def decode(q, k, v, g, beta, state_pool, state_indices, out=None):
+    """One decode step.  q, k [B,H,K] (or [B,1,H,K]) bf16; v [B,HV,V] bf16;
+    g [B,HV,K] fp32; beta [B,HV] bf16; state_pool bf16 [N,HV,K,V] (outer
+    stride may be padded, inner dims compact), updated in place;
+    state_indices int32 [B].  Returns o [B,1,HV,V] bf16."""
+    lib = load()
+    if q.dim() == 4:
+        q, k, v, g, beta = q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    B, H, K = q.shape
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    HV, V = v.shape[1], v.shape[2]
+    _need(g, "g", torch.float32, 3, dev)
+    _need(beta, "beta", torch.bfloat16, 2, dev)
+    _need(state_indices, "state_indices", torch.int32, 1, dev)
+    if state_pool.dtype != torch.bfloat16 or not state_pool.is_cuda or state_pool.device != dev:
+        raise TypeError("state_pool must be a bf16 GPU tensor on q's device")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (HV, K, V):
+        raise ValueError(f"state_pool must be [N,{HV},{K},{V}]")
+    if state_pool.stride()[1:] != (K * V, V, 1):
+        raise ValueError("state_pool inner dims must be compact")
+    if out is None:
+        out = torch.empty((B, 1, HV, V), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    code = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                          _ptr(state_pool), state_pool.stride(0), state_pool.shape[0],
+                          _ptr(state_indices), B, H, HV, K, V, _ptr(out), _stream())
+    _check(code, "kda_decode")
+    return out

@@ -1,0 +1,94 @@
+"""The C-ABI library loads on the host and exports every entry point that
+include/kda.h declares; metadata errors are reported without touching a GPU
+(each failing call returns before any HIP runtime call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kda_gated_delta_amd as kda
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_chunk_prefill", "kda_decode", "kda_qk_l2norm", "kda_status_string"):
+        assert n in names
+    assert set(names) == set(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = kda.load()
+    for code in range(6):
+        assert lib.kda_status_string(code).startswith(b"KDA_")
+    assert b"unknown" in lib.kda_status_string(99)
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every call below fails its checks first
+MISALIGNED = ctypes.c_void_p(0x1008)
+
+
+def test_l2norm_metadata_errors():
+    lib = kda.load()
+    assert lib.kda_qk_l2norm(FAKE, FAKE, 0, 128, NULL) == 0          # nothing to do
+    assert lib.kda_qk_l2norm(FAKE, FAKE, -1, 128, NULL) == 2
+    assert lib.kda_qk_l2norm(FAKE, FAKE, 4, 64, NULL) == 3
+    assert lib.kda_qk_l2norm(NULL, FAKE, 4, 128, NULL) == 1
+    assert lib.kda_qk_l2norm(MISALIGNED, FAKE, 4, 128, NULL) == 4
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
+             B=1, T=64, H=1, HV=1, K=128, V=128, o=FAKE, fs=FAKE)
+    a.update(kw)
+    return lib.kda_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
+                                 a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"], NULL)
+
+
+def test_prefill_metadata_errors():
+    lib = kda.load()
+    assert _prefill(lib, q=NULL) == 1
+    assert _prefill(lib, fs=NULL) == 1
+    assert _prefill(lib, H=3, HV=4) == 2
+    assert _prefill(lib, B=0) == 2
+    assert _prefill(lib, T=-1) == 2
+    assert _prefill(lib, K=64) == 3
+    assert _prefill(lib, V=256) == 3
+    assert _prefill(lib, cu=FAKE, n=2, B=2) == 2          # packed sequences need B == 1
+    assert _prefill(lib, cu=FAKE, n=0) == 2
+    assert _prefill(lib, v=MISALIGNED) == 4
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, stride=12 * 128 * 128, n=8,
+             idx=FAKE, B=4, H=12, HV=12, K=128, V=128, o=FAKE)
+    a.update(kw)
+    return lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["stride"], a["n"],
+                          a["idx"], a["B"], a["H"], a["HV"], a["K"], a["V"], a["o"], NULL)
+
+
+def test_decode_metadata_errors():
+    lib = kda.load()
+    assert _decode(lib, B=0) == 0
+    assert _decode(lib, idx=NULL) == 1
+    assert _decode(lib, H=5) == 2
+    assert _decode(lib, stride=100) == 2
+    assert _decode(lib, stride=12 * 128 * 128 + 4) == 4
+    assert _decode(lib, K=64) == 3
+    assert _decode(lib, o=MISALIGNED) == 4
