@@ -93,7 +93,8 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *   num_seqs       N when cu_seqlens is given (>= 1); ignored otherwise
  *   o              bf16 [B, T, HV, V]  output
  *   final_state    fp32 [N, HV, K, V]  output, always written
- * Sizes: B, T, H, HV >= 1 (T == 0 is accepted and only writes final_state),
+ * Sizes: B, T, H, HV >= 1 (T == 0 is accepted, may pass NULL token tensors,
+ * and only writes final_state),
  * HV % H == 0, K == V == 128.  q, k, v, g, beta, o must not alias.
  */
 int kda_chunk_prefill(const void* q, const void* k, const void* v,
