@@ -67,19 +67,64 @@ __device__ __forceinline__ float dd_to_f32(double hi, double lo) {
   return r;
 }
 
+// ---------------------------------------------------------------- row reductions
+
+// All-reduce across the 16 lanes of a DPP row (lanes sharing lane/16), with
+// register-only DPP moves: swap neighbours, swap pairs, then rotate the row
+// by 4 and by 8.  Every lane ends with the reduction of its row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = dpp32<CTRL>(uint32_t(u));
+  const uint32_t hi = dpp32<CTRL>(uint32_t(u >> 32));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;   // row_ror:4
+constexpr int kDppRor8 = 0x128;   // row_ror:8
+
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp64<kDppXor1>(x);
+  x += dpp64<kDppXor2>(x);
+  x += dpp64<kDppRor4>(x);
+  x += dpp64<kDppRor8>(x);
+  return x;
+}
+__device__ __forceinline__ int row16_max(int x) {
+  x = max(x, int(dpp32<kDppXor1>(uint32_t(x))));
+  x = max(x, int(dpp32<kDppXor2>(uint32_t(x))));
+  x = max(x, int(dpp32<kDppRor4>(uint32_t(x))));
+  x = max(x, int(dpp32<kDppRor8>(uint32_t(x))));
+  return x;
+}
+__device__ __forceinline__ int row16_min(int x) {
+  x = min(x, int(dpp32<kDppXor1>(uint32_t(x))));
+  x = min(x, int(dpp32<kDppXor2>(uint32_t(x))));
+  x = min(x, int(dpp32<kDppRor4>(uint32_t(x))));
+  x = min(x, int(dpp32<kDppRor8>(uint32_t(x))));
+  return x;
+}
+
 // ---------------------------------------------------------------- row norm
 
 // Normalise one row of 128 bf16 held by a 16-lane group (lanes sharing
 // lane/16): each lane holds 8 consecutive elements packed in `x`.  Every
-// lane of the wave must call this (cross-lane shuffles).  Returns the 8
+// lane of the wave must call this (cross-lane operations).  Returns the 8
 // normalised bf16 values, packed the same way.
 //
 // Sum of squares: each square of a bf16 value is exact in float32.  When the
 // row's nonzero magnitudes span at most 2^15 (biased exponents differ by
 // <= 15), every partial sum of the squares is exact in float64, so the
-// float64 tree sum is exact in any order and one conversion rounds it
-// correctly.  Otherwise (rare) the whole wave takes an error-free
-// double-double path, exact while the span is at most 2^38.
+// float64 sum is exact in any order (each lane of the row may add in its own
+// order and all get the same value) and one conversion rounds it correctly.
+// Otherwise (rare) the whole wave takes an error-free double-double path,
+// exact while the span is at most 2^38; its result is taken from the row's
+// first lane so that every lane of the row divides by the same value.
 //
 // Division: with d the correctly rounded float32 square root, the float64
 // product x * RN64(1/d) lies within 2^-51.9 relative of x/d, while x/d (x
@@ -89,67 +134,65 @@ __device__ __forceinline__ float dd_to_f32(double hi, double lo) {
 // in float64 and rounded to float32, which is correctly rounded because
 // 53 >= 2*24 + 2.
 __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  float xf[8];
+  double xd[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    xf[2 * i] = bf16lo(w[i]);
-    xf[2 * i + 1] = bf16hi(w[i]);
+    xd[2 * i] = (double)bf16lo(w[i]);
+    xd[2 * i + 1] = (double)bf16hi(w[i]);
   }
+  // Largest magnitude and smallest nonzero magnitude (bf16 bit patterns
+  // order like their values), two elements per packed 16-bit operation.
+  u16x2 mx = {0, 0};
+  u16x2 mn = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
+    mx = __builtin_elementwise_max(mx, m);
+    mn = __builtin_elementwise_min(mn, m - (u16x2){1, 1});   // zero wraps to 0xffff
+  }
+  int emax = int(mx[0] > mx[1] ? mx[0] : mx[1]);           // magnitude bits
+  int emin = int(mn[0] < mn[1] ? mn[0] : mn[1]) + 1;       // 0x10000 if all zero
   double s = 0.0;
-  int emax = 0, emin = 255;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float sq = xf[i] * xf[i];
-    s += (double)sq;
-    uint32_t mag = (__float_as_uint(xf[i]) >> 16) & 0x7fffu;
-    int e = int(mag >> 7);
-    e = e < 1 ? 1 : e;
-    if (mag != 0u) {
-      emax = emax > e ? emax : e;
-      emin = emin < e ? emin : e;
-    }
-  }
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    s += __shfl_xor(s, off, 64);
-    int a = __shfl_xor(emax, off, 64);
-    int b = __shfl_xor(emin, off, 64);
-    emax = emax > a ? emax : a;
-    emin = emin < b ? emin : b;
-  }
-  const bool exact = (emax == 0) || (emax - emin <= 15);
+  for (int i = 0; i < 8; ++i) s = fma(xd[i], xd[i], s);    // x*x is exact in float32 and float64
+  s = row16_sum(s);
+  emax = row16_max(emax) >> 7;                              // biased exponents
+  emin = row16_min(emin) >> 7;
+  const bool exact = (emax == 0 && emin == 512) || (max(emax, 1) - max(emin, 1) <= 15);
   float s32 = (float)s;
   if (!__all(exact)) {
     double hi = 0.0, lo = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       double t, e;
-      two_sum(hi, (double)(xf[i] * xf[i]), t, e);
+      two_sum(hi, xd[i] * xd[i], t, e);
       hi = t;
       lo += e;
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
-      double oh = __shfl_xor(hi, off, 64);
-      double ol = __shfl_xor(lo, off, 64);
+      const double oh = __shfl_xor(hi, off, 64);
+      const double ol = __shfl_xor(lo, off, 64);
       double t, e;
       two_sum(hi, oh, t, e);
-      double l = lo + ol + e;
+      const double l = lo + ol + e;
       hi = t + l;
       lo = l - (hi - t);
     }
-    if (!exact) s32 = dd_to_f32(hi, lo);
+    const float r = __shfl(dd_to_f32(hi, lo), (threadIdx.x & 63) & ~15, 64);
+    if (!exact) s32 = r;
   }
   const float t = s32 + 1e-6f;
   const float d = (float)__builtin_sqrt((double)t);
   const double r = 1.0 / (double)d;
-  uint4 y;
-  y.x = pack_bf16((float)((double)xf[0] * r), (float)((double)xf[1] * r));
-  y.y = pack_bf16((float)((double)xf[2] * r), (float)((double)xf[3] * r));
-  y.z = pack_bf16((float)((double)xf[4] * r), (float)((double)xf[5] * r));
-  y.w = pack_bf16((float)((double)xf[6] * r), (float)((double)xf[7] * r));
-  return y;
+  // Integer round-to-nearest-even: the hardware float32 -> bf16 conversion
+  // does not break ties to even.
+  uint32_t y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = pack_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
+  return make_uint4(y[0], y[1], y[2], y[3]);
 }
 
 }  // namespace kda

@@ -7,20 +7,24 @@
 // Vnew, S = exp(G_last) S + Kg^T Vnew; chunk size 64 with a zero-padded last
 // chunk).
 //
-// Design (one fused kernel, no workspace):
-//   * one workgroup per (sequence, value head, V-tile); the V-tile is 64 or
-//     128 columns of the 128-column state, because the state's columns
-//     evolve independently (each column of S only ever meets the same column
-//     of v).  Each wave owns 16 columns of the tile and keeps that 128x16
-//     slice of S in registers as float32 for the whole sequence.
-//   * per 64-token chunk, all waves build the chunk-local quantities in LDS:
-//     normalised q and k (bit-exact routine shared with kda_qk_l2norm), the
-//     gate prefix G (kept in log2 units), the gated L and Aqk on MFMA, the
-//     unit-lower-triangular inverse by blocked forward substitution in
-//     float32, A, W = A (exp(G) k), Qg, Kg and exp(G_last).
-//   * then each wave runs the carry for its columns on MFMA: U = A v and
-//     Vnew = U - W S accumulate in float32 (U is never rounded), O = Qg S +
-//     Aqk Vnew, S = exp(G_last) S + Kg^T Vnew.
+// Design: one fused kernel, no workspace, one 512-thread workgroup (8 waves)
+// per (sequence, value head).  Wave w owns state columns 16w..16w+15 and
+// keeps that 128x16 slice of S in registers as float32 for the whole
+// sequence (the state's columns evolve independently: column v of S only
+// ever meets column v of the values).  For each 64-token chunk:
+//   1. the raw q, k, g, beta and v of the chunk, prefetched into registers
+//      while the previous chunk was computed, are normalised (bit-exact
+//      routine shared with kda_qk_l2norm), scanned (G, kept in log2 units)
+//      and staged in LDS; the loads for the next chunk are issued;
+//   2. the gated L and Aqk, 16x16 blocks on MFMA;
+//   3. T = (I+L)^-1 by blocked forward substitution in float32 (diagonal
+//      blocks by substitution, off-diagonal blocks on fp32 MFMA), then
+//      A = T diag(beta);
+//   4. W = A (exp(G) k), Qg, Kg, exp(G_last);
+//   5. each wave runs the carry for its columns on MFMA: U = A v and Vnew =
+//      U - W S accumulate in float32 (U is never rounded), O = Qg S + Aqk
+//      Vnew (staged in LDS, written with 16-byte stores), S = exp(G_last) S +
+//      Kg^T Vnew.
 //
 // Precision: every MFMA operand is fp16 with float32 accumulation, and the
 // state is carried in float32.  fp16's 11-bit significand keeps the final
@@ -57,41 +61,45 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;            // chunk length
 constexpr int KD = 128;          // key width == value width
+constexpr int NW = 8;            // waves per workgroup
+constexpr int NT = NW * 64;      // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SCALE = 0.08838834764831845f;   // 128^-1/2
 constexpr float SAFE_EXP2 = 120.0f;             // largest split-factor exponent (base 2)
 constexpr float F16_EXP2 = 14.0f;               // largest split-factor exponent for fp16 operands
 
-// LDS row strides (elements); the padding breaks power-of-two bank strides.
-constexpr int QS = 136;          // bf16 [64][128] arrays
-constexpr int GS = 132;          // fp32 G [64][128]
+// LDS row strides (elements).  Row strides of 68 or 36 words put eight
+// consecutive rows' 16-byte accesses in distinct bank groups.
+constexpr int QS = 136;          // 16-bit [64][128] arrays
+constexpr int GS = 132;          // fp32 [64][128] (G)
+constexpr int OS = 136;          // bf16 [64][128] (o staging, in the G region)
 constexpr int LS = 68;           // fp32 [64][64] arrays
 constexpr int AS = 72;           // 16-bit [*][64] arrays
 
-// LDS map (bytes).  U1 holds L and T during the solve and W and E^T after.
-constexpr int OFF_Q = 0;                                  // bf16 q^ -> Qg   [64][QS]
-constexpr int OFF_K = OFF_Q + C * QS * 2;                 // bf16 k^         [64][QS]
-constexpr int OFF_G = OFF_K + C * QS * 2;                 // fp32 G (log2)   [64][GS]
+// LDS map (bytes).  Regions are reused across phases:
+//   G    : fp32 G (phases 1-4), then bf16 o staging (phase 5)
+//   U1   : fp32 L and T (phases 2-3), then fp16 -W and E^T (phases 4-5)
+//   AREG : fp32 scan totals (phase 1), fp16 A (phases 3-5)
+constexpr int OFF_Q = 0;                                  // bf16 q^, then fp16 Qg  [64][QS]
+constexpr int OFF_K = OFF_Q + C * QS * 2;                 // bf16 k^                [64][QS]
+constexpr int OFF_G = OFF_K + C * QS * 2;                 // fp32 G (log2 units)    [64][GS]
 constexpr int OFF_U1 = OFF_G + C * GS * 4;
-constexpr int OFF_L = OFF_U1;                             // fp32 L          [64][LS]
-constexpr int OFF_T = OFF_U1 + C * LS * 4;                // fp32 (I+L)^-1   [64][LS]
-constexpr int OFF_W = OFF_U1;                             // bf16 -W         [64][QS]
-constexpr int OFF_ET = OFF_U1 + C * QS * 2;               // bf16 (e^G k)^T  [128][AS]
+constexpr int OFF_L = OFF_U1;                             // fp32 L                 [64][LS]
+constexpr int OFF_T = OFF_U1 + C * LS * 4;                // fp32 (I+L)^-1          [64][LS]
+constexpr int OFF_W = OFF_U1;                             // fp16 -W                [64][QS]
+constexpr int OFF_ET = OFF_U1 + C * QS * 2;               // fp16 (e^G k)^T         [128][AS]
 constexpr int U1_BYTES = (2 * C * LS * 4 > C * QS * 2 + KD * AS * 2) ? 2 * C * LS * 4
                                                                      : C * QS * 2 + KD * AS * 2;
-constexpr int OFF_AQK = OFF_U1 + U1_BYTES;                // bf16 Aqk        [64][AS]
-constexpr int OFF_A = OFF_AQK + C * AS * 2;               // bf16 A [64][AS]; fp32 solve scratch
-constexpr int OFF_KGT = OFF_A + C * AS * 2;               // fp16 Kg^T       [128][AS]
-constexpr int OFF_VT = OFF_KGT + KD * AS * 2;             // bf16 v^T        [VT][AS]
-
-template <int VT>
-struct Lds {
-  static constexpr int OFF_BETA = OFF_VT + VT * AS * 2;   // fp32 [64]
-  static constexpr int OFF_GAM = OFF_BETA + C * 4;        // fp32 [128]
-  static constexpr int BYTES = OFF_GAM + KD * 4;
-};
-static_assert(Lds<128>::BYTES <= 160 * 1024, "LDS budget");
-static_assert(C * AS * 2 >= 3 * 256 * 4, "solve scratch fits in the A region");
+constexpr int OFF_AQK = OFF_U1 + U1_BYTES;                // fp16 Aqk               [64][AS]
+constexpr int OFF_A = OFF_AQK + C * AS * 2;               // fp16 A [64][AS] / scan totals
+constexpr int OFF_KGT = OFF_A + C * AS * 2;               // fp16 Kg^T              [128][AS]
+constexpr int OFF_V = OFF_KGT + KD * AS * 2;              // fp16 v                 [64][QS]
+constexpr int OFF_BETA = OFF_V + C * QS * 2;              // fp32 [64]
+constexpr int OFF_GAM = OFF_BETA + C * 4;                 // fp32 [128]
+constexpr int LDS_BYTES = OFF_GAM + KD * 4;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
+static_assert(C * GS * 4 >= C * OS * 2, "o staging fits in the G region");
 
 struct Params {
   const uint16_t* q;
@@ -103,7 +111,7 @@ struct Params {
   const int32_t* cu;
   uint16_t* o;
   float* sfin;
-  int B, T, H, HV, N;
+  int T, H, HV, N;
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -111,36 +119,97 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ f16x8 lds_f16x8(const uint16_t* p) {
   return *reinterpret_cast<const f16x8*>(p);
 }
-__device__ __forceinline__ f16x8 lds_f16_2x4(const uint16_t* p0, const uint16_t* p1) {
-  uint2 a = *reinterpret_cast<const uint2*>(p0);
-  uint2 b = *reinterpret_cast<const uint2*>(p1);
-  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-  return __builtin_bit_cast(f16x8, u);
+// Storage position of contraction index c in the "permuted" LDS layout used
+// for MFMA A operands whose B operand comes straight from a float32
+// accumulator: within each group of 32, index 4g + e (e < 4) goes to 8g + e
+// and index 16 + 4g + e goes to 8g + 4 + e, so the 8 values lane group g
+// needs for one k-step are one contiguous 16-byte read.
+__device__ __forceinline__ int perm32(int c) {
+  const int cp = c & 31;
+  return (c & ~31) + 8 * ((cp & 15) >> 2) + 4 * (cp >> 4) + (cp & 3);
+}
+
+// Value of `v` in lane `src` (0..3) of each lane's quad.
+__device__ __forceinline__ float quad_bcast(float v, int src) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  switch (src) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x00, 0xf, 0xf, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x55, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0xAA, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0xFF, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
 }
 __device__ __forceinline__ uint16_t f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return uint32_t(f16_bits(lo)) | (uint32_t(f16_bits(hi)) << 16);
+}
+__device__ __forceinline__ void unpack_bf16x8(const uint4& x, float* f) {
+  f[0] = bf16lo(x.x); f[1] = bf16hi(x.x);
+  f[2] = bf16lo(x.y); f[3] = bf16hi(x.y);
+  f[4] = bf16lo(x.z); f[5] = bf16hi(x.z);
+  f[6] = bf16lo(x.w); f[7] = bf16hi(x.w);
+}
 
-template <int VT>
-__global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
-  constexpr int NW = VT / 16;          // waves; wave w owns tile columns 16w..16w+15
-  constexpr int NT = NW * 64;
-  constexpr int NV = KD / VT;          // V-tiles per head
+// Raw inputs of one chunk held in registers (prefetch buffer).
+//   qk[m]: row rg + 32m of the 128 stacked rows (q rows 0..63, k rows 64..127),
+//          8 bf16 at column 8*l16, with rg = tid/16, l16 = tid%16
+//   gv[r]: g of token 4*seg + r, channels 4*c4..4*c4+3 (seg = tid/32, c4 = tid%32)
+//   vv[m]: v of token tid/16 + 32m, columns 8*(tid%16)..+7
+struct Raw {
+  uint4 qk[4];
+  float4 gv[4];
+  uint4 vv[2];
+  float beta;
+};
+
+__device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
+                                         int hv, int tid) {
+  const int rg = tid >> 4, l16 = tid & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = (rg + 32 * m) & (C - 1);
+    const uint16_t* base = (m < 2) ? p.q : p.k;
+    R.qk[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < nvalid) R.qk[m] = *reinterpret_cast<const uint4*>(base + ((trow + i) * p.H + hq) * KD + 8 * l16);
+  }
+  const int seg = tid >> 5, c4 = tid & 31;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * seg + r;
+    R.gv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < nvalid) R.gv[r] = *reinterpret_cast<const float4*>(p.g + ((trow + i) * p.HV + hv) * KD + 4 * c4);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int i = rg + 32 * m;
+    R.vv[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < nvalid) R.vv[m] = *reinterpret_cast<const uint4*>(p.v + ((trow + i) * p.HV + hv) * KD + 8 * l16);
+  }
+  R.beta = 0.f;
+  if (tid < nvalid) R.beta = bf16f(p.beta[(trow + tid) * p.HV + hv]);
+}
+
+__global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
   float* sG = reinterpret_cast<float*>(smem + OFF_G);
+  uint16_t* sO = reinterpret_cast<uint16_t*>(smem + OFF_G);
   float* sL = reinterpret_cast<float*>(smem + OFF_L);
   float* sT = reinterpret_cast<float*>(smem + OFF_T);
   uint16_t* sW = reinterpret_cast<uint16_t*>(smem + OFF_W);
   uint16_t* sET = reinterpret_cast<uint16_t*>(smem + OFF_ET);
   uint16_t* sAqk = reinterpret_cast<uint16_t*>(smem + OFF_AQK);
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem + OFF_A);
-  float* sP = reinterpret_cast<float*>(smem + OFF_A);      // solve scratch [3][16][16]
+  float* sScr = reinterpret_cast<float*>(smem + OFF_A);
   uint16_t* sKgT = reinterpret_cast<uint16_t*>(smem + OFF_KGT);
-  uint16_t* sVT = reinterpret_cast<uint16_t*>(smem + OFF_VT);
-  float* sBeta = reinterpret_cast<float*>(smem + Lds<VT>::OFF_BETA);
-  float* sGam = reinterpret_cast<float*>(smem + Lds<VT>::OFF_GAM);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + OFF_V);
+  float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
+  float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,19 +217,13 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  // Workgroup -> (unit = sequence*HV + head, V-tile); the NV tiles of a unit
-  // get ids congruent mod 8 so they share an XCD (and its L2).
-  const int id = blockIdx.x;
-  const int grp = id / (8 * NV);
-  const int rem = id % (8 * NV);
-  const int vt = rem / 8;
-  const int unit = grp * 8 + (rem % 8);
+  const int unit = blockIdx.x;
   if (unit >= p.N * p.HV) return;
   const int n = unit / p.HV;
   const int hv = unit % p.HV;
   const int hq = hv / (p.HV / p.H);
 
-  int64_t tok0;   // row index (into the [B*T] token axis) of the sequence's first token
+  int64_t tok0;   // row of the sequence's first token in the [B*T] token axis
   int len;
   if (p.cu) {
     tok0 = p.cu[n];
@@ -170,7 +233,7 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
     len = p.T;
   }
 
-  const int col = vt * VT + wave * 16 + l16;     // this lane's state / output column
+  const int col = wave * 16 + l16;               // this lane's state column
   f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
   {
     const float* s0 = p.s0 ? p.s0 + (int64_t(n) * p.HV + hv) * KD * KD : nullptr;
@@ -180,220 +243,307 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
       for (int r = 0; r < 4; ++r) S[rt][r] = s0 ? s0[(16 * rt + 4 * gq + r) * KD + col] : 0.f;
   }
 
+  Raw R;
+  if (len > 0) load_raw(R, p, tok0, min(C, len), hq, hv, tid);
+
   for (int c0 = 0; c0 < len; c0 += C) {
     const int nvalid = min(C, len - c0);
     const int64_t trow = tok0 + c0;              // token row of chunk position 0
 
-    // ---------------------------------------------------------- phase 1: loads
-    // q^ and k^: 128 rows, one 16-lane group per row, bit-exact normalisation.
-    for (int r = tid >> 4; r < 2 * C; r += NT / 16) {
-      const int i = r & (C - 1);
-      const bool isk = r >= C;
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (i < nvalid) {
-        const uint16_t* src = (isk ? p.k : p.q) + ((trow + i) * p.H + hq) * KD + 8 * l16;
-        x = *reinterpret_cast<const uint4*>(src);
-      }
-      uint4 y = l2norm_row16(x);
-      *reinterpret_cast<uint4*>((isk ? sK : sQ) + i * QS + 8 * l16) = y;
-    }
-    // g (scaled to log2 units), beta, v tile (transposed).
-    for (int e = tid; e < C * (KD / 4); e += NT) {
-      const int i = e / (KD / 4);
-      const int c4 = e % (KD / 4);
-      float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < nvalid) gv = *reinterpret_cast<const float4*>(p.g + ((trow + i) * p.HV + hv) * KD + 4 * c4);
-      float* d = sG + i * GS + 4 * c4;
-      d[0] = gv.x * LOG2E;
-      d[1] = gv.y * LOG2E;
-      d[2] = gv.z * LOG2E;
-      d[3] = gv.w * LOG2E;
-    }
-    if (tid < C) sBeta[tid] = tid < nvalid ? bf16f(p.beta[(trow + tid) * p.HV + hv]) : 0.f;
-    for (int e = tid; e < C * (VT / 8); e += NT) {
-      const int i = e / (VT / 8);
-      const int c8 = e % (VT / 8);
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (i < nvalid)
-        x = *reinterpret_cast<const uint4*>(p.v + ((trow + i) * p.HV + hv) * KD + vt * VT + 8 * c8);
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    // ---------------------------------------------------------- phase 1
+    {
+      const int rg = tid >> 4;
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        sVT[(8 * c8 + 2 * q2) * AS + i] = f16_bits(bf16lo(w[q2]));
-        sVT[(8 * c8 + 2 * q2 + 1) * AS + i] = f16_bits(bf16hi(w[q2]));
+      for (int m = 0; m < 4; ++m) {
+        const uint4 y = l2norm_row16(R.qk[m]);
+        *reinterpret_cast<uint4*>(((m < 2) ? sQ : sK) + ((rg + 32 * m) & (C - 1)) * QS + 8 * l16) = y;
+        __builtin_amdgcn_sched_barrier(0);   // one row at a time keeps register use low
       }
-    }
-    __syncthreads();
-    // G = inclusive prefix over the chunk, per channel (padding has g = 0).
-    if (tid < KD) {
-      float run = 0.f;
-      for (int i = 0; i < C; ++i) {
-        run += sG[i * GS + tid];
-        sG[i * GS + tid] = run;
+      // v (bf16 -> fp16), row-major.
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float f[8];
+        unpack_bf16x8(R.vv[m], f);
+        *reinterpret_cast<uint4*>(sV + (rg + 32 * m) * QS + 8 * l16) =
+            make_uint4(pack_f16(f[0], f[1]), pack_f16(f[2], f[3]), pack_f16(f[4], f[5]), pack_f16(f[6], f[7]));
       }
+      if (tid < C) sBeta[tid] = R.beta;
+      // g in log2 units, inclusive scan over the 4 tokens this thread holds,
+      // then across the 16 four-token segments through LDS.
+      const int seg = tid >> 5, c4 = tid & 31;
+      float4 gs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gs[r].x = R.gv[r].x * LOG2E + (r ? gs[r - 1].x : 0.f);
+        gs[r].y = R.gv[r].y * LOG2E + (r ? gs[r - 1].y : 0.f);
+        gs[r].z = R.gv[r].z * LOG2E + (r ? gs[r - 1].z : 0.f);
+        gs[r].w = R.gv[r].w * LOG2E + (r ? gs[r - 1].w : 0.f);
+      }
+      *reinterpret_cast<float4*>(sScr + seg * KD + 4 * c4) = gs[3];
+      __syncthreads();
+      // The raw registers are consumed: prefetch the next chunk.
+      if (c0 + C < len) load_raw(R, p, trow + C, min(C, len - c0 - C), hq, hv, tid);
+      float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s2 = 0; s2 < seg; ++s2) {
+        const float4 t = *reinterpret_cast<const float4*>(sScr + s2 * KD + 4 * c4);
+        off.x += t.x;
+        off.y += t.y;
+        off.z += t.z;
+        off.w += t.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4*>(sG + (4 * seg + r) * GS + 4 * c4) =
+            make_float4(gs[r].x + off.x, gs[r].y + off.y, gs[r].z + off.z, gs[r].w + off.w);
     }
     __syncthreads();
 
     // ---------------------------------------------------------- phase 2: L, Aqk
-    for (int pb = wave; pb < 16; pb += NW) {
-      const int I = pb >> 2;
-      const int J = pb & 3;
-      if (J > I) {   // strictly upper blocks of Aqk are zero
+    // The 10 blocks on or below the diagonal over 8 waves; waves 2..7 also
+    // zero one strictly-upper block of Aqk each.
+    {
+      if (wave >= 2) {
+        const int ub = wave - 2;
+        const int UI = ub < 3 ? 0 : (ub < 5 ? 1 : 2);
+        const int UJ = ub < 3 ? ub + 1 : (ub < 5 ? ub - 1 : 3);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * gq + r) * AS + 16 * J + l16] = 0;
-        continue;
+        for (int r = 0; r < 4; ++r) sAqk[(16 * UI + 4 * gq + r) * AS + perm32(16 * UJ + l16)] = 0;
       }
-      const int ref = (J < I) ? 16 * I : 16 * I + 8;
-      const int i = 16 * I + l16;     // operand row (A side)
-      const int j = 16 * J + l16;     // operand row (B side)
-      // Largest split-factor exponent this lane will form (<= 0 below the diagonal).
-      float emax = 0.f;
-      if (J == I) {
+      for (int pb = wave; pb < 10; pb += NW) {
+        // blocks ordered (3,0) (3,1) (3,2) (3,3) (2,0) (2,1) (2,2) (1,0) (1,1) (0,0)
+        const int I = pb < 4 ? 3 : (pb < 7 ? 2 : (pb < 9 ? 1 : 0));
+        const int J = pb < 4 ? pb : (pb < 7 ? pb - 4 : (pb < 9 ? pb - 7 : 0));
+        const int ref = (J < I) ? 16 * I : 16 * I + 8;
+        const int i = 16 * I + l16;     // operand row (A side)
+        const int j = 16 * J + l16;     // operand row (B side)
+        // Largest split-factor exponent of this lane's entries (<= 0 below the
+        // diagonal, so only diagonal blocks need the check).
+        float emax = 0.f;
+        if (J == I) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+          for (int s = 0; s < 4; ++s) {
+            const int ch0 = 32 * s + 8 * gq;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int ch = 32 * s + 8 * gq + e;
-            const float gr = sG[ref * GS + ch];
-            emax = fmaxf(emax, fmaxf(sG[i * GS + ch] - gr, gr - sG[j * GS + ch]));
+            for (int h = 0; h < 2; ++h) {
+              const float4 gi = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
+              const float4 gj = *reinterpret_cast<const float4*>(sG + j * GS + ch0 + 4 * h);
+              const float4 gr = *reinterpret_cast<const float4*>(sG + ref * GS + ch0 + 4 * h);
+              emax = fmaxf(emax, fmaxf(fmaxf(gi.x - gr.x, gi.y - gr.y), fmaxf(gi.z - gr.z, gi.w - gr.w)));
+              emax = fmaxf(emax, fmaxf(fmaxf(gr.x - gj.x, gr.y - gj.y), fmaxf(gr.z - gj.z, gr.w - gj.w)));
+            }
           }
-      }
-      f32x4 accL = {0.f, 0.f, 0.f, 0.f};
-      f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
-      if (!__any(emax > F16_EXP2)) {
+        }
+        f32x4 accL = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
+        const bool wide = __any(emax > F16_EXP2);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int ch0 = 32 * s + 8 * gq;
-          f16x8 kr, qr, kc;
+          float ki[8], qi[8], kj[8];
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + i * QS + ch0), ki);
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + i * QS + ch0), qi);
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + j * QS + ch0), kj);
+          float kr[8], qr[8], kc[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int ch = ch0 + e;
-            const float gr = sG[ref * GS + ch];
-            const float fr = ex2(sG[i * GS + ch] - gr);
-            const float fc = ex2(gr - sG[j * GS + ch]);
-            kr[e] = (_Float16)(bf16f(sK[i * QS + ch]) * fr);
-            qr[e] = (_Float16)(bf16f(sQ[i * QS + ch]) * fr);
-            kc[e] = (_Float16)(bf16f(sK[j * QS + ch]) * fc);
+          for (int h = 0; h < 2; ++h) {
+            const float4 gi4 = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
+            const float4 gj4 = *reinterpret_cast<const float4*>(sG + j * GS + ch0 + 4 * h);
+            const float4 gr4 = *reinterpret_cast<const float4*>(sG + ref * GS + ch0 + 4 * h);
+            const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+            const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+            const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float fr = ex2(gi[e] - gr[e]);
+              const float fc = ex2(gr[e] - gj[e]);
+              kr[4 * h + e] = ki[4 * h + e] * fr;
+              qr[4 * h + e] = qi[4 * h + e] * fr;
+              kc[4 * h + e] = kj[4 * h + e] * fc;
+            }
           }
-          accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr, kc, accL, 0, 0, 0);
-          accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(qr, kc, accQ, 0, 0, 0);
-        }
-      } else {
-        // Steep decay inside a diagonal block: bf16 operands keep the range.
+          if (!wide) {
+            f16x8 a, b, c;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int ch0 = 32 * s + 8 * gq;
-          bf16x8 kr, qr, kc;
+            for (int e = 0; e < 8; ++e) {
+              a[e] = (_Float16)kr[e];
+              b[e] = (_Float16)qr[e];
+              c[e] = (_Float16)kc[e];
+            }
+            accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, c, accL, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, c, accQ, 0, 0, 0);
+          } else {
+            // Steep decay inside a diagonal block: bf16 operands keep the range.
+            bf16x8 a, b, c;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int ch = ch0 + e;
-            const float gr = sG[ref * GS + ch];
-            const float fr = ex2(sG[i * GS + ch] - gr);
-            const float fc = ex2(gr - sG[j * GS + ch]);
-            kr[e] = (__bf16)(bf16f(sK[i * QS + ch]) * fr);
-            qr[e] = (__bf16)(bf16f(sQ[i * QS + ch]) * fr);
-            kc[e] = (__bf16)(bf16f(sK[j * QS + ch]) * fc);
+            for (int e = 0; e < 8; ++e) {
+              a[e] = (__bf16)kr[e];
+              b[e] = (__bf16)qr[e];
+              c[e] = (__bf16)kc[e];
+            }
+            accL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c, accL, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, c, accQ, 0, 0, 0);
           }
-          accL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, kc, accL, 0, 0, 0);
-          accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr, kc, accQ, 0, 0, 0);
         }
-      }
-      const int jc = 16 * J + l16;    // result column
-      if (__any(emax > SAFE_EXP2)) {
-        // Extreme decay inside a diagonal block: evaluate each pair directly.
+        const int jc = 16 * J + l16;    // result column
+        if (__any(emax > SAFE_EXP2)) {
+          // Extreme decay inside a diagonal block: evaluate each pair directly.
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ir = 16 * I + 4 * gq + r;
+            float aL = 0.f, aQ = 0.f;
+            if (jc <= ir) {
+              for (int ch = 0; ch < KD; ++ch) {
+                const float f = ex2(sG[ir * GS + ch] - sG[jc * GS + ch]);
+                const float kjf = bf16f(sK[jc * QS + ch]) * f;
+                aL = fmaf(bf16f(sK[ir * QS + ch]), kjf, aL);
+                aQ = fmaf(bf16f(sQ[ir * QS + ch]), kjf, aQ);
+              }
+            }
+            accL[r] = aL;
+            accQ[r] = aQ;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ir = 16 * I + 4 * gq + r;
-          float aL = 0.f, aQ = 0.f;
-          if (jc <= ir) {
-            for (int ch = 0; ch < KD; ++ch) {
-              const float f = ex2(sG[ir * GS + ch] - sG[jc * GS + ch]);
-              const float kj = bf16f(sK[jc * QS + ch]) * f;
-              aL = fmaf(bf16f(sK[ir * QS + ch]), kj, aL);
-              aQ = fmaf(bf16f(sQ[ir * QS + ch]), kj, aQ);
-            }
-          }
-          accL[r] = aL;
-          accQ[r] = aQ;
+          sL[ir * LS + jc] = (jc < ir) ? sBeta[ir] * accL[r] : 0.f;
+          sAqk[ir * AS + perm32(jc)] = f16_bits((jc <= ir) ? SCALE * accQ[r] : 0.f);
         }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ir = 16 * I + 4 * gq + r;
-        sL[ir * LS + jc] = (jc < ir) ? sBeta[ir] * accL[r] : 0.f;
-        const float aq = (jc <= ir) ? SCALE * accQ[r] : 0.f;
-        sAqk[ir * AS + jc] = f16_bits(aq);
       }
     }
     __syncthreads();
 
     // ---------------------------------------------------------- phase 3: solve
-    // T = (I + L)^-1, unit lower triangular.  Diagonal 16x16 blocks by forward
-    // substitution, one lane per (block, column).
-    if (wave == 0) {
-      const int blk = lane >> 4;
-      const int cc = lane & 15;
-      float x[16];
+    // T = (I + L)^-1, unit lower triangular.
+    // Diagonal 16x16 blocks: wave b < 4 inverts block b.  Lane 4*cc + h holds
+    // rows 4h..4h+3 of column cc and the matching rows of L in registers;
+    // column-oriented forward substitution broadcasts x[m] within the quad.
+    if (wave < 4) {
+      const int blk = wave;
+      const int cc = lane >> 2;
+      const int h = lane & 3;
+      float Lr[4][16];
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        float s = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 4 * h + r;
 #pragma unroll
-        for (int m = 0; m < ii; ++m) s = fmaf(sL[(16 * blk + ii) * LS + 16 * blk + m], x[m], s);
-        x[ii] = (ii == cc) ? 1.f : (ii > cc ? -s : 0.f);
+        for (int m4 = 0; m4 < 4; ++m4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(sL + (16 * blk + ii) * LS + 16 * blk + 4 * m4);
+          Lr[r][4 * m4 + 0] = (4 * m4 + 0 < ii) ? l4.x : 0.f;
+          Lr[r][4 * m4 + 1] = (4 * m4 + 1 < ii) ? l4.y : 0.f;
+          Lr[r][4 * m4 + 2] = (4 * m4 + 2 < ii) ? l4.z : 0.f;
+          Lr[r][4 * m4 + 3] = (4 * m4 + 3 < ii) ? l4.w : 0.f;
+        }
+      }
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = (4 * h + r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < 15; ++m) {
+        // x[m] lives in quad lane m/4, register m%4; broadcast it to the quad.
+        const float xm = quad_bcast(x[m & 3], m >> 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = fmaf(-Lr[r][m], xm, x[r]);
       }
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) sT[(16 * blk + ii) * LS + 16 * blk + cc] = x[ii];
+      for (int r = 0; r < 4; ++r) sT[(16 * blk + 4 * h + r) * LS + 16 * blk + cc] = x[r];
     }
     __syncthreads();
-    // Off-diagonal blocks, one block row at a time:
-    //   T_IJ = -T_II * sum_{M=J}^{I-1} L_IM T_MJ.
+    // Off-diagonal blocks, one block row at a time, on fp32 MFMA (16x16x4):
+    //   P_IJ = sum_{M=J}^{I-1} L_IM T_MJ,   T_IJ = -T_II P_IJ.
+    // For the second product the contraction index of k-step s in lane group
+    // gq is 4gq + s, which is where P's accumulator already holds it.
     for (int I = 1; I < 4; ++I) {
-      for (int e = tid; e < I * 256; e += NT) {
-        const int J = e >> 8;
-        const int ii = (e >> 4) & 15;
-        const int jj = e & 15;
-        float s = 0.f;
-        for (int m = 16 * J; m < 16 * I; ++m) s = fmaf(sL[(16 * I + ii) * LS + m], sT[m * LS + 16 * J + jj], s);
-        sP[J * 256 + ii * 16 + jj] = s;
-      }
-      __syncthreads();
-      for (int e = tid; e < I * 256; e += NT) {
-        const int J = e >> 8;
-        const int ii = (e >> 4) & 15;
-        const int jj = e & 15;
-        float s = 0.f;
+      if (wave < I) {
+        const int J = wave;
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+        for (int M = J; M < I; ++M) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) s = fmaf(sT[(16 * I + ii) * LS + 16 * I + m], sP[J * 256 + m * 16 + jj], s);
-        sT[(16 * I + ii) * LS + 16 * J + jj] = -s;
+          for (int s = 0; s < 4; ++s) {
+            const float a = sL[(16 * I + l16) * LS + 16 * M + 4 * s + gq];
+            const float b = sT[(16 * M + 4 * s + gq) * LS + 16 * J + l16];
+            P = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, P, 0, 0, 0);
+          }
+        }
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float a = -sT[(16 * I + l16) * LS + 16 * I + 4 * gq + s];
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, P[s], X, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * gq + r) * LS + 16 * J + l16] = X[r];
       }
       __syncthreads();
     }
-    // A = T diag(beta), lower triangular, as fp16.
-    for (int e = tid; e < C * C; e += NT) {
-      const int ii = e >> 6;
-      const int jj = e & 63;
-      const float a = (jj <= ii) ? sT[ii * LS + jj] * sBeta[jj] : 0.f;
-      sA[ii * AS + jj] = f16_bits(a);
+    // A = T diag(beta), lower triangular, as fp16 (8 entries per thread).
+    {
+      const int ii = tid >> 3;
+      const int j0 = 8 * (tid & 7);
+      const float4 t0 = *reinterpret_cast<const float4*>(sT + ii * LS + j0);
+      const float4 t1 = *reinterpret_cast<const float4*>(sT + ii * LS + j0 + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(sBeta + j0);
+      const float4 b1 = *reinterpret_cast<const float4*>(sBeta + j0 + 4);
+      const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = (j0 + e <= ii) ? tv[e] * bv[e] : 0.f;
+      *reinterpret_cast<uint4*>(sA + ii * AS + j0) =
+          make_uint4(pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]), pack_f16(a[6], a[7]));
     }
+    if (tid < KD) sGam[tid] = ex2(sG[(C - 1) * GS + tid]);
     __syncthreads();
 
-    // ---------------------------------------------------------- phase 4: W, Qg, Kg
-    if (tid < KD) sGam[tid] = ex2(sG[(C - 1) * GS + tid]);
-    for (int e = tid; e < C * KD; e += NT) {
-      const int jj = e >> 7;
-      const int c = e & (KD - 1);
-      const float gj = sG[jj * GS + c];
-      const float glast = sG[(C - 1) * GS + c];
-      const float kk = bf16f(sK[jj * QS + c]);
-      const float eg = ex2(gj);
-      sET[c * AS + jj] = f16_bits(kk * eg);
-      sKgT[c * AS + jj] = f16_bits(kk * ex2(glast - gj));
-      const float qq = bf16f(sQ[jj * QS + c]);
-      sQ[jj * QS + c] = f16_bits(SCALE * qq * eg);
+    // ---------------------------------------------------------- phase 4: E, Kg, Qg, W
+    // Thread t handles channels c2, c2+1 (c2 = 2*(t%64)) for tokens
+    // 8*(t/64)..+7.
+    uint32_t qg_pk[8];   // Qg of this thread's entries, stored after the barrier
+    {
+      const int c2 = 2 * (tid & 63);
+      const int j0 = 8 * (tid >> 6);
+      const float2 glast = *reinterpret_cast<const float2*>(sG + (C - 1) * GS + c2);
+      float ev0[8], ev1[8], kv0[8], kv1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = j0 + e;
+        const float2 gj = *reinterpret_cast<const float2*>(sG + jj * GS + c2);
+        const uint32_t kk = *reinterpret_cast<const uint32_t*>(sK + jj * QS + c2);
+        const uint32_t qq = *reinterpret_cast<const uint32_t*>(sQ + jj * QS + c2);
+        const float eg0 = ex2(gj.x), eg1 = ex2(gj.y);
+        const float k0 = bf16lo(kk), k1 = bf16hi(kk);
+        ev0[e] = k0 * eg0;
+        ev1[e] = k1 * eg1;
+        kv0[e] = k0 * ex2(glast.x - gj.x);
+        kv1[e] = k1 * ex2(glast.y - gj.y);
+        qg_pk[e] = pack_f16(SCALE * bf16lo(qq) * eg0, SCALE * bf16hi(qq) * eg1);
+      }
+      *reinterpret_cast<uint4*>(sET + c2 * AS + j0) =
+          make_uint4(pack_f16(ev0[0], ev0[1]), pack_f16(ev0[2], ev0[3]), pack_f16(ev0[4], ev0[5]), pack_f16(ev0[6], ev0[7]));
+      *reinterpret_cast<uint4*>(sET + (c2 + 1) * AS + j0) =
+          make_uint4(pack_f16(ev1[0], ev1[1]), pack_f16(ev1[2], ev1[3]), pack_f16(ev1[4], ev1[5]), pack_f16(ev1[6], ev1[7]));
+      // Kg^T in the permuted token layout: tokens j0..j0+3 and j0+4..j0+7 each
+      // land as one contiguous 8-byte group.
+      const int pj0 = perm32(j0), pj4 = perm32(j0 + 4);
+      *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj0) = make_uint2(pack_f16(kv0[0], kv0[1]), pack_f16(kv0[2], kv0[3]));
+      *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj4) = make_uint2(pack_f16(kv0[4], kv0[5]), pack_f16(kv0[6], kv0[7]));
+      *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj0) = make_uint2(pack_f16(kv1[0], kv1[1]), pack_f16(kv1[2], kv1[3]));
+      *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj4) = make_uint2(pack_f16(kv1[4], kv1[5]), pack_f16(kv1[6], kv1[7]));
     }
     __syncthreads();
-    // W = A (e^G k): 4 x 8 output tiles, A is lower triangular.
-    for (int pt = wave; pt < 32; pt += NW) {
+    // Qg (over q^, now no longer read) in the permuted channel layout; c2 and
+    // c2 + 1 stay adjacent there.
+    {
+      const int pc = perm32(2 * (tid & 63));
+      const int j0 = 8 * (tid >> 6);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sQ + (j0 + e) * QS + pc) = qg_pk[e];
+    }
+    // W = A (e^G k): 4 x 8 output tiles, 4 per wave; A is lower triangular.
+    // -W is stored in the permuted channel layout.
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int pt = wave + NW * q4;
       const int mt = pt >> 3;
       const int nt = pt & 7;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -402,8 +552,9 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
         const f16x8 b = lds_f16x8(sET + (16 * nt + l16) * AS + 32 * s + 8 * gq);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
       }
+      const int pc = perm32(16 * nt + l16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sW[(16 * mt + 4 * gq + r) * QS + 16 * nt + l16] = f16_bits(-acc[r]);
+      for (int r = 0; r < 4; ++r) sW[(16 * mt + 4 * gq + r) * QS + pc] = f16_bits(-acc[r]);
     }
     __syncthreads();
 
@@ -412,72 +563,90 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
     // (gq, e) is 32s + 4gq + e (e < 4) or 32s + 16 + 4gq + (e - 4), which is
     // exactly where the float32 S accumulator already holds it; products with
     // Vnew use the same permutation over tokens.
-    f16x8 Sh[4];
+    {
+      f16x8 Sh[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Sh[s][r] = (_Float16)S[2 * s][r];
-        Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
-      }
-    const int tcol = wave * 16 + l16;   // column within the tile
-    f32x4 Vn[4];
+        for (int r = 0; r < 4; ++r) {
+          Sh[s][r] = (_Float16)S[2 * s][r];
+          Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
+        }
+      // v as the B operand of U = A v: tokens 32s + 8gq + e of column `col`.
+      f16x8 Vv[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s) {   // U = A v
-        const f16x8 a = lds_f16x8(sA + (16 * mt + l16) * AS + 32 * s + 8 * gq);
-        const f16x8 b = lds_f16x8(sVT + tcol * AS + 32 * s + 8 * gq);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-      }
+        for (int e = 0; e < 8; ++e)
+          Vv[s][e] = __builtin_bit_cast(_Float16, sV[(32 * s + 8 * gq + e) * QS + col]);
+      // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
+      // accumulation chains, interleaved.
+      f32x4 Vn[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {            // Vnew = U + (-W) S
-        const uint16_t* row = sW + (16 * mt + l16) * QS + 32 * s + 4 * gq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16_2x4(row, row + 16), Sh[s], acc, 0, 0, 0);
-      }
-      Vn[mt] = acc;
-    }
-    f16x8 Vh[2];
+      for (int mt = 0; mt < 4; ++mt) Vn[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Vh[s][r] = (_Float16)Vn[2 * s][r];
-        Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
-      }
+        for (int mt = 0; mt < 4; ++mt)
+          if (s <= (mt >> 1))
+            Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                lds_f16x8(sA + (16 * mt + l16) * AS + 32 * s + 8 * gq), Vv[s], Vn[mt], 0, 0, 0);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {            // Qg S
-        const uint16_t* row = sQ + (16 * mt + l16) * QS + 32 * s + 4 * gq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16_2x4(row, row + 16), Sh[s], acc, 0, 0, 0);
-      }
+        for (int mt = 0; mt < 4; ++mt)
+          Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              lds_f16x8(sW + (16 * mt + l16) * QS + 32 * s + 8 * gq), Sh[s], Vn[mt], 0, 0, 0);
+      f16x8 Vh[2];
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s) {   // + Aqk Vnew
-        const uint16_t* row = sAqk + (16 * mt + l16) * AS + 32 * s + 4 * gq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16_2x4(row, row + 16), Vh[s], acc, 0, 0, 0);
-      }
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mt + 4 * gq + r;
-        if (i < nvalid) p.o[((trow + i) * p.HV + hv) * KD + col] = uint16_t(bf16_rne(acc[r]));
-      }
-    }
+        for (int r = 0; r < 4; ++r) {
+          Vh[s][r] = (_Float16)Vn[2 * s][r];
+          Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
+        }
+      // O = Qg S + Aqk Vnew.
+      f32x4 Ot[4];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {           // S = e^{G_last} S + Kg^T Vnew
-      f32x4 acc;
+      for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = S[rt][r] * sGam[16 * rt + 4 * gq + r];
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint16_t* row = sKgT + (16 * rt + l16) * AS + 32 * s + 4 * gq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16_2x4(row, row + 16), Vh[s], acc, 0, 0, 0);
-      }
-      S[rt] = acc;
+        for (int mt = 0; mt < 4; ++mt)
+          Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              lds_f16x8(sQ + (16 * mt + l16) * QS + 32 * s + 8 * gq), Sh[s], Ot[mt], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (s <= (mt >> 1))
+            Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                lds_f16x8(sAqk + (16 * mt + l16) * AS + 32 * s + 8 * gq), Vh[s], Ot[mt], 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sO[(16 * mt + 4 * gq + r) * OS + col] = uint16_t(bf16_rne(Ot[mt][r]));
+      // S = e^{G_last} S + Kg^T Vnew; eight independent row tiles.
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[rt][r] *= sGam[16 * rt + 4 * gq + r];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+          S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              lds_f16x8(sKgT + (16 * rt + l16) * AS + 32 * s + 8 * gq), Vh[s], S[rt], 0, 0, 0);
     }
     __syncthreads();
+    // o: 16-byte stores of the staged bf16 tile (two per thread).
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = (tid >> 4) + 32 * m;
+      if (i < nvalid)
+        *reinterpret_cast<uint4*>(p.o + ((trow + i) * p.HV + hv) * KD + 8 * l16) =
+            *reinterpret_cast<const uint4*>(sO + i * OS + 8 * l16);
+    }
   }
 
   float* sf = p.sfin + (int64_t(n) * p.HV + hv) * KD * KD;
@@ -487,20 +656,17 @@ __global__ __launch_bounds__(VT * 4) void prefill_kernel(Params p) {
     for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
 }
 
-template <int VT>
 int launch(const Params& p, hipStream_t stream) {
-  constexpr int NV = KD / VT;
-  const int64_t units = int64_t(p.N) * p.HV;
-  const int64_t blocks = (units + 7) / 8 * 8 * NV;
+  const int64_t blocks = int64_t(p.N) * p.HV;
   if (blocks > 0x7fffffff) return KDA_ERR_SHAPE;
   static std::atomic<bool> configured{false};   // raise the dynamic LDS limit once
   if (!configured.load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<VT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Lds<VT>::BYTES) != hipSuccess)
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) != hipSuccess)
       return KDA_ERR_HIP;
     configured.store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(prefill_kernel<VT>, dim3(unsigned(blocks)), dim3(VT * 4), Lds<VT>::BYTES, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3(unsigned(blocks)), dim3(NT), LDS_BYTES, stream, p);
   return launch_status();
 }
 
@@ -528,14 +694,9 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
   p.cu = cu_seqlens;
   p.o = static_cast<uint16_t*>(o);
   p.sfin = final_state;
-  p.B = B;
   p.T = T;
   p.H = H;
   p.HV = HV;
   p.N = cu_seqlens ? num_seqs : B;
-  // Fewer (sequence, head) units than compute units: split V in two tiles so
-  // twice as many workgroups share the work.
-  const int64_t units = int64_t(p.N) * HV;
-  hipStream_t st = as_stream(stream);
-  return units < 256 ? launch<64>(p, st) : launch<128>(p, st);
+  return launch(p, as_stream(stream));
 }

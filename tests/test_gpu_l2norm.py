@@ -64,6 +64,11 @@ def test_l2norm_crafted_rows(gpu_lib):
     sub = np.zeros(128, np.float32)                     # bf16 subnormal magnitudes
     sub[:5] = [1e-39, -2e-39, 5e-40, 3e-39, 1e-38]
     rows.append(sub)
+    for tiny_val in (1e-39, -3e-39, 5e-40, 2e-38, 1e-40):   # quotients below float32's normal range
+        r = np.zeros(128, np.float32)
+        r[0] = 1.0
+        r[1:6] = tiny_val * np.arange(1, 6)
+        rows.append(r)
     big = (rng.standard_normal(128) * 1e18).astype(np.float32)
     rows.append(big)
     tiny = (rng.standard_normal(128) * 1e-5).astype(np.float32)
