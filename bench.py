@@ -143,6 +143,7 @@ def main():
     HV = pin.v.shape[2]
     o = torch.empty(B, T, HV, V, dtype=torch.bfloat16, device=dev)
     sf = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
 
     din = synth.decode_config(args.decode_B)
     dq, dk, dv, dg, db = (t.to(dev) for t in (din.q, din.k, din.v, din.g, din.beta))
@@ -156,7 +157,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf)
+        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         kda.decode(dq, dk, dv, dg, db, pool, idx, out=dout)

@@ -40,7 +40,8 @@ typedef enum {
   KDA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
   KDA_ERR_UNSUPPORTED = 3,  /* valid request this build does not support (K, V != 128) */
   KDA_ERR_ALIGN = 4,        /* a pointer or stride is not 16-byte aligned */
-  KDA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+  KDA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+  KDA_ERR_WORKSPACE = 6     /* workspace missing or smaller than required */
 } kda_status;
 
 /* Human-readable name of a status code (static storage). */
@@ -80,7 +81,7 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  * the page's golden does; o is written only for real tokens.
  *
  *   q, k           bf16 [B, T, H, K]   raw (unnormalised) queries and keys
- *   v              bf16 [B, T, HV, V]
+ *   v              bf16 [B, T, HV, V]  magnitudes below 2^14
  *   g              fp32 [B, T, HV, K]  per-channel log decay (finite, <= 0)
  *   beta           bf16 [B, T, HV]
  *   initial_state  fp32 [N, HV, K, V]  or NULL (zeros)
@@ -93,9 +94,14 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *   num_seqs       N when cu_seqlens is given (>= 1); ignored otherwise
  *   o              bf16 [B, T, HV, V]  output
  *   final_state    fp32 [N, HV, K, V]  output, always written
+ *   workspace      device scratch of at least
+ *                  kda_chunk_prefill_workspace_size(...) bytes, owned by the
+ *                  caller; its contents on entry do not matter and are
+ *                  overwritten (the chunk-local matrices of every chunk).
+ *                  Calls that share a workspace must not overlap.
  * Sizes: B, T, H, HV >= 1 (T == 0 is accepted, may pass NULL token tensors,
- * and only writes final_state),
- * HV % H == 0, K == V == 128.  q, k, v, g, beta, o must not alias.
+ * and only writes final_state), HV % H == 0, K == V == 128.  q, k, v, g,
+ * beta, o and the workspace must not alias.
  */
 int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* g, const void* beta,
@@ -103,7 +109,18 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const int32_t* cu_seqlens, int32_t num_seqs,
                       int32_t B, int32_t T, int32_t H, int32_t HV,
                       int32_t K, int32_t V,
-                      void* o, float* final_state, void* stream);
+                      void* o, float* final_state,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill
+ * needs for these sizes (num_seqs as for kda_chunk_prefill; pass 0 when
+ * cu_seqlens is NULL).  Returns 0 for sizes kda_chunk_prefill rejects.
+ * It is about 1 KB per token and value head: one 66048-byte block per
+ * 64-token chunk slot, with floor(B*T/64) + N + 1 slots per value head.
+ */
+size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t HV,
+                                        int32_t K, int32_t V, int32_t num_seqs);
 
 /*
  * kda_decode -- one recurrent KDA step per batch row against a bf16 state

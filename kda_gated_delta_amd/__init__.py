@@ -21,7 +21,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
-EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill", "kda_decode")
+EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill",
+           "kda_chunk_prefill_workspace_size", "kda_decode")
 
 _lib = None
 
@@ -48,7 +49,10 @@ def load():
     lib.kda_qk_l2norm.argtypes = [_vp, _vp, _i64, _i32, _vp]
     lib.kda_chunk_prefill.restype = ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
-                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                      _vp, ctypes.c_size_t, _vp]
+    lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                _i32, _i32, _i32, _i32, _i32, _vp, _vp]
@@ -103,11 +107,18 @@ def qk_l2norm(x, out=None):
     return out
 
 
+def workspace_size(B, T, H, HV, num_seqs=0, K=128, V=128):
+    """Bytes of workspace kda_chunk_prefill needs (num_seqs = 0 without cu_seqlens)."""
+    return int(load().kda_chunk_prefill_workspace_size(B, T, H, HV, K, V, num_seqs))
+
+
 def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
-                  out=None, final_state=None):
+                  out=None, final_state=None, workspace=None):
     """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
     fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
-    cu_seqlens int32 [N+1] (with B == 1) or None.  Returns (o, final_state)."""
+    cu_seqlens int32 [N+1] (with B == 1) or None; workspace: a uint8 GPU
+    tensor of at least workspace_size(...) bytes, or None to allocate one.
+    Returns (o, final_state)."""
     lib = load()
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
@@ -135,9 +146,15 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
         final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
     _need(out, "out", torch.bfloat16, 4, dev)
     _need(final_state, "final_state", torch.float32, 4, dev)
+    nseq_arg = N if cu_seqlens is not None else 0
+    need = workspace_size(B, T, H, HV, nseq_arg, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
     code = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
-                                 B, T, H, HV, K, V, _ptr(out), _ptr(final_state), _stream())
+                                 _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
+                                 B, T, H, HV, K, V, _ptr(out), _ptr(final_state),
+                                 _ptr(workspace), workspace.numel(), _stream())
     _check(code, "kda_chunk_prefill")
     return out, final_state
 

@@ -49,10 +49,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int i = 0; i < 8; ++i) sv[i] = slot[(kr + 16 * i) * (V / 8) + cg];
 
   if (wave == 0) {
+    // Lanes 0-15 hold the q row, 16-31 the k row; the loads are unconditional
+    // (a load inside a branch would be waited for inside it).
     const int lane = t;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 16) x = q[(int64_t(b) * H + hq) * (K / 8) + lane];
-    else if (lane < 32) x = k[(int64_t(b) * H + hq) * (K / 8) + (lane - 16)];
+    const uint4* src = (lane < 16 ? q : k) + (int64_t(b) * H + hq) * (K / 8) + (lane & 15);
+    const uint4 xl = *src;
+    const uint4 x = lane < 32 ? xl : make_uint4(0u, 0u, 0u, 0u);
     uint4 y = kda::l2norm_row16(x);
     float* dst = lane < 16 ? s_q : s_k;
     if (lane < 32) {

@@ -7,24 +7,32 @@
 // Vnew, S = exp(G_last) S + Kg^T Vnew; chunk size 64 with a zero-padded last
 // chunk).
 //
-// Design: one fused kernel, no workspace, one 512-thread workgroup (8 waves)
-// per (sequence, value head).  Wave w owns state columns 16w..16w+15 and
-// keeps that 128x16 slice of S in registers as float32 for the whole
-// sequence (the state's columns evolve independently: column v of S only
-// ever meets column v of the values).  For each 64-token chunk:
-//   1. the raw q, k, g, beta and v of the chunk, prefetched into registers
-//      while the previous chunk was computed, are normalised (bit-exact
-//      routine shared with kda_qk_l2norm), scanned (G, kept in log2 units)
-//      and staged in LDS; the loads for the next chunk are issued;
-//   2. the gated L and Aqk, 16x16 blocks on MFMA;
-//   3. T = (I+L)^-1 by blocked forward substitution in float32 (diagonal
-//      blocks by substitution, off-diagonal blocks on fp32 MFMA), then
-//      A = T diag(beta);
-//   4. W = A (exp(G) k), Qg, Kg, exp(G_last);
-//   5. each wave runs the carry for its columns on MFMA: U = A v and Vnew =
-//      U - W S accumulate in float32 (U is never rounded), O = Qg S + Aqk
-//      Vnew (staged in LDS, written with 16-byte stores), S = exp(G_last) S +
-//      Kg^T Vnew.
+// Two kernels, split where the method splits: everything inside a chunk is
+// independent of the state, so it runs chunk-parallel over the whole chip;
+// only the carry is sequential.
+//
+// intra_kernel -- one 512-thread workgroup (8 waves) per run of up to four
+//   consecutive chunks of one (sequence, value head).  Per chunk:
+//     1. the raw q, k, g and beta, prefetched into registers while the
+//        previous chunk was computed, are normalised (bit-exact routine
+//        shared with kda_qk_l2norm), scanned (G, kept in log2 units) and
+//        staged in LDS;
+//     2. the gated L and Aqk, 16x16 blocks on MFMA;
+//     3. T = (I+L)^-1 by blocked forward substitution in float32 (diagonal
+//        blocks by substitution, off-diagonal blocks on fp32 MFMA), then
+//        A = T diag(beta);
+//     4. E = exp(G) k, Kg, Qg, exp(G_last) and W = A E;
+//   and the chunk's W, Qg, Kg^T, Aqk, A and exp(G_last) are written to the
+//   workspace (66 KB per chunk and head, fp16 except exp(G_last)).
+//
+// inter_kernel -- one 512-thread workgroup per (sequence, value head).  Wave w
+//   owns state columns 16w..16w+15 and keeps that 128x16 slice of S in
+//   registers as float32 for the whole sequence (the state's columns evolve
+//   independently: column v of S only ever meets column v of the values).
+//   Chunk blocks stream through two LDS buffers (the next chunk is loaded
+//   while the current one is computed).  Per chunk, on MFMA: U = A v and
+//   Vnew = U - W S accumulate in float32 (U is never rounded), O = Qg S +
+//   Aqk Vnew, S = exp(G_last) S + Kg^T Vnew.
 //
 // Precision: every MFMA operand is fp16 with float32 accumulation, and the
 // state is carried in float32.  fp16's 11-bit significand keeps the final
@@ -46,6 +54,21 @@
 // 8 tokens; if that exceeds 2^120 for any channel the block is computed
 // pair by pair instead (exact, slow, only for extreme gates).  exp(-G) over a
 // whole chunk is never formed.
+//
+// Workspace.  Chunk c of sequence n of value head hv lives in slot
+// base(n) + c of head hv, with base(n) = floor(first_token(n) / 64) + n; the
+// slots of consecutive sequences never overlap because a sequence of L
+// tokens has ceil(L/64) <= floor(L/64) + 1 chunks.  A slot holds, in order:
+//   W     fp16 [64][128]  channels in the permuted order below
+//   Qg    fp16 [64][128]  channels permuted
+//   Kg^T  fp16 [128][64]  tokens permuted
+//   Aqk   fp16 [64][64]   tokens permuted
+//   A     fp16 [64][64]   natural order
+//   gamma fp32 [128]      exp(G_last)
+// Within each row of the four matrices, the 16-byte piece p is stored at
+// position p ^ (row & 7) (an XOR swizzle), so that sixteen lanes reading the
+// same logical piece of sixteen consecutive rows hit distinct LDS banks once
+// the slot is copied verbatim into LDS.
 #include <atomic>
 
 #include "kda_device.h"
@@ -63,23 +86,33 @@ constexpr int C = 64;            // chunk length
 constexpr int KD = 128;          // key width == value width
 constexpr int NW = 8;            // waves per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
+constexpr int CPW = 4;           // chunks per intra workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SCALE = 0.08838834764831845f;   // 128^-1/2
 constexpr float SAFE_EXP2 = 120.0f;             // largest split-factor exponent (base 2)
 constexpr float F16_EXP2 = 14.0f;               // largest split-factor exponent for fp16 operands
 
+// Workspace slot layout (bytes).
+constexpr int WS_W = 0;
+constexpr int WS_QG = WS_W + C * KD * 2;
+constexpr int WS_KGT = WS_QG + C * KD * 2;
+constexpr int WS_AQK = WS_KGT + KD * C * 2;
+constexpr int WS_A = WS_AQK + C * C * 2;
+constexpr int WS_GAM = WS_A + C * C * 2;
+constexpr int WS_SLOT = WS_GAM + KD * 4;          // 66048 bytes
+static_assert(WS_SLOT % 16 == 0, "slots stay 16-byte aligned");
+
 // LDS row strides (elements).  Row strides of 68 or 36 words put eight
 // consecutive rows' 16-byte accesses in distinct bank groups.
 constexpr int QS = 136;          // 16-bit [64][128] arrays
 constexpr int GS = 132;          // fp32 [64][128] (G)
-constexpr int OS = 136;          // bf16 [64][128] (o staging, in the G region)
+constexpr int OS = 136;          // bf16 [64][128] (o staging)
 constexpr int LS = 68;           // fp32 [64][64] arrays
 constexpr int AS = 72;           // 16-bit [*][64] arrays
 
-// LDS map (bytes).  Regions are reused across phases:
-//   G    : fp32 G (phases 1-4), then bf16 o staging (phase 5)
-//   U1   : fp32 L and T (phases 2-3), then fp16 -W and E^T (phases 4-5)
-//   AREG : fp32 scan totals (phase 1), fp16 A (phases 3-5)
+// intra_kernel LDS map (bytes).  Regions are reused across phases:
+//   U1   : fp32 L and T (phases 2-3), then fp16 -W and E^T (phase 4)
+//   AREG : fp32 scan totals (phase 1), fp16 A (phases 3-4)
 constexpr int OFF_Q = 0;                                  // bf16 q^, then fp16 Qg  [64][QS]
 constexpr int OFF_K = OFF_Q + C * QS * 2;                 // bf16 k^                [64][QS]
 constexpr int OFF_G = OFF_K + C * QS * 2;                 // fp32 G (log2 units)    [64][GS]
@@ -93,13 +126,22 @@ constexpr int U1_BYTES = (2 * C * LS * 4 > C * QS * 2 + KD * AS * 2) ? 2 * C * L
 constexpr int OFF_AQK = OFF_U1 + U1_BYTES;                // fp16 Aqk               [64][AS]
 constexpr int OFF_A = OFF_AQK + C * AS * 2;               // fp16 A [64][AS] / scan totals
 constexpr int OFF_KGT = OFF_A + C * AS * 2;               // fp16 Kg^T              [128][AS]
-constexpr int OFF_V = OFF_KGT + KD * AS * 2;              // fp16 v                 [64][QS]
-constexpr int OFF_BETA = OFF_V + C * QS * 2;              // fp32 [64]
+constexpr int OFF_BETA = OFF_KGT + KD * AS * 2;           // fp32 [64]
 constexpr int OFF_GAM = OFF_BETA + C * 4;                 // fp32 [128]
-constexpr int LDS_BYTES = OFF_GAM + KD * 4;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+constexpr int INTRA_LDS = OFF_GAM + KD * 4;
+static_assert(INTRA_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
-static_assert(C * GS * 4 >= C * OS * 2, "o staging fits in the G region");
+
+// inter_kernel LDS map: two verbatim copies of workspace slots (filled by
+// direct global-to-LDS loads, one 1 KB block per wave instruction; the last
+// block overhangs the slot, hence the padding) and, per wave, the v tile of
+// its 16 columns.
+constexpr int SLOT_U4 = WS_SLOT / 16;                     // 16-byte pieces per slot
+constexpr int SLOT_BLOCKS = (WS_SLOT + 1023) / 1024;      // 1 KB load blocks per slot
+constexpr int BUF_BYTES = SLOT_BLOCKS * 1024;
+constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [8 waves][64 tokens][16 columns]
+constexpr int INTER_LDS = OFF_V + NW * C * 16 * 2;
+static_assert(INTER_LDS <= 160 * 1024, "LDS budget");
 
 struct Params {
   const uint16_t* q;
@@ -111,6 +153,8 @@ struct Params {
   const int32_t* cu;
   uint16_t* o;
   float* sfin;
+  unsigned char* ws;
+  int64_t nslots;          // slots per value head
   int T, H, HV, N;
 };
 
@@ -158,47 +202,76 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& x, float* f) {
 //   qk[m]: row rg + 32m of the 128 stacked rows (q rows 0..63, k rows 64..127),
 //          8 bf16 at column 8*l16, with rg = tid/16, l16 = tid%16
 //   gv[r]: g of token 4*seg + r, channels 4*c4..4*c4+3 (seg = tid/32, c4 = tid%32)
-//   vv[m]: v of token tid/16 + 32m, columns 8*(tid%16)..+7
 struct Raw {
   uint4 qk[4];
   float4 gv[4];
-  uint4 vv[2];
   float beta;
 };
 
+// Loads are unconditional (rows past the chunk's end are clamped to its last
+// valid row and zeroed by a select): a load inside a branch would be waited
+// for inside that branch.
 __device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
                                          int hv, int tid) {
   const int rg = tid >> 4, l16 = tid & 15;
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int i = (rg + 32 * m) & (C - 1);
     const uint16_t* base = (m < 2) ? p.q : p.k;
-    R.qk[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (i < nvalid) R.qk[m] = *reinterpret_cast<const uint4*>(base + ((trow + i) * p.H + hq) * KD + 8 * l16);
+    const uint4 x = *reinterpret_cast<const uint4*>(base + ((trow + min(i, nvalid - 1)) * p.H + hq) * KD + 8 * l16);
+    R.qk[m] = (i < nvalid) ? x : z4;
   }
   const int seg = tid >> 5, c4 = tid & 31;
+  const float4 zf = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = 4 * seg + r;
-    R.gv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < nvalid) R.gv[r] = *reinterpret_cast<const float4*>(p.g + ((trow + i) * p.HV + hv) * KD + 4 * c4);
+    const float4 x = *reinterpret_cast<const float4*>(p.g + ((trow + min(i, nvalid - 1)) * p.HV + hv) * KD + 4 * c4);
+    R.gv[r] = (i < nvalid) ? x : zf;
   }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int i = rg + 32 * m;
-    R.vv[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (i < nvalid) R.vv[m] = *reinterpret_cast<const uint4*>(p.v + ((trow + i) * p.HV + hv) * KD + 8 * l16);
-  }
-  R.beta = 0.f;
-  if (tid < nvalid) R.beta = bf16f(p.beta[(trow + tid) * p.HV + hv]);
+  const float b = bf16f(p.beta[(trow + min(tid, nvalid - 1)) * p.HV + hv]);
+  R.beta = (tid < nvalid) ? b : 0.f;
 }
 
-__global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
+// First token row and length of sequence n.
+__device__ __forceinline__ void seq_range(const Params& p, int n, int64_t& tok0, int& len) {
+  if (p.cu) {
+    tok0 = p.cu[n];
+    len = p.cu[n + 1] - p.cu[n];
+  } else {
+    tok0 = int64_t(n) * p.T;
+    len = p.T;
+  }
+}
+
+// Workspace slot of chunk 0 of sequence n.
+__device__ __forceinline__ int64_t slot_base(const Params& p, int n) {
+  const int64_t tok0 = p.cu ? int64_t(p.cu[n]) : int64_t(n) * p.T;
+  return tok0 / C + n;
+}
+
+// The sequence owning workspace slot s, or -1 for a slot between sequences.
+__device__ __forceinline__ int slot_owner(const Params& p, int64_t s, int& chunk) {
+  int lo = 0, hi = p.N - 1;                 // largest n with slot_base(n) <= s
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_base(p, mid) <= s) lo = mid; else hi = mid - 1;
+  }
+  int64_t tok0;
+  int len;
+  seq_range(p, lo, tok0, len);
+  const int64_t c = s - slot_base(p, lo);
+  if (c < 0 || c * C >= len) return -1;
+  chunk = int(c);
+  return lo;
+}
+
+__global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
   float* sG = reinterpret_cast<float*>(smem + OFF_G);
-  uint16_t* sO = reinterpret_cast<uint16_t*>(smem + OFF_G);
   float* sL = reinterpret_cast<float*>(smem + OFF_L);
   float* sT = reinterpret_cast<float*>(smem + OFF_T);
   uint16_t* sW = reinterpret_cast<uint16_t*>(smem + OFF_W);
@@ -207,7 +280,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem + OFF_A);
   float* sScr = reinterpret_cast<float*>(smem + OFF_A);
   uint16_t* sKgT = reinterpret_cast<uint16_t*>(smem + OFF_KGT);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + OFF_V);
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
 
@@ -217,38 +289,39 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  const int unit = blockIdx.x;
-  if (unit >= p.N * p.HV) return;
-  const int n = unit / p.HV;
-  const int hv = unit % p.HV;
+  // Workgroup -> value head and a run of CPW consecutive slots.
+  const int hv = blockIdx.x % p.HV;
+  const int64_t s0 = int64_t(blockIdx.x / p.HV) * CPW;
   const int hq = hv / (p.HV / p.H);
 
-  int64_t tok0;   // row of the sequence's first token in the [B*T] token axis
-  int len;
-  if (p.cu) {
-    tok0 = p.cu[n];
-    len = p.cu[n + 1] - p.cu[n];
-  } else {
-    tok0 = int64_t(n) * p.T;
-    len = p.T;
+  // The chunks of this run that exist (slots between sequences are skipped).
+  int nit = 0;
+  int64_t trows[CPW];
+  int nvalids[CPW];
+  int64_t slots[CPW];
+  for (int u = 0; u < CPW; ++u) {
+    const int64_t s = s0 + u;
+    if (s >= p.nslots) break;
+    int c;
+    const int n = slot_owner(p, s, c);
+    if (n < 0) continue;
+    int64_t tok0;
+    int len;
+    seq_range(p, n, tok0, len);
+    trows[nit] = tok0 + int64_t(c) * C;
+    nvalids[nit] = min(C, len - c * C);
+    slots[nit] = s;
+    ++nit;
   }
-
-  const int col = wave * 16 + l16;               // this lane's state column
-  f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
-  {
-    const float* s0 = p.s0 ? p.s0 + (int64_t(n) * p.HV + hv) * KD * KD : nullptr;
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[rt][r] = s0 ? s0[(16 * rt + 4 * gq + r) * KD + col] : 0.f;
-  }
+  if (nit == 0) return;
 
   Raw R;
-  if (len > 0) load_raw(R, p, tok0, min(C, len), hq, hv, tid);
+  load_raw(R, p, trows[0], nvalids[0], hq, hv, tid);
 
-  for (int c0 = 0; c0 < len; c0 += C) {
-    const int nvalid = min(C, len - c0);
-    const int64_t trow = tok0 + c0;              // token row of chunk position 0
+  for (int it = 0; it < nit; ++it) {
+    const int nvalid = nvalids[it];
+    const int64_t trow_next = (it + 1 < nit) ? trows[it + 1] : 0;
+    const int nvalid_next = (it + 1 < nit) ? nvalids[it + 1] : 0;
 
     // ---------------------------------------------------------- phase 1
     {
@@ -258,14 +331,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
         const uint4 y = l2norm_row16(R.qk[m]);
         *reinterpret_cast<uint4*>(((m < 2) ? sQ : sK) + ((rg + 32 * m) & (C - 1)) * QS + 8 * l16) = y;
         __builtin_amdgcn_sched_barrier(0);   // one row at a time keeps register use low
-      }
-      // v (bf16 -> fp16), row-major.
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float f[8];
-        unpack_bf16x8(R.vv[m], f);
-        *reinterpret_cast<uint4*>(sV + (rg + 32 * m) * QS + 8 * l16) =
-            make_uint4(pack_f16(f[0], f[1]), pack_f16(f[2], f[3]), pack_f16(f[4], f[5]), pack_f16(f[6], f[7]));
       }
       if (tid < C) sBeta[tid] = R.beta;
       // g in log2 units, inclusive scan over the 4 tokens this thread holds,
@@ -282,7 +347,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
       *reinterpret_cast<float4*>(sScr + seg * KD + 4 * c4) = gs[3];
       __syncthreads();
       // The raw registers are consumed: prefetch the next chunk.
-      if (c0 + C < len) load_raw(R, p, trow + C, min(C, len - c0 - C), hq, hv, tid);
+      if (it + 1 < nit) load_raw(R, p, trow_next, nvalid_next, hq, hv, tid);
       float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s2 = 0; s2 < seg; ++s2) {
         const float4 t = *reinterpret_cast<const float4*>(sScr + s2 * KD + 4 * c4);
@@ -558,95 +623,220 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
     }
     __syncthreads();
 
-    // ---------------------------------------------------------- phase 5: carry
+    // Chunk outputs -> workspace slot, in slot order (coalesced 16-byte
+    // stores), gathering each piece from its swizzled source position.
+    {
+      unsigned char* dst = p.ws + (int64_t(hv) * p.nslots + slots[it]) * WS_SLOT;
+      for (int u = tid; u < SLOT_U4; u += NT) {
+        const int b = u * 16;
+        const unsigned char* src;
+        if (b < WS_KGT) {          // W, Qg: 64 rows of 16 pieces
+          const int off = b < WS_QG ? b : b - WS_QG;
+          const int r = off >> 8, pp = (off >> 4) & 15;
+          const uint16_t* base = b < WS_QG ? sW : sQ;
+          src = reinterpret_cast<const unsigned char*>(base + r * QS) + ((pp ^ (r & 7)) << 4);
+        } else if (b < WS_GAM) {   // Kg^T, Aqk, A: rows of 8 pieces
+          const uint16_t* base;
+          int off;
+          if (b < WS_AQK) { base = sKgT; off = b - WS_KGT; }
+          else if (b < WS_A) { base = sAqk; off = b - WS_AQK; }
+          else { base = sA; off = b - WS_A; }
+          const int r = off >> 7, pp = (off >> 4) & 7;
+          src = reinterpret_cast<const unsigned char*>(base + r * AS) + ((pp ^ (r & 7)) << 4);
+        } else {
+          src = reinterpret_cast<const unsigned char*>(sGam) + (b - WS_GAM);
+        }
+        *reinterpret_cast<uint4*>(dst + b) = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global-to-LDS copy of one workspace slot: 1 KB blocks, wave w
+// issuing blocks w, w + 8, ...  Each lane moves 16 bytes to the block base +
+// 16 * lane; pieces past the end of the slot re-read its last piece into the
+// buffer's padding.
+__device__ __forceinline__ void load_slot_lds(unsigned char* buf, const unsigned char* slot, int wave,
+                                              int lane) {
+#pragma unroll
+  for (int blk = wave; blk < SLOT_BLOCKS; blk += NW) {
+    const int u = min(blk * 64 + lane, SLOT_U4 - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(slot + u * 16),
+                                     (lds_void*)(buf + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Direct load of this wave's v tile (64 tokens x 16 columns, bf16) into its
+// LDS region: two 1 KB blocks, lane l carrying token 32h + l/2, columns
+// 16*wave + 8*(l&1)..+7.  Rows past the chunk's end are clamped here and
+// zeroed when read.
+__device__ __forceinline__ void load_v_lds(unsigned char* sv, const Params& p, int64_t trow, int nvalid,
+                                           int hv, int wave, int lane) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = min(32 * h + (lane >> 1), nvalid - 1);
+    const uint16_t* src = p.v + ((trow + t) * p.HV + hv) * KD + 16 * wave + 8 * (lane & 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (lds_void*)(sv + h * 1024), 16, 0, 0);
+  }
+}
+
+// 16-byte operand read of logical piece `piece` of swizzled row `row`.
+__device__ __forceinline__ f16x8 swz_read(const unsigned char* base, int row, int row_bytes, int piece) {
+  return *reinterpret_cast<const f16x8*>(base + row * row_bytes + ((piece ^ (row & 7)) << 4));
+}
+
+constexpr int WAIT_LDS = 0xC07F;   // s_waitcnt lgkmcnt(0)
+constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
+
+__global__ __launch_bounds__(NT) void inter_kernel(Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+
+  const int unit = blockIdx.x;
+  if (unit >= p.N * p.HV) return;
+  const int n = unit / p.HV;
+  const int hv = unit % p.HV;
+  int64_t tok0;
+  int len;
+  seq_range(p, n, tok0, len);
+  const int nch = (len + C - 1) / C;
+  const unsigned char* wsh = p.ws + (int64_t(hv) * p.nslots + slot_base(p, n)) * WS_SLOT;
+  unsigned char* sv = smem + OFF_V + wave * (C * 16 * 2);
+
+  const int col = wave * 16 + l16;               // this lane's state column
+  f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
+  {
+    const float* s0 = p.s0 ? p.s0 + (int64_t(n) * p.HV + hv) * KD * KD : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[rt][r] = s0 ? s0[(16 * rt + 4 * gq + r) * KD + col] : 0.f;
+  }
+
+  if (nch > 0) {
+    load_slot_lds(smem, wsh, wave, lane);
+    load_v_lds(sv, p, tok0, min(C, len), hv, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int nvalid = min(C, len - c * C);
+    const int64_t trow = tok0 + int64_t(c) * C;
+    const unsigned char* cur = smem + (c & 1) * BUF_BYTES;
+    const bool more = c + 1 < nch;
+    // The other buffer was last read in the previous chunk: refill it now.
+    if (more) load_slot_lds(smem + ((c + 1) & 1) * BUF_BYTES, wsh + int64_t(c + 1) * WS_SLOT, wave, lane);
+
+    const unsigned char* sW = cur + WS_W;
+    const unsigned char* sQg = cur + WS_QG;
+    const unsigned char* sKgT = cur + WS_KGT;
+    const unsigned char* sAqk = cur + WS_AQK;
+    const unsigned char* sA = cur + WS_A;
+    const float* sGam = reinterpret_cast<const float*>(cur + WS_GAM);
+
+    // v as the B operand of U = A v: tokens 32s + 8gq + e of column `col`.
+    f16x8 Vv[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 32 * s + 8 * gq + e;
+        const float x = bf16f(*reinterpret_cast<const uint16_t*>(sv + i * 32 + l16 * 2));
+        Vv[s][e] = (_Float16)((i < nvalid) ? x : 0.f);
+      }
+    // This wave's v slot is free once its reads are done: fetch the next chunk's.
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+      load_v_lds(sv, p, trow + C, min(C, len - (c + 1) * C), hv, wave, lane);
+    }
+
     // Contraction orders: for products with S the channel index of k-slot
     // (gq, e) is 32s + 4gq + e (e < 4) or 32s + 16 + 4gq + (e - 4), which is
     // exactly where the float32 S accumulator already holds it; products with
-    // Vnew use the same permutation over tokens.
-    {
-      f16x8 Sh[4];
+    // Vnew use the same permutation over tokens.  The workspace stores W, Qg,
+    // Kg^T and Aqk in that order, so each operand is one 16-byte read.
+    f16x8 Sh[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Sh[s][r] = (_Float16)S[2 * s][r];
-          Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
-        }
-      // v as the B operand of U = A v: tokens 32s + 8gq + e of column `col`.
-      f16x8 Vv[2];
+      for (int r = 0; r < 4; ++r) {
+        Sh[s][r] = (_Float16)S[2 * s][r];
+        Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
+      }
+    // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
+    // accumulation chains, interleaved.
+    f32x4 Vn[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+    for (int mt = 0; mt < 4; ++mt) Vn[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Vv[s][e] = __builtin_bit_cast(_Float16, sV[(32 * s + 8 * gq + e) * QS + col]);
-      // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
-      // accumulation chains, interleaved.
-      f32x4 Vn[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) Vn[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          if (s <= (mt >> 1))
-            Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                lds_f16x8(sA + (16 * mt + l16) * AS + 32 * s + 8 * gq), Vv[s], Vn[mt], 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              lds_f16x8(sW + (16 * mt + l16) * QS + 32 * s + 8 * gq), Sh[s], Vn[mt], 0, 0, 0);
-      f16x8 Vh[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Vh[s][r] = (_Float16)Vn[2 * s][r];
-          Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
-        }
-      // O = Qg S + Aqk Vnew.
-      f32x4 Ot[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              lds_f16x8(sQ + (16 * mt + l16) * QS + 32 * s + 8 * gq), Sh[s], Ot[mt], 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          if (s <= (mt >> 1))
-            Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                lds_f16x8(sAqk + (16 * mt + l16) * AS + 32 * s + 8 * gq), Vh[s], Ot[mt], 0, 0, 0);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
+        if (s <= (mt >> 1))
+          Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sA, 16 * mt + l16, 128, 4 * s + gq), Vv[s],
+                                                          Vn[mt], 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sO[(16 * mt + 4 * gq + r) * OS + col] = uint16_t(bf16_rne(Ot[mt][r]));
-      // S = e^{G_last} S + Kg^T Vnew; eight independent row tiles.
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sW, 16 * mt + l16, 256, 4 * s + gq), Sh[s],
+                                                        Vn[mt], 0, 0, 0);
+    f16x8 Vh[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Vh[s][r] = (_Float16)Vn[2 * s][r];
+        Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
+      }
+    // O = Qg S + Aqk Vnew, stored straight from the accumulators.
+    f32x4 Ot[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sQg, 16 * mt + l16, 256, 4 * s + gq), Sh[s],
+                                                        Ot[mt], 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        if (s <= (mt >> 1))
+          Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sAqk, 16 * mt + l16, 128, 4 * s + gq), Vh[s],
+                                                          Ot[mt], 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mt + 4 * gq + r;
+        if (i < nvalid) p.o[((trow + i) * p.HV + hv) * KD + col] = uint16_t(bf16_rne(Ot[mt][r]));
+      }
+    // S = e^{G_last} S + Kg^T Vnew; eight independent row tiles.
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[rt][r] *= sGam[16 * rt + 4 * gq + r];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt][r] *= sGam[16 * rt + 4 * gq + r];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-          S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              lds_f16x8(sKgT + (16 * rt + l16) * AS + 32 * s + 8 * gq), Vh[s], S[rt], 0, 0, 0);
-    }
+        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq), Vh[s],
+                                                       S[rt], 0, 0, 0);
+    // The next chunk's slot and v tile must have landed before anyone reads them.
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     __syncthreads();
-    // o: 16-byte stores of the staged bf16 tile (two per thread).
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int i = (tid >> 4) + 32 * m;
-      if (i < nvalid)
-        *reinterpret_cast<uint4*>(p.o + ((trow + i) * p.HV + hv) * KD + 8 * l16) =
-            *reinterpret_cast<const uint4*>(sO + i * OS + 8 * l16);
-    }
   }
 
   float* sf = p.sfin + (int64_t(n) * p.HV + hv) * KD * KD;
@@ -656,34 +846,60 @@ __global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
     for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
 }
 
-int launch(const Params& p, hipStream_t stream) {
-  const int64_t blocks = int64_t(p.N) * p.HV;
-  if (blocks > 0x7fffffff) return KDA_ERR_SHAPE;
-  static std::atomic<bool> configured{false};   // raise the dynamic LDS limit once
-  if (!configured.load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) != hipSuccess)
+template <typename Kern>
+int set_lds(Kern kern, int bytes, std::atomic<bool>& done) {
+  if (!done.load(std::memory_order_acquire)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            bytes) != hipSuccess)
       return KDA_ERR_HIP;
-    configured.store(true, std::memory_order_release);
+    done.store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(prefill_kernel, dim3(unsigned(blocks)), dim3(NT), LDS_BYTES, stream, p);
+  return KDA_OK;
+}
+
+int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq + 1; }
+
+int launch(const Params& p, hipStream_t stream) {
+  static std::atomic<bool> intra_set{false}, inter_set{false};
+  if (set_lds(&intra_kernel, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
+  const int64_t intra_blocks = (p.nslots + CPW - 1) / CPW * p.HV;
+  const int64_t inter_blocks = int64_t(p.N) * p.HV;
+  if (intra_blocks > 0x7fffffff || inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
+  hipLaunchKernelGGL(intra_kernel, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
+  const int st = launch_status();
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NT), INTER_LDS, stream, p);
   return launch_status();
 }
 
 }  // namespace
 
+extern "C" size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t HV,
+                                                   int32_t Kd, int32_t Vd, int32_t num_seqs) {
+  (void)H;
+  if (B < 1 || T < 0 || HV < 1 || Kd != KD || Vd != KD) return 0;
+  const int64_t nseq = num_seqs > 0 ? num_seqs : B;
+  return size_t(slots_per_head(int64_t(B) * T, nseq) * HV) * WS_SLOT;
+}
+
 extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
                                  const void* beta, const float* initial_state,
                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
                                  int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
-                                 void* o, float* final_state, void* stream) {
+                                 void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
   if (!final_state || (T > 0 && (!q || !k || !v || !g || !beta || !o))) return KDA_ERR_NULL;
   if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
-      !aligned16(final_state) || (initial_state && !aligned16(initial_state)))
+      !aligned16(final_state) || (initial_state && !aligned16(initial_state)) || !aligned16(workspace))
     return KDA_ERR_ALIGN;
+  const int64_t nseq = cu_seqlens ? num_seqs : B;
+  const size_t need = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, int32_t(nseq));
+  if (!workspace) return KDA_ERR_NULL;
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
   Params p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -694,9 +910,11 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
   p.cu = cu_seqlens;
   p.o = static_cast<uint16_t*>(o);
   p.sfin = final_state;
+  p.ws = static_cast<unsigned char*>(workspace);
+  p.nslots = slots_per_head(int64_t(B) * T, nseq);
   p.T = T;
   p.H = H;
   p.HV = HV;
-  p.N = cu_seqlens ? num_seqs : B;
+  p.N = int(nseq);
   return launch(p, as_stream(stream));
 }

@@ -9,6 +9,7 @@ extern "C" const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: K and V must be 128";
     case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer or stride is not 16-byte aligned";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported a launch error";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
     default: return "unknown kda_status";
   }
 }

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_prefill", "kda_decode", "kda_qk_l2norm", "kda_status_string"):
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_qk_l2norm",
+              "kda_status_string"):
         assert n in names
     assert set(names) == set(kda.EXPORTS)
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = kda.load()
-    for code in range(6):
+    for code in range(7):
         assert lib.kda_status_string(code).startswith(b"KDA_")
     assert b"unknown" in lib.kda_status_string(99)
 
@@ -55,10 +56,11 @@ def test_l2norm_metadata_errors():
 
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
-             B=1, T=64, H=1, HV=1, K=128, V=128, o=FAKE, fs=FAKE)
+             B=1, T=64, H=1, HV=1, K=128, V=128, o=FAKE, fs=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.kda_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
-                                 a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"], NULL)
+                                 a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"],
+                                 a["ws"], a["wsb"], NULL)
 
 
 def test_prefill_metadata_errors():
@@ -73,6 +75,18 @@ def test_prefill_metadata_errors():
     assert _prefill(lib, cu=FAKE, n=2, B=2) == 2          # packed sequences need B == 1
     assert _prefill(lib, cu=FAKE, n=0) == 2
     assert _prefill(lib, v=MISALIGNED) == 4
+    assert _prefill(lib, ws=NULL) == 1
+    assert _prefill(lib, wsb=1000) == 6                    # workspace too small
+
+
+def test_workspace_size_formula():
+    lib = kda.load()
+    slot = 66048
+    # floor(B*T/64) + N + 1 slots per value head
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) == (128 + 1 + 1) * 96 * slot
+    assert lib.kda_chunk_prefill_workspace_size(2, 1000, 8, 8, 128, 128, 0) == (31 + 2 + 1) * 8 * slot
+    assert lib.kda_chunk_prefill_workspace_size(1, 500, 2, 4, 128, 128, 5) == (7 + 5 + 1) * 4 * slot
+    assert lib.kda_chunk_prefill_workspace_size(1, 64, 1, 1, 64, 128, 0) == 0
 
 
 def _decode(lib, **kw):
