@@ -15,6 +15,22 @@ namespace kda {
 constexpr int kHead = 128;        // K == V
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also fences
+// global memory, which makes every wave wait for all of its outstanding
+// global loads and stores -- including prefetches meant to stay in flight
+// across the barrier.  Here the compiler is kept from moving memory accesses
+// across the barrier, the wave waits for its own LDS operations, and the
+// hardware barrier does the rest.  Global data shared through LDS by direct
+// loads must be waited for (vmcnt) by the caller before this.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- bf16 bits
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -110,6 +126,38 @@ __device__ __forceinline__ int row16_min(int x) {
   return x;
 }
 
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i <-> 7 - i within 8 lanes
+
+// All-reduce across 8-lane groups (lanes sharing lane/8): neighbours, pairs,
+// then the mirrored quad.
+__device__ __forceinline__ double row8_sum(double x) {
+  x += dpp64<kDppXor1>(x);
+  x += dpp64<kDppXor2>(x);
+  x += dpp64<kDppHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ int row8_max(int x) {
+  x = max(x, int(dpp32<kDppXor1>(uint32_t(x))));
+  x = max(x, int(dpp32<kDppXor2>(uint32_t(x))));
+  x = max(x, int(dpp32<kDppHalfMirror>(uint32_t(x))));
+  return x;
+}
+__device__ __forceinline__ int row8_min(int x) {
+  x = min(x, int(dpp32<kDppXor1>(uint32_t(x))));
+  x = min(x, int(dpp32<kDppXor2>(uint32_t(x))));
+  x = min(x, int(dpp32<kDppHalfMirror>(uint32_t(x))));
+  return x;
+}
+
+// float32 pair -> packed bf16, round to nearest even, with the hardware
+// conversion; inline assembly keeps the compiler from merging it with the
+// float64 -> float32 rounding that precedes it.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+
 // ---------------------------------------------------------------- row norm
 
 // Normalise one row of 128 bf16 held by a 16-lane group (lanes sharing
@@ -193,6 +241,70 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] = pack_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
   return make_uint4(y[0], y[1], y[2], y[3]);
+}
+
+// The same normalisation with a row held by an 8-lane group (lanes sharing
+// lane/8), 16 consecutive elements per lane (x0: elements 0..7, x1: 8..15).
+// Identical results: the sum is exact on the fast path (any order), the
+// slow path rounds in the group's first lane, and the division is per
+// element.
+__device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  double xd[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xd[2 * i] = (double)bf16lo(w[i]);
+    xd[2 * i + 1] = (double)bf16hi(w[i]);
+  }
+  u16x2 mx = {0, 0};
+  u16x2 mn = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
+    mx = __builtin_elementwise_max(mx, m);
+    mn = __builtin_elementwise_min(mn, m - (u16x2){1, 1});
+  }
+  int emax = int(mx[0] > mx[1] ? mx[0] : mx[1]);
+  int emin = int(mn[0] < mn[1] ? mn[0] : mn[1]) + 1;
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s = fma(xd[i], xd[i], s);
+  s = row8_sum(s);
+  emax = row8_max(emax) >> 7;
+  emin = row8_min(emin) >> 7;
+  const bool exact = (emax == 0 && emin == 512) || (max(emax, 1) - max(emin, 1) <= 15);
+  float s32 = (float)s;
+  if (!__all(exact)) {
+    double hi = 0.0, lo = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      double t, e;
+      two_sum(hi, xd[i] * xd[i], t, e);
+      hi = t;
+      lo += e;
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      const double oh = __shfl_xor(hi, off, 64);
+      const double ol = __shfl_xor(lo, off, 64);
+      double t, e;
+      two_sum(hi, oh, t, e);
+      const double l = lo + ol + e;
+      hi = t + l;
+      lo = l - (hi - t);
+    }
+    const float r = __shfl(dd_to_f32(hi, lo), (threadIdx.x & 63) & ~7, 64);
+    if (!exact) s32 = r;
+  }
+  const float t = s32 + 1e-6f;
+  const float d = (float)__builtin_sqrt((double)t);
+  const double r = 1.0 / (double)d;
+  uint32_t y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = cvt_pk_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
+  x0 = make_uint4(y[0], y[1], y[2], y[3]);
+  x1 = make_uint4(y[4], y[5], y[6], y[7]);
 }
 
 }  // namespace kda

@@ -11,8 +11,10 @@
 // independent of the state, so it runs chunk-parallel over the whole chip;
 // only the carry is sequential.
 //
-// intra_kernel -- one 512-thread workgroup (8 waves) per run of up to four
-//   consecutive chunks of one (sequence, value head).  Per chunk:
+// intra_kernel -- persistent: one 512-thread workgroup (8 waves) per compute
+//   unit walks the (value head, chunk slot) work items with a grid stride,
+//   prefetching the next item's inputs while it computes the current one.
+//   Per chunk:
 //     1. the raw q, k, g and beta, prefetched into registers while the
 //        previous chunk was computed, are normalised (bit-exact routine
 //        shared with kda_qk_l2norm), scanned (G, kept in log2 units) and
@@ -86,7 +88,6 @@ constexpr int C = 64;            // chunk length
 constexpr int KD = 128;          // key width == value width
 constexpr int NW = 8;            // waves per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
-constexpr int CPW = 4;           // chunks per intra workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SCALE = 0.08838834764831845f;   // 128^-1/2
 constexpr float SAFE_EXP2 = 120.0f;             // largest split-factor exponent (base 2)
@@ -198,47 +199,77 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& x, float* f) {
   f[6] = bf16lo(x.w); f[7] = bf16hi(x.w);
 }
 
-// Raw inputs of one chunk held in registers (prefetch buffer).
-//   qk[m]: row rg + 32m of the 128 stacked rows (q rows 0..63, k rows 64..127),
-//          8 bf16 at column 8*l16, with rg = tid/16, l16 = tid%16
+// Raw inputs of one chunk held in registers (prefetch buffer), exactly as
+// loaded; rows past the chunk's end (clamped to its last row when loading)
+// are zeroed only when the buffer is consumed, so that nothing touches the
+// loaded registers until then and the loads stay in flight.
+//   qk[2m], qk[2m+1]: q (m = 0) or k (m = 1) row tid/8, 16 bf16 at column
+//          16*(tid%8)
 //   gv[r]: g of token 4*seg + r, channels 4*c4..4*c4+3 (seg = tid/32, c4 = tid%32)
 struct Raw {
   uint4 qk[4];
   float4 gv[4];
-  float beta;
+  uint32_t beta;   // bf16 bits of beta for token tid (tid < 64)
+  int nvalid;
 };
 
-// Loads are unconditional (rows past the chunk's end are clamped to its last
-// valid row and zeroed by a select): a load inside a branch would be waited
-// for inside that branch.
 __device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
                                          int hv, int tid) {
-  const int rg = tid >> 4, l16 = tid & 15;
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  const int rg = tid >> 3, l8 = tid & 7;
+  const int64_t row = (trow + min(rg, nvalid - 1)) * p.H + hq;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int i = (rg + 32 * m) & (C - 1);
-    const uint16_t* base = (m < 2) ? p.q : p.k;
-    const uint4 x = *reinterpret_cast<const uint4*>(base + ((trow + min(i, nvalid - 1)) * p.H + hq) * KD + 8 * l16);
-    R.qk[m] = (i < nvalid) ? x : z4;
+  for (int m = 0; m < 2; ++m) {
+    const uint4* src = reinterpret_cast<const uint4*>((m == 0 ? p.q : p.k) + row * KD + 16 * l8);
+    R.qk[2 * m] = src[0];
+    R.qk[2 * m + 1] = src[1];
   }
   const int seg = tid >> 5, c4 = tid & 31;
-  const float4 zf = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * seg + r;
-    const float4 x = *reinterpret_cast<const float4*>(p.g + ((trow + min(i, nvalid - 1)) * p.HV + hv) * KD + 4 * c4);
-    R.gv[r] = (i < nvalid) ? x : zf;
-  }
-  const float b = bf16f(p.beta[(trow + min(tid, nvalid - 1)) * p.HV + hv]);
-  R.beta = (tid < nvalid) ? b : 0.f;
+  for (int r = 0; r < 4; ++r)
+    R.gv[r] = *reinterpret_cast<const float4*>(p.g + ((trow + min(4 * seg + r, nvalid - 1)) * p.HV + hv) * KD + 4 * c4);
+  R.beta = p.beta[(trow + min(tid & (C - 1), nvalid - 1)) * p.HV + hv];
+  R.nvalid = nvalid;
 }
 
-// First token row and length of sequence n.
+// Zero the rows of a consumed prefetch buffer that lie past the chunk's end.
+__device__ __forceinline__ void mask_raw(Raw& R, int tid) {
+  // Component-wise selects: a select of whole aggregates becomes a select of
+  // their addresses and pushes the buffer out of registers.
+  const bool qk_ok = (tid >> 3) < R.nvalid;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    R.qk[m].x = qk_ok ? R.qk[m].x : 0u;
+    R.qk[m].y = qk_ok ? R.qk[m].y : 0u;
+    R.qk[m].z = qk_ok ? R.qk[m].z : 0u;
+    R.qk[m].w = qk_ok ? R.qk[m].w : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = (4 * (tid >> 5) + r) < R.nvalid;
+    R.gv[r].x = ok ? R.gv[r].x : 0.f;
+    R.gv[r].y = ok ? R.gv[r].y : 0.f;
+    R.gv[r].z = ok ? R.gv[r].z : 0.f;
+    R.gv[r].w = ok ? R.gv[r].w : 0.f;
+  }
+  R.beta = (tid < R.nvalid) ? R.beta : 0u;
+}
+
+// cu_seqlens is read-only for the whole launch, so it is read through the
+// constant address space: with a wave-uniform index the reads become scalar
+// loads, which do not wait on the vector-memory counter (and so not on the
+// prefetch loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+
+__device__ __forceinline__ int32_t cu_at(const Params& p, int n) {
+  return ((const_i32p)(p.cu))[__builtin_amdgcn_readfirstlane(n)];
+}
+
+// First token row and length of sequence n (n is wave-uniform).
 __device__ __forceinline__ void seq_range(const Params& p, int n, int64_t& tok0, int& len) {
   if (p.cu) {
-    tok0 = p.cu[n];
-    len = p.cu[n + 1] - p.cu[n];
+    const int32_t a = cu_at(p, n);
+    tok0 = a;
+    len = cu_at(p, n + 1) - a;
   } else {
     tok0 = int64_t(n) * p.T;
     len = p.T;
@@ -247,7 +278,7 @@ __device__ __forceinline__ void seq_range(const Params& p, int n, int64_t& tok0,
 
 // Workspace slot of chunk 0 of sequence n.
 __device__ __forceinline__ int64_t slot_base(const Params& p, int n) {
-  const int64_t tok0 = p.cu ? int64_t(p.cu[n]) : int64_t(n) * p.T;
+  const int64_t tok0 = p.cu ? int64_t(cu_at(p, n)) : int64_t(n) * p.T;
   return tok0 / C + n;
 }
 
@@ -289,50 +320,59 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  // Workgroup -> value head and a run of CPW consecutive slots.
-  const int hv = blockIdx.x % p.HV;
-  const int64_t s0 = int64_t(blockIdx.x / p.HV) * CPW;
-  const int hq = hv / (p.HV / p.H);
+  // Work item i = slot * HV + hv; this workgroup takes items blockIdx.x,
+  // blockIdx.x + gridDim.x, ...  Slots between sequences are skipped.
+  const int64_t items = p.nslots * p.HV;
+  const int64_t stride = gridDim.x;
+  struct Item {
+    int64_t id, trow, slot;
+    int hv, hq, nvalid;
+  };
+  auto find = [&](int64_t i) {
+    Item it;
+    for (; i < items; i += stride) {
+      const int64_t s = i / p.HV;
+      int c;
+      const int n = slot_owner(p, s, c);
+      if (n < 0) continue;
+      int64_t tok0;
+      int len;
+      seq_range(p, n, tok0, len);
+      it.trow = tok0 + int64_t(c) * C;
+      it.nvalid = min(C, len - c * C);
+      it.slot = s;
+      it.hv = int(i % p.HV);
+      it.hq = it.hv / (p.HV / p.H);
+      break;
+    }
+    it.id = i;
+    return it;
+  };
 
-  // The chunks of this run that exist (slots between sequences are skipped).
-  int nit = 0;
-  int64_t trows[CPW];
-  int nvalids[CPW];
-  int64_t slots[CPW];
-  for (int u = 0; u < CPW; ++u) {
-    const int64_t s = s0 + u;
-    if (s >= p.nslots) break;
-    int c;
-    const int n = slot_owner(p, s, c);
-    if (n < 0) continue;
-    int64_t tok0;
-    int len;
-    seq_range(p, n, tok0, len);
-    trows[nit] = tok0 + int64_t(c) * C;
-    nvalids[nit] = min(C, len - c * C);
-    slots[nit] = s;
-    ++nit;
-  }
-  if (nit == 0) return;
-
+  Item cur = find(blockIdx.x);
+  if (cur.id >= items) return;
   Raw R;
-  load_raw(R, p, trows[0], nvalids[0], hq, hv, tid);
+  load_raw(R, p, cur.trow, cur.nvalid, cur.hq, cur.hv, tid);
 
-  for (int it = 0; it < nit; ++it) {
-    const int nvalid = nvalids[it];
-    const int64_t trow_next = (it + 1 < nit) ? trows[it + 1] : 0;
-    const int nvalid_next = (it + 1 < nit) ? nvalids[it + 1] : 0;
+  while (cur.id < items) {
+    const Item nxt = find(cur.id + stride);
+    const int hv = cur.hv;
+    (void)hv;
 
     // ---------------------------------------------------------- phase 1
     {
-      const int rg = tid >> 4;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint4 y = l2norm_row16(R.qk[m]);
-        *reinterpret_cast<uint4*>(((m < 2) ? sQ : sK) + ((rg + 32 * m) & (C - 1)) * QS + 8 * l16) = y;
-        __builtin_amdgcn_sched_barrier(0);   // one row at a time keeps register use low
+      mask_raw(R, tid);
+      // q^ and k^: one 8-lane group per row, bit-exact normalisation.
+      {
+        const int rg = tid >> 3, l8 = tid & 7;
+        l2norm_row8(R.qk[0], R.qk[1]);
+        l2norm_row8(R.qk[2], R.qk[3]);
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 16 * l8) = R.qk[0];
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 16 * l8 + 8) = R.qk[1];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 16 * l8) = R.qk[2];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 16 * l8 + 8) = R.qk[3];
       }
-      if (tid < C) sBeta[tid] = R.beta;
+      if (tid < C) sBeta[tid] = bf16f(uint16_t(R.beta));
       // g in log2 units, inclusive scan over the 4 tokens this thread holds,
       // then across the 16 four-token segments through LDS.
       const int seg = tid >> 5, c4 = tid & 31;
@@ -345,9 +385,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         gs[r].w = R.gv[r].w * LOG2E + (r ? gs[r - 1].w : 0.f);
       }
       *reinterpret_cast<float4*>(sScr + seg * KD + 4 * c4) = gs[3];
-      __syncthreads();
+      lds_barrier();
       // The raw registers are consumed: prefetch the next chunk.
-      if (it + 1 < nit) load_raw(R, p, trow_next, nvalid_next, hq, hv, tid);
+      if (nxt.id < items) load_raw(R, p, nxt.trow, nxt.nvalid, nxt.hq, nxt.hv, tid);
       float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s2 = 0; s2 < seg; ++s2) {
         const float4 t = *reinterpret_cast<const float4*>(sScr + s2 * KD + 4 * c4);
@@ -361,7 +401,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         *reinterpret_cast<float4*>(sG + (4 * seg + r) * GS + 4 * c4) =
             make_float4(gs[r].x + off.x, gs[r].y + off.y, gs[r].z + off.z, gs[r].w + off.w);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------------------------------------------------- phase 2: L, Aqk
     // The 10 blocks on or below the diagonal over 8 waves; waves 2..7 also
@@ -476,7 +516,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------------------------------------------------- phase 3: solve
     // T = (I + L)^-1, unit lower triangular.
@@ -513,7 +553,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[(16 * blk + 4 * h + r) * LS + 16 * blk + cc] = x[r];
     }
-    __syncthreads();
+    lds_barrier();
     // Off-diagonal blocks, one block row at a time, on fp32 MFMA (16x16x4):
     //   P_IJ = sum_{M=J}^{I-1} L_IM T_MJ,   T_IJ = -T_II P_IJ.
     // For the second product the contraction index of k-step s in lane group
@@ -539,7 +579,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * gq + r) * LS + 16 * J + l16] = X[r];
       }
-      __syncthreads();
+      lds_barrier();
     }
     // A = T diag(beta), lower triangular, as fp16 (8 entries per thread).
     {
@@ -558,7 +598,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
           make_uint4(pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]), pack_f16(a[6], a[7]));
     }
     if (tid < KD) sGam[tid] = ex2(sG[(C - 1) * GS + tid]);
-    __syncthreads();
+    lds_barrier();
 
     // ---------------------------------------------------------- phase 4: E, Kg, Qg, W
     // Thread t handles channels c2, c2+1 (c2 = 2*(t%64)) for tokens
@@ -595,7 +635,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj0) = make_uint2(pack_f16(kv1[0], kv1[1]), pack_f16(kv1[2], kv1[3]));
       *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj4) = make_uint2(pack_f16(kv1[4], kv1[5]), pack_f16(kv1[6], kv1[7]));
     }
-    __syncthreads();
+    lds_barrier();
     // Qg (over q^, now no longer read) in the permuted channel layout; c2 and
     // c2 + 1 stay adjacent there.
     {
@@ -621,13 +661,18 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sW[(16 * mt + 4 * gq + r) * QS + pc] = f16_bits(-acc[r]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // Chunk outputs -> workspace slot, in slot order (coalesced 16-byte
-    // stores), gathering each piece from its swizzled source position.
+    // stores), gathering each piece from its swizzled source position.  A
+    // fixed number of unconditional stores per thread (the overhang repeats
+    // the slot's last piece) keeps the store count known at compile time, so
+    // the next chunk waits only for its prefetched inputs, not for these.
     {
-      unsigned char* dst = p.ws + (int64_t(hv) * p.nslots + slots[it]) * WS_SLOT;
-      for (int u = tid; u < SLOT_U4; u += NT) {
+      unsigned char* dst = p.ws + (int64_t(cur.hv) * p.nslots + cur.slot) * WS_SLOT;
+#pragma unroll
+      for (int k = 0; k < (SLOT_U4 + NT - 1) / NT; ++k) {
+        const int u = min(tid + k * NT, SLOT_U4 - 1);
         const int b = u * 16;
         const unsigned char* src;
         if (b < WS_KGT) {          // W, Qg: 64 rows of 16 pieces
@@ -649,7 +694,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         *reinterpret_cast<uint4*>(dst + b) = *reinterpret_cast<const uint4*>(src);
       }
     }
-    __syncthreads();
+    lds_barrier();
+    cur = nxt;
   }
 }
 
@@ -691,6 +737,7 @@ __device__ __forceinline__ f16x8 swz_read(const unsigned char* base, int row, in
 
 constexpr int WAIT_LDS = 0xC07F;   // s_waitcnt lgkmcnt(0)
 constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
+constexpr int WAIT_VM16 = 0x4F70;  // s_waitcnt vmcnt(16)
 
 __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -727,7 +774,7 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
     load_v_lds(sv, p, tok0, min(C, len), hv, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-  __syncthreads();
+  lds_barrier();
 
   for (int c = 0; c < nch; ++c) {
     const int nvalid = min(C, len - c * C);
@@ -834,9 +881,13 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
       for (int rt = 0; rt < 8; ++rt)
         S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq), Vh[s],
                                                        S[rt], 0, 0, 0);
-    // The next chunk's slot and v tile must have landed before anyone reads them.
-    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-    __syncthreads();
+    // The next chunk's slot and v tile must have landed before anyone reads
+    // them.  They were issued before this chunk's 16 o stores; a full chunk
+    // issues exactly those 16 stores afterwards, so waiting until at most 16
+    // memory operations remain covers the loads without waiting for the stores.
+    if (nvalid == C) __builtin_amdgcn_s_waitcnt(WAIT_VM16);
+    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    lds_barrier();
   }
 
   float* sf = p.sfin + (int64_t(n) * p.HV + hv) * KD * KD;
@@ -859,13 +910,26 @@ int set_lds(Kern kern, int bytes, std::atomic<bool>& done) {
 
 int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq + 1; }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 int launch(const Params& p, hipStream_t stream) {
   static std::atomic<bool> intra_set{false}, inter_set{false};
   if (set_lds(&intra_kernel, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
-  const int64_t intra_blocks = (p.nslots + CPW - 1) / CPW * p.HV;
+  const int64_t items = p.nslots * p.HV;
+  const int64_t intra_blocks = items < device_cus() ? items : device_cus();
   const int64_t inter_blocks = int64_t(p.N) * p.HV;
-  if (intra_blocks > 0x7fffffff || inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
+  if (inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
   hipLaunchKernelGGL(intra_kernel, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
   const int st = launch_status();
   if (st != KDA_OK) return st;
