@@ -213,21 +213,51 @@ struct Raw {
   int nvalid;
 };
 
+// A wave-uniform global pointer, held in scalar registers.
+typedef const __attribute__((address_space(1))) unsigned char* gbytes;
+
+__device__ __forceinline__ gbytes uniform_ptr(const void* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return (gbytes)((uint64_t(hi) << 32) | lo);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_u4(gbytes base, uint32_t byte_off) {
+  const u32x4_t x = *(const __attribute__((address_space(1))) u32x4_t*)(base + byte_off);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+__device__ __forceinline__ float4 load_f4(gbytes base, uint32_t byte_off) {
+  const f32x4_t x = *(const __attribute__((address_space(1))) f32x4_t*)(base + byte_off);
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+__device__ __forceinline__ uint16_t load_u16(gbytes base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(1))) uint16_t*)(base + byte_off);
+}
+
 __device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
                                          int hv, int tid) {
+  // Scalar 64-bit bases plus 32-bit lane byte offsets.
   const int rg = tid >> 3, l8 = tid & 7;
-  const int64_t row = (trow + min(rg, nvalid - 1)) * p.H + hq;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const uint4* src = reinterpret_cast<const uint4*>((m == 0 ? p.q : p.k) + row * KD + 16 * l8);
-    R.qk[2 * m] = src[0];
-    R.qk[2 * m + 1] = src[1];
-  }
+  const uint32_t oqk = uint32_t(min(rg, nvalid - 1) * p.H * KD + 16 * l8) * 2u;
+  const gbytes bq = uniform_ptr(p.q + (trow * p.H + hq) * KD);
+  const gbytes bk = uniform_ptr(p.k + (trow * p.H + hq) * KD);
+  R.qk[0] = load_u4(bq, oqk);
+  R.qk[1] = load_u4(bq, oqk + 16u);
+  R.qk[2] = load_u4(bk, oqk);
+  R.qk[3] = load_u4(bk, oqk + 16u);
   const int seg = tid >> 5, c4 = tid & 31;
+  const gbytes bg = uniform_ptr(p.g + (trow * p.HV + hv) * KD);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    R.gv[r] = *reinterpret_cast<const float4*>(p.g + ((trow + min(4 * seg + r, nvalid - 1)) * p.HV + hv) * KD + 4 * c4);
-  R.beta = p.beta[(trow + min(tid & (C - 1), nvalid - 1)) * p.HV + hv];
+    R.gv[r] = load_f4(bg, uint32_t(min(4 * seg + r, nvalid - 1) * p.HV * KD + 4 * c4) * 4u);
+  const gbytes bb = uniform_ptr(p.beta + trow * p.HV + hv);
+  R.beta = load_u16(bb, uint32_t(min(tid & (C - 1), nvalid - 1) * p.HV) * 2u);
   R.nvalid = nvalid;
 }
 
@@ -283,7 +313,7 @@ __device__ __forceinline__ int64_t slot_base(const Params& p, int n) {
 }
 
 // The sequence owning workspace slot s, or -1 for a slot between sequences.
-__device__ __forceinline__ int slot_owner(const Params& p, int64_t s, int& chunk) {
+__device__ __forceinline__ int slot_owner(const Params& p, int s, int& chunk) {
   int lo = 0, hi = p.N - 1;                 // largest n with slot_base(n) <= s
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -322,16 +352,17 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 
   // Work item i = slot * HV + hv; this workgroup takes items blockIdx.x,
   // blockIdx.x + gridDim.x, ...  Slots between sequences are skipped.
-  const int64_t items = p.nslots * p.HV;
-  const int64_t stride = gridDim.x;
+  // Item ids fit in 32 bits (checked on the host).
+  const int items = int(p.nslots) * p.HV;
+  const int stride = gridDim.x;
   struct Item {
-    int64_t id, trow, slot;
-    int hv, hq, nvalid;
+    int64_t trow;
+    int id, slot, hv, hq, nvalid;
   };
-  auto find = [&](int64_t i) {
+  auto find = [&](int i) {
     Item it;
     for (; i < items; i += stride) {
-      const int64_t s = i / p.HV;
+      const int s = i / p.HV;
       int c;
       const int n = slot_owner(p, s, c);
       if (n < 0) continue;
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       it.trow = tok0 + int64_t(c) * C;
       it.nvalid = min(C, len - c * C);
       it.slot = s;
-      it.hv = int(i % p.HV);
+      it.hv = i - s * p.HV;
       it.hq = it.hv / (p.HV / p.H);
       break;
     }
@@ -349,13 +380,13 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     return it;
   };
 
-  Item cur = find(blockIdx.x);
-  if (cur.id >= items) return;
+  Item first = find(blockIdx.x);
+  if (first.id >= items) return;
   Raw R;
-  load_raw(R, p, cur.trow, cur.nvalid, cur.hq, cur.hv, tid);
+  load_raw(R, p, first.trow, first.nvalid, first.hq, first.hv, tid);
 
-  while (cur.id < items) {
-    const Item nxt = find(cur.id + stride);
+  // One chunk item: consumes R (cur's inputs), refills it with nxt's.
+  auto chunk = [&](const Item& cur, const Item& nxt) __attribute__((always_inline)) {
     const int hv = cur.hv;
     (void)hv;
 
@@ -388,13 +419,17 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       lds_barrier();
       // The raw registers are consumed: prefetch the next chunk.
       if (nxt.id < items) load_raw(R, p, nxt.trow, nxt.nvalid, nxt.hq, nxt.hv, tid);
+      // Exclusive offset of this segment: all 15 candidate totals are read
+      // (independent reads) and the earlier ones summed in order.
       float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s2 = 0; s2 < seg; ++s2) {
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2) {
         const float4 t = *reinterpret_cast<const float4*>(sScr + s2 * KD + 4 * c4);
-        off.x += t.x;
-        off.y += t.y;
-        off.z += t.z;
-        off.w += t.w;
+        const bool use = s2 < seg;
+        off.x += use ? t.x : 0.f;
+        off.y += use ? t.y : 0.f;
+        off.z += use ? t.z : 0.f;
+        off.w += use ? t.w : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -695,7 +730,20 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       }
     }
     lds_barrier();
-    cur = nxt;
+  };
+
+  // Loads and stores share one in-order completion counter.  Every item
+  // issues the next item's loads and then its own 9 workspace stores, so the
+  // wait for the prefetched registers may leave those stores in flight.  The
+  // first item is peeled off the loop so that the loop is entered in that
+  // same state; with a plain loop the entry path (loads only) would make the
+  // compiler's wait at the loop head conservative and drain the stores too.
+  Item nxt = find(first.id + stride);
+  chunk(first, nxt);
+  while (nxt.id < items) {
+    const Item cur = nxt;
+    nxt = find(cur.id + stride);
+    chunk(cur, nxt);
   }
 }
 
@@ -927,6 +975,7 @@ int launch(const Params& p, hipStream_t stream) {
   if (set_lds(&intra_kernel, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t items = p.nslots * p.HV;
+  if (items > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
   const int64_t intra_blocks = items < device_cus() ? items : device_cus();
   const int64_t inter_blocks = int64_t(p.N) * p.HV;
   if (inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
