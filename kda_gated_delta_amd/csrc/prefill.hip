@@ -133,16 +133,22 @@ constexpr int INTRA_LDS = OFF_GAM + KD * 4;
 static_assert(INTRA_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
 
-// inter_kernel LDS map: two verbatim copies of workspace slots (filled by
-// direct global-to-LDS loads, one 1 KB block per wave instruction; the last
-// block overhangs the slot, hence the padding) and, per wave, the v tile of
-// its 16 columns.
+// inter_kernel: two workgroups per (sequence, value head), each owning 64 of
+// the 128 state columns with 4 waves of 16 columns.  LDS map: two verbatim
+// copies of workspace slots (filled by direct global-to-LDS loads, one 1 KB
+// block per wave instruction; the last block overhangs the slot, hence the
+// padding) and, per wave, the v tile of its 16 columns.
+constexpr int NWI = 4;                                    // waves per inter workgroup
+constexpr int NTI = NWI * 64;
+constexpr int VT = NWI * 16;                              // state columns per workgroup
 constexpr int SLOT_U4 = WS_SLOT / 16;                     // 16-byte pieces per slot
 constexpr int SLOT_BLOCKS = (WS_SLOT + 1023) / 1024;      // 1 KB load blocks per slot
+constexpr int BLOCKS_PER_WAVE = (SLOT_BLOCKS + NWI - 1) / NWI;
 constexpr int BUF_BYTES = SLOT_BLOCKS * 1024;
-constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [8 waves][64 tokens][16 columns]
-constexpr int INTER_LDS = OFF_V + NW * C * 16 * 2;
+constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [4 waves][64 tokens][16 columns]
+constexpr int INTER_LDS = OFF_V + NWI * C * 16 * 2;
 static_assert(INTER_LDS <= 160 * 1024, "LDS budget");
+static_assert(2 * VT == KD, "two workgroups cover the state columns");
 
 struct Params {
   const uint16_t* q;
@@ -749,30 +755,33 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global-to-LDS copy of one workspace slot: 1 KB blocks, wave w
-// issuing blocks w, w + 8, ...  Each lane moves 16 bytes to the block base +
-// 16 * lane; pieces past the end of the slot re-read its last piece into the
-// buffer's padding.
-__device__ __forceinline__ void load_slot_lds(unsigned char* buf, const unsigned char* slot, int wave,
-                                              int lane) {
+// Direct global-to-LDS copy of part of one workspace slot: 1 KB blocks,
+// wave w issuing blocks w, w + 4, ... (its j-th block for j in [j0, j1)).
+// Each lane moves 16 bytes to the block base + 16 * lane; pieces past the end
+// of the slot re-read its last piece into the buffer's padding, and a wave
+// with fewer blocks repeats the last block (same bytes to the same place), so
+// every wave issues the same number of loads.
+__device__ __forceinline__ void load_slot_part(unsigned char* buf, const unsigned char* slot, int wave, int lane,
+                                               int j0, int j1) {
 #pragma unroll
-  for (int blk = wave; blk < SLOT_BLOCKS; blk += NW) {
+  for (int j = j0; j < j1; ++j) {
+    const int blk = min(wave + NWI * j, SLOT_BLOCKS - 1);
     const int u = min(blk * 64 + lane, SLOT_U4 - 1);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(slot + u * 16),
                                      (lds_void*)(buf + blk * 1024), 16, 0, 0);
   }
 }
 
-// Direct load of this wave's v tile (64 tokens x 16 columns, bf16) into its
-// LDS region: two 1 KB blocks, lane l carrying token 32h + l/2, columns
-// 16*wave + 8*(l&1)..+7.  Rows past the chunk's end are clamped here and
-// zeroed when read.
+// Direct load of this wave's v tile (64 tokens x 16 columns from column c0,
+// bf16) into its LDS region: two 1 KB blocks, lane l carrying token
+// 32h + l/2, columns c0 + 8*(l&1)..+7.  Rows past the chunk's end are clamped
+// here and zeroed when read.
 __device__ __forceinline__ void load_v_lds(unsigned char* sv, const Params& p, int64_t trow, int nvalid,
-                                           int hv, int wave, int lane) {
+                                           int hv, int c0, int lane) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = min(32 * h + (lane >> 1), nvalid - 1);
-    const uint16_t* src = p.v + ((trow + t) * p.HV + hv) * KD + 16 * wave + 8 * (lane & 1);
+    const uint16_t* src = p.v + ((trow + t) * p.HV + hv) * KD + c0 + 8 * (lane & 1);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                      (lds_void*)(sv + h * 1024), 16, 0, 0);
   }
@@ -785,9 +794,19 @@ __device__ __forceinline__ f16x8 swz_read(const unsigned char* base, int row, in
 
 constexpr int WAIT_LDS = 0xC07F;   // s_waitcnt lgkmcnt(0)
 constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
-constexpr int WAIT_VM16 = 0x4F70;  // s_waitcnt vmcnt(16)
+// Word 3 of a raw (untyped) buffer resource on gfx9-family chips: 32-bit
+// data format, no swizzle.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+constexpr int WAIT_VM4 = 0x0F74;   // s_waitcnt vmcnt(4): low vmcnt bits 3:0, high bits 15:14 zero
 
-__global__ __launch_bounds__(NT) void inter_kernel(Params p) {
+// Slot prefetch split into three groups issued between the products of a
+// chunk, so the vector-memory pipe drains while the matrix cores work.
+constexpr int PF1 = 6, PF2 = 12;
+
+// One workgroup per CU (its LDS footprint), so one wave per SIMD: telling the
+// compiler lets it schedule for latency with the full register file.
+__global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) void inter_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -796,30 +815,39 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  const int unit = blockIdx.x;
+  // Workgroups 16g + j and 16g + 8 + j (j < 8) are the two column halves of
+  // unit 8g + j: with workgroups dealt round-robin over the 8 XCDs, both
+  // halves of a unit run on one XCD and share its L2 for the slot reads.
+  const int grp = blockIdx.x >> 4, within = blockIdx.x & 15;
+  const int half = within >> 3;
+  const int unit = 8 * grp + (within & 7);
   if (unit >= p.N * p.HV) return;
   const int n = unit / p.HV;
-  const int hv = unit % p.HV;
+  const int hv = unit - n * p.HV;
   int64_t tok0;
   int len;
   seq_range(p, n, tok0, len);
   const int nch = (len + C - 1) / C;
   const unsigned char* wsh = p.ws + (int64_t(hv) * p.nslots + slot_base(p, n)) * WS_SLOT;
   unsigned char* sv = smem + OFF_V + wave * (C * 16 * 2);
+  const int c0 = half * VT + wave * 16;          // first state column of this wave
 
-  const int col = wave * 16 + l16;               // this lane's state column
+  const int col = c0 + l16;                      // this lane's state column
   f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
-  {
-    const float* s0 = p.s0 ? p.s0 + (int64_t(n) * p.HV + hv) * KD * KD : nullptr;
+  if (p.s0) {   // one branch around all 32 loads, so they are in flight together
+    const float* s0 = p.s0 + (int64_t(n) * p.HV + hv) * KD * KD;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[rt][r] = s0 ? s0[(16 * rt + 4 * gq + r) * KD + col] : 0.f;
+      for (int r = 0; r < 4; ++r) S[rt][r] = s0[(16 * rt + 4 * gq + r) * KD + col];
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   if (nch > 0) {
-    load_slot_lds(smem, wsh, wave, lane);
-    load_v_lds(sv, p, tok0, min(C, len), hv, wave, lane);
+    load_slot_part(smem, wsh, wave, lane, 0, BLOCKS_PER_WAVE);
+    load_v_lds(sv, p, tok0, min(C, len), hv, c0, lane);
   }
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);
   lds_barrier();
@@ -828,9 +856,11 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
     const int nvalid = min(C, len - c * C);
     const int64_t trow = tok0 + int64_t(c) * C;
     const unsigned char* cur = smem + (c & 1) * BUF_BYTES;
-    const bool more = c + 1 < nch;
-    // The other buffer was last read in the previous chunk: refill it now.
-    if (more) load_slot_lds(smem + ((c + 1) & 1) * BUF_BYTES, wsh + int64_t(c + 1) * WS_SLOT, wave, lane);
+    unsigned char* nbuf = smem + ((c + 1) & 1) * BUF_BYTES;   // last read in the previous chunk
+    // The next chunk's inputs, prefetched unconditionally (the last chunk
+    // re-reads its own, which nothing uses) so the body has no branches.
+    const int cn = min(c + 1, nch - 1);
+    const unsigned char* nslot = wsh + int64_t(cn) * WS_SLOT;
 
     const unsigned char* sW = cur + WS_W;
     const unsigned char* sQg = cur + WS_QG;
@@ -849,17 +879,30 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
         const float x = bf16f(*reinterpret_cast<const uint16_t*>(sv + i * 32 + l16 * 2));
         Vv[s][e] = (_Float16)((i < nvalid) ? x : 0.f);
       }
-    // This wave's v slot is free once its reads are done: fetch the next chunk's.
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(WAIT_LDS);
-      load_v_lds(sv, p, trow + C, min(C, len - (c + 1) * C), hv, wave, lane);
-    }
+    // This wave's v slot is free once its reads are done: fetch the next
+    // chunk's, then the first part of the next slot.
+    __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+    load_v_lds(sv, p, tok0 + int64_t(cn) * C, min(C, len - cn * C), hv, c0, lane);
+    load_slot_part(nbuf, nslot, wave, lane, 0, PF1);
 
     // Contraction orders: for products with S the channel index of k-slot
     // (gq, e) is 32s + 4gq + e (e < 4) or 32s + 16 + 4gq + (e - 4), which is
     // exactly where the float32 S accumulator already holds it; products with
     // Vnew use the same permutation over tokens.  The workspace stores W, Qg,
     // Kg^T and Aqk in that order, so each operand is one 16-byte read.
+    //
+    // With one wave per SIMD nothing else hides LDS latency, so every
+    // product's operands are read in one burst a product ahead of its MFMAs;
+    // sched_barrier keeps the compiler from re-interleaving them one by one.
+    f16x8 oA[6], oW[16];
+#pragma unroll
+    for (int mt = 0, i = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s) oA[i++] = swz_read(sA, 16 * mt + l16, 128, 4 * s + gq);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oW[4 * s + mt] = swz_read(sW, 16 * mt + l16, 256, 4 * s + gq);
     f16x8 Sh[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -868,24 +911,50 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
         Sh[s][r] = (_Float16)S[2 * s][r];
         Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
       }
+    __builtin_amdgcn_sched_barrier(0);
+
     // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
-    // accumulation chains, interleaved.
+    // accumulation chains.
     f32x4 Vn[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Vn[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int mt = 0, i = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        if (s <= (mt >> 1))
-          Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sA, 16 * mt + l16, 128, 4 * s + gq), Vv[s],
-                                                          Vn[mt], 0, 0, 0);
+      for (int s = 0; s <= (mt >> 1); ++s)
+        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oA[i++], Vv[s], Vn[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_slot_part(nbuf, nslot, wave, lane, PF1, PF2);
+    f16x8 oQ[16];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oQ[4 * s + mt] = swz_read(sQg, 16 * mt + l16, 256, 4 * s + gq);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sW, 16 * mt + l16, 256, 4 * s + gq), Sh[s],
-                                                        Vn[mt], 0, 0, 0);
+        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oW[4 * s + mt], Sh[s], Vn[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_slot_part(nbuf, nslot, wave, lane, PF2, BLOCKS_PER_WAVE);
+    f16x8 oQK[6];
+#pragma unroll
+    for (int mt = 0, i = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s) oQK[i++] = swz_read(sAqk, 16 * mt + l16, 128, 4 * s + gq);
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T = S^T Qg^T + Vnew^T Aqk^T: the same operands as O = Qg S + Aqk Vnew
+    // with their roles swapped, so each lane ends up holding four adjacent
+    // columns of one token and writes them with one 8-byte store.
+    f32x4 Ot[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Sh[s], oQ[4 * s + mt], Ot[mt], 0, 0, 0);
     f16x8 Vh[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -894,47 +963,48 @@ __global__ __launch_bounds__(NT) void inter_kernel(Params p) {
         Vh[s][r] = (_Float16)Vn[2 * s][r];
         Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
       }
-    // O = Qg S + Aqk Vnew, stored straight from the accumulators.
-    f32x4 Ot[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sQg, 16 * mt + l16, 256, 4 * s + gq), Sh[s],
-                                                        Ot[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 oK[16];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        if (s <= (mt >> 1))
-          Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sAqk, 16 * mt + l16, 128, 4 * s + gq), Vh[s],
-                                                          Ot[mt], 0, 0, 0);
+      for (int rt = 0; rt < 8; ++rt) oK[8 * s + rt] = swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq);
+    f32x4 gam[8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int rt = 0; rt < 8; ++rt) gam[rt] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * gq);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mt + 4 * gq + r;
-        if (i < nvalid) p.o[((trow + i) * p.HV + hv) * KD + col] = uint16_t(bf16_rne(Ot[mt][r]));
-      }
+    for (int mt = 0, i = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s)
+        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vh[s], oQK[i++], Ot[mt], 0, 0, 0);
     // S = e^{G_last} S + Kg^T Vnew; eight independent row tiles.
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[rt][r] *= sGam[16 * rt + 4 * gq + r];
+      for (int r = 0; r < 4; ++r) S[rt][r] *= gam[rt][r];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq), Vh[s],
-                                                       S[rt], 0, 0, 0);
+        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oK[8 * s + rt], Vh[s], S[rt], 0, 0, 0);
+    // Buffer stores against a range of exactly the chunk's valid rows: the
+    // hardware drops the rows past the end, with no branch.
+    {
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          p.o + (trow * p.HV + hv) * KD, 0, nvalid * p.HV * KD * 2, BUF_RSRC_WORD3);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int t = 16 * mt + l16;
+        const u32x2_t w = {pack_bf16(Ot[mt][0], Ot[mt][1]), pack_bf16(Ot[mt][2], Ot[mt][3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, (t * p.HV * KD + c0 + 4 * gq) * 2, 0, 0);
+      }
+    }
     // The next chunk's slot and v tile must have landed before anyone reads
-    // them.  They were issued before this chunk's 16 o stores; a full chunk
-    // issues exactly those 16 stores afterwards, so waiting until at most 16
-    // memory operations remain covers the loads without waiting for the stores.
-    if (nvalid == C) __builtin_amdgcn_s_waitcnt(WAIT_VM16);
-    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    // them.  They were issued before this chunk's 4 o stores, and exactly
+    // those 4 stores follow them, so waiting until at most 4 memory
+    // operations remain covers the loads without waiting for the stores.
+    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
     lds_barrier();
   }
 
@@ -977,12 +1047,13 @@ int launch(const Params& p, hipStream_t stream) {
   const int64_t items = p.nslots * p.HV;
   if (items > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
   const int64_t intra_blocks = items < device_cus() ? items : device_cus();
-  const int64_t inter_blocks = int64_t(p.N) * p.HV;
+  const int64_t units = int64_t(p.N) * p.HV;
+  const int64_t inter_blocks = 16 * ((units + 7) / 8);   // two column halves per unit
   if (inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
   hipLaunchKernelGGL(intra_kernel, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
   const int st = launch_status();
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NT), INTER_LDS, stream, p);
+  hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NTI), INTER_LDS, stream, p);
   return launch_status();
 }
 
