@@ -10,10 +10,12 @@ decode runs cache-cold.
 
 Prints one JSON line:
   value        prefill tokens/s (T / mean prefill kernel time)
-  roofline     the prefill kernel against the HBM roofline (algorithmic
-               bytes per launch / mean launch time, HIP events on the launch
-               stream); traffic is filled from committed rocprofv3 counter
-               summaries when they were taken on the current kernel source
+  roofline     the prefill entry point -- its two kernels, intra_kernel then
+               inter_kernel, timed together by HIP events on the launch
+               stream -- against the HBM roofline: algorithmic bytes per
+               call / mean call time.  traffic is the measured HBM bytes per
+               call from the committed rocprofv3 counter summary when that
+               was taken on the current kernel source, else null
   cpu_baseline the fp64 oracle (token-by-token form) on a bounded sample of
                the same prefill workload, on this host's cores
 Only --gpus 1 is supported: the library runs on one GPU.
@@ -80,33 +82,111 @@ def traffic_from_profiles():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, heads, seconds_hint):
-    """Time the fp64 recurrent oracle on `heads` value heads of the prefill
-    workload (all T tokens); scale to the full workload's tokens/s."""
+def cpu_baseline(inp, heads, target_s):
+    """Time the fp64 recurrent oracle on a bounded sample of the prefill
+    workload: the first value heads over the first tokens, sized from pilot
+    runs so that the timed run takes about `target_s` seconds.  Reported as
+    tokens/s of the full workload (all value heads)."""
     import numpy as np
     import oracle
     h = slice(0, heads)
-    q = inp.q[:, :, h].float().numpy()
-    k = inp.k[:, :, h].float().numpy()
-    v = inp.v[:, :, h].float().numpy()
-    g = inp.g[:, :, h].numpy()
-    b = inp.beta[:, :, h].float().numpy()
-    s0 = inp.initial_state[:, h].numpy()
-    c0 = time.process_time()
-    t0 = time.perf_counter()
-    oracle.recurrent(q, k, v, g, b, s0)
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
     T = inp.q.shape[1]
     HV = inp.v.shape[2]
+
+    def run(n):
+        q = inp.q[:, :n, h].float().numpy()
+        k = inp.k[:, :n, h].float().numpy()
+        v = inp.v[:, :n, h].float().numpy()
+        g = inp.g[:, :n, h].numpy()
+        b = inp.beta[:, :n, h].float().numpy()
+        s0 = inp.initial_state[:, h].numpy()
+        c0 = time.process_time()
+        t0 = time.perf_counter()
+        oracle.recurrent(q, k, v, g, b, s0)
+        return time.perf_counter() - t0, time.process_time() - c0
+
+    # Pilot on `heads` heads over all tokens (the oracle is fast enough on the
+    # hosts here), then widen the head count so the timed run lands near
+    # target_s; on a slow host shorten the token range instead.
+    n = min(T, 256)
+    w, _ = run(n)
+    n = int(min(T, max(n, n * target_s / max(w, 1e-6))))
+    if n == T:
+        w, _ = run(n)
+        heads = int(min(HV, max(heads, heads * target_s / max(w, 1e-6))))
+        h = slice(0, heads)
+    wall, cpu = run(n)
     return {
-        "value": T * heads / HV / wall,
+        "value": n * heads / HV / wall,
         "unit": "tokens/s",
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": f"fp64 token-by-token oracle on {heads} of {HV} value heads x all {T} tokens "
-                  f"({wall:.1f} s); tokens/s scaled to all {HV} heads; host has {os.cpu_count()} cpus",
+        "sample": f"fp64 token-by-token oracle on the prefill workload's first {heads} of {HV} value heads "
+                  f"x first {n} of {T} tokens ({wall:.1f} s wall, {cpu:.1f} s cpu); tokens/s scaled to all "
+                  f"{HV} heads; host reports {os.cpu_count()} cpus",
     }
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out_path):
+    """Per-launch HBM bytes of the prefill entry point from rocprofv3 counter
+    collections (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by
+    what the counter reads for a plain copy of copy_bytes bytes."""
+    import csv
+
+    def per_kernel(path, counter):
+        sums = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                sums.setdefault(name, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in sums.items()}
+
+    def pick(d, key):
+        vals = [v for k, v in d.items() if key in k]
+        if not vals:
+            raise SystemExit(f"no {key} dispatches in the counter file")
+        return vals[0]
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    cf = max(per_kernel(copy_fetch_csv, "FETCH_SIZE").values())
+    cw = max(per_kernel(copy_write_csv, "WRITE_SIZE").values())
+    kib = copy_bytes / 1024.0
+    f_scale, w_scale = cf / kib, cw / kib
+    rec = {
+        "workload": "prefill B=1 H=HV=96 T=8192 K=V=128",
+        "prefill_source_sha256_16": source_hash("prefill.hip"),
+        "copy_bytes": copy_bytes,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "kernels": {},
+    }
+    total = 0.0
+    for key in ("intra_kernel", "inter_kernel"):
+        fb = pick(f, key) / f_scale * 1024.0
+        wb = pick(w, key) / w_scale * 1024.0
+        rec["kernels"][key] = {"fetch_bytes": fb, "write_bytes": wb}
+        total += fb + wb
+    rec["hbm_bytes_per_launch"] = total
+    with open(out_path, "w") as fo:
+        json.dump(rec, fo, indent=1)
+        fo.write("\n")
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -118,7 +198,17 @@ def main():
     ap.add_argument("--H", type=int, default=96)
     ap.add_argument("--decode-B", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=8, help="value heads in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                           "COPY_WRITE_CSV", "COPY_BYTES", "OUT_JSON"),
+                    help="only summarise rocprofv3 counter files into the traffic record")
     args = ap.parse_args()
+    if args.traffic_summary:
+        a = args.traffic_summary
+        traffic_summary(a[0], a[1], a[2], a[3], int(a[4]), a[5])
+        return
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               f"(run with --gpus 1)", file=sys.stderr)
@@ -131,6 +221,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     kda.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -217,6 +310,7 @@ def main():
             "parallelism": "single-gpu",
         },
         "roofline": {
+            "kernel": "kda_chunk_prefill (intra_kernel + inter_kernel)",
             "bound": "hbm",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
@@ -245,7 +339,7 @@ def main():
     }
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, 20)
+        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
