@@ -27,14 +27,16 @@
 //   and the chunk's W, Qg, Kg^T, Aqk, A and exp(G_last) are written to the
 //   workspace (66 KB per chunk and head, fp16 except exp(G_last)).
 //
-// inter_kernel -- one 512-thread workgroup per (sequence, value head).  Wave w
-//   owns state columns 16w..16w+15 and keeps that 128x16 slice of S in
-//   registers as float32 for the whole sequence (the state's columns evolve
-//   independently: column v of S only ever meets column v of the values).
-//   Chunk blocks stream through two LDS buffers (the next chunk is loaded
-//   while the current one is computed).  Per chunk, on MFMA: U = A v and
-//   Vnew = U - W S accumulate in float32 (U is never rounded), O = Qg S +
-//   Aqk Vnew, S = exp(G_last) S + Kg^T Vnew.
+// inter_kernel -- two 256-thread workgroups per (sequence, value head), one
+//   per half of the state's 128 columns (the columns evolve independently:
+//   column v of S only ever meets column v of the values), placed on the
+//   same XCD so the second read of each chunk's workspace slot hits L2.
+//   Wave w of a half owns 16 columns and keeps that 128x16 slice of S in
+//   registers as float32 for the whole sequence.  Chunk slots stream through
+//   two LDS buffers (the next chunk is loaded while the current one is
+//   computed).  Per chunk, on MFMA: U = A v and Vnew = U - W S accumulate in
+//   float32 (U is never rounded), O^T = S^T Qg^T + Vnew^T Aqk^T, and
+//   S = exp(G_last) S + Kg^T Vnew.
 //
 // Precision: every MFMA operand is fp16 with float32 accumulation, and the
 // state is carried in float32.  fp16's 11-bit significand keeps the final
