@@ -92,6 +92,10 @@ constexpr int NW = 8;            // waves per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SCALE = 0.08838834764831845f;   // 128^-1/2
+// Phase 2 block assignment, one 4-bit field per wave: blocks (3,3) (2,2)
+// (1,1) (0,0) (3,2) (2,1) (1,0) (3,1).
+constexpr uint32_t FULL_I = 0x31230123u;
+constexpr uint32_t FULL_J = 0x10120123u;
 constexpr float SAFE_EXP2 = 120.0f;             // largest split-factor exponent (base 2)
 constexpr float F16_EXP2 = 14.0f;               // largest split-factor exponent for fp16 operands
 
@@ -134,6 +138,7 @@ constexpr int OFF_GAM = OFF_BETA + C * 4;                 // fp32 [128]
 constexpr int INTRA_LDS = OFF_GAM + KD * 4;
 static_assert(INTRA_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
+static_assert(KD * AS * 2 >= 2 * 4 * 512 * 4, "phase 2 partial sums fit in the Kg^T region");
 
 // inter_kernel: two workgroups per (sequence, value head), each owning 64 of
 // the 128 state columns with 4 waves of 16 columns.  LDS map: two verbatim
@@ -211,8 +216,8 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& x, float* f) {
 // loaded; rows past the chunk's end (clamped to its last row when loading)
 // are zeroed only when the buffer is consumed, so that nothing touches the
 // loaded registers until then and the loads stay in flight.
-//   qk[2m], qk[2m+1]: q (m = 0) or k (m = 1) row tid/8, 16 bf16 at column
-//          16*(tid%8)
+//   qk[2m], qk[2m+1]: q (m = 0) or k (m = 1) row tid/8, 8 bf16 at columns
+//          8*(tid%8) and 64 + 8*(tid%8)
 //   gv[r]: g of token 4*seg + r, channels 4*c4..4*c4+3 (seg = tid/32, c4 = tid%32)
 struct Raw {
   uint4 qk[4];
@@ -248,17 +253,24 @@ __device__ __forceinline__ uint16_t load_u16(gbytes base, uint32_t byte_off) {
   return *(const __attribute__((address_space(1))) uint16_t*)(base + byte_off);
 }
 
-__device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
-                                         int hv, int tid) {
+// q and k of the chunk: lane tid%8 of row tid/8 takes channels 8*l8..8*l8+7
+// and 64+8*l8..64+8*l8+7, so each load instruction reads whole 128-byte spans.
+__device__ __forceinline__ void load_raw_qk(Raw& R, const Params& p, int64_t trow, int nvalid, int hq,
+                                            int tid) {
   // Scalar 64-bit bases plus 32-bit lane byte offsets.
   const int rg = tid >> 3, l8 = tid & 7;
-  const uint32_t oqk = uint32_t(min(rg, nvalid - 1) * p.H * KD + 16 * l8) * 2u;
+  const uint32_t oqk = uint32_t(min(rg, nvalid - 1) * p.H * KD + 8 * l8) * 2u;
   const gbytes bq = uniform_ptr(p.q + (trow * p.H + hq) * KD);
   const gbytes bk = uniform_ptr(p.k + (trow * p.H + hq) * KD);
   R.qk[0] = load_u4(bq, oqk);
-  R.qk[1] = load_u4(bq, oqk + 16u);
+  R.qk[1] = load_u4(bq, oqk + 128u);
   R.qk[2] = load_u4(bk, oqk);
-  R.qk[3] = load_u4(bk, oqk + 16u);
+  R.qk[3] = load_u4(bk, oqk + 128u);
+  R.nvalid = nvalid;
+}
+
+// g and beta of the chunk.
+__device__ __forceinline__ void load_raw_g(Raw& R, const Params& p, int64_t trow, int nvalid, int hv, int tid) {
   const int seg = tid >> 5, c4 = tid & 31;
   const gbytes bg = uniform_ptr(p.g + (trow * p.HV + hv) * KD);
 #pragma unroll
@@ -266,7 +278,6 @@ __device__ __forceinline__ void load_raw(Raw& R, const Params& p, int64_t trow, 
     R.gv[r] = load_f4(bg, uint32_t(min(4 * seg + r, nvalid - 1) * p.HV * KD + 4 * c4) * 4u);
   const gbytes bb = uniform_ptr(p.beta + trow * p.HV + hv);
   R.beta = load_u16(bb, uint32_t(min(tid & (C - 1), nvalid - 1) * p.HV) * 2u);
-  R.nvalid = nvalid;
 }
 
 // Zero the rows of a consumed prefetch buffer that lie past the chunk's end.
@@ -349,6 +360,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem + OFF_A);
   float* sScr = reinterpret_cast<float*>(smem + OFF_A);
   uint16_t* sKgT = reinterpret_cast<uint16_t*>(smem + OFF_KGT);
+  float* sPart = reinterpret_cast<float*>(smem + OFF_KGT);   // phase 2-3 scratch, before Kg^T
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
 
@@ -391,7 +403,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   Item first = find(blockIdx.x);
   if (first.id >= items) return;
   Raw R;
-  load_raw(R, p, first.trow, first.nvalid, first.hq, first.hv, tid);
+  load_raw_qk(R, p, first.trow, first.nvalid, first.hq, tid);
+  load_raw_g(R, p, first.trow, first.nvalid, first.hv, tid);
 
   // One chunk item: consumes R (cur's inputs), refills it with nxt's.
   auto chunk = [&](const Item& cur, const Item& nxt) __attribute__((always_inline)) {
@@ -406,10 +419,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         const int rg = tid >> 3, l8 = tid & 7;
         l2norm_row8(R.qk[0], R.qk[1]);
         l2norm_row8(R.qk[2], R.qk[3]);
-        *reinterpret_cast<uint4*>(sQ + rg * QS + 16 * l8) = R.qk[0];
-        *reinterpret_cast<uint4*>(sQ + rg * QS + 16 * l8 + 8) = R.qk[1];
-        *reinterpret_cast<uint4*>(sK + rg * QS + 16 * l8) = R.qk[2];
-        *reinterpret_cast<uint4*>(sK + rg * QS + 16 * l8 + 8) = R.qk[3];
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 8 * l8) = R.qk[0];
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 64 + 8 * l8) = R.qk[1];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 8 * l8) = R.qk[2];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 64 + 8 * l8) = R.qk[3];
       }
       if (tid < C) sBeta[tid] = bf16f(uint16_t(R.beta));
       // g in log2 units, inclusive scan over the 4 tokens this thread holds,
@@ -425,20 +438,21 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       }
       *reinterpret_cast<float4*>(sScr + seg * KD + 4 * c4) = gs[3];
       lds_barrier();
-      // The raw registers are consumed: prefetch the next chunk.
-      if (nxt.id < items) load_raw(R, p, nxt.trow, nxt.nvalid, nxt.hq, nxt.hv, tid);
-      // Exclusive offset of this segment: all 15 candidate totals are read
-      // (independent reads) and the earlier ones summed in order.
-      float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+      // Exclusive prefix of the 16 segment totals, one thread per channel,
+      // written back in place.
+      if (tid < KD) {
+        float t[16];
 #pragma unroll
-      for (int s2 = 0; s2 < 15; ++s2) {
-        const float4 t = *reinterpret_cast<const float4*>(sScr + s2 * KD + 4 * c4);
-        const bool use = s2 < seg;
-        off.x += use ? t.x : 0.f;
-        off.y += use ? t.y : 0.f;
-        off.z += use ? t.z : 0.f;
-        off.w += use ? t.w : 0.f;
+        for (int s2 = 0; s2 < 16; ++s2) t[s2] = sScr[s2 * KD + tid];
+        float run = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+          sScr[s2 * KD + tid] = run;
+          run += t[s2];
+        }
       }
+      lds_barrier();
+      const float4 off = *reinterpret_cast<const float4*>(sScr + seg * KD + 4 * c4);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         *reinterpret_cast<float4*>(sG + (4 * seg + r) * GS + 4 * c4) =
@@ -447,8 +461,14 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     lds_barrier();
 
     // ---------------------------------------------------------- phase 2: L, Aqk
-    // The 10 blocks on or below the diagonal over 8 waves; waves 2..7 also
-    // zero one strictly-upper block of Aqk each.
+    // The raw registers are consumed: prefetch the next chunk, q and k now,
+    // g and beta at the start of phase 3, so that the loads do not all queue
+    // in the memory pipe at once.
+    if (nxt.id < items) load_raw_qk(R, p, nxt.trow, nxt.nvalid, nxt.hq, tid);
+    // The 10 blocks on or below the diagonal: wave w computes one whole block
+    // (FULL_I/J below) plus one 32-channel quarter of one of the two blocks
+    // (3,0) and (2,0), whose four partial products are summed after the
+    // barrier.  Waves 2..7 also zero one strictly-upper block of Aqk each.
     {
       if (wave >= 2) {
         const int ub = wave - 2;
@@ -457,10 +477,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sAqk[(16 * UI + 4 * gq + r) * AS + perm32(16 * UJ + l16)] = 0;
       }
-      for (int pb = wave; pb < 10; pb += NW) {
-        // blocks ordered (3,0) (3,1) (3,2) (3,3) (2,0) (2,1) (2,2) (1,0) (1,1) (0,0)
-        const int I = pb < 4 ? 3 : (pb < 7 ? 2 : (pb < 9 ? 1 : 0));
-        const int J = pb < 4 ? pb : (pb < 7 ? pb - 4 : (pb < 9 ? pb - 7 : 0));
+      {
+        const int I = (FULL_I >> (4 * wave)) & 15;
+        const int J = (FULL_J >> (4 * wave)) & 15;
         const int ref = (J < I) ? 16 * I : 16 * I + 8;
         const int i = 16 * I + l16;     // operand row (A side)
         const int j = 16 * J + l16;     // operand row (B side)
@@ -558,10 +577,52 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
           sAqk[ir * AS + perm32(jc)] = f16_bits((jc <= ir) ? SCALE * accQ[r] : 0.f);
         }
       }
+      {
+        // Quarter (channels 32s..32s+31) of block (I, 0), I = 3 - wave/4:
+        // below the diagonal, so both split factors are <= 1.
+        const int X = wave >> 2;
+        const int I = 3 - X;
+        const int s = wave & 3;
+        const int i = 16 * I + l16;
+        const int j = l16;
+        const int ch0 = 32 * s + 8 * gq;
+        float ki[8], qi[8], kj[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + i * QS + ch0), ki);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + i * QS + ch0), qi);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + j * QS + ch0), kj);
+        f16x8 a, b, c;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 gi4 = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
+          const float4 gj4 = *reinterpret_cast<const float4*>(sG + j * GS + ch0 + 4 * h);
+          const float4 gr4 = *reinterpret_cast<const float4*>(sG + 16 * I * GS + ch0 + 4 * h);
+          const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+          const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+          const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float fr = ex2(gi[e] - gr[e]);
+            const float fc = ex2(gr[e] - gj[e]);
+            a[4 * h + e] = (_Float16)(ki[4 * h + e] * fr);
+            b[4 * h + e] = (_Float16)(qi[4 * h + e] * fr);
+            c[4 * h + e] = (_Float16)(kj[4 * h + e] * fc);
+          }
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 pL = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, c, z, 0, 0, 0);
+        const f32x4 pQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, c, z, 0, 0, 0);
+        float* part = sPart + (X * 4 + s) * 512;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          part[(4 * gq + r) * 16 + l16] = pL[r];
+          part[256 + (4 * gq + r) * 16 + l16] = pQ[r];
+        }
+      }
     }
     lds_barrier();
 
     // ---------------------------------------------------------- phase 3: solve
+    if (nxt.id < items) load_raw_g(R, p, nxt.trow, nxt.nvalid, nxt.hv, tid);
     // T = (I + L)^-1, unit lower triangular.
     // Diagonal 16x16 blocks: wave b < 4 inverts block b.  Lane 4*cc + h holds
     // rows 4h..4h+3 of column cc and the matching rows of L in registers;
@@ -602,6 +663,30 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // For the second product the contraction index of k-step s in lane group
     // gq is 4gq + s, which is where P's accumulator already holds it.
     for (int I = 1; I < 4; ++I) {
+      if (I == 1 && wave >= 4) {
+        // Meanwhile waves 4..7 finish blocks (3,0) and (2,0) of L and Aqk
+        // (first needed at I = 2): the four quarter products are summed in
+        // channel order.
+        // Wave 4 + k takes block X = k / 2, matrix k % 2 (L or Aqk); lane l
+        // sums entries 4l..4l+3 (row l / 4, columns 4 (l % 4)..+3).
+        const int k = wave - 4;
+        const int X = k >> 1;
+        const float* part = sPart + X * 4 * 512 + (k & 1) * 256 + 4 * lane;
+        const float4 p0 = *reinterpret_cast<const float4*>(part);
+        const float4 p1 = *reinterpret_cast<const float4*>(part + 512);
+        const float4 p2 = *reinterpret_cast<const float4*>(part + 1024);
+        const float4 p3 = *reinterpret_cast<const float4*>(part + 1536);
+        const float v[4] = {((p0.x + p1.x) + p2.x) + p3.x, ((p0.y + p1.y) + p2.y) + p3.y,
+                            ((p0.z + p1.z) + p2.z) + p3.z, ((p0.w + p1.w) + p2.w) + p3.w};
+        const int ir = 16 * (3 - X) + (lane >> 2), jc = 4 * (lane & 3);
+        if ((k & 1) == 0) {
+          const float bi = sBeta[ir];
+          *reinterpret_cast<float4*>(sL + ir * LS + jc) = make_float4(bi * v[0], bi * v[1], bi * v[2], bi * v[3]);
+        } else {
+          *reinterpret_cast<uint2*>(sAqk + ir * AS + perm32(jc)) =
+              make_uint2(pack_f16(SCALE * v[0], SCALE * v[1]), pack_f16(SCALE * v[2], SCALE * v[3]));
+        }
+      }
       if (wave < I) {
         const int J = wave;
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
