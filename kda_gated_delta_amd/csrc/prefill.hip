@@ -656,57 +656,92 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[(16 * blk + 4 * h + r) * LS + 16 * blk + cc] = x[r];
+    } else {
+      // Meanwhile waves 4..7 finish blocks (3,0) and (2,0) of L and Aqk: the
+      // four quarter products are summed in channel order.
+      // Wave 4 + k takes block X = k / 2, matrix k % 2 (L or Aqk); lane l
+      // sums entries 4l..4l+3 (row l / 4, columns 4 (l % 4)..+3).
+      const int k = wave - 4;
+      const int X = k >> 1;
+      const float* part = sPart + X * 4 * 512 + (k & 1) * 256 + 4 * lane;
+      const float4 p0 = *reinterpret_cast<const float4*>(part);
+      const float4 p1 = *reinterpret_cast<const float4*>(part + 512);
+      const float4 p2 = *reinterpret_cast<const float4*>(part + 1024);
+      const float4 p3 = *reinterpret_cast<const float4*>(part + 1536);
+      const float v[4] = {((p0.x + p1.x) + p2.x) + p3.x, ((p0.y + p1.y) + p2.y) + p3.y,
+                          ((p0.z + p1.z) + p2.z) + p3.z, ((p0.w + p1.w) + p2.w) + p3.w};
+      const int ir = 16 * (3 - X) + (lane >> 2), jc = 4 * (lane & 3);
+      if ((k & 1) == 0) {
+        const float bi = sBeta[ir];
+        *reinterpret_cast<float4*>(sL + ir * LS + jc) = make_float4(bi * v[0], bi * v[1], bi * v[2], bi * v[3]);
+      } else {
+        *reinterpret_cast<uint2*>(sAqk + ir * AS + perm32(jc)) =
+            make_uint2(pack_f16(SCALE * v[0], SCALE * v[1]), pack_f16(SCALE * v[2], SCALE * v[3]));
+      }
     }
     lds_barrier();
-    // Off-diagonal blocks, one block row at a time, on fp32 MFMA (16x16x4):
-    //   P_IJ = sum_{M=J}^{I-1} L_IM T_MJ,   T_IJ = -T_II P_IJ.
-    // For the second product the contraction index of k-step s in lane group
-    // gq is 4gq + s, which is where P's accumulator already holds it.
-    for (int I = 1; I < 4; ++I) {
-      if (I == 1 && wave >= 4) {
-        // Meanwhile waves 4..7 finish blocks (3,0) and (2,0) of L and Aqk
-        // (first needed at I = 2): the four quarter products are summed in
-        // channel order.
-        // Wave 4 + k takes block X = k / 2, matrix k % 2 (L or Aqk); lane l
-        // sums entries 4l..4l+3 (row l / 4, columns 4 (l % 4)..+3).
-        const int k = wave - 4;
-        const int X = k >> 1;
-        const float* part = sPart + X * 4 * 512 + (k & 1) * 256 + 4 * lane;
-        const float4 p0 = *reinterpret_cast<const float4*>(part);
-        const float4 p1 = *reinterpret_cast<const float4*>(part + 512);
-        const float4 p2 = *reinterpret_cast<const float4*>(part + 1024);
-        const float4 p3 = *reinterpret_cast<const float4*>(part + 1536);
-        const float v[4] = {((p0.x + p1.x) + p2.x) + p3.x, ((p0.y + p1.y) + p2.y) + p3.y,
-                            ((p0.z + p1.z) + p2.z) + p3.z, ((p0.w + p1.w) + p2.w) + p3.w};
-        const int ir = 16 * (3 - X) + (lane >> 2), jc = 4 * (lane & 3);
-        if ((k & 1) == 0) {
-          const float bi = sBeta[ir];
-          *reinterpret_cast<float4*>(sL + ir * LS + jc) = make_float4(bi * v[0], bi * v[1], bi * v[2], bi * v[3]);
-        } else {
-          *reinterpret_cast<uint2*>(sAqk + ir * AS + perm32(jc)) =
-              make_uint2(pack_f16(SCALE * v[0], SCALE * v[1]), pack_f16(SCALE * v[2], SCALE * v[3]));
-        }
-      }
-      if (wave < I) {
-        const int J = wave;
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-        for (int M = J; M < I; ++M) {
+    // Off-diagonal blocks of T on fp32 MFMA (16x16x4), through the inverse
+    // of the two 32x32 diagonal halves Z0 = [[T00, 0], [T10, T11]] and
+    // Z1 = [[T22, 0], [T32, T33]]:
+    //   T10 = -T11 L10 T00,  T32 = -T33 L32 T22,
+    //   [[T20, T21], [T30, T31]] = -Z1 Y,  Y = [[L20, L21], [L30, L31]] Z0,
+    // in three steps whose longest dependent chain is 8 + 4 + 8 MFMAs.
+    // In k-step s, lane group gq takes contraction index 4gq + s for
+    // products whose right operand is an accumulator (which holds exactly
+    // those entries) and 4s + gq when both operands come from LDS.
+    {
+      float* sY20 = sPart;          // Y20 and Y21, 16x16 row-major (the
+      float* sY21 = sPart + 256;    // partial sums were consumed above)
+      // acc += L_IM T_MJ, both from LDS.
+      auto lt = [&](f32x4 acc, int I, int M, int J) __attribute__((always_inline)) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float a = sL[(16 * I + l16) * LS + 16 * M + 4 * s + gq];
-            const float b = sT[(16 * M + 4 * s + gq) * LS + 16 * J + l16];
-            P = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, P, 0, 0, 0);
-          }
-        }
-        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sL[(16 * I + l16) * LS + 16 * M + 4 * s + gq],
+                                                     sT[(16 * M + 4 * s + gq) * LS + 16 * J + l16], acc, 0, 0, 0);
+        return acc;
+      };
+      // acc -= T_IK P, P an accumulator.
+      auto tp = [&](f32x4 acc, int I, int K, const f32x4& P) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float a = -sT[(16 * I + l16) * LS + 16 * I + 4 * gq + s];
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, P[s], X, 0, 0, 0);
-        }
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-sT[(16 * I + l16) * LS + 16 * K + 4 * gq + s], P[s], acc, 0, 0, 0);
+        return acc;
+      };
+      // acc -= T_IK Y, Y a 16x16 block in LDS.
+      auto ty = [&](f32x4 acc, int I, int K, const float* Y) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-sT[(16 * I + l16) * LS + 16 * K + 4 * s + gq],
+                                                     Y[(4 * s + gq) * 16 + l16], acc, 0, 0, 0);
+        return acc;
+      };
+      auto put_t = [&](const f32x4& X, int I, int J) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * gq + r) * LS + 16 * J + l16] = X[r];
-      }
+      };
+      auto put_y = [&](const f32x4& X, float* Y) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[(4 * gq + r) * 16 + l16] = X[r];
+      };
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 Y = z;
+      // Step 1: T10, T32; Y21, Y31 and the T00 terms of Y20, Y30.
+      if (wave == 0) put_t(tp(z, 1, 1, lt(z, 1, 0, 0)), 1, 0);
+      else if (wave == 1) put_t(tp(z, 3, 3, lt(z, 3, 2, 2)), 3, 2);
+      else if (wave == 2) { Y = lt(z, 2, 1, 1); put_y(Y, sY21); }
+      else if (wave == 3) Y = lt(z, 3, 1, 1);
+      else if (wave == 4) Y = lt(z, 2, 0, 0);
+      else if (wave == 5) Y = lt(z, 3, 0, 0);
+      lds_barrier();
+      // Step 2: the T10 terms of Y20, Y30.
+      if (wave == 4) { Y = lt(Y, 2, 1, 0); put_y(Y, sY20); }
+      else if (wave == 5) Y = lt(Y, 3, 1, 0);
+      lds_barrier();
+      // Step 3: T20, T21, T30, T31.
+      if (wave == 4) put_t(tp(z, 2, 2, Y), 2, 0);
+      else if (wave == 2) put_t(tp(z, 2, 2, Y), 2, 1);
+      else if (wave == 5) put_t(tp(ty(z, 3, 2, sY20), 3, 3, Y), 3, 0);
+      else if (wave == 3) put_t(tp(ty(z, 3, 2, sY21), 3, 3, Y), 3, 1);
       lds_barrier();
     }
     // A = T diag(beta), lower triangular, as fp16 (8 entries per thread).
