@@ -40,10 +40,10 @@ __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint
 // float32 -> bfloat16 bits, round to nearest, ties to even (exact for
 // subnormals and infinities; NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded;   // a select, not a branch
 }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
