@@ -205,12 +205,18 @@ __device__ __forceinline__ uint16_t f16_bits(float f) {
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return uint32_t(f16_bits(lo)) | (uint32_t(f16_bits(hi)) << 16);
 }
-__device__ __forceinline__ void unpack_bf16x8(const uint4& x, float* f) {
-  f[0] = bf16lo(x.x); f[1] = bf16hi(x.x);
-  f[2] = bf16lo(x.y); f[3] = bf16hi(x.y);
-  f[4] = bf16lo(x.z); f[5] = bf16hi(x.z);
-  f[6] = bf16lo(x.w); f[7] = bf16hi(x.w);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two bf16 values (one word) as two fp16 values (exact for the normalised
+// q^, k^ entries except below 2^-14, where fp16 keeps 2^-24 absolute steps).
+__device__ __forceinline__ uint32_t bf16w_to_f16w(uint32_t w) {
+  const f32x2 v = {bf16lo(w), bf16hi(w)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
+__device__ __forceinline__ float f16f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 
 // Raw inputs of one chunk held in registers (prefetch buffer), exactly as
 // loaded; rows past the chunk's end (clamped to its last row when loading)
@@ -419,10 +425,16 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         const int rg = tid >> 3, l8 = tid & 7;
         l2norm_row8(R.qk[0], R.qk[1]);
         l2norm_row8(R.qk[2], R.qk[3]);
-        *reinterpret_cast<uint4*>(sQ + rg * QS + 8 * l8) = R.qk[0];
-        *reinterpret_cast<uint4*>(sQ + rg * QS + 64 + 8 * l8) = R.qk[1];
-        *reinterpret_cast<uint4*>(sK + rg * QS + 8 * l8) = R.qk[2];
-        *reinterpret_cast<uint4*>(sK + rg * QS + 64 + 8 * l8) = R.qk[3];
+        // Staged as fp16, the MFMA operand type (see the phase-2 note).
+        uint4 h[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          h[m] = make_uint4(bf16w_to_f16w(R.qk[m].x), bf16w_to_f16w(R.qk[m].y), bf16w_to_f16w(R.qk[m].z),
+                            bf16w_to_f16w(R.qk[m].w));
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 8 * l8) = h[0];
+        *reinterpret_cast<uint4*>(sQ + rg * QS + 64 + 8 * l8) = h[1];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 8 * l8) = h[2];
+        *reinterpret_cast<uint4*>(sK + rg * QS + 64 + 8 * l8) = h[3];
       }
       if (tid < C) sBeta[tid] = bf16f(uint16_t(R.beta));
       // g in log2 units, inclusive scan over the 4 tokens this thread holds,
@@ -506,11 +518,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int ch0 = 32 * s + 8 * gq;
-          float ki[8], qi[8], kj[8];
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + i * QS + ch0), ki);
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + i * QS + ch0), qi);
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + j * QS + ch0), kj);
-          float kr[8], qr[8], kc[8];
+          const f16x8 ki = *reinterpret_cast<const f16x8*>(sK + i * QS + ch0);
+          const f16x8 qi = *reinterpret_cast<const f16x8*>(sQ + i * QS + ch0);
+          const f16x8 kj = *reinterpret_cast<const f16x8*>(sK + j * QS + ch0);
+          f32x8 fr, fc;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const float4 gi4 = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
@@ -521,31 +532,24 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
             const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float fr = ex2(gi[e] - gr[e]);
-              const float fc = ex2(gr[e] - gj[e]);
-              kr[4 * h + e] = ki[4 * h + e] * fr;
-              qr[4 * h + e] = qi[4 * h + e] * fr;
-              kc[4 * h + e] = kj[4 * h + e] * fc;
+              fr[4 * h + e] = ex2(gi[e] - gr[e]);
+              fc[4 * h + e] = ex2(gr[e] - gj[e]);
             }
           }
           if (!wide) {
-            f16x8 a, b, c;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              a[e] = (_Float16)kr[e];
-              b[e] = (_Float16)qr[e];
-              c[e] = (_Float16)kc[e];
-            }
-            accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, c, accL, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, c, accQ, 0, 0, 0);
+            // Split factors rounded to fp16, products in packed fp16.
+            const f16x8 frh = __builtin_convertvector(fr, f16x8);
+            const f16x8 fch = __builtin_convertvector(fc, f16x8);
+            accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ki * frh, kj * fch, accL, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(qi * frh, kj * fch, accQ, 0, 0, 0);
           } else {
             // Steep decay inside a diagonal block: bf16 operands keep the range.
             bf16x8 a, b, c;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              a[e] = (__bf16)kr[e];
-              b[e] = (__bf16)qr[e];
-              c[e] = (__bf16)kc[e];
+              a[e] = (__bf16)((float)ki[e] * fr[e]);
+              b[e] = (__bf16)((float)qi[e] * fr[e]);
+              c[e] = (__bf16)((float)kj[e] * fc[e]);
             }
             accL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c, accL, 0, 0, 0);
             accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, c, accQ, 0, 0, 0);
@@ -561,9 +565,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
             if (jc <= ir) {
               for (int ch = 0; ch < KD; ++ch) {
                 const float f = ex2(sG[ir * GS + ch] - sG[jc * GS + ch]);
-                const float kjf = bf16f(sK[jc * QS + ch]) * f;
-                aL = fmaf(bf16f(sK[ir * QS + ch]), kjf, aL);
-                aQ = fmaf(bf16f(sQ[ir * QS + ch]), kjf, aQ);
+                const float kjf = f16f(sK[jc * QS + ch]) * f;
+                aL = fmaf(f16f(sK[ir * QS + ch]), kjf, aL);
+                aQ = fmaf(f16f(sQ[ir * QS + ch]), kjf, aQ);
               }
             }
             accL[r] = aL;
@@ -586,11 +590,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         const int i = 16 * I + l16;
         const int j = l16;
         const int ch0 = 32 * s + 8 * gq;
-        float ki[8], qi[8], kj[8];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + i * QS + ch0), ki);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + i * QS + ch0), qi);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + j * QS + ch0), kj);
-        f16x8 a, b, c;
+        const f16x8 ki = *reinterpret_cast<const f16x8*>(sK + i * QS + ch0);
+        const f16x8 qi = *reinterpret_cast<const f16x8*>(sQ + i * QS + ch0);
+        const f16x8 kj = *reinterpret_cast<const f16x8*>(sK + j * QS + ch0);
+        f32x8 fr, fc;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const float4 gi4 = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
@@ -601,16 +604,15 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
           const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float fr = ex2(gi[e] - gr[e]);
-            const float fc = ex2(gr[e] - gj[e]);
-            a[4 * h + e] = (_Float16)(ki[4 * h + e] * fr);
-            b[4 * h + e] = (_Float16)(qi[4 * h + e] * fr);
-            c[4 * h + e] = (_Float16)(kj[4 * h + e] * fc);
+            fr[4 * h + e] = ex2(gi[e] - gr[e]);
+            fc[4 * h + e] = ex2(gr[e] - gj[e]);
           }
         }
+        const f16x8 frh = __builtin_convertvector(fr, f16x8);
+        const f16x8 fch = __builtin_convertvector(fc, f16x8);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 pL = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, c, z, 0, 0, 0);
-        const f32x4 pQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, c, z, 0, 0, 0);
+        const f32x4 pL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ki * frh, kj * fch, z, 0, 0, 0);
+        const f32x4 pQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(qi * frh, kj * fch, z, 0, 0, 0);
         float* part = sPart + (X * 4 + s) * 512;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -779,12 +781,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         const uint32_t kk = *reinterpret_cast<const uint32_t*>(sK + jj * QS + c2);
         const uint32_t qq = *reinterpret_cast<const uint32_t*>(sQ + jj * QS + c2);
         const float eg0 = ex2(gj.x), eg1 = ex2(gj.y);
-        const float k0 = bf16lo(kk), k1 = bf16hi(kk);
+        const float k0 = f16lo(kk), k1 = f16hi(kk);
         ev0[e] = k0 * eg0;
         ev1[e] = k1 * eg1;
         kv0[e] = k0 * ex2(glast.x - gj.x);
         kv1[e] = k1 * ex2(glast.y - gj.y);
-        qg_pk[e] = pack_f16(SCALE * bf16lo(qq) * eg0, SCALE * bf16hi(qq) * eg1);
+        qg_pk[e] = pack_f16(SCALE * f16lo(qq) * eg0, SCALE * f16hi(qq) * eg1);
       }
       *reinterpret_cast<uint4*>(sET + c2 * AS + j0) =
           make_uint4(pack_f16(ev0[0], ev0[1]), pack_f16(ev0[2], ev0[3]), pack_f16(ev0[4], ev0[5]), pack_f16(ev0[6], ev0[7]));
