@@ -810,7 +810,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sQ + (j0 + e) * QS + pc) = qg_pk[e];
     }
     // W = A (e^G k): 4 x 8 output tiles, 4 per wave; A is lower triangular.
-    // -W is stored in the permuted channel layout.
+    // Computed as W^T = E^T A^T (the same two operand reads, roles swapped),
+    // so each lane holds four adjacent channels of one token; -W is stored in
+    // the permuted channel layout, where those four stay adjacent (8 bytes).
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int pt = wave + NW * q4;
@@ -820,11 +822,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       for (int s = 0; s <= (mt >> 1); ++s) {
         const f16x8 a = lds_f16x8(sA + (16 * mt + l16) * AS + 32 * s + 8 * gq);
         const f16x8 b = lds_f16x8(sET + (16 * nt + l16) * AS + 32 * s + 8 * gq);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, acc, 0, 0, 0);
       }
-      const int pc = perm32(16 * nt + l16);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sW[(16 * mt + 4 * gq + r) * QS + pc] = f16_bits(-acc[r]);
+      *reinterpret_cast<uint2*>(sW + (16 * mt + l16) * QS + perm32(16 * nt + 4 * gq)) =
+          make_uint2(pack_f16(-acc[0], -acc[1]), pack_f16(-acc[2], -acc[3]));
     }
     lds_barrier();
 
