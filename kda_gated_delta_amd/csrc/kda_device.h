@@ -235,8 +235,9 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
   const float t = s32 + 1e-6f;
   const float d = (float)__builtin_sqrt((double)t);
   const double r = 1.0 / (double)d;
-  // Integer round-to-nearest-even: the hardware float32 -> bf16 conversion
-  // does not break ties to even.
+  // Integer round-to-nearest-even on the float32 quotient: written as a
+  // (__bf16) cast of (float)(double), the two roundings can be folded into
+  // one conversion from float64, which is not the same result.
   uint32_t y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] = pack_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
@@ -247,11 +248,13 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
 // lane/8), 16 consecutive elements per lane (x0: elements 0..7, x1: 8..15).
 // Identical results: the sum is exact on the fast path (any order), the
 // slow path rounds in the group's first lane, and the division is per
-// element.
-__device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
+// element.  Split in three steps so that two rows can be interleaved.
+
+// Step 1: the elements as float64, their sum of squares, and whether that
+// float64 sum is exact (the row's magnitudes span at most 15 binades).
+__device__ __forceinline__ void row8_sum_sq(const uint4& x0, const uint4& x1, double* xd, double& s, bool& exact) {
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  double xd[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     xd[2 * i] = (double)bf16lo(w[i]);
@@ -267,36 +270,41 @@ __device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
   }
   int emax = int(mx[0] > mx[1] ? mx[0] : mx[1]);
   int emin = int(mn[0] < mn[1] ? mn[0] : mn[1]) + 1;
-  double s = 0.0;
+  s = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s = fma(xd[i], xd[i], s);
   s = row8_sum(s);
   emax = row8_max(emax) >> 7;
   emin = row8_min(emin) >> 7;
-  const bool exact = (emax == 0 && emin == 512) || (max(emax, 1) - max(emin, 1) <= 15);
-  float s32 = (float)s;
-  if (!__all(exact)) {
-    double hi = 0.0, lo = 0.0;
+  exact = (emax == 0 && emin == 512) || (max(emax, 1) - max(emin, 1) <= 15);
+}
+
+// Slow path: the exact sum of squares in double-double, rounded once to
+// float32 in the group's first lane and broadcast to the group.
+__device__ __forceinline__ float row8_sum_sq_dd(const double* xd) {
+  double hi = 0.0, lo = 0.0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      double t, e;
-      two_sum(hi, xd[i] * xd[i], t, e);
-      hi = t;
-      lo += e;
-    }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      const double oh = __shfl_xor(hi, off, 64);
-      const double ol = __shfl_xor(lo, off, 64);
-      double t, e;
-      two_sum(hi, oh, t, e);
-      const double l = lo + ol + e;
-      hi = t + l;
-      lo = l - (hi - t);
-    }
-    const float r = __shfl(dd_to_f32(hi, lo), (threadIdx.x & 63) & ~7, 64);
-    if (!exact) s32 = r;
+  for (int i = 0; i < 16; ++i) {
+    double t, e;
+    two_sum(hi, xd[i] * xd[i], t, e);
+    hi = t;
+    lo += e;
   }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    const double oh = __shfl_xor(hi, off, 64);
+    const double ol = __shfl_xor(lo, off, 64);
+    double t, e;
+    two_sum(hi, oh, t, e);
+    const double l = lo + ol + e;
+    hi = t + l;
+    lo = l - (hi - t);
+  }
+  return __shfl(dd_to_f32(hi, lo), (threadIdx.x & 63) & ~7, 64);
+}
+
+// Step 3: y = bf16(x / sqrt(s32 + 1e-6)), correctly rounded.
+__device__ __forceinline__ void row8_scale(uint4& x0, uint4& x1, const double* xd, float s32) {
   const float t = s32 + 1e-6f;
   const float d = (float)__builtin_sqrt((double)t);
   const double r = 1.0 / (double)d;
@@ -305,6 +313,37 @@ __device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
   for (int i = 0; i < 8; ++i) y[i] = cvt_pk_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
   x0 = make_uint4(y[0], y[1], y[2], y[3]);
   x1 = make_uint4(y[4], y[5], y[6], y[7]);
+}
+
+__device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
+  double xd[16], s;
+  bool exact;
+  row8_sum_sq(x0, x1, xd, s, exact);
+  float s32 = (float)s;
+  if (!__all(exact)) {
+    const float r = row8_sum_sq_dd(xd);
+    if (!exact) s32 = r;
+  }
+  row8_scale(x0, x1, xd, s32);
+}
+
+// Two rows per 8-lane group (a q row and a k row), normalised together with
+// one shared slow-path test so that their independent dependency chains
+// interleave; each row's result is exactly that of l2norm_row8.
+__device__ __forceinline__ void l2norm_row8_pair(uint4& a0, uint4& a1, uint4& b0, uint4& b1) {
+  double xa[16], xb[16], sa, sb;
+  bool ea, eb;
+  row8_sum_sq(a0, a1, xa, sa, ea);
+  row8_sum_sq(b0, b1, xb, sb, eb);
+  float sa32 = (float)sa, sb32 = (float)sb;
+  if (!__all(ea && eb)) {
+    const float ra = row8_sum_sq_dd(xa);
+    const float rb = row8_sum_sq_dd(xb);
+    if (!ea) sa32 = ra;
+    if (!eb) sb32 = rb;
+  }
+  row8_scale(a0, a1, xa, sa32);
+  row8_scale(b0, b1, xb, sb32);
 }
 
 }  // namespace kda

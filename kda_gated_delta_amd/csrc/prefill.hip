@@ -423,8 +423,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       // q^ and k^: one 8-lane group per row, bit-exact normalisation.
       {
         const int rg = tid >> 3, l8 = tid & 7;
-        l2norm_row8(R.qk[0], R.qk[1]);
-        l2norm_row8(R.qk[2], R.qk[3]);
+        l2norm_row8_pair(R.qk[0], R.qk[1], R.qk[2], R.qk[3]);
         // Staged as fp16, the MFMA operand type (see the phase-2 note).
         uint4 h[4];
 #pragma unroll

@@ -207,3 +207,85 @@ def test_zero_length(gpu_lib):
     inp = synth.prefill_basic(95, 2, 0, 2, 2, init="none")
     o, s = _gpu(gpu_lib, inp)
     assert torch.all(s == 0)
+
+
+# ---------------------------------------------------------------------------
+# The normalisation fused into the prefill equals the canonical one bit for
+# bit.  With g = 0 every decay factor is exactly 1, so the workspace block Qg
+# holds fp16(fp32(K^-1/2 * fp16(q^))) and Kg^T holds fp16(k^): a q^ or k^ off
+# by one bf16 step changes them (unless both round to zero in fp16).  This reads the chunk slots back through
+# their documented layout (slot = W | Qg | Kg^T | Aqk | A | gamma; rows of
+# 16-byte pieces stored at piece ^ (row % 8); contraction indices permuted
+# within each group of 32 as 4g+e -> 8g+e, 16+4g+e -> 8g+4+e).
+
+_WS_SLOT, _WS_QG, _WS_KGT = 66048, 16384, 32768
+
+
+def _perm32(c):
+    cp = c & 31
+    return (c & ~31) + 8 * ((cp & 15) >> 2) + 4 * (cp >> 4) + (cp & 3)
+
+
+def _read_block(slot, off, rows, cols):
+    """Logical [rows][cols] fp16 block (cols permuted, pieces swizzled) as uint16."""
+    raw = slot[off:off + rows * cols * 2].view(np.uint16).reshape(rows, cols)
+    out = np.empty((rows, cols), np.uint16)
+    for r in range(rows):
+        for c in range(cols):
+            pos = _perm32(c)
+            piece, e = pos // 8, pos % 8
+            out[r, c] = raw[r, (piece ^ (r & 7)) * 8 + e]
+    return out
+
+
+def _crafted_rows(rng, n):
+    rows = []
+    e0 = np.zeros(128, np.float32)
+    e0[0] = 1
+    rows += [e0, -e0, np.zeros(128, np.float32), np.full(128, 3.0, np.float32)]
+    for span in (10, 15, 16, 17, 30, 38, 60, 120):      # fast path and both sides of its limit
+        for _ in range(4):
+            r = rng.standard_normal(128) * np.exp2(rng.integers(-span // 2, span // 2 + 1, 128))
+            rows.append(r.astype(np.float32))
+    rows.append((rng.standard_normal(128) * 1e-5).astype(np.float32))
+    while len(rows) < n:
+        rows.append((rng.standard_normal(128) * np.exp(0.6 * rng.standard_normal())).astype(np.float32))
+    rows = np.stack(rows[:n])
+    return rows[rng.permutation(n)]
+
+
+def test_fused_normalisation_bit_exact(gpu_lib):
+    kda = gpu_lib
+    rng = np.random.default_rng(11)
+    B, T, H = 1, 256, 2
+    q = torch.from_numpy(_crafted_rows(rng, T * H).reshape(B, T, H, 128)).to(torch.bfloat16)
+    k = torch.from_numpy(_crafted_rows(rng, T * H).reshape(B, T, H, 128)).to(torch.bfloat16)
+    v = torch.randn(B, T, H, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    g = torch.zeros(B, T, H, 128)
+    beta = torch.full((B, T, H), 0.5).to(torch.bfloat16)
+    dev = "cuda"
+    ws = torch.zeros(kda.workspace_size(B, T, H, H), dtype=torch.uint8, device=dev)
+    kda.chunk_prefill(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev), None, None, workspace=ws)
+    torch.cuda.synchronize()
+    wsn = ws.cpu().numpy()
+    nslots = wsn.size // (_WS_SLOT * H)
+    qhat = oracle.l2norm_bf16(q.float().numpy())          # exact bf16 values as float32
+    khat = oracle.l2norm_bf16(k.float().numpy())
+    scale = np.float32(0.08838834764831845)
+    bad_q = bad_k = 0
+    for hv in range(H):
+        for c in range(T // 64):
+            slot = wsn[(hv * nslots + c) * _WS_SLOT:(hv * nslots + c + 1) * _WS_SLOT]
+            qg = _read_block(slot, _WS_QG, 64, 128)
+            kgt = _read_block(slot, _WS_KGT, 128, 64)
+            qh = qhat[0, 64 * c:64 * c + 64, hv].astype(np.float16)
+            kh = khat[0, 64 * c:64 * c + 64, hv].astype(np.float16)
+            want_q = (qh.astype(np.float32) * scale).astype(np.float16)
+            want_k = kh.T
+            # Compared as values: the kernel forms these products with a fused
+            # multiply-add whose zero addend turns -0 into +0, which no MFMA
+            # sum can see; every nonzero value must match bit for bit.
+            bad_q += np.count_nonzero(qg.view(np.float16) != want_q)
+            bad_k += np.count_nonzero(kgt.view(np.float16) != want_k)
+    say(f"fused normalisation: q mismatches {bad_q}, k mismatches {bad_k} of {T * H * 128} each")
+    assert bad_q == 0 and bad_k == 0
