@@ -248,7 +248,7 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
 // lane/8), 16 consecutive elements per lane (x0: elements 0..7, x1: 8..15).
 // Identical results: the sum is exact on the fast path (any order), the
 // slow path rounds in the group's first lane, and the division is per
-// element.  Split in three steps so that two rows can be interleaved.
+// element.
 
 // Step 1: the elements as float64, their sum of squares, and whether that
 // float64 sum is exact (the row's magnitudes span at most 15 binades).
@@ -325,25 +325,6 @@ __device__ __forceinline__ void l2norm_row8(uint4& x0, uint4& x1) {
     if (!exact) s32 = r;
   }
   row8_scale(x0, x1, xd, s32);
-}
-
-// Two rows per 8-lane group (a q row and a k row), normalised together with
-// one shared slow-path test so that their independent dependency chains
-// interleave; each row's result is exactly that of l2norm_row8.
-__device__ __forceinline__ void l2norm_row8_pair(uint4& a0, uint4& a1, uint4& b0, uint4& b1) {
-  double xa[16], xb[16], sa, sb;
-  bool ea, eb;
-  row8_sum_sq(a0, a1, xa, sa, ea);
-  row8_sum_sq(b0, b1, xb, sb, eb);
-  float sa32 = (float)sa, sb32 = (float)sb;
-  if (!__all(ea && eb)) {
-    const float ra = row8_sum_sq_dd(xa);
-    const float rb = row8_sum_sq_dd(xb);
-    if (!ea) sa32 = ra;
-    if (!eb) sb32 = rb;
-  }
-  row8_scale(a0, a1, xa, sa32);
-  row8_scale(b0, b1, xb, sb32);
 }
 
 }  // namespace kda

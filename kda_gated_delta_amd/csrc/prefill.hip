@@ -287,9 +287,9 @@ __device__ __forceinline__ void load_raw_g(Raw& R, const Params& p, int64_t trow
 }
 
 // Zero the rows of a consumed prefetch buffer that lie past the chunk's end.
-__device__ __forceinline__ void mask_raw(Raw& R, int tid) {
-  // Component-wise selects: a select of whole aggregates becomes a select of
-  // their addresses and pushes the buffer out of registers.
+// Component-wise selects: a select of whole aggregates becomes a select of
+// their addresses and pushes the buffer out of registers.
+__device__ __forceinline__ void mask_raw_qk(Raw& R, int tid) {
   const bool qk_ok = (tid >> 3) < R.nvalid;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -298,6 +298,9 @@ __device__ __forceinline__ void mask_raw(Raw& R, int tid) {
     R.qk[m].z = qk_ok ? R.qk[m].z : 0u;
     R.qk[m].w = qk_ok ? R.qk[m].w : 0u;
   }
+}
+
+__device__ __forceinline__ void mask_raw_g(Raw& R, int tid) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool ok = (4 * (tid >> 5) + r) < R.nvalid;
@@ -307,6 +310,13 @@ __device__ __forceinline__ void mask_raw(Raw& R, int tid) {
     R.gv[r].w = ok ? R.gv[r].w : 0.f;
   }
   R.beta = (tid < R.nvalid) ? R.beta : 0u;
+}
+
+// Normalise the q and k rows held in a prefetch buffer, in place.
+__device__ __forceinline__ void norm_raw_qk(Raw& R, int tid) {
+  mask_raw_qk(R, tid);
+  l2norm_row8(R.qk[0], R.qk[1]);
+  l2norm_row8(R.qk[2], R.qk[3]);
 }
 
 // cu_seqlens is read-only for the whole launch, so it is read through the
@@ -413,17 +423,20 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   load_raw_g(R, p, first.trow, first.nvalid, first.hv, tid);
 
   // One chunk item: consumes R (cur's inputs), refills it with nxt's.
-  auto chunk = [&](const Item& cur, const Item& nxt) __attribute__((always_inline)) {
+  // `first`: q and k of this item were not normalised at the end of the
+  // previous one.
+  auto chunk = [&](const Item& cur, const Item& nxt, const bool first) __attribute__((always_inline)) {
     const int hv = cur.hv;
     (void)hv;
 
     // ---------------------------------------------------------- phase 1
     {
-      mask_raw(R, tid);
-      // q^ and k^: one 8-lane group per row, bit-exact normalisation.
+      // q^ and k^: one 8-lane group per row, bit-exact normalisation (done at
+      // the end of the previous item, except for a workgroup's first).
+      if (first) norm_raw_qk(R, tid);
+      mask_raw_g(R, tid);
       {
         const int rg = tid >> 3, l8 = tid & 7;
-        l2norm_row8_pair(R.qk[0], R.qk[1], R.qk[2], R.qk[3]);
         // Staged as fp16, the MFMA operand type (see the phase-2 note).
         uint4 h[4];
 #pragma unroll
@@ -859,6 +872,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         *reinterpret_cast<uint4*>(dst + b) = *reinterpret_cast<const uint4*>(src);
       }
     }
+    // While those stores drain (the vector ALUs are otherwise idle here),
+    // normalise the next item's q and k, prefetched in phase 2.
+    if (nxt.id < items) norm_raw_qk(R, tid);
     lds_barrier();
   };
 
@@ -869,11 +885,11 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   // same state; with a plain loop the entry path (loads only) would make the
   // compiler's wait at the loop head conservative and drain the stores too.
   Item nxt = find(first.id + stride);
-  chunk(first, nxt);
+  chunk(first, nxt, true);
   while (nxt.id < items) {
     const Item cur = nxt;
     nxt = find(cur.id + stride);
-    chunk(cur, nxt);
+    chunk(cur, nxt, false);
   }
 }
 
