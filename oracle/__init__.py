@@ -19,6 +19,7 @@ Modules
   recurrent  the token-by-token recurrence, fp64
   chunked    the chunk construction (G, L, A, W, U, Qg, Kg, Aqk, carry), fp64
   decode     one recurrent step against a bf16 state pool
+  handoff    prefill final states stored into the bf16 decode pool
 
 Pinning status: every public function here is pinned by tests that do not
 re-type its formula (closed forms, the pages' worked example, invariants,
@@ -31,6 +32,7 @@ from .l2norm import l2norm_bf16
 from .recurrent import recurrent
 from .chunked import chunked
 from .decode import decode_step
+from .handoff import state_to_pool
 
 __all__ = [
     "bf16_round",
@@ -41,4 +43,5 @@ __all__ = [
     "recurrent",
     "chunked",
     "decode_step",
+    "state_to_pool",
 ]
