@@ -127,6 +127,12 @@ def cpu_baseline(inp, heads, target_s):
     }
 
 
+def handoff_alg_bytes(n_act, n_states, HV):
+    """Active states are read as fp32 and written as bf16; plus the int32
+    indices."""
+    return n_act * HV * K * V * (4 + 2) + 4 * n_states
+
+
 def copy_calibration(nbytes):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -336,6 +342,35 @@ def main():
             "state_gbs": dec_gbs,
             "hbm_frac": dec_gbs / HBM_PEAK_GBS,
         },
+    }
+    # Prefill-to-decode handoff, timed on its own after the steps: the decode
+    # workload's rows each hand a fresh fp32 state to their pool slot.  A
+    # 512 MB fill between launches evicts the last-level cache, so every
+    # launch streams its states from HBM.
+    print("[bench] handoff", file=sys.stderr, flush=True)
+    hstate, _, _ = synth.handoff_config(args.decode_B, slots=args.decode_B, HV=din.v.shape[1])
+    hstate = hstate.to(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    h_ms = []
+    for i in range(args.warmup + args.steps):
+        flush.fill_(i & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kda.state_to_pool(hstate, pool, idx)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            h_ms.append(e0.elapsed_time(e1))
+    del flush
+    h_mean = sum(h_ms) / len(h_ms)
+    hbytes = handoff_alg_bytes(n_act, args.decode_B, din.v.shape[1])
+    result["handoff"] = {
+        "states": args.decode_B,
+        "active": n_act,
+        "kernel_us_mean": h_mean * 1e3,
+        "alg_bytes": hbytes,
+        "gbs": hbytes / (h_mean * 1e-3) / 1e9,
+        "hbm_frac": hbytes / (h_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)

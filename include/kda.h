@@ -161,6 +161,37 @@ int kda_decode(const void* q, const void* k, const void* v,
                int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
                void* o, void* stream);
 
+/*
+ * kda_state_to_pool -- prefill-to-decode handoff: store each sequence's
+ * float32 state into its slot of the bf16 decode pool.
+ *
+ * Joins the two halves of the path: "KDA Chunk Prefill on Ascend A3",
+ * section "Function and tensor contract" (the fp32 final_state
+ * [N, HV, K, V] that kda_chunk_prefill returns) and
+ * "flashinfer.kda_decode.packed_kda_decode", section "Parameters" (the
+ * bf16 pool [slots, HV, K, V] that kda_decode reads and updates, with an
+ * int32 slot index per row).  The stored value is the state rounded once
+ * to bfloat16, nearest-even -- the same rounding kda_decode applies when it
+ * writes a slot back.  NaN stays NaN (quiet); infinities and subnormals
+ * round like any other value.
+ *
+ *   state          fp32 [N, HV, K, V]  input, read-only (e.g. final_state)
+ *   N              number of states (>= 0; 0 enqueues nothing)
+ *   state_pool     bf16, slot s at state_pool + s * slot_stride elements,
+ *                  each slot [HV, K, V] compact; slot_stride >= HV*K*V and a
+ *                  multiple of 8 elements
+ *   num_slots      number of slots in the pool
+ *   state_indices  int32 [N] device array: state n goes to slot
+ *                  state_indices[n].  An index outside [0, num_slots) --
+ *                  including -1 -- skips that state (no pool access).
+ *                  Active indices must be unique (duplicates race).
+ * Only the addressed slots are written; every other slot is untouched.
+ * K == V == 128.
+ */
+int kda_state_to_pool(const float* state, int32_t N, int32_t HV, int32_t K, int32_t V,
+                      void* state_pool, int64_t slot_stride, int64_t num_slots,
+                      const int32_t* state_indices, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, without the ``kda_`` prefix):
   chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
                                                   -> (o, final_state)
   decode(q, k, v, g, beta, state_pool, state_indices)   -> o
+  state_to_pool(state, state_pool, state_indices)       -> state_pool
 """
 
 import ctypes
@@ -22,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill",
-           "kda_chunk_prefill_workspace_size", "kda_decode")
+           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_state_to_pool")
 
 _lib = None
 
@@ -56,6 +57,8 @@ def load():
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                _i32, _i32, _i32, _i32, _i32, _vp, _vp]
+    lib.kda_state_to_pool.restype = ctypes.c_int
+    lib.kda_state_to_pool.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
     _lib = lib
     return lib
 
@@ -190,3 +193,28 @@ def decode(q, k, v, g, beta, state_pool, state_indices, out=None):
                           _ptr(state_indices), B, H, HV, K, V, _ptr(out), _stream())
     _check(code, "kda_decode")
     return out
+
+
+def state_to_pool(state, state_pool, state_indices):
+    """Prefill-to-decode handoff: state fp32 [N,HV,K,V] (e.g. a prefill's
+    final_state) is stored, rounded to bf16, into state_pool bf16
+    [slots,HV,K,V] (outer stride may be padded, inner dims compact) at slot
+    state_indices[n] (int32 [N]; -1 or out of range skips the state).
+    Updates state_pool in place and returns it."""
+    lib = load()
+    _need(state, "state", torch.float32, 4)
+    dev = state.device
+    N, HV, K, V = state.shape
+    _need(state_indices, "state_indices", torch.int32, 1, dev)
+    if state_indices.shape[0] != N:
+        raise ValueError(f"state_indices must have {N} entries")
+    if state_pool.dtype != torch.bfloat16 or not state_pool.is_cuda or state_pool.device != dev:
+        raise TypeError("state_pool must be a bf16 GPU tensor on state's device")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (HV, K, V):
+        raise ValueError(f"state_pool must be [slots,{HV},{K},{V}]")
+    if state_pool.stride()[1:] != (K * V, V, 1):
+        raise ValueError("state_pool inner dims must be compact")
+    code = lib.kda_state_to_pool(_ptr(state), N, HV, K, V, _ptr(state_pool), state_pool.stride(0),
+                                 state_pool.shape[0], _ptr(state_indices), _stream())
+    _check(code, "kda_state_to_pool")
+    return state_pool

@@ -165,6 +165,18 @@ def decode_config(B, N=1024, H=12, HV=12, seed=4):
     return DecodeInputs(q, k, v, g, beta, pool, idx, f"decode_b{B}_h{HV}")
 
 
+def handoff_config(N, slots=1024, HV=12, seed=6):
+    """Prefill-to-decode handoff: N fp32 states 0.25*N(0,1) [N,HV,K,V] (the
+    pages' nonzero state), a bf16 pool 0.1*N(0,1) [slots,HV,K,V] and unique
+    slots from a permutation with rows r % 8 == 7 set to -1."""
+    gen = _gen(seed * 1000 + N)
+    state = 0.25 * _randn(gen, N, HV, K_DIM, V_DIM)
+    pool = (0.1 * _randn(gen, slots, HV, K_DIM, V_DIM)).to(torch.bfloat16)
+    idx = torch.randperm(slots, generator=gen)[:N].to(torch.int32)
+    idx[torch.arange(N) % 8 == 7] = -1
+    return state, pool, idx
+
+
 def worked_example(T=128, beta_value=1.0):
     """The pages' worked example: B=H=HV=1, K=V=128, q=k=e0, v=1, g=0,
     beta=1 (or beta_value), no initial state."""

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_qk_l2norm",
-              "kda_status_string"):
+              "kda_state_to_pool", "kda_status_string"):
         assert n in names
     assert set(names) == set(kda.EXPORTS)
 
@@ -106,3 +106,26 @@ def test_decode_metadata_errors():
     assert _decode(lib, stride=12 * 128 * 128 + 4) == 4
     assert _decode(lib, K=64) == 3
     assert _decode(lib, o=MISALIGNED) == 4
+
+
+def _to_pool(lib, **kw):
+    a = dict(state=FAKE, N=4, HV=12, K=128, V=128, pool=FAKE, stride=12 * 128 * 128, n=8, idx=FAKE)
+    a.update(kw)
+    return lib.kda_state_to_pool(a["state"], a["N"], a["HV"], a["K"], a["V"], a["pool"], a["stride"],
+                                 a["n"], a["idx"], NULL)
+
+
+def test_state_to_pool_metadata_errors():
+    lib = kda.load()
+    assert _to_pool(lib, N=0) == 0
+    assert _to_pool(lib, N=-1) == 2
+    assert _to_pool(lib, HV=0) == 2
+    assert _to_pool(lib, n=-1) == 2
+    assert _to_pool(lib, K=64) == 3
+    assert _to_pool(lib, state=NULL) == 1
+    assert _to_pool(lib, idx=NULL) == 1
+    assert _to_pool(lib, pool=NULL) == 1
+    assert _to_pool(lib, stride=100) == 2
+    assert _to_pool(lib, stride=12 * 128 * 128 + 4) == 4
+    assert _to_pool(lib, state=MISALIGNED) == 4
+    assert _to_pool(lib, pool=MISALIGNED) == 4
