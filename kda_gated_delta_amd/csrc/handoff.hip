@@ -10,10 +10,11 @@
 // slot indices where -1 means no state access).
 //
 // Pure streaming: per (sequence, value head) 64 KB of fp32 in and 32 KB of
-// bf16 out.  A 256-thread workgroup converts one quarter of a state
-// (4096 elements): each thread issues its four 16-byte loads before any
-// store, then writes two 16-byte words of eight bf16 each.  A wave covers
-// whole 256-byte pool rows, so every access is coalesced.
+// bf16 out.  A 256-thread workgroup converts one eighth of a state (2048
+// elements): each thread issues both of its 16-byte loads before its store
+// of eight bf16.  A wave covers whole 256-byte pool rows, so every access is
+// coalesced.  (Eighths measured faster than quarters or halves of a state
+// per workgroup; the nontemporal hint measured slower after a prefill.)
 #include "kda_device.h"
 #include "kda_host.h"
 
@@ -21,9 +22,10 @@ namespace {
 
 constexpr int K = kda::kHead;
 constexpr int V = kda::kHead;
-constexpr int kParts = 4;                       // workgroups per state
-constexpr int kPerBlock = K * V / kParts;       // 4096 elements
+constexpr int kParts = 8;                       // workgroups per state
+constexpr int kPerBlock = K * V / kParts;       // 2048 elements
 constexpr int kThreads = 256;
+static_assert(kPerBlock == 8 * kThreads, "one group of eight elements per thread");
 
 __global__ __launch_bounds__(kThreads) void state_to_pool_kernel(
     const float4* __restrict__ state, uint16_t* __restrict__ pool, int64_t slot_stride,
@@ -39,19 +41,11 @@ __global__ __launch_bounds__(kThreads) void state_to_pool_kernel(
   uint4* dst = reinterpret_cast<uint4*>(pool + idx * slot_stride + int64_t(hv) * K * V +
                                         part * kPerBlock);
   const int t = threadIdx.x;
-  // Thread t converts elements 8t..8t+7 and 2048+8t..2048+8t+7 of the part.
-  float4 x[4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    x[2 * h] = src[h * (kPerBlock / 8) + 2 * t];
-    x[2 * h + 1] = src[h * (kPerBlock / 8) + 2 * t + 1];
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4 a = x[2 * h], b = x[2 * h + 1];
-    dst[h * (kPerBlock / 16) + t] = make_uint4(kda::pack_bf16(a.x, a.y), kda::pack_bf16(a.z, a.w),
-                                               kda::pack_bf16(b.x, b.y), kda::pack_bf16(b.z, b.w));
-  }
+  // Thread t converts elements 8t..8t+7 of the part.
+  const float4 a = src[2 * t];
+  const float4 b = src[2 * t + 1];
+  dst[t] = make_uint4(kda::pack_bf16(a.x, a.y), kda::pack_bf16(a.z, a.w), kda::pack_bf16(b.x, b.y),
+                      kda::pack_bf16(b.z, b.w));
 }
 
 }  // namespace

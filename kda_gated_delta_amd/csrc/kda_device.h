@@ -49,6 +49,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// ---------------------------------------------------------------- streaming access
+
+// 16-byte global store with the nontemporal hint, for data that is written
+// once and read back only after it has long left the caches.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
+  const u32x4_nt w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
+}
+
 // ---------------------------------------------------------------- exact sums
 
 // Error-free sum: a + b = s + e exactly.
