@@ -20,11 +20,14 @@ Modules
   chunked    the chunk construction (G, L, A, W, U, Qg, Kg, Aqk, carry), fp64
   decode     one recurrent step against a bf16 state pool
   handoff    prefill final states stored into the bf16 decode pool
+  packed_decode  the decode step from packed QKV and raw gate/beta logits
 
 Pinning status: every public function here is pinned by tests that do not
 re-type its formula (closed forms, the pages' worked example, invariants,
 brute force against exact rational arithmetic, and the two independent
-forms checked against each other).  See tests/test_oracle_*.py.
+forms checked against each other).  See tests/test_oracle_*.py.  The one
+exception is the packed decode's gate transform, whose formula the pages do
+not give: "parity unpinned" -- only its closed-form properties are pinned.
 """
 
 from .bf16 import bf16_round, bf16_bits, bits_to_f32, f64_to_bf16_round
@@ -33,6 +36,7 @@ from .recurrent import recurrent
 from .chunked import chunked
 from .decode import decode_step
 from .handoff import state_to_pool
+from .packed_decode import packed_decode_step
 
 __all__ = [
     "bf16_round",
@@ -44,4 +48,5 @@ __all__ = [
     "chunked",
     "decode_step",
     "state_to_pool",
+    "packed_decode_step",
 ]

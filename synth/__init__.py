@@ -165,6 +165,40 @@ def decode_config(B, N=1024, H=12, HV=12, seed=4):
     return DecodeInputs(q, k, v, g, beta, pool, idx, f"decode_b{B}_h{HV}")
 
 
+@dataclass
+class PackedDecodeInputs:
+    mixed_qkv: torch.Tensor    # [B, 3*H*K + row_pad] bf16 (rows q | k | v, then padding)
+    raw_gate: torch.Tensor     # [B, H*K] bf16
+    raw_beta: torch.Tensor     # [B, H] bf16
+    A_log: torch.Tensor        # [H] fp32
+    dt_bias: torch.Tensor      # [H*K] fp32
+    pool: torch.Tensor         # [N,H,K,V] bf16
+    state_indices: torch.Tensor  # [B] int32
+    H: int
+    name: str = ""
+
+
+def packed_decode_config(B, N=1024, H=12, row_pad=0, seed=7):
+    """Packed decode inputs: q,k,v ~ N(0,1) packed in one bf16 row per batch
+    row (row_pad trailing elements of each row hold NaN, which must never be
+    read); raw gate and beta logits ~ N(0,1) bf16; A_log = log U(1,16) per
+    head and dt_bias ~ N(0,1) per channel (fp32); bf16 pool 0.1*N(0,1);
+    unique slots from a permutation with rows r % 8 == 7 set to -1."""
+    gen = _gen(seed * 1000 + B)
+    qkv = _randn(gen, B, 3 * H * K_DIM)
+    mixed = torch.full((B, 3 * H * K_DIM + row_pad), float("nan"))
+    mixed[:, : 3 * H * K_DIM] = qkv
+    raw_gate = _randn(gen, B, H * K_DIM).to(torch.bfloat16)
+    raw_beta = _randn(gen, B, H).to(torch.bfloat16)
+    A_log = torch.log(1.0 + 15.0 * torch.rand(H, generator=gen))
+    dt_bias = _randn(gen, H * K_DIM)
+    pool = (0.1 * _randn(gen, N, H, K_DIM, V_DIM)).to(torch.bfloat16)
+    idx = torch.randperm(N, generator=gen)[:B].to(torch.int32)
+    idx[torch.arange(B) % 8 == 7] = -1
+    return PackedDecodeInputs(mixed.to(torch.bfloat16), raw_gate, raw_beta, A_log, dt_bias, pool, idx, H,
+                              f"packed_decode_b{B}_h{H}_pad{row_pad}")
+
+
 def handoff_config(N, slots=1024, HV=12, seed=6):
     """Prefill-to-decode handoff: N fp32 states 0.25*N(0,1) [N,HV,K,V] (the
     pages' nonzero state), a bf16 pool 0.1*N(0,1) [slots,HV,K,V] and unique
