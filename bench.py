@@ -16,6 +16,10 @@ Prints one JSON line:
                call / mean call time.  traffic is the measured HBM bytes per
                call from the committed rocprofv3 counter summary when that
                was taken on the current kernel source, else null
+  handoff,     the prefill-to-decode handoff (256 x 12 fp32 states into the
+  packed_decode  pool) and the packed-input decode (B=256, H=12), each timed
+               after the steps with a prefill before every launch, so they
+               too meet the caches the way they would in serving
   cpu_baseline the fp64 oracle (token-by-token form) on a bounded sample of
                the same prefill workload, on this host's cores
 Only --gpus 1 is supported: the library runs on one GPU.
@@ -131,6 +135,14 @@ def handoff_alg_bytes(n_act, n_states, HV):
     """Active states are read as fp32 and written as bf16; plus the int32
     indices."""
     return n_act * HV * K * V * (4 + 2) + 4 * n_states
+
+
+def packed_decode_alg_bytes(n_act, n_inact, H):
+    """Active rows read and write their bf16 state slot and read their packed
+    q|k|v row, raw gate and raw beta and write o; inactive rows write zero
+    o; plus A_log, dt_bias and the int32 indices."""
+    per = 2 * K * V * 2 + 3 * K * 2 + K * 2 + 2 + V * 2
+    return n_act * H * per + n_inact * H * V * 2 + H * 4 + H * K * 4 + 4 * (n_act + n_inact)
 
 
 def copy_calibration(nbytes):
@@ -372,6 +384,35 @@ def main():
         "gbs": hbytes / (h_mean * 1e-3) / 1e9,
         "hbm_frac": hbytes / (h_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
+    # Packed decode (the page's serving-native inputs), timed the same way.
+    print("[bench] packed decode", file=sys.stderr, flush=True)
+    pk = synth.packed_decode_config(args.decode_B)
+    pk_args = [t.to(dev) for t in (pk.mixed_qkv, pk.raw_gate, pk.raw_beta, pk.A_log, pk.dt_bias)]
+    pk_pool = pk.pool.to(dev)
+    pk_idx = pk.state_indices.to(dev)
+    pk_out = torch.empty(args.decode_B, 1, pk.H, V, dtype=torch.bfloat16, device=dev)
+    p_ev = []
+    for i in range(args.warmup + args.steps):
+        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kda.packed_decode(*pk_args, pk_pool, pk_idx, out=pk_out)
+        e1.record(stream)
+        if i >= args.warmup:
+            p_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    p_mean = sum(a.elapsed_time(b) for a, b in p_ev) / len(p_ev)
+    pk_act = int((pk.state_indices >= 0).sum())
+    pkbytes = packed_decode_alg_bytes(pk_act, args.decode_B - pk_act, pk.H)
+    result["packed_decode"] = {
+        "B": args.decode_B,
+        "active_rows": pk_act,
+        "kernel_us_mean": p_mean * 1e3,
+        "alg_bytes": pkbytes,
+        "gbs": pkbytes / (p_mean * 1e-3) / 1e9,
+        "hbm_frac": pkbytes / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    del pk_pool
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)

@@ -162,6 +162,45 @@ int kda_decode(const void* q, const void* k, const void* v,
                void* o, void* stream);
 
 /*
+ * kda_packed_decode -- kda_decode from the serving-native packed inputs:
+ * Q/K/V extraction, the gate transform and the beta sigmoid fused into the
+ * same kernel.
+ *
+ * Defined on "flashinfer.kda_decode.packed_kda_decode" (its description
+ * and section "Parameters"): one post-convolution packed bf16 row per batch
+ * row, raw per-channel gate logits and raw beta logits, per-head A_log and
+ * per-channel dt_bias, lower_bound = -5; the state pool, slot indices,
+ * -1 rows and output as kda_decode.  Per batch row b and head h
+ * (H == HV; value head h reads Q/K head h):
+ *     q, k, v = the three [H, K] blocks of mixed_qkv[b], in that order
+ *     g       = -5 * sigmoid(exp(A_log[h]) * (raw_gate[b, h, :] + dt_bias[h, :]))
+ *     beta    = sigmoid(raw_beta[b, h])
+ * then exactly the step of kda_decode (normalisation, decay, delta update,
+ * output, bf16 write-back), all in float32.  The page names the gate
+ * transform, its parameters and its lower bound but prints no formula; the
+ * line above is this library's reading of it.
+ *
+ *   mixed_qkv      bf16, row b at mixed_qkv + b * qkv_row_stride elements,
+ *                  each row [3, H, K] compact; qkv_row_stride >= 3*H*K and a
+ *                  multiple of 8 (the padding is never read)
+ *   raw_gate       bf16 [B, H*K]
+ *   raw_beta       bf16 [B, H]
+ *   A_log          fp32 [H]
+ *   dt_bias        fp32 [H*K]
+ *   state_pool, slot_stride, num_slots, state_indices   as kda_decode (HV = H)
+ *   o              bf16 [B, H, V]  (the [B, 1, H, V] output)
+ * Sizes: B >= 0 (0 enqueues nothing), H >= 1 (the page's operator is
+ * specialised to H = 12), K == V == 128.
+ */
+int kda_packed_decode(const void* mixed_qkv, int64_t qkv_row_stride,
+                      const void* raw_gate, const void* raw_beta,
+                      const float* A_log, const float* dt_bias,
+                      void* state_pool, int64_t slot_stride, int64_t num_slots,
+                      const int32_t* state_indices,
+                      int32_t B, int32_t H, int32_t K, int32_t V,
+                      void* o, void* stream);
+
+/*
  * kda_state_to_pool -- prefill-to-decode handoff: store each sequence's
  * float32 state into its slot of the bf16 decode pool.
  *

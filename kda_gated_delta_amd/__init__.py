@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the ``kda_`` prefix):
   chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
                                                   -> (o, final_state)
   decode(q, k, v, g, beta, state_pool, state_indices)   -> o
+  packed_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool,
+                state_indices)                    -> o
   state_to_pool(state, state_pool, state_indices)       -> state_pool
 """
 
@@ -23,7 +25,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill",
-           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_state_to_pool")
+           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
+           "kda_state_to_pool")
 
 _lib = None
 
@@ -57,6 +60,9 @@ def load():
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                _i32, _i32, _i32, _i32, _i32, _vp, _vp]
+    lib.kda_packed_decode.restype = ctypes.c_int
+    lib.kda_packed_decode.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                      _i32, _i32, _i32, _i32, _vp, _vp]
     lib.kda_state_to_pool.restype = ctypes.c_int
     lib.kda_state_to_pool.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
     _lib = lib
@@ -218,3 +224,44 @@ def state_to_pool(state, state_pool, state_indices):
                                  state_pool.shape[0], _ptr(state_indices), _stream())
     _check(code, "kda_state_to_pool")
     return state_pool
+
+
+def packed_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, state_indices, out=None):
+    """One decode step from packed serving inputs.  mixed_qkv bf16 [B, 3*H*K]
+    (rows q | k | v; row stride may be padded to a multiple of 8, last dim
+    contiguous); raw_gate bf16 [B, H*K]; raw_beta bf16 [B, H]; A_log fp32
+    [H]; dt_bias fp32 [H*K]; state_pool bf16 [N,H,K,V] updated in place;
+    state_indices int32 [B].  Returns o [B,1,H,V] bf16."""
+    lib = load()
+    if not isinstance(mixed_qkv, torch.Tensor) or mixed_qkv.dtype != torch.bfloat16 or not mixed_qkv.is_cuda:
+        raise TypeError("mixed_qkv must be a bf16 GPU tensor")
+    if mixed_qkv.dim() != 2 or mixed_qkv.stride(1) != 1:
+        raise ValueError("mixed_qkv must be [B, 3*H*K] with a contiguous last dim")
+    dev = mixed_qkv.device
+    _need(A_log, "A_log", torch.float32, 1, dev)
+    H = A_log.shape[0]
+    B = mixed_qkv.shape[0]
+    K = V = 128
+    if mixed_qkv.shape[1] != 3 * H * K:
+        raise ValueError(f"mixed_qkv rows must hold 3*{H}*{K} elements")
+    _need(raw_gate, "raw_gate", torch.bfloat16, 2, dev)
+    _need(raw_beta, "raw_beta", torch.bfloat16, 2, dev)
+    _need(dt_bias, "dt_bias", torch.float32, 1, dev)
+    _need(state_indices, "state_indices", torch.int32, 1, dev)
+    if tuple(raw_gate.shape) != (B, H * K) or tuple(raw_beta.shape) != (B, H) or dt_bias.shape[0] != H * K:
+        raise ValueError("raw_gate [B,H*K], raw_beta [B,H], dt_bias [H*K] expected")
+    if state_pool.dtype != torch.bfloat16 or not state_pool.is_cuda or state_pool.device != dev:
+        raise TypeError("state_pool must be a bf16 GPU tensor on mixed_qkv's device")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, K, V):
+        raise ValueError(f"state_pool must be [N,{H},{K},{V}]")
+    if state_pool.stride()[1:] != (K * V, V, 1):
+        raise ValueError("state_pool inner dims must be compact")
+    if out is None:
+        out = torch.empty((B, 1, H, V), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    row_stride = mixed_qkv.stride(0) if B > 1 else 3 * H * K
+    code = lib.kda_packed_decode(_ptr(mixed_qkv), row_stride, _ptr(raw_gate), _ptr(raw_beta), _ptr(A_log),
+                                 _ptr(dt_bias), _ptr(state_pool), state_pool.stride(0), state_pool.shape[0],
+                                 _ptr(state_indices), B, H, K, V, _ptr(out), _stream())
+    _check(code, "kda_packed_decode")
+    return out

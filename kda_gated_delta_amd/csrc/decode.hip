@@ -1,4 +1,5 @@
-// Single-token KDA decode against a bf16 state pool (export kda_decode).
+// Single-token KDA decode against a bf16 state pool (exports kda_decode and,
+// from the page's packed serving inputs, kda_packed_decode).
 //
 // Pages: "flashinfer.kda_decode.packed_kda_decode" (section "Parameters":
 // bf16 pool [N, HV, K, V] updated in place, -1 rows inactive) and "KDA Chunk
@@ -20,18 +21,72 @@ namespace {
 constexpr int K = kda::kHead;
 constexpr int V = kda::kHead;
 
-__global__ __launch_bounds__(256) void decode_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const uint16_t* __restrict__ beta,
-    uint16_t* __restrict__ pool, int64_t slot_stride, int64_t num_slots,
-    const int32_t* __restrict__ state_indices, int H, int HV, uint4* __restrict__ o) {
+// Where one decode step reads its per-row inputs.  The kernel is the same
+// for both forms; only these accessors differ.
+
+// Separate tensors: q, k [B, H, K]; v [B, HV, V]; g [B, HV, K] (log decay);
+// beta [B, HV].  Value head hv reads Q/K head hv / (HV / H).
+struct SplitInputs {
+  const uint4* q;
+  const uint4* k;
+  const uint16_t* v;
+  const float* g;
+  const uint16_t* beta;
+  int H;
+  __device__ const uint4* qk_row(int b, int hv, int HV, bool key) const {
+    const int hq = hv / (HV / H);
+    return (key ? k : q) + (int64_t(b) * H + hq) * (K / 8);
+  }
+  __device__ float decay(int b, int hv, int HV, int j) const {
+    return expf(g[(int64_t(b) * HV + hv) * K + j]);
+  }
+  __device__ float value(int b, int hv, int HV, int j) const {
+    return kda::bf16f(v[(int64_t(b) * HV + hv) * V + j]);
+  }
+  __device__ float beta_of(int b, int hv, int HV) const { return kda::bf16f(beta[int64_t(b) * HV + hv]); }
+};
+
+// Page "flashinfer.kda_decode.packed_kda_decode": one packed bf16 row per
+// batch row holding q | k | v (each [H, 128], head-major; H == HV), raw
+// gate logits [B, H*K], raw beta logits [B, H], per-head A_log and
+// per-channel dt_bias.  The lower-bound gate transform (lower_bound = -5)
+// is read as g = -5 * sigmoid(exp(A_log[h]) * (raw + dt_bias)) -- the page
+// names the transform and its parameters but not the formula -- and
+// beta = sigmoid(raw_beta).  All in float32.
+struct PackedInputs {
+  const uint16_t* qkv;
+  int64_t row_stride;
+  const uint16_t* raw_gate;
+  const uint16_t* raw_beta;
+  const float* A_log;
+  const float* dt_bias;
+  static constexpr float kLowerBound = -5.0f;
+  __device__ const uint4* qk_row(int b, int hv, int HV, bool key) const {
+    return reinterpret_cast<const uint4*>(qkv + int64_t(b) * row_stride + (key ? HV * K : 0) + hv * K);
+  }
+  __device__ float decay(int b, int hv, int HV, int j) const {
+    const float x = kda::bf16f(raw_gate[(int64_t(b) * HV + hv) * K + j]) + dt_bias[hv * K + j];
+    const float z = expf(A_log[hv]) * x;
+    return expf(kLowerBound / (1.0f + expf(-z)));
+  }
+  __device__ float value(int b, int hv, int HV, int j) const {
+    return kda::bf16f(qkv[int64_t(b) * row_stride + 2 * HV * K + hv * V + j]);
+  }
+  __device__ float beta_of(int b, int hv, int HV) const {
+    return 1.0f / (1.0f + expf(-kda::bf16f(raw_beta[int64_t(b) * HV + hv])));
+  }
+};
+
+template <class In>
+__global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict__ pool, int64_t slot_stride,
+                                                     int64_t num_slots, const int32_t* __restrict__ state_indices,
+                                                     int HV, uint4* __restrict__ o) {
   __shared__ float s_q[K], s_k[K], s_eg[K], s_v[V];
   __shared__ float s_red[3][4][V];   // [k^T S | q^T S | q.k][wave][column]
 
   const int t = threadIdx.x;
   const int hv = blockIdx.x;
   const int b = blockIdx.y;
-  const int hq = hv / (HV / H);
   const int cg = t & 15;        // column group: columns 8*cg .. 8*cg+7
   const int kr = t >> 4;        // row group: rows kr + 16*i
   const int wave = t >> 6;
@@ -52,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     // Lanes 0-15 hold the q row, 16-31 the k row; the loads are unconditional
     // (a load inside a branch would be waited for inside it).
     const int lane = t;
-    const uint4* src = (lane < 16 ? q : k) + (int64_t(b) * H + hq) * (K / 8) + (lane & 15);
+    const uint4* src = in.qk_row(b, hv, HV, lane >= 16) + (lane & 15);
     const uint4 xl = *src;
     const uint4 x = lane < 32 ? xl : make_uint4(0u, 0u, 0u, 0u);
     uint4 y = kda::l2norm_row16(x);
@@ -68,14 +123,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
   } else if (wave == 1) {
     const int j = t - 64;
-    s_eg[j] = expf(g[row_head * K + j]);
-    s_eg[j + 64] = expf(g[row_head * K + j + 64]);
+    s_eg[j] = in.decay(b, hv, HV, j);
+    s_eg[j + 64] = in.decay(b, hv, HV, j + 64);
   } else if (wave == 2) {
     const int j = t - 128;
-    s_v[j] = kda::bf16f(v[row_head * V + j]);
-    s_v[j + 64] = kda::bf16f(v[row_head * V + j + 64]);
+    s_v[j] = in.value(b, hv, HV, j);
+    s_v[j + 64] = in.value(b, hv, HV, j + 64);
   }
-  const float bt = kda::bf16f(beta[row_head]);
+  const float bt = in.beta_of(b, hv, HV);
   __syncthreads();
 
   float sd[8][8];
@@ -174,10 +229,45 @@ extern "C" int kda_decode(const void* q, const void* k, const void* v, const flo
       (state_pool && !kda::aligned16(state_pool)))
     return KDA_ERR_ALIGN;
   if (B > 65535) return KDA_ERR_SHAPE;
-  hipLaunchKernelGGL(decode_kernel, dim3(HV, B), dim3(256), 0, kda::as_stream(stream),
-                     static_cast<const uint4*>(q), static_cast<const uint4*>(k),
-                     static_cast<const uint16_t*>(v), g, static_cast<const uint16_t*>(beta),
-                     static_cast<uint16_t*>(state_pool), slot_stride, num_slots, state_indices,
-                     int(H), int(HV), static_cast<uint4*>(o));
+  SplitInputs in;
+  in.q = static_cast<const uint4*>(q);
+  in.k = static_cast<const uint4*>(k);
+  in.v = static_cast<const uint16_t*>(v);
+  in.g = g;
+  in.beta = static_cast<const uint16_t*>(beta);
+  in.H = H;
+  hipLaunchKernelGGL(decode_kernel<SplitInputs>, dim3(HV, B), dim3(256), 0, kda::as_stream(stream), in,
+                     static_cast<uint16_t*>(state_pool), slot_stride, num_slots, state_indices, int(HV),
+                     static_cast<uint4*>(o));
+  return kda::launch_status();
+}
+
+extern "C" int kda_packed_decode(const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_gate,
+                                 const void* raw_beta, const float* A_log, const float* dt_bias,
+                                 void* state_pool, int64_t slot_stride, int64_t num_slots,
+                                 const int32_t* state_indices, int32_t B, int32_t H, int32_t Kd,
+                                 int32_t Vd, void* o, void* stream) {
+  if (B < 0 || H < 1 || num_slots < 0) return KDA_ERR_SHAPE;
+  if (Kd != K || Vd != V) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (!mixed_qkv || !raw_gate || !raw_beta || !A_log || !dt_bias || !state_indices || !o)
+    return KDA_ERR_NULL;
+  if (num_slots > 0 && !state_pool) return KDA_ERR_NULL;
+  if (qkv_row_stride < int64_t(3) * H * K) return KDA_ERR_SHAPE;
+  if (slot_stride < int64_t(H) * K * V) return KDA_ERR_SHAPE;
+  if (qkv_row_stride % 8 != 0 || slot_stride % 8 != 0) return KDA_ERR_ALIGN;
+  if (!kda::aligned16(mixed_qkv) || !kda::aligned16(o) || (state_pool && !kda::aligned16(state_pool)))
+    return KDA_ERR_ALIGN;
+  if (B > 65535) return KDA_ERR_SHAPE;
+  PackedInputs in;
+  in.qkv = static_cast<const uint16_t*>(mixed_qkv);
+  in.row_stride = qkv_row_stride;
+  in.raw_gate = static_cast<const uint16_t*>(raw_gate);
+  in.raw_beta = static_cast<const uint16_t*>(raw_beta);
+  in.A_log = A_log;
+  in.dt_bias = dt_bias;
+  hipLaunchKernelGGL(decode_kernel<PackedInputs>, dim3(H, B), dim3(256), 0, kda::as_stream(stream), in,
+                     static_cast<uint16_t*>(state_pool), slot_stride, num_slots, state_indices, int(H),
+                     static_cast<uint4*>(o));
   return kda::launch_status();
 }

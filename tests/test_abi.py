@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_qk_l2norm",
-              "kda_state_to_pool", "kda_status_string"):
+              "kda_packed_decode", "kda_state_to_pool", "kda_status_string"):
         assert n in names
     assert set(names) == set(kda.EXPORTS)
 
@@ -129,3 +129,28 @@ def test_state_to_pool_metadata_errors():
     assert _to_pool(lib, stride=12 * 128 * 128 + 4) == 4
     assert _to_pool(lib, state=MISALIGNED) == 4
     assert _to_pool(lib, pool=MISALIGNED) == 4
+
+
+def _packed(lib, **kw):
+    a = dict(qkv=FAKE, rs=3 * 12 * 128, rg=FAKE, rb=FAKE, al=FAKE, dt=FAKE, pool=FAKE,
+             stride=12 * 128 * 128, n=8, idx=FAKE, B=4, H=12, K=128, V=128, o=FAKE)
+    a.update(kw)
+    return lib.kda_packed_decode(a["qkv"], a["rs"], a["rg"], a["rb"], a["al"], a["dt"], a["pool"], a["stride"],
+                                 a["n"], a["idx"], a["B"], a["H"], a["K"], a["V"], a["o"], NULL)
+
+
+def test_packed_decode_metadata_errors():
+    lib = kda.load()
+    assert _packed(lib, B=0) == 0
+    assert _packed(lib, B=-1) == 2
+    assert _packed(lib, H=0) == 2
+    assert _packed(lib, K=64) == 3
+    assert _packed(lib, qkv=NULL) == 1
+    assert _packed(lib, al=NULL) == 1
+    assert _packed(lib, dt=NULL) == 1
+    assert _packed(lib, pool=NULL) == 1
+    assert _packed(lib, rs=3 * 12 * 128 - 8) == 2
+    assert _packed(lib, rs=3 * 12 * 128 + 4) == 4
+    assert _packed(lib, stride=100) == 2
+    assert _packed(lib, qkv=MISALIGNED) == 4
+    assert _packed(lib, o=MISALIGNED) == 4
