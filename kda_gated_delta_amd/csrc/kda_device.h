@@ -37,17 +37,18 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float32 -> bfloat16 bits, round to nearest, ties to even (exact for
-// subnormals and infinities; NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet_nan = (u >> 16) | 0x40u;
-  return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded;   // a select, not a branch
+// float32 pair -> packed bf16 (lo in bits 0..15), round to nearest, ties
+// to even, with the hardware conversion.  Checked on MI355X against an
+// integer round-to-nearest-even over all 2^32 float32 inputs: identical,
+// subnormals and infinities included, and NaN stays NaN.  Inline assembly
+// keeps the compiler from merging it with a float64 -> float32 rounding
+// that precedes it (the two roundings must stay two).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return cvt_pk_bf16(lo, hi); }
 
 // ---------------------------------------------------------------- streaming access
 
@@ -159,15 +160,6 @@ __device__ __forceinline__ int row8_min(int x) {
   return x;
 }
 
-// float32 pair -> packed bf16, round to nearest even, with the hardware
-// conversion; inline assembly keeps the compiler from merging it with the
-// float64 -> float32 rounding that precedes it.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
-}
-
 // ---------------------------------------------------------------- row norm
 
 // Normalise one row of 128 bf16 held by a 16-lane group (lanes sharing
@@ -245,9 +237,10 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
   const float t = s32 + 1e-6f;
   const float d = (float)__builtin_sqrt((double)t);
   const double r = 1.0 / (double)d;
-  // Integer round-to-nearest-even on the float32 quotient: written as a
-  // (__bf16) cast of (float)(double), the two roundings can be folded into
-  // one conversion from float64, which is not the same result.
+  // Round the float32 quotient to bf16: two separate roundings (float64 ->
+  // float32, then float32 -> bf16).  A (__bf16) cast of (float)(double)
+  // could be folded into one conversion from float64, which is not the same
+  // result; the conversion is therefore written in assembly.
   uint32_t y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] = pack_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
