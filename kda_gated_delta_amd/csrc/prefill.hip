@@ -1014,14 +1014,16 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float* sGam = reinterpret_cast<const float*>(cur + WS_GAM);
 
     // v as the B operand of U = A v: tokens 32s + 8gq + e of column `col`.
+    // Rows past the chunk's end hold copies of its last row (finite) and
+    // need no masking: their beta is zero, so their columns of A are exact
+    // zeros.
     f16x8 Vv[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 32 * s + 8 * gq + e;
-        const float x = bf16f(*reinterpret_cast<const uint16_t*>(sv + i * 32 + l16 * 2));
-        Vv[s][e] = (_Float16)((i < nvalid) ? x : 0.f);
+        Vv[s][e] = (_Float16)bf16f(*reinterpret_cast<const uint16_t*>(sv + i * 32 + l16 * 2));
       }
     // This wave's v slot is free once its reads are done: fetch the next
     // chunk's, then the first part of the next slot.
@@ -1047,6 +1049,8 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) oW[4 * s + mt] = swz_read(sW, 16 * mt + l16, 256, 4 * s + gq);
+    // S as the fp16 operand of the products with S; then, in the same pass
+    // over the accumulators, the decay e^{G_last} S of the state update.
     f16x8 Sh[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1055,6 +1059,15 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         Sh[s][r] = (_Float16)S[2 * s][r];
         Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
       }
+    {
+      f32x4 gam[8];
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) gam[rt] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * gq);
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[rt][r] *= gam[rt][r];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
@@ -1113,20 +1126,13 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) oK[8 * s + rt] = swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq);
-    f32x4 gam[8];
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) gam[rt] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * gq);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0, i = 0; mt < 4; ++mt)
 #pragma unroll
       for (int s = 0; s <= (mt >> 1); ++s)
         Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vh[s], oQK[i++], Ot[mt], 0, 0, 0);
-    // S = e^{G_last} S + Kg^T Vnew; eight independent row tiles.
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[rt][r] *= gam[rt][r];
+    // S = (e^{G_last} S) + Kg^T Vnew; eight independent row tiles.
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
