@@ -123,6 +123,30 @@ size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
                                         int32_t K, int32_t V, int32_t num_seqs);
 
 /*
+ * kda_chunk_prefill_fused -- the same operation as kda_chunk_prefill, in
+ * the fused partition: one workgroup per (sequence, value head) walks that
+ * sequence's chunks in order and keeps everything on chip -- the chunk-local
+ * matrices of each chunk go straight from LDS into the carry, against a
+ * float32 state held in registers -- so no workspace is read or written.
+ *
+ * Defined on "KDA Chunk Prefill on Ascend A3", sections "Function and
+ * tensor contract" and "Mathematical definition", exactly as
+ * kda_chunk_prefill (same arguments minus the workspace, same results up
+ * to floating-point rounding: both use the same per-chunk arithmetic and
+ * operand precisions).  The page's design discussion weighs the two
+ * partitions; this export lets them be measured side by side.  It
+ * parallelises over N * HV (sequence, value head) units only, so it fills
+ * the chip only when N * HV is at least the number of compute units.
+ */
+int kda_chunk_prefill_fused(const void* q, const void* k, const void* v,
+                            const float* g, const void* beta,
+                            const float* initial_state,
+                            const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t B, int32_t T, int32_t H, int32_t HV,
+                            int32_t K, int32_t V,
+                            void* o, float* final_state, void* stream);
+
+/*
  * kda_decode -- one recurrent KDA step per batch row against a bf16 state
  * pool, updated in place.
  *

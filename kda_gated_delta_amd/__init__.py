@@ -11,6 +11,7 @@ Entry points (same names as the C ABI, without the ``kda_`` prefix):
   qk_l2norm(x)                                    -> y
   chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
                                                   -> (o, final_state)
+  chunk_prefill_fused(...same...)                 -> (o, final_state)
   decode(q, k, v, g, beta, state_pool, state_indices)   -> o
   packed_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool,
                 state_indices)                    -> o
@@ -24,7 +25,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
-EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill",
+EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
            "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
            "kda_state_to_pool")
 
@@ -55,6 +56,9 @@ def load():
     lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                       _vp, ctypes.c_size_t, _vp]
+    lib.kda_chunk_prefill_fused.restype = ctypes.c_int
+    lib.kda_chunk_prefill_fused.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.kda_decode.restype = ctypes.c_int
@@ -121,14 +125,7 @@ def workspace_size(B, T, H, HV, num_seqs=0, K=128, V=128):
     return int(load().kda_chunk_prefill_workspace_size(B, T, H, HV, K, V, num_seqs))
 
 
-def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
-                  out=None, final_state=None, workspace=None):
-    """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
-    fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
-    cu_seqlens int32 [N+1] (with B == 1) or None; workspace: a uint8 GPU
-    tensor of at least workspace_size(...) bytes, or None to allocate one.
-    Returns (o, final_state)."""
-    lib = load()
+def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state):
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
     B, T, H, K = q.shape
@@ -156,6 +153,19 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     _need(out, "out", torch.bfloat16, 4, dev)
     _need(final_state, "final_state", torch.float32, 4, dev)
     nseq_arg = N if cu_seqlens is not None else 0
+    return dev, (B, T, H, HV, K, V), nseq_arg, out, final_state
+
+
+def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                  out=None, final_state=None, workspace=None):
+    """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
+    fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
+    cu_seqlens int32 [N+1] (with B == 1) or None; workspace: a uint8 GPU
+    tensor of at least workspace_size(...) bytes, or None to allocate one.
+    Returns (o, final_state)."""
+    lib = load()
+    dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     need = workspace_size(B, T, H, HV, nseq_arg, K, V)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -165,6 +175,20 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                                  B, T, H, HV, K, V, _ptr(out), _ptr(final_state),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(code, "kda_chunk_prefill")
+    return out, final_state
+
+
+def chunk_prefill_fused(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                        out=None, final_state=None):
+    """The same prefill in the fused partition (one workgroup per sequence
+    and value head, no workspace).  Arguments and result as chunk_prefill."""
+    lib = load()
+    dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    code = lib.kda_chunk_prefill_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
+                                       B, T, H, HV, K, V, _ptr(out), _ptr(final_state), _stream())
+    _check(code, "kda_chunk_prefill_fused")
     return out, final_state
 
 

@@ -38,17 +38,27 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 // float32 pair -> packed bf16 (lo in bits 0..15), round to nearest, ties
-// to even, with the hardware conversion.  Checked on MI355X against an
-// integer round-to-nearest-even over all 2^32 float32 inputs: identical,
-// subnormals and infinities included, and NaN stays NaN.  Inline assembly
-// keeps the compiler from merging it with a float64 -> float32 rounding
-// that precedes it (the two roundings must stay two).
+// to even: the hardware conversion v_cvt_pk_bf16_f32, checked on MI355X
+// against an integer round-to-nearest-even over all 2^32 float32 inputs
+// (identical, subnormals and infinities included; NaN stays NaN).
+//
+// pack_bf16 is the compiler-visible form, for any float32 input -- in
+// particular MFMA results, whose readers need wait states that the compiler
+// inserts only for instructions it can see.  cvt_pk_bf16 is the same
+// instruction in inline assembly, used only where the inputs come from a
+// float64 -> float32 rounding by ordinary vector instructions: there it
+// keeps the compiler from merging the two roundings into one.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   uint32_t r;
   asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
   return r;
 }
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return cvt_pk_bf16(lo, hi); }
 
 // ---------------------------------------------------------------- streaming access
 
@@ -243,7 +253,7 @@ __device__ __forceinline__ uint4 l2norm_row16(uint4 x) {
   // result; the conversion is therefore written in assembly.
   uint32_t y[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = pack_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
+  for (int i = 0; i < 4; ++i) y[i] = cvt_pk_bf16((float)(xd[2 * i] * r), (float)(xd[2 * i + 1] * r));
   return make_uint4(y[0], y[1], y[2], y[3]);
 }
 

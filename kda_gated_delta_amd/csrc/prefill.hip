@@ -137,6 +137,10 @@ constexpr int OFF_BETA = OFF_KGT + KD * AS * 2;           // fp32 [64]
 constexpr int OFF_GAM = OFF_BETA + C * 4;                 // fp32 [128]
 constexpr int INTRA_LDS = OFF_GAM + KD * 4;
 static_assert(INTRA_LDS <= 160 * 1024, "LDS budget");
+// The fused form adds one v tile per wave (64 tokens x 16 columns, bf16).
+constexpr int OFF_VT = INTRA_LDS;
+constexpr int FUSED_LDS = OFF_VT + NW * C * 16 * 2;
+static_assert(FUSED_LDS <= 160 * 1024, "LDS budget (fused)");
 static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
 static_assert(KD * AS * 2 >= 2 * 4 * 512 * 4, "phase 2 partial sums fit in the Kg^T region");
 
@@ -363,6 +367,39 @@ __device__ __forceinline__ int slot_owner(const Params& p, int s, int& chunk) {
   return lo;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int WAIT_LDS = 0xC07F;   // s_waitcnt lgkmcnt(0)
+constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
+// Word 3 of a raw (untyped) buffer resource on gfx9-family chips: 32-bit
+// data format, no swizzle.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+constexpr int WAIT_VM4 = 0x0F74;   // s_waitcnt vmcnt(4): low vmcnt bits 3:0, high bits 15:14 zero
+constexpr int WAIT_VM0 = 0x0F70;   // s_waitcnt vmcnt(0) only
+
+// Direct load of this wave's v tile (64 tokens x 16 columns from column c0,
+// bf16) into its LDS region: two 1 KB blocks, lane l carrying token
+// 32h + l/2, columns c0 + 8*(l&1)..+7.  Rows past the chunk's end are clamped
+// here and zeroed when read.
+__device__ __forceinline__ void load_v_lds(unsigned char* sv, const Params& p, int64_t trow, int nvalid,
+                                           int hv, int c0, int lane) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = min(32 * h + (lane >> 1), nvalid - 1);
+    const uint16_t* src = p.v + ((trow + t) * p.HV + hv) * KD + c0 + 8 * (lane & 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (lds_void*)(sv + h * 1024), 16, 0, 0);
+  }
+}
+
+// kFused = false: the chunk-parallel half of the split form (persistent,
+// items over the whole chip, outputs to the workspace).  kFused = true: the
+// fused form -- one workgroup per (sequence, value head) walks its chunks in
+// order and, instead of writing the chunk's matrices out, applies the carry
+// to a float32 state held in registers (wave w owns state columns
+// 16w..16w+15), reading every operand from LDS where phase 4 left it.
+template <bool kFused>
 __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
@@ -386,17 +423,40 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  // Work item i = slot * HV + hv; this workgroup takes items blockIdx.x,
-  // blockIdx.x + gridDim.x, ...  Slots between sequences are skipped.
-  // Item ids fit in 32 bits (checked on the host).
-  const int items = int(p.nslots) * p.HV;
-  const int stride = gridDim.x;
+  // Split form: work item i = slot * HV + hv; this workgroup takes items
+  // blockIdx.x, blockIdx.x + gridDim.x, ...  Slots between sequences are
+  // skipped.  Item ids fit in 32 bits (checked on the host).
+  // Fused form: workgroup u owns unit u = (sequence n, value head hv) and its
+  // items are that sequence's chunks, in order.
+  int items, stride;
+  int unit_n = 0, unit_hv = 0, unit_len = 0;
+  int64_t unit_tok0 = 0;
+  if constexpr (kFused) {
+    const int unit = blockIdx.x;             // the grid has exactly N * HV workgroups
+    unit_n = unit / p.HV;
+    unit_hv = unit - unit_n * p.HV;
+    seq_range(p, unit_n, unit_tok0, unit_len);
+    items = (unit_len + C - 1) / C;
+    stride = 1;
+  } else {
+    items = int(p.nslots) * p.HV;
+    stride = gridDim.x;
+  }
   struct Item {
     int64_t trow;
     int id, slot, hv, hq, nvalid;
   };
   auto find = [&](int i) {
     Item it;
+    if constexpr (kFused) {
+      it.id = i;
+      it.trow = unit_tok0 + int64_t(i) * C;
+      it.nvalid = min(C, unit_len - i * C);
+      it.slot = i;
+      it.hv = unit_hv;
+      it.hq = unit_hv / (p.HV / p.H);
+      return it;
+    }
     for (; i < items; i += stride) {
       const int s = i / p.HV;
       int c;
@@ -416,11 +476,123 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     return it;
   };
 
-  Item first = find(blockIdx.x);
-  if (first.id >= items) return;
+  // Fused form: this wave's 128x16 slice of the state (rows 16rt + 4gq + r of
+  // column 16 * wave + l16), float32, for the whole sequence.
+  f32x4 S[8];
+  unsigned char* sVt = smem + OFF_VT + wave * (C * 16 * 2);
+  if constexpr (kFused) {
+    const int col = 16 * wave + l16;
+    if (p.s0) {   // one branch around all 32 loads, so they are in flight together
+      const float* s0 = p.s0 + (int64_t(unit_n) * p.HV + unit_hv) * KD * KD;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[rt][r] = s0[(16 * rt + 4 * gq + r) * KD + col];
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  auto write_final_state = [&]() __attribute__((always_inline)) {
+    if constexpr (kFused) {
+      float* sf = p.sfin + (int64_t(unit_n) * p.HV + unit_hv) * KD * KD;
+      const int col = 16 * wave + l16;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
+    }
+  };
+
+  Item first = find(kFused ? 0 : int(blockIdx.x));
+  if (first.id >= items) {
+    write_final_state();   // fused form, empty sequence: the state passes through
+    return;
+  }
   Raw R;
   load_raw_qk(R, p, first.trow, first.nvalid, first.hq, tid);
   load_raw_g(R, p, first.trow, first.nvalid, first.hv, tid);
+
+  // Fused form: the carry of chunk `cur` on this wave's 16 state columns,
+  //   U = A v,  Vnew = U - W S,  O = Qg S + Aqk Vnew,
+  //   S = e^{G_last} S + Kg^T Vnew,
+  // on MFMA with the operands where phase 4 left them in LDS (logical
+  // order; W, Qg, Kg^T and Aqk in the permuted contraction order that lets
+  // the float32 accumulators serve directly as fp16 operands).
+  auto carry = [&](const Item& cur) __attribute__((always_inline)) {
+    const int c0 = 16 * wave;
+    // The v tile was loaded with direct global-to-LDS loads by this wave.
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    f16x8 Vv[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Vv[s][e] = (_Float16)bf16f(*reinterpret_cast<const uint16_t*>(sVt + (32 * s + 8 * gq + e) * 32 + l16 * 2));
+    f16x8 Sh[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Sh[s][r] = (_Float16)S[2 * s][r];
+        Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
+      }
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * gq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[rt][r] *= gm[r];
+    }
+    // U = A v, then Vnew = U + (-W) S; A is lower triangular.
+    f32x4 Vn[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16x8(sA + (16 * mt + l16) * AS + 32 * s + 8 * gq), Vv[s],
+                                                     acc, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16x8(sW + (16 * mt + l16) * QS + 32 * s + 8 * gq), Sh[s],
+                                                     acc, 0, 0, 0);
+      Vn[mt] = acc;
+    }
+    f16x8 Vh[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Vh[s][r] = (_Float16)Vn[2 * s][r];
+        Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
+      }
+    // O^T = S^T Qg^T + Vnew^T Aqk^T: each lane ends with four adjacent
+    // columns of one token.
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.o + (cur.trow * p.HV + cur.hv) * KD, 0, cur.nvalid * p.HV * KD * 2, BUF_RSRC_WORD3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Sh[s], lds_f16x8(sQ + (16 * mt + l16) * QS + 32 * s + 8 * gq),
+                                                     acc, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vh[s], lds_f16x8(sAqk + (16 * mt + l16) * AS + 32 * s + 8 * gq),
+                                                     acc, 0, 0, 0);
+      const int t = 16 * mt + l16;
+      const u32x2_t w = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, (t * p.HV * KD + c0 + 4 * gq) * 2, 0, 0);
+    }
+    // S = (e^{G_last} S) + Kg^T Vnew.
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds_f16x8(sKgT + (16 * rt + l16) * AS + 32 * s + 8 * gq), Vh[s],
+                                                       S[rt], 0, 0, 0);
+  };
 
   // One chunk item: consumes R (cur's inputs), refills it with nxt's.
   // `first`: q and k of this item were not normalised at the end of the
@@ -637,6 +809,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 
     // ---------------------------------------------------------- phase 3: solve
     if (nxt.id < items) load_raw_g(R, p, nxt.trow, nxt.nvalid, nxt.hv, tid);
+    // Fused form: this chunk's v tile for the wave's 16 state columns, for
+    // the carry at the end of the item.
+    if constexpr (kFused) load_v_lds(sVt, p, cur.trow, cur.nvalid, cur.hv, 16 * wave, lane);
     // T = (I + L)^-1, unit lower triangular.
     // Diagonal 16x16 blocks: wave b < 4 inverts block b.  Lane 4*cc + h holds
     // rows 4h..4h+3 of column cc and the matching rows of L in registers;
@@ -841,6 +1016,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     }
     lds_barrier();
 
+    if constexpr (!kFused) {
     // Chunk outputs -> workspace slot, in slot order (coalesced 16-byte
     // stores), gathering each piece from its swizzled source position.  A
     // fixed number of unconditional stores per thread (the overhang repeats
@@ -876,8 +1052,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         kda::store_nt(reinterpret_cast<uint4*>(dst + b), *reinterpret_cast<const uint4*>(src));
       }
     }
+    } else {
+      carry(cur);
+    }
     // While those stores drain (the vector ALUs are otherwise idle here),
-    // normalise the next item's q and k, prefetched in phase 2.
+    // normalise the next item's q and k, prefetched in phase 2.  (Fused
+    // form: after the carry.)
     if (nxt.id < items) norm_raw_qk(R, tid);
     lds_barrier();
   };
@@ -895,9 +1075,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     nxt = find(cur.id + stride);
     chunk(cur, nxt, false);
   }
+  write_final_state();
 }
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global-to-LDS copy of part of one workspace slot: 1 KB blocks,
 // wave w issuing blocks w, w + 4, ... (its j-th block for j in [j0, j1)).
@@ -916,33 +1095,11 @@ __device__ __forceinline__ void load_slot_part(unsigned char* buf, const unsigne
   }
 }
 
-// Direct load of this wave's v tile (64 tokens x 16 columns from column c0,
-// bf16) into its LDS region: two 1 KB blocks, lane l carrying token
-// 32h + l/2, columns c0 + 8*(l&1)..+7.  Rows past the chunk's end are clamped
-// here and zeroed when read.
-__device__ __forceinline__ void load_v_lds(unsigned char* sv, const Params& p, int64_t trow, int nvalid,
-                                           int hv, int c0, int lane) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = min(32 * h + (lane >> 1), nvalid - 1);
-    const uint16_t* src = p.v + ((trow + t) * p.HV + hv) * KD + c0 + 8 * (lane & 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                     (lds_void*)(sv + h * 1024), 16, 0, 0);
-  }
-}
-
 // 16-byte operand read of logical piece `piece` of swizzled row `row`.
 __device__ __forceinline__ f16x8 swz_read(const unsigned char* base, int row, int row_bytes, int piece) {
   return *reinterpret_cast<const f16x8*>(base + row * row_bytes + ((piece ^ (row & 7)) << 4));
 }
 
-constexpr int WAIT_LDS = 0xC07F;   // s_waitcnt lgkmcnt(0)
-constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
-// Word 3 of a raw (untyped) buffer resource on gfx9-family chips: 32-bit
-// data format, no swizzle.
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
-typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-constexpr int WAIT_VM4 = 0x0F74;   // s_waitcnt vmcnt(4): low vmcnt bits 3:0, high bits 15:14 zero
 
 // Slot prefetch split into three groups issued between the products of a
 // chunk, so the vector-memory pipe drains while the matrix cores work.
@@ -1192,7 +1349,7 @@ int device_cus() {
 
 int launch(const Params& p, hipStream_t stream) {
   static std::atomic<bool> intra_set{false}, inter_set{false};
-  if (set_lds(&intra_kernel, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t items = p.nslots * p.HV;
   if (items > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
@@ -1200,11 +1357,52 @@ int launch(const Params& p, hipStream_t stream) {
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t inter_blocks = 16 * ((units + 7) / 8);   // two column halves per unit
   if (inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
-  hipLaunchKernelGGL(intra_kernel, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
+  hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
   const int st = launch_status();
   if (st != KDA_OK) return st;
   hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NTI), INTER_LDS, stream, p);
   return launch_status();
+}
+
+// Fused form: one workgroup per (sequence, value head); no workspace.
+int launch_fused(const Params& p, hipStream_t stream) {
+  static std::atomic<bool> fused_set{false};
+  if (set_lds(&intra_kernel<true>, FUSED_LDS, fused_set) != KDA_OK) return KDA_ERR_HIP;
+  const int64_t units = int64_t(p.N) * p.HV;
+  if (units > 0x7fffffff) return KDA_ERR_SHAPE;
+  hipLaunchKernelGGL(intra_kernel<true>, dim3(unsigned(units)), dim3(NT), FUSED_LDS, stream, p);
+  return launch_status();
+}
+
+// Metadata checks shared by both forms; fills everything but the workspace.
+int prepare(const void* q, const void* k, const void* v, const float* g, const void* beta,
+            const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+            int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd, void* o, float* final_state,
+            Params& p) {
+  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
+  if (!final_state || (T > 0 && (!q || !k || !v || !g || !beta || !o))) return KDA_ERR_NULL;
+  if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+      !aligned16(final_state) || (initial_state && !aligned16(initial_state)))
+    return KDA_ERR_ALIGN;
+  const int64_t nseq = cu_seqlens ? num_seqs : B;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = g;
+  p.beta = static_cast<const uint16_t*>(beta);
+  p.s0 = initial_state;
+  p.cu = cu_seqlens;
+  p.o = static_cast<uint16_t*>(o);
+  p.sfin = final_state;
+  p.ws = nullptr;
+  p.nslots = slots_per_head(int64_t(B) * T, nseq);
+  p.T = T;
+  p.H = H;
+  p.HV = HV;
+  p.N = int(nseq);
+  return KDA_OK;
 }
 
 }  // namespace
@@ -1223,32 +1421,26 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
                                  int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
                                  void* o, float* final_state, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
-  if (!final_state || (T > 0 && (!q || !k || !v || !g || !beta || !o))) return KDA_ERR_NULL;
-  if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
-  if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
-      !aligned16(final_state) || (initial_state && !aligned16(initial_state)) || !aligned16(workspace))
-    return KDA_ERR_ALIGN;
-  const int64_t nseq = cu_seqlens ? num_seqs : B;
-  const size_t need = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, int32_t(nseq));
+  Params p;
+  const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
+                         final_state, p);
+  if (st != KDA_OK) return st;
+  if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+  const size_t need = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N);
   if (!workspace) return KDA_ERR_NULL;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
-  Params p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.g = g;
-  p.beta = static_cast<const uint16_t*>(beta);
-  p.s0 = initial_state;
-  p.cu = cu_seqlens;
-  p.o = static_cast<uint16_t*>(o);
-  p.sfin = final_state;
   p.ws = static_cast<unsigned char*>(workspace);
-  p.nslots = slots_per_head(int64_t(B) * T, nseq);
-  p.T = T;
-  p.H = H;
-  p.HV = HV;
-  p.N = int(nseq);
   return launch(p, as_stream(stream));
+}
+
+extern "C" int kda_chunk_prefill_fused(const void* q, const void* k, const void* v, const float* g,
+                                       const void* beta, const float* initial_state,
+                                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                                       int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
+                                       void* o, float* final_state, void* stream) {
+  Params p;
+  const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
+                         final_state, p);
+  if (st != KDA_OK) return st;
+  return launch_fused(p, as_stream(stream));
 }

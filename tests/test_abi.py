@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_qk_l2norm",
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_fused", "kda_chunk_prefill_workspace_size", "kda_decode",
+              "kda_qk_l2norm",
               "kda_packed_decode", "kda_state_to_pool", "kda_status_string"):
         assert n in names
     assert set(names) == set(kda.EXPORTS)
@@ -154,3 +155,21 @@ def test_packed_decode_metadata_errors():
     assert _packed(lib, stride=100) == 2
     assert _packed(lib, qkv=MISALIGNED) == 4
     assert _packed(lib, o=MISALIGNED) == 4
+
+
+def test_fused_prefill_metadata_errors():
+    lib = kda.load()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
+                 B=1, T=64, H=1, HV=1, K=128, V=128, o=FAKE, fs=FAKE)
+        a.update(kw)
+        return lib.kda_chunk_prefill_fused(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
+                                           a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"], NULL)
+    assert call(q=NULL) == 1
+    assert call(fs=NULL) == 1
+    assert call(H=3, HV=4) == 2
+    assert call(B=0) == 2
+    assert call(K=64) == 3
+    assert call(cu=FAKE, n=2, B=2) == 2
+    assert call(v=MISALIGNED) == 4

@@ -76,7 +76,7 @@ def test_ragged_lengths(gpu_lib, T):
 
 
 def test_many_units_wide_tile(gpu_lib):
-    """(sequence, head) units >= 256 select the 128-column tile."""
+    """256 (sequence, value head) units: more than one per compute unit."""
     _full_check(gpu_lib, synth.prefill_basic(61, 2, 130, 128, 128, init="normal0.1"))
 
 

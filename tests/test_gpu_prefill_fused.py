@@ -1,0 +1,115 @@
+"""kda_chunk_prefill_fused (the fused partition) on the GPU.
+
+Both partitions run the same per-chunk arithmetic with the same operand
+precisions and the same MFMA accumulation orders; the split form only
+passes the chunk-local matrices through the workspace, which stores exactly
+the values the fused form reads from LDS.  So the fused results must equal
+the split results bit for bit, which is checked on every workload shape the
+split form is tested on (the split form itself is checked against the
+oracle in test_gpu_prefill.py); a few cases are also compared with the
+oracle directly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_o, check_state, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _args(inp):
+    dev = "cuda"
+    s0 = None if inp.initial_state is None else inp.initial_state.to(dev)
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev)
+    return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), s0, cu)
+
+
+def _both(kda, inp):
+    say(f"fused vs split {inp.name} shape={inp.shape}")
+    a = _args(inp)
+    of, sf = kda.chunk_prefill_fused(*a)
+    os_, ss = kda.chunk_prefill(*a)
+    torch.cuda.synchronize()
+    return of, sf, os_, ss
+
+
+def _bitwise(kda, inp):
+    of, sf, os_, ss = _both(kda, inp)
+    assert torch.equal(of.view(torch.int16), os_.view(torch.int16)), f"{inp.name}: o differs"
+    assert torch.equal(sf, ss), f"{inp.name}: final state differs"
+    return of, sf
+
+
+def _oracle(inp):
+    a = synth.to_numpy(inp)
+    return oracle.recurrent(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"], a["cu_seqlens"])
+
+
+def test_fused_small_against_oracle(gpu_lib):
+    inp = synth.config0()
+    of, sf = _bitwise(gpu_lib, inp)
+    o_ref, s_ref = _oracle(inp)
+    check_o(of, o_ref, inp.name)
+    check_state(sf, s_ref, inp.name)
+
+
+def test_fused_harsh_decay_ragged_tail(gpu_lib):
+    inp = synth.config1()
+    of, sf = _bitwise(gpu_lib, inp)
+    o_ref, s_ref = _oracle(inp)
+    say(f"  o_err={check_o(of, o_ref, inp.name):.2e} state_err={check_state(sf, s_ref, inp.name):.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129, 200])
+def test_fused_ragged_lengths(gpu_lib, T):
+    _bitwise(gpu_lib, synth.prefill_basic(50 + T, 2, T, 2, 2, init="normal0.1"))
+
+
+def test_fused_worked_example_exact(gpu_lib):
+    inp = synth.worked_example()
+    of, sf = _bitwise(gpu_lib, inp)
+    assert torch.all(of.float() == 0.08837890625)
+
+
+@pytest.mark.parametrize("mode", [("gain", "strong", "edge", "normal"), ("zero_rows", "zero", "edge", "none"),
+                                  ("tiny", "moderate", "sigmoid", "zero")], ids=lambda m: "-".join(m))
+def test_fused_stress(gpu_lib, mode):
+    qk, gate, bm, st = mode
+    _bitwise(gpu_lib, synth.prefill_stress(70, 2, 300, 2, 4, qk_mode=qk, gate=gate, beta_mode=bm, state=st))
+
+
+def test_fused_extreme_gates(gpu_lib):
+    inp = synth.prefill_basic(80, 1, 200, 2, 2, init="normal0.1")
+    inp.g[..., :8] = -15.0
+    inp.g[:, 100:110, :, 8:16] = -40.0
+    _bitwise(gpu_lib, inp)
+
+
+def test_fused_gqa_and_varlen(gpu_lib):
+    lens = [70, 0, 1, 129, 64, 33]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    inp = synth.prefill_basic(90, 1, int(cu[-1]), 2, 4, init="normal0.1", cu_seqlens=cu, name="varlen_small")
+    _bitwise(gpu_lib, inp)
+    _bitwise(gpu_lib, synth.prefill_basic(91, 1, 150, 2, 4, init="none"))
+
+
+def test_fused_zero_length(gpu_lib):
+    inp = synth.prefill_basic(94, 2, 0, 2, 2, init="normal0.1")
+    of, sf = gpu_lib.chunk_prefill_fused(*_args(inp))
+    torch.cuda.synchronize()
+    assert of.numel() == 0 and torch.equal(sf.cpu(), inp.initial_state)
+
+
+def test_fused_full_scale(gpu_lib):
+    """The bench workload (H=HV=96, T=8192), fused == split bitwise."""
+    _bitwise(gpu_lib, synth.config2())
+
+
+def test_fused_many_units_varlen(gpu_lib):
+    """The packed 16-sequence GQA batch (512 units, more than the compute
+    units), fused == split bitwise."""
+    _bitwise(gpu_lib, synth.config3())
