@@ -20,6 +20,9 @@ Prints one JSON line:
   packed_decode  pool) and the packed-input decode (B=256, H=12), each timed
                after the steps with a prefill before every launch, so they
                too meet the caches the way they would in serving
+  prefill_partitions  mean call time of the split and the fused prefill
+               partitions on this workload, on the 16-sequence varlen GQA
+               batch (512 units) and on B=16 H=HV=64 T=2048 (1024 units)
   cpu_baseline the fp64 oracle (token-by-token form) on a bounded sample of
                the same prefill workload, on this host's cores
 Only --gpus 1 is supported: the library runs on one GPU.
@@ -413,6 +416,58 @@ def main():
         "hbm_frac": pkbytes / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     del pk_pool
+    # The two prefill partitions side by side: split (the entry point timed
+    # above: chunk-parallel kernel + workspace + carry kernel) and fused (one
+    # workgroup per sequence and value head, no workspace), on this workload
+    # (96 units) and on the 16-sequence varlen GQA batch (512 units).
+    print("[bench] prefill partitions", file=sys.stderr, flush=True)
+
+    def time_calls(fn, n):
+        evs = []
+        for i in range(args.warmup + n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            if i >= args.warmup:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+
+    partitions = {}
+    n_part = max(3, args.steps // 2)
+    partitions[f"B=1 H=HV={HV} T={T}"] = {
+        "units": B * HV,
+        "split_us": time_calls(lambda: kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf,
+                                                         workspace=ws), n_part),
+        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(q, k, v, g, beta, s0, None, out=o,
+                                                               final_state=sf), n_part),
+    }
+    c3 = synth.config3()
+    c3a = [t.to(dev) for t in (c3.q, c3.k, c3.v, c3.g, c3.beta, c3.initial_state, c3.cu_seqlens)]
+    T3, N3, H3, HV3 = c3.q.shape[1], c3.cu_seqlens.numel() - 1, c3.q.shape[2], c3.v.shape[2]
+    o3 = torch.empty(1, T3, HV3, V, dtype=torch.bfloat16, device=dev)
+    sf3 = torch.empty(N3, HV3, K, V, dtype=torch.float32, device=dev)
+    ws3 = torch.empty(kda.workspace_size(1, T3, H3, HV3, N3), dtype=torch.uint8, device=dev)
+    partitions[f"varlen N={N3} H={H3} HV={HV3} T={T3}"] = {
+        "units": N3 * HV3,
+        "split_us": time_calls(lambda: kda.chunk_prefill(*c3a, out=o3, final_state=sf3, workspace=ws3), n_part),
+        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(*c3a, out=o3, final_state=sf3), n_part),
+    }
+    del c3a, o3, sf3, ws3
+    # Many equal sequences: B=16, H=HV=64, T=2048 (1024 units).
+    c4 = synth.prefill_basic(5, 16, 2048, 64, 64, init="normal0.1", name="b16_h64_t2048")
+    c4a = [t.to(dev) for t in (c4.q, c4.k, c4.v, c4.g, c4.beta, c4.initial_state)]
+    o4 = torch.empty(16, 2048, 64, V, dtype=torch.bfloat16, device=dev)
+    sf4 = torch.empty(16, 64, K, V, dtype=torch.float32, device=dev)
+    ws4 = torch.empty(kda.workspace_size(16, 2048, 64, 64), dtype=torch.uint8, device=dev)
+    partitions["B=16 H=HV=64 T=2048"] = {
+        "units": 16 * 64,
+        "split_us": time_calls(lambda: kda.chunk_prefill(*c4a, None, out=o4, final_state=sf4, workspace=ws4), n_part),
+        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(*c4a, None, out=o4, final_state=sf4), n_part),
+    }
+    del c4a, o4, sf4, ws4
+    result["prefill_partitions"] = partitions
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)
