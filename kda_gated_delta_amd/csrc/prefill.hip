@@ -399,6 +399,26 @@ __device__ __forceinline__ void load_v_lds(unsigned char* sv, const Params& p, i
 // order and, instead of writing the chunk's matrices out, applies the carry
 // to a float32 state held in registers (wave w owns state columns
 // 16w..16w+15), reading every operand from LDS where phase 4 left it.
+// The B operand of U = A v from a wave's v tile ([64 tokens][16 columns],
+// bf16): lane (l16, gq) takes column l16 at tokens 32s + 8gq .. +7.  Each
+// transposing LDS read (ds_read_b64_tr_b16) gathers, in every 16-lane group,
+// element (i & 3) of the 8-byte pieces addressed by lanes (i >> 2) + 4m into
+// lane i: with lane j addressing token base + (j >> 2), columns
+// 4(j & 3)..+3, lane i receives column i of tokens base .. base + 3.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void read_v_operand(const unsigned char* sv, int l16, int gq, f16x8 (&Vv)[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int base = 32 * s + 8 * gq + 4 * h;
+      const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(sv + (base + (l16 >> 2)) * 32 + (l16 & 3) * 8));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Vv[s][4 * h + m] = (_Float16)bf16f(uint16_t(r[m]));
+    }
+}
+
 template <bool kFused>
 __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -524,11 +544,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // The v tile was loaded with direct global-to-LDS loads by this wave.
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
     f16x8 Vv[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vv[s][e] = (_Float16)bf16f(*reinterpret_cast<const uint16_t*>(sVt + (32 * s + 8 * gq + e) * 32 + l16 * 2));
+    read_v_operand(sVt, l16, gq, Vv);
     f16x8 Sh[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1175,13 +1191,7 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // need no masking: their beta is zero, so their columns of A are exact
     // zeros.
     f16x8 Vv[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 32 * s + 8 * gq + e;
-        Vv[s][e] = (_Float16)bf16f(*reinterpret_cast<const uint16_t*>(sv + i * 32 + l16 * 2));
-      }
+    read_v_operand(sv, l16, gq, Vv);
     // This wave's v slot is free once its reads are done: fetch the next
     // chunk's, then the first part of the next slot.
     __builtin_amdgcn_s_waitcnt(WAIT_LDS);
