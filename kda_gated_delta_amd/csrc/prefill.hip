@@ -38,6 +38,14 @@
 //   float32 (U is never rounded), O^T = S^T Qg^T + Vnew^T Aqk^T, and
 //   S = exp(G_last) S + Kg^T Vnew.
 //
+// Fused partition (export kda_chunk_prefill_fused): intra_kernel<true>, one
+//   workgroup per (sequence, value head), runs steps 1-4 for that unit's
+//   chunks in order and, in place of the workspace write, applies the carry
+//   (the inter kernel's products, same order and precision) to a float32
+//   state held by its 8 waves, 16 columns each, reading the operands from
+//   LDS.  It saves the workspace round trip but puts the chunk-local work
+//   on each unit's sequential path, so it pays off only with many units.
+//
 // Precision: every MFMA operand is fp16 with float32 accumulation, and the
 // state is carried in float32.  fp16's 11-bit significand keeps the final
 // state within a few 1e-4 (relative Frobenius) of the float64 recurrence
