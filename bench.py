@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--decode-B", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=8, help="value heads in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--only-steps", action="store_true",
+                    help="time only the steps (prefill + decode); skip the handoff, packed decode and "
+                         "partition measurements (for profiler runs that average per kernel name)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -367,6 +370,11 @@ def main():
             "hbm_frac": dec_gbs / HBM_PEAK_GBS,
         },
     }
+    if args.only_steps:
+        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds) if args.cpu_heads > 0 else None
+        print(json.dumps(result), flush=True)
+        return
+
     # Prefill-to-decode handoff, timed on its own after the steps: the decode
     # workload's rows each hand a fresh fp32 state to their pool slot.  As
     # for the decode, a prefill runs before every launch, so each launch
