@@ -118,10 +118,13 @@ constexpr int WS_SLOT = WS_GAM + KD * 4;          // 66048 bytes
 static_assert(WS_SLOT % 16 == 0, "slots stay 16-byte aligned");
 
 // LDS row strides (elements).  Row strides of 68 or 36 words put eight
-// consecutive rows' 16-byte accesses in distinct bank groups.
+// consecutive rows' 16-byte accesses in distinct bank groups.  (Measured:
+// the phase-2 reads, whose four lane groups sit 16 or 32 bytes apart, still
+// see two-way conflicts; 288- and 544-byte strides with a channel
+// permutation of G remove a third of the kernel's conflict cycles but ran no
+// faster, the kernel being bound by vector ALU work and latency.)
 constexpr int QS = 136;          // 16-bit [64][128] arrays
 constexpr int GS = 132;          // fp32 [64][128] (G)
-constexpr int OS = 136;          // bf16 [64][128] (o staging)
 constexpr int LS = 68;           // fp32 [64][64] arrays
 constexpr int AS = 72;           // 16-bit [*][64] arrays
 
@@ -1340,13 +1343,18 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
 }
 
+// Raise a kernel's dynamic-LDS limit, once per device (the attribute is a
+// property of the function on the current device).
+constexpr int kMaxDevices = 64;
 template <typename Kern>
-int set_lds(Kern kern, int bytes, std::atomic<bool>& done) {
-  if (!done.load(std::memory_order_acquire)) {
+int set_lds(Kern kern, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+  if (!done[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             bytes) != hipSuccess)
       return KDA_ERR_HIP;
-    done.store(true, std::memory_order_release);
+    done[dev].store(true, std::memory_order_release);
   }
   return KDA_OK;
 }
@@ -1355,9 +1363,9 @@ int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq 
 
 // Compute units of the current device (cached per device).
 int device_cus() {
-  static std::atomic<int> cache[64];
+  static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
@@ -1366,7 +1374,7 @@ int device_cus() {
 }
 
 int launch(const Params& p, hipStream_t stream) {
-  static std::atomic<bool> intra_set{false}, inter_set{false};
+  static std::atomic<bool> intra_set[kMaxDevices], inter_set[kMaxDevices];
   if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t items = p.nslots * p.HV;
@@ -1384,7 +1392,7 @@ int launch(const Params& p, hipStream_t stream) {
 
 // Fused form: one workgroup per (sequence, value head); no workspace.
 int launch_fused(const Params& p, hipStream_t stream) {
-  static std::atomic<bool> fused_set{false};
+  static std::atomic<bool> fused_set[kMaxDevices];
   if (set_lds(&intra_kernel<true>, FUSED_LDS, fused_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t units = int64_t(p.N) * p.HV;
   if (units > 0x7fffffff) return KDA_ERR_SHAPE;
