@@ -21,6 +21,7 @@ Modules
   decode     one recurrent step against a bf16 state pool
   handoff    prefill final states stored into the bf16 decode pool
   packed_decode  the decode step from packed QKV and raw gate/beta logits
+  backward   gradients of the forward by float64 autodiff of the recurrence
 
 Pinning status: every public function here is pinned by tests that do not
 re-type its formula (closed forms, the pages' worked example, invariants,
@@ -37,6 +38,7 @@ from .chunked import chunked
 from .decode import decode_step
 from .handoff import state_to_pool
 from .packed_decode import packed_decode_step
+from .backward import recurrent_backward
 
 __all__ = [
     "bf16_round",
@@ -49,4 +51,5 @@ __all__ = [
     "decode_step",
     "state_to_pool",
     "packed_decode_step",
+    "recurrent_backward",
 ]

@@ -1,0 +1,104 @@
+"""Pins for the oracle's backward (float64 autodiff of the recurrence).
+
+The differentiation is checked against central finite differences of an
+independently written float64 forward (plain NumPy loop) on tiny shapes,
+with the bf16 rounding of q^, k^ switched off so that the function is
+smooth; against the closed form of a single token from a zero state; and
+against two structural identities (beta = 0 makes v irrelevant; a shared
+Q/K head receives the sum of its value heads' gradients).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _forward_loss(q, k, v, g, beta, s0, do, dht):
+    """Independent float64 forward: normalise, run the recurrence, return
+    sum(o * do) + sum(S_T * dht).  B = 1, no cu_seqlens."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    grp = HV // H
+    scale = K ** -0.5
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6)
+    kn = k / np.sqrt((k * k).sum(-1, keepdims=True) + 1e-6)
+    loss = 0.0
+    S = [s0[0, h].copy() for h in range(HV)]
+    for t in range(T):
+        for h in range(HV):
+            qq, kk = qn[0, t, h // grp], kn[0, t, h // grp]
+            Sd = np.exp(g[0, t, h])[:, None] * S[h]
+            r = v[0, t, h] - kk @ Sd
+            S[h] = Sd + beta[0, t, h] * np.outer(kk, r)
+            loss += scale * (qq @ S[h]) @ do[0, t, h]
+    for h in range(HV):
+        loss += (S[h] * dht[0, h]).sum()
+    return loss
+
+
+def _inputs(rng, T=4, H=1, HV=2, K=6, V=5):
+    q = rng.standard_normal((1, T, H, K))
+    k = rng.standard_normal((1, T, H, K))
+    v = rng.standard_normal((1, T, HV, V))
+    g = -0.5 * rng.random((1, T, HV, K))
+    beta = rng.random((1, T, HV))
+    s0 = 0.3 * rng.standard_normal((1, HV, K, V))
+    do = rng.standard_normal((1, T, HV, V))
+    dht = rng.standard_normal((1, HV, K, V))
+    return q, k, v, g, beta, s0, do, dht
+
+
+def test_finite_differences():
+    rng = np.random.default_rng(1)
+    args = _inputs(rng)
+    grads = oracle.recurrent_backward(*args[:6], args[6], args[7], round_bf16=False)
+    eps = 1e-6
+    for which in range(6):
+        x = args[which]
+        for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(4)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            fd = (_forward_loss(*ap) - _forward_loss(*am)) / (2 * eps)
+            ad = grads[which][idx]
+            assert abs(fd - ad) <= 1e-6 * max(1.0, abs(fd)), (which, idx, fd, ad)
+
+
+def test_single_token_closed_form():
+    # one token from a zero state: S = beta k^ v^T, o = K^-1/2 beta (q^.k^) v
+    rng = np.random.default_rng(2)
+    q, k, v, g, beta, s0, do, dht = _inputs(rng, T=1, H=1, HV=1)
+    s0[:] = 0
+    dq, dk, dv, dg, db, dh0 = oracle.recurrent_backward(q, k, v, g, beta, s0, do, dht, round_bf16=False)
+    K = q.shape[-1]
+    qn = q[0, 0, 0] / np.sqrt((q[0, 0, 0] ** 2).sum() + 1e-6)
+    kn = k[0, 0, 0] / np.sqrt((k[0, 0, 0] ** 2).sum() + 1e-6)
+    b = beta[0, 0, 0]
+    dv_ref = K ** -0.5 * b * (qn @ kn) * do[0, 0, 0] + b * (kn @ dht[0, 0])
+    db_ref = K ** -0.5 * (qn @ kn) * (v[0, 0, 0] @ do[0, 0, 0]) + kn @ dht[0, 0] @ v[0, 0, 0]
+    np.testing.assert_allclose(dv[0, 0, 0], dv_ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(db[0, 0, 0], db_ref, rtol=1e-12, atol=1e-14)
+    # from a zero state the gate only scales zeros
+    np.testing.assert_allclose(dg, 0.0, atol=1e-15)
+
+
+def test_beta_zero_leaves_v_out():
+    rng = np.random.default_rng(3)
+    q, k, v, g, beta, s0, do, dht = _inputs(rng)
+    beta[:] = 0
+    dq, dk, dv, dg, db, dh0 = oracle.recurrent_backward(q, k, v, g, beta, s0, do, dht)
+    assert np.all(dv == 0) and np.all(dk == 0)
+
+
+def test_shared_qk_head_sums_value_heads():
+    rng = np.random.default_rng(4)
+    q, k, v, g, beta, s0, do, dht = _inputs(rng, H=1, HV=2)
+    dq, dk, dv, dg, db, dh0 = oracle.recurrent_backward(q, k, v, g, beta, s0, do, dht)
+    qe, ke = np.repeat(q, 2, axis=2), np.repeat(k, 2, axis=2)
+    eq, ek, ev, eg, eb, eh = oracle.recurrent_backward(qe, ke, v, g, beta, s0, do, dht)
+    np.testing.assert_allclose(dq[:, :, 0], eq.sum(2), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[:, :, 0], ek.sum(2), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv, ev, rtol=1e-12, atol=1e-14)
