@@ -17,8 +17,9 @@
 //   Per chunk:
 //     1. the raw q, k, g and beta, prefetched into registers while the
 //        previous chunk was computed, are normalised (bit-exact routine
-//        shared with kda_qk_l2norm), scanned (G, kept in log2 units) and
-//        staged in LDS;
+//        shared with kda_qk_l2norm; except for a workgroup's first item this
+//        runs at the end of the previous item, behind its workspace
+//        stores), scanned (G, kept in log2 units) and staged in LDS;
 //     2. the gated L and Aqk, 16x16 blocks on MFMA;
 //     3. T = (I+L)^-1 by blocked forward substitution in float32 (diagonal
 //        blocks by substitution, off-diagonal blocks on fp32 MFMA), then
@@ -131,8 +132,8 @@ constexpr int AS = 72;           // 16-bit [*][64] arrays
 // intra_kernel LDS map (bytes).  Regions are reused across phases:
 //   U1   : fp32 L and T (phases 2-3), then fp16 -W and E^T (phase 4)
 //   AREG : fp32 scan totals (phase 1), fp16 A (phases 3-4)
-constexpr int OFF_Q = 0;                                  // bf16 q^, then fp16 Qg  [64][QS]
-constexpr int OFF_K = OFF_Q + C * QS * 2;                 // bf16 k^                [64][QS]
+constexpr int OFF_Q = 0;                                  // fp16 q^, then fp16 Qg  [64][QS]
+constexpr int OFF_K = OFF_Q + C * QS * 2;                 // fp16 k^                [64][QS]
 constexpr int OFF_G = OFF_K + C * QS * 2;                 // fp32 G (log2 units)    [64][GS]
 constexpr int OFF_U1 = OFF_G + C * GS * 4;
 constexpr int OFF_L = OFF_U1;                             // fp32 L                 [64][LS]
@@ -636,7 +637,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       mask_raw_g(R, tid);
       {
         const int rg = tid >> 3, l8 = tid & 7;
-        // Staged as fp16, the MFMA operand type (see the phase-2 note).
+        // Staged as fp16, the MFMA operand type (see the precision note at
+        // the top of this file).
         uint4 h[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
