@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -70,8 +71,13 @@ def decode_alg_bytes(B_act, B_inact, H, HV):
 
 
 def source_hash(name):
+    """Hash of a kernel source's code with comments and blank lines removed,
+    so that a comment edit does not invalidate a counter record."""
     path = os.path.join(ROOT, "kda_gated_delta_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    lines = [re.sub(r"//.*", "", line).rstrip() for line in text.splitlines()]
+    code = "\n".join(line for line in lines if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles():
@@ -84,7 +90,7 @@ def traffic_from_profiles():
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("prefill_source_sha256_16") != source_hash("prefill.hip"):
+    if rec.get("prefill_code_sha256_16") != source_hash("prefill.hip"):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -191,7 +197,7 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
     f_scale, w_scale = cf / kib, cw / kib
     rec = {
         "workload": "prefill B=1 H=HV=96 T=8192 K=V=128",
-        "prefill_source_sha256_16": source_hash("prefill.hip"),
+        "prefill_code_sha256_16": source_hash("prefill.hip"),
         "copy_bytes": copy_bytes,
         "fetch_scale": f_scale,
         "write_scale": w_scale,
