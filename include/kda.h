@@ -260,6 +260,67 @@ int kda_state_to_pool(const float* state, int32_t N, int32_t HV, int32_t K, int3
                       void* state_pool, int64_t slot_stride, int64_t num_slots,
                       const int32_t* state_indices, void* stream);
 
+/*
+ * kda_chunk_backward -- gradients of the chunked prefill.
+ *
+ * Defined on "KDA Chunk Prefill on Ascend A3": section "Function and tensor
+ * contract" (the optional backward: gradients with respect to q, k, v, g,
+ * beta and initial_state) and section "Mathematical definition" (the
+ * forward being differentiated, exactly as kda_chunk_prefill).  The page
+ * gives no backward formulas.  This computes the exact gradients of
+ *     sum(o * d_out) + sum(final_state * d_final_state)
+ * through the forward's definition, with one reading: the bf16 rounding of
+ * the normalised q and k passes gradients unchanged, so dq and dk are the
+ * gradients of x / sqrt(sum(x*x) + 1e-6) at the given q and k.  Every step
+ * runs in float32 (it recomputes the chunk-local matrices, the chunk-start
+ * states and the reverse state-gradient carry; it does not use the
+ * forward's workspace or outputs).
+ *
+ * Inputs are the forward's inputs, with the same meaning and layout
+ * (q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, K,
+ * V as for kda_chunk_prefill), plus:
+ *   d_out            bf16 [B, T, HV, V]  gradient of o
+ *   d_final_state    fp32 [N, HV, K, V]  gradient of final_state, or NULL
+ *                    (zero)
+ * Outputs (float32, always written unless stated; all 16-byte aligned):
+ *   dq, dk           [B, T, H, K]   (summed over the value heads that share
+ *                    a Q/K head)
+ *   dv               [B, T, HV, V]
+ *   dg               [B, T, HV, K]
+ *   dbeta            [B, T, HV]
+ *   d_initial_state  [N, HV, K, V], or NULL to skip it.  When initial_state
+ *                    is NULL it is the gradient with respect to a zero
+ *                    initial state.
+ *   workspace        device scratch of at least
+ *                    kda_chunk_backward_workspace_size(...) bytes, owned by
+ *                    the caller; contents on entry do not matter.  Calls
+ *                    that share a workspace must not overlap.
+ * Sizes and errors as kda_chunk_prefill (T == 0 writes only
+ * d_initial_state, which then equals d_final_state).  Outputs must not
+ * alias inputs or each other.
+ */
+int kda_chunk_backward(const void* q, const void* k, const void* v,
+                       const float* g, const void* beta,
+                       const float* initial_state,
+                       const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t HV,
+                       int32_t K, int32_t V,
+                       const void* d_out, const float* d_final_state,
+                       float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                       float* d_initial_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_backward_workspace_size -- bytes of workspace kda_chunk_backward
+ * needs (num_seqs as for kda_chunk_prefill; 0 when cu_seqlens is NULL);
+ * 0 for sizes it rejects.  About 8.2 KB per token and value head: one
+ * 524,800-byte float32 record per 64-token chunk slot (floor(B*T/64) + N + 1
+ * slots per value head) plus 1 KB per token and value head for the
+ * per-value-head q and k gradients before the GQA sum.
+ */
+size_t kda_chunk_backward_workspace_size(int32_t B, int32_t T, int32_t H, int32_t HV,
+                                         int32_t K, int32_t V, int32_t num_seqs);
+
 #ifdef __cplusplus
 }
 #endif

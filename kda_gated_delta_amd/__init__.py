@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
            "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
-           "kda_state_to_pool")
+           "kda_state_to_pool", "kda_chunk_backward", "kda_chunk_backward_workspace_size")
 
 _lib = None
 
@@ -69,6 +69,12 @@ def load():
                                       _i32, _i32, _i32, _i32, _vp, _vp]
     lib.kda_state_to_pool.restype = ctypes.c_int
     lib.kda_state_to_pool.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
+    lib.kda_chunk_backward.restype = ctypes.c_int
+    lib.kda_chunk_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.kda_chunk_backward_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_backward_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     _lib = lib
     return lib
 
@@ -176,6 +182,49 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(code, "kda_chunk_prefill")
     return out, final_state
+
+
+def backward_workspace_size(B, T, H, HV, num_seqs=0, K=128, V=128):
+    """Bytes of workspace kda_chunk_backward needs (num_seqs = 0 without cu_seqlens)."""
+    return int(load().kda_chunk_backward_workspace_size(B, T, H, HV, K, V, num_seqs))
+
+
+def chunk_backward(q, k, v, g, beta, initial_state, d_out, d_final_state=None, cu_seqlens=None,
+                   workspace=None, want_d_initial_state=True):
+    """Gradients of sum(o * d_out) + sum(final_state * d_final_state) for
+    the prefill with the same inputs.  d_out [B,T,HV,V] bf16; d_final_state
+    [N,HV,K,V] fp32 or None (zero).  Returns float32 (dq, dk, dv, dg,
+    dbeta, d_initial_state); d_initial_state is None when initial_state is
+    None and want_d_initial_state is False."""
+    lib = load()
+    dev, (B, T, H, HV, K, V), nseq_arg, _, _ = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens, None, None)
+    N = nseq_arg if cu_seqlens is not None else B
+    _need(d_out, "d_out", torch.bfloat16, 4, dev)
+    if d_out.shape != (B, T, HV, V):
+        raise ValueError(f"d_out must be {(B, T, HV, V)}")
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", torch.float32, 4, dev)
+        if d_final_state.shape != (N, HV, K, V):
+            raise ValueError(f"d_final_state must be {(N, HV, K, V)}")
+    need = backward_workspace_size(B, T, H, HV, nseq_arg, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, K), **f32)
+    dk = torch.empty((B, T, H, K), **f32)
+    dv = torch.empty((B, T, HV, V), **f32)
+    dg = torch.empty((B, T, HV, K), **f32)
+    dbeta = torch.empty((B, T, HV), **f32)
+    dh0 = torch.empty((N, HV, K, V), **f32) if (initial_state is not None or want_d_initial_state) else None
+    code = lib.kda_chunk_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
+                                  B, T, H, HV, K, V, _ptr(d_out), _ptr(d_final_state),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                  _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "kda_chunk_backward")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def chunk_prefill_fused(q, k, v, g, beta, initial_state=None, cu_seqlens=None,

@@ -277,6 +277,18 @@ def prefill_stress(seed, B, T, H, HV, *, qk_mode="gain", gate="moderate",
                          f"stress_{qk_mode}_{gate}_{beta_mode}_{state}")
 
 
+def upstream_grads(inp, seed=11):
+    """Upstream gradients for a backward call on a prefill workload: d_out
+    ~ N(0,1) as bf16 [B,T,HV,V] (the dtype of o) and d_final_state ~ N(0,1)
+    fp32 [N,HV,K,V]."""
+    gen = _gen(seed)
+    B, T, HV = inp.v.shape[0], inp.v.shape[1], inp.v.shape[2]
+    N = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    d_out = _randn(gen, B, T, HV, V_DIM).to(torch.bfloat16)
+    d_final = _randn(gen, N, HV, K_DIM, V_DIM)
+    return d_out, d_final
+
+
 def to_numpy(inp):
     """float32 numpy copies of every tensor field (bf16 values are exact)."""
     out = {}

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_prefill", "kda_chunk_prefill_fused", "kda_chunk_prefill_workspace_size", "kda_decode",
               "kda_qk_l2norm",
-              "kda_packed_decode", "kda_state_to_pool", "kda_status_string"):
+              "kda_packed_decode", "kda_state_to_pool", "kda_status_string",
+              "kda_chunk_backward", "kda_chunk_backward_workspace_size"):
         assert n in names
     assert set(names) == set(kda.EXPORTS)
 
@@ -173,3 +174,39 @@ def test_fused_prefill_metadata_errors():
     assert call(K=64) == 3
     assert call(cu=FAKE, n=2, B=2) == 2
     assert call(v=MISALIGNED) == 4
+
+
+def _backward(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
+             B=1, T=64, H=1, HV=1, K=128, V=128, do=FAKE, dht=NULL, dq=FAKE, dk=FAKE, dv=FAKE,
+             dg=FAKE, db=FAKE, dh0=NULL, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.kda_chunk_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
+                                  a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["do"], a["dht"],
+                                  a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["ws"], a["wsb"], NULL)
+
+
+def test_backward_metadata_errors():
+    lib = kda.load()
+    assert _backward(lib, q=NULL) == 1
+    assert _backward(lib, do=NULL) == 1
+    assert _backward(lib, dg=NULL) == 1
+    assert _backward(lib, H=3, HV=4) == 2
+    assert _backward(lib, B=0) == 2
+    assert _backward(lib, T=-1) == 2
+    assert _backward(lib, K=64) == 3
+    assert _backward(lib, cu=FAKE, n=2, B=2) == 2
+    assert _backward(lib, dv=MISALIGNED) == 4
+    assert _backward(lib, ws=NULL) == 1
+    assert _backward(lib, wsb=1000) == 6
+
+
+def test_backward_workspace_size_formula():
+    lib = kda.load()
+    rec = 131200 * 4     # float32 record per chunk slot
+    # floor(B*T/64) + N + 1 slots per value head, plus two float32 [tokens, HV, 128] buffers
+    assert lib.kda_chunk_backward_workspace_size(1, 8192, 96, 96, 128, 128, 0) == \
+        (128 + 1 + 1) * 96 * rec + 8192 * 96 * 128 * 4 * 2
+    assert lib.kda_chunk_backward_workspace_size(1, 500, 2, 4, 128, 128, 5) == \
+        (7 + 5 + 1) * 4 * rec + 500 * 4 * 128 * 4 * 2
+    assert lib.kda_chunk_backward_workspace_size(1, 64, 1, 1, 64, 128, 0) == 0

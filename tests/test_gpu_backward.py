@@ -1,0 +1,119 @@
+"""kda_chunk_backward on the GPU against the oracle's backward (float64
+automatic differentiation of the token recurrence, oracle/backward.py).
+
+Bar (float32 arithmetic throughout the GPU path): for every gradient
+tensor, ||grad_gpu - grad_ref||_F <= 1e-5 ||grad_ref||_F, and the same per
+(sequence, head) for d_initial_state.  Cases cover several chunks with a
+ragged tail, GQA, varlen batches (including an empty sequence and one
+shorter than a chunk), a missing initial state and a missing final-state
+gradient, harsh gates and beta = 0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-5
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _rel(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.abs(a).max(initial=0.0))
+
+
+def _run(kda, inp, d_out, d_final, use_dht=True):
+    say(f"backward {inp.name} shape={tuple(inp.q.shape)} HV={inp.v.shape[2]} "
+        f"cu={None if inp.cu_seqlens is None else inp.cu_seqlens.tolist()} dht={use_dht}")
+    dev = "cuda"
+    s0 = None if inp.initial_state is None else inp.initial_state.to(dev)
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev)
+    got = kda.chunk_backward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                             inp.beta.to(dev), s0, d_out.to(dev),
+                             d_final.to(dev) if use_dht else None, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    got = [None if x is None else x.cpu().numpy().astype(np.float64) for x in got]
+    a = synth.to_numpy(inp)
+    dht = d_final.numpy() if use_dht else np.zeros(d_final.shape)
+    ref = oracle.recurrent_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"],
+                                    d_out.float().numpy(), dht, cu_seqlens=a["cu_seqlens"])
+    return got, ref
+
+
+def _check(got, ref, what):
+    errs = {}
+    for name, x, r in zip(NAMES, got, ref):
+        if r is None:
+            continue
+        assert x is not None and np.all(np.isfinite(x)), f"{what}: {name} missing or non-finite"
+        assert x.shape == r.shape, f"{what}: {name} shape {x.shape} vs {r.shape}"
+        if name == "dh0":
+            flat_x = x.reshape(-1, x.shape[-2] * x.shape[-1])
+            flat_r = r.reshape(-1, r.shape[-2] * r.shape[-1])
+            e = max(_rel(flat_x[i], flat_r[i]) for i in range(flat_r.shape[0]))
+        else:
+            e = _rel(x, r)
+        errs[name] = e
+    say(f"  {what}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for name, e in errs.items():
+        assert e <= GRAD_TOL, f"{what}: {name} rel-Frobenius {e:.3e} > {GRAD_TOL}"
+
+
+CASES = [
+    ("gqa_tail", dict(seed=30, B=1, T=150, H=1, HV=2, init="normal0.1")),
+    ("batch_noinit", dict(seed=31, B=2, T=70, H=2, HV=2, init="none")),
+    ("one_chunk", dict(seed=32, B=1, T=64, H=1, HV=1, init="normal0.1")),
+    ("short", dict(seed=33, B=1, T=5, H=1, HV=1, init="normal0.1")),
+    ("sixteen_chunks", dict(seed=34, B=1, T=1000, H=2, HV=4, init="normal0.1")),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_vs_oracle(gpu_lib, name, kw):
+    seed = kw.pop("seed")
+    inp = synth.prefill_basic(seed, **kw, name=name)
+    d_out, d_final = synth.upstream_grads(inp, seed + 100)
+    got, ref = _run(gpu_lib, inp, d_out, d_final)
+    _check(got, ref, name)
+
+
+def test_backward_varlen(gpu_lib):
+    cu = torch.tensor([0, 37, 37, 120, 200], dtype=torch.int32)
+    inp = synth.prefill_basic(35, 1, 200, 1, 2, init="normal0.1", cu_seqlens=cu, name="varlen")
+    d_out, d_final = synth.upstream_grads(inp, 135)
+    got, ref = _run(gpu_lib, inp, d_out, d_final)
+    _check(got, ref, "varlen")
+
+
+def test_backward_no_final_grad(gpu_lib):
+    inp = synth.prefill_basic(36, 1, 130, 1, 1, init="none", name="no_dht")
+    d_out, d_final = synth.upstream_grads(inp, 136)
+    got, ref = _run(gpu_lib, inp, d_out, d_final, use_dht=False)
+    _check(got, ref, "no_dht")
+
+
+def test_backward_harsh_gates(gpu_lib):
+    inp = synth.config1()
+    B, T = 1, 300
+    inp = synth.PrefillInputs(inp.q[:B, :T, :2].contiguous(), inp.k[:B, :T, :2].contiguous(),
+                              inp.v[:B, :T, :2].contiguous(), inp.g[:B, :T, :2].contiguous(),
+                              inp.beta[:B, :T, :2].contiguous(), inp.initial_state[:B, :2].contiguous(),
+                              None, "harsh")
+    d_out, d_final = synth.upstream_grads(inp, 137)
+    got, ref = _run(gpu_lib, inp, d_out, d_final)
+    _check(got, ref, "harsh")
+
+
+def test_backward_beta_zero(gpu_lib):
+    inp = synth.prefill_basic(38, 1, 100, 1, 1, init="normal0.1", name="beta0")
+    inp.beta.zero_()
+    d_out, d_final = synth.upstream_grads(inp, 138)
+    got, ref = _run(gpu_lib, inp, d_out, d_final)
+    assert np.all(got[2] == 0), "beta = 0: v must get exactly zero gradient"
+    _check(got, ref, "beta0")
