@@ -63,6 +63,38 @@ def prefill_alg_flops(T_tot, HV):
     return T_tot * HV * per
 
 
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector (and fp32 MFMA)
+
+
+def backward_alg_bytes(T_tot, H, HV, N, has_init, has_dht):
+    """Backward inputs read once (q, k, v, beta, d_out bf16; g fp32; initial
+    state and final-state gradient fp32) and float32 gradients written once
+    (dq, dk, dv, dg, dbeta, d_initial_state)."""
+    per_tok = H * 2 * K * 2 + HV * (V * 2 + K * 4 + 2 + V * 2)          # inputs
+    per_tok += H * 2 * K * 4 + HV * (V * 4 + K * 4 + 4)                 # gradients
+    states = N * HV * K * V * 4 * ((1 if has_init else 0) + (1 if has_dht else 0) + 1)
+    return T_tot * per_tok + states
+
+
+def backward_alg_flops(n_chunk_heads):
+    """Per (64-token chunk, value head), multiply-adds counted as 2 flops,
+    triangles exploited (P = C(C+1)/2 lower-triangle pairs incl. the
+    diagonal, M = C*K*V):
+      recompute: P, Aqk, W, U over the triangle: 4 * 2 P K; solve 2 C^3/6
+      forward carry: W S, Kg^T Vnew: 2 * 2M
+      reverse carry: Kg dS', Qg^T dO, W^T dVnew: 3 * 2M; Aqk^T dO: 2 P V
+      gradients: dO S^T, Vnew dS'^T, dVnew S^T: 3 * 2M; dAqk, dA (two
+      terms), dv, dE: 5 * 2 P K; dT T^T and T^T X: 2 C^3/3 + 2 C^3/6;
+      the four gated sums: 4 * 2 P K; dgamma 2 K V."""
+    P = C * (C + 1) // 2
+    M = C * K * V
+    per = (4 * 2 * P * K + 2 * C ** 3 / 6
+           + 2 * 2 * M
+           + 3 * 2 * M + 2 * P * V
+           + 3 * 2 * M + 5 * 2 * P * K + 2 * C ** 3 / 3 + 2 * C ** 3 / 6 + 4 * 2 * P * K + 2 * K * V)
+    return n_chunk_heads * per
+
+
 def decode_alg_bytes(B_act, B_inact, H, HV):
     """Active rows read and write their bf16 state slot and read q,k,v,g,beta
     and write o; inactive rows write zero o; plus the int32 indices."""
@@ -491,6 +523,28 @@ def main():
     }
     del c4a, o4, sf4, ws4
     result["prefill_partitions"] = partitions
+    # Backward of the bench workload: gradients of sum(o * d_out) +
+    # sum(final_state * d_final_state) for random upstream gradients.
+    print("[bench] backward", file=sys.stderr, flush=True)
+    d_out, d_final = synth.upstream_grads(pin)
+    d_out, d_final = d_out.to(dev), d_final.to(dev)
+    bws = torch.empty(kda.backward_workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
+    bw_us = time_calls(lambda: kda.chunk_backward(q, k, v, g, beta, s0, d_out, d_final, workspace=bws),
+                       max(3, args.steps // 2))
+    n_ch = B * ((T + C - 1) // C) * HV
+    bw_flops = backward_alg_flops(n_ch)
+    bw_bytes = backward_alg_bytes(B * T, H, HV, B, True, True)
+    result["backward"] = {
+        "workload": f"B={B} H=HV={HV} T={T}, float32",
+        "call_us_mean": bw_us,
+        "tokens_per_s": B * T / (bw_us * 1e-6),
+        "alg_flops": bw_flops,
+        "alg_bytes": bw_bytes,
+        "roofline": {"bound": "alu", "achieved": bw_flops / (bw_us * 1e-6) / 1e12, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": bw_flops / (bw_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS},
+        "hbm_frac": bw_bytes / (bw_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+    del bws, d_out, d_final
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)

@@ -58,8 +58,7 @@ constexpr int KD = kda::kHead;    // K == V == 128
 constexpr int NTB = 256;          // threads per workgroup
 constexpr int KP = KD + 4;        // LDS row stride of [C][KD] fp32 tiles (16-byte aligned rows)
 constexpr int CP = C + 2;         // LDS row stride of [C][C] fp32 tiles
-constexpr int SP = 33;            // LDS row stride of 32-column state slices
-constexpr int NCOL = 32;          // state columns per carry workgroup
+constexpr int NCOL = 64;          // state columns per carry workgroup
 constexpr float kScale = 0.08838834764831845f;   // 128^-1/2
 
 // Per-chunk record in the workspace (float offsets), one per (value head,
@@ -82,7 +81,12 @@ constexpr int R_ST = R_GAM + KD;            // [V][K] entering state, transposed
 constexpr int R_VN = R_ST + KD * KD;        // [C][V] Vnew
 constexpr int R_DST = R_VN + C * KD;        // [V][K] gradient of the exiting state, transposed
 constexpr int R_DVN = R_DST + KD * KD;      // [C][V] dVnew
-constexpr int REC = R_DVN + C * KD;         // floats per record
+constexpr int R_WT = R_DVN + C * KD;        // [K][C] W transposed
+constexpr int R_KGT = R_WT + KD * C;        // [K][C] Kg transposed
+constexpr int R_ET = R_KGT + KD * C;        // [K][C] E transposed
+constexpr int R_VNT = R_ET + KD * C;        // [V][C] Vnew transposed
+constexpr int R_DVNT = R_VNT + KD * C;      // [V][C] dVnew transposed
+constexpr int REC = R_DVNT + KD * C;        // floats per record
 static_assert(REC % 4 == 0, "records stay 16-byte aligned");
 
 struct BParams {
@@ -292,9 +296,12 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
     const float eg = expf(gv);
     const float kv = sK[i * KP + d];
     rec[R_QG + t] = kScale * sQ[i * KP + d] * eg;
-    rec[R_KG + t] = kv * expf(sG[(C - 1) * KP + d] - gv);
+    const float kg = kv * expf(sG[(C - 1) * KP + d] - gv);
+    rec[R_KG + t] = kg;
+    rec[R_KGT + d * C + i] = kg;
     const float ev = eg * kv;
     rec[R_E + t] = ev;
+    rec[R_ET + d * C + i] = ev;
     sQ[i * KP + d] = ev;
   }
   __syncthreads();
@@ -315,6 +322,7 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
         u = fmaf(a, sK[j * KP + d], u);
       }
       rec[R_W + i * KD + d] = w;
+      rec[R_WT + d * C + i] = w;
       rec[R_U + i * KD + d] = u;
     }
   }
@@ -322,86 +330,51 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
 
 // --------------------------------------------------------------- carries
 // Workgroup (column group cg, value head hv, sequence n) owns state columns
-// 32 cg .. 32 cg + 31.  Thread t works on column j = t % 32.
-constexpr int FWD_LDS = (KD * SP + 2 * C * KP + 2 * C * SP) * 4;
-constexpr int REV_LDS = (KD * SP + C * CP + 3 * C * KP + 2 * C * SP + KD) * 4;
+// 64 cg .. 64 cg + 63.  Every product is register-blocked: thread t
+// computes a 4x4 or 8x4 tile (rows from t / 16, columns 4 (t % 16) ..+3)
+// from 16-byte LDS reads of operands stored contraction-index-major, so
+// one pair of reads feeds 16 or 32 fused multiply-adds.
+constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
+constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ) * 4;
+constexpr int REV_LDS = (2 * KD * SQ + 3 * C * SQ + KD) * 4;
 static_assert(FWD_LDS <= 160 * 1024 && REV_LDS <= 160 * 1024, "LDS budget");
+static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where Kg^T was");
 
-__global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
-  extern __shared__ __align__(16) float smem[];
-  float* sS = smem;                 // [K][32] state slice
-  float* sW = sS + KD * SP;         // [C][K]
-  float* sKg = sW + C * KP;         // [C][K]
-  float* sU = sKg + C * KP;         // [C][32]
-  float* sV = sU + C * SP;          // [C][32] Vnew
-
-  const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
-  const int c0 = cg * NCOL;
-  const int tid = threadIdx.x;
-  const int j = tid & (NCOL - 1);
-  const int rg = tid >> 5;          // 0..7
-  int64_t tok0;
-  int len;
-  seq_range(p, n, tok0, len);
-  const int nch = (len + C - 1) / C;
-  const int64_t sb = slot_base(p, n);
-
-  for (int d = rg; d < KD; d += 8)
-    sS[d * SP + j] = p.s0 ? p.s0[((int64_t(n) * p.HV + hv) * KD + d) * KD + c0 + j] : 0.0f;
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    float* rec = record(p, hv, sb + c);
-    // Entering state, transposed: ST[v][d] for this group's columns v.
-    for (int t = tid; t < NCOL * KD; t += NTB) {
-      const int vv = t / KD, d = t - vv * KD;
-      rec[R_ST + (c0 + vv) * KD + d] = sS[d * SP + vv];
-    }
-    load_tile(sW, rec + R_W, tid);
-    load_tile(sKg, rec + R_KG, tid);
-    for (int i = rg; i < C; i += 8) sU[i * SP + j] = rec[R_U + i * KD + c0 + j];
-    __syncthreads();
-    // Vnew = U - W S.
-    for (int i = rg; i < C; i += 8) {
-      float acc = sU[i * SP + j];
-      const float* w = sW + i * KP;
-      for (int d = 0; d < KD; ++d) acc = fmaf(-w[d], sS[d * SP + j], acc);
-      sV[i * SP + j] = acc;
-      rec[R_VN + i * KD + c0 + j] = acc;
-    }
-    __syncthreads();
-    // S = gamma S + Kg^T Vnew.
-    float ns[KD / 8];
-#pragma unroll
-    for (int m = 0; m < KD / 8; ++m) {
-      const int d = rg + 8 * m;
-      float acc = rec[R_GAM + d] * sS[d * SP + j];
-      for (int i = 0; i < C; ++i) acc = fmaf(sKg[i * KP + d], sV[i * SP + j], acc);
-      ns[m] = acc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < KD / 8; ++m) sS[(rg + 8 * m) * SP + j] = ns[m];
-    __syncthreads();
+// Copy rows [r0, r0 + rows) of a [*][cols] fp32 record matrix, columns
+// [c0, c0 + w), into LDS with row stride ld (all multiples of 4).
+__device__ __forceinline__ void load_rows(float* dst, int ld, const float* src, int cols, int r0, int rows, int c0,
+                                          int w, int tid) {
+  const int q4 = w / 4;
+  for (int u = tid; u < rows * q4; u += NTB) {
+    const int r = u / q4, c4 = u - r * q4;
+    *reinterpret_cast<float4*>(dst + r * ld + 4 * c4) =
+        *reinterpret_cast<const float4*>(src + (r0 + r) * cols + c0 + 4 * c4);
   }
 }
 
-__global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// acc[r][c] += a[r] * b[c] for a 4-row (or 8-row, two calls) tile.
+__device__ __forceinline__ void fma4x4(float (*acc)[4], const float4 a, const float4 b, float sign) {
+  const float av[4] = {sign * a.x, sign * a.y, sign * a.z, sign * a.w};
+  const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+}
+
+__global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
-  float* sD = smem;                 // [K][32] dS' slice
-  float* sAqk = sD + KD * SP;       // [C][C]
-  float* sKg = sAqk + C * CP;       // [C][K]
-  float* sQg = sKg + C * KP;        // [C][K]
-  float* sW = sQg + C * KP;         // [C][K]
-  float* sO = sW + C * KP;          // [C][32] dO
-  float* sV = sO + C * SP;          // [C][32] dVnew
-  float* sGam = sV + C * SP;        // [K]
+  float* sS = smem;                 // [K][64] state slice
+  float* sWT = sS + KD * SQ;        // [K][C] W^T
+  float* sKg = sWT + KD * SQ;       // [C][K] Kg
+  float* sV = sKg + C * KP;         // [C][64] U, then Vnew
 
   const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
   const int c0 = cg * NCOL;
   const int tid = threadIdx.x;
-  const int j = tid & (NCOL - 1);
-  const int rg = tid >> 5;
+  const int tr = tid >> 4, j0 = 4 * (tid & 15);
   int64_t tok0;
   int len;
   seq_range(p, n, tok0, len);
@@ -409,7 +382,98 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
   const int64_t sb = slot_base(p, n);
   const int64_t sh = (int64_t(n) * p.HV + hv) * KD;
 
-  for (int d = rg; d < KD; d += 8) sD[d * SP + j] = p.dht ? p.dht[(sh + d) * KD + c0 + j] : 0.0f;
+  for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+    const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
+    *reinterpret_cast<float4*>(sS + d * SQ + 4 * c4) =
+        p.s0 ? *reinterpret_cast<const float4*>(p.s0 + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    float* rec = record(p, hv, sb + c);
+    // Entering state, transposed: ST[v][d] for this group's columns v.
+    for (int t = tid; t < NCOL * KD; t += NTB) {
+      const int vv = t / KD, d = t - vv * KD;
+      rec[R_ST + (c0 + vv) * KD + d] = sS[d * SQ + vv];
+    }
+    load_rows(sWT, SQ, rec + R_WT, C, 0, KD, 0, C, tid);
+    load_rows(sKg, KP, rec + R_KG, KD, 0, C, 0, KD, tid);
+    load_rows(sV, SQ, rec + R_U, KD, 0, C, c0, NCOL, tid);
+    __syncthreads();
+    // Vnew = U - W S: rows 4 tr .. +3.
+    {
+      const int i0 = 4 * tr;
+      float acc[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 u = lds4(sV + (i0 + r) * SQ + j0);
+        acc[r][0] = u.x; acc[r][1] = u.y; acc[r][2] = u.z; acc[r][3] = u.w;
+      }
+#pragma unroll 4
+      for (int d = 0; d < KD; ++d) fma4x4(acc, lds4(sWT + d * SQ + i0), lds4(sS + d * SQ + j0), -1.0f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
+        *reinterpret_cast<float4*>(rec + R_VN + (i0 + r) * KD + c0 + j0) = o4;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<float4*>(rec + R_VNT + (c0 + j0 + cc) * C + i0) =
+            make_float4(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
+    }
+    __syncthreads();
+    // S = gamma S + Kg^T Vnew: rows 8 tr .. +7.
+    {
+      const int d0 = 8 * tr;
+      float acc[8][4];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float gm = rec[R_GAM + d0 + r];
+        const float4 s4 = lds4(sS + (d0 + r) * SQ + j0);
+        acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
+      }
+#pragma unroll 4
+      for (int i = 0; i < C; ++i) {
+        const float4 b = lds4(sV + i * SQ + j0);
+        fma4x4(acc, lds4(sKg + i * KP + d0), b, 1.0f);
+        fma4x4(acc + 4, lds4(sKg + i * KP + d0 + 4), b, 1.0f);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        *reinterpret_cast<float4*>(sS + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
+  extern __shared__ __align__(16) float smem[];
+  float* sD = smem;                 // [K][64] dS' slice
+  float* sKgT = sD + KD * SQ;       // [K][C] Kg^T; later half tiles of Qg and W
+  float* sAqk = sKgT + KD * SQ;     // [C][C] Aqk
+  float* sO = sAqk + C * SQ;        // [C][64] dO
+  float* sV = sO + C * SQ;          // [C][64] dVnew
+  float* sGam = sV + C * SQ;        // [K]
+  float* sQh = sKgT;                // [C/2][K] half of Qg
+  float* sWh = sKgT + (C / 2) * KP; // [C/2][K] half of W
+
+  const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
+  const int c0 = cg * NCOL;
+  const int tid = threadIdx.x;
+  const int tr = tid >> 4, j0 = 4 * (tid & 15);
+  int64_t tok0;
+  int len;
+  seq_range(p, n, tok0, len);
+  const int nch = (len + C - 1) / C;
+  const int64_t sb = slot_base(p, n);
+  const int64_t sh = (int64_t(n) * p.HV + hv) * KD;
+
+  for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+    const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
+    *reinterpret_cast<float4*>(sD + d * SQ + 4 * c4) =
+        p.dht ? *reinterpret_cast<const float4*>(p.dht + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
 
   for (int c = nch - 1; c >= 0; --c) {
@@ -418,71 +482,121 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
     const int64_t t0 = tok0 + int64_t(c) * C;
     for (int t = tid; t < NCOL * KD; t += NTB) {
       const int vv = t / KD, d = t - vv * KD;
-      rec[R_DST + (c0 + vv) * KD + d] = sD[d * SP + vv];
+      rec[R_DST + (c0 + vv) * KD + d] = sD[d * SQ + vv];
     }
-    for (int t = tid; t < C * C; t += NTB) {
-      const int i = t / C, jj = t - i * C;
-      sAqk[i * CP + jj] = rec[R_AQK + t];
+    load_rows(sKgT, SQ, rec + R_KGT, C, 0, KD, 0, C, tid);
+    load_rows(sAqk, SQ, rec + R_AQK, C, 0, C, 0, C, tid);
+    for (int t = tid; t < C * NCOL; t += NTB) {
+      const int i = t / NCOL, jj = t - i * NCOL;
+      sO[i * SQ + jj] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + c0 + jj]) : 0.0f;
     }
-    load_tile(sKg, rec + R_KG, tid);
-    load_tile(sQg, rec + R_QG, tid);
-    load_tile(sW, rec + R_W, tid);
-    for (int i = rg; i < C; i += 8)
-      sO[i * SP + j] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + c0 + j]) : 0.0f;
     if (tid < KD) sGam[tid] = rec[R_GAM + tid];
     __syncthreads();
-    // dVnew = Aqk^T dO + Kg dS'.
-    for (int i = rg; i < C; i += 8) {
-      float acc = 0.0f;
-      for (int m = i; m < C; ++m) acc = fmaf(sAqk[m * CP + i], sO[m * SP + j], acc);
-      const float* kg = sKg + i * KP;
-      for (int d = 0; d < KD; ++d) acc = fmaf(kg[d], sD[d * SP + j], acc);
-      sV[i * SP + j] = acc;
-      rec[R_DVN + i * KD + c0 + j] = acc;
-    }
-    __syncthreads();
-    // dS = gamma dS' + Qg^T dO - W^T dVnew.
-    float nd[KD / 8];
+    // dVnew = Aqk^T dO + Kg dS': rows 4 tr .. +3 (Aqk[m][i] = 0 for m < i).
+    {
+      const int i0 = 4 * tr;
+      float acc[4][4] = {};
+#pragma unroll 4
+      for (int m = i0; m < C; ++m) fma4x4(acc, lds4(sAqk + m * SQ + i0), lds4(sO + m * SQ + j0), 1.0f);
+#pragma unroll 4
+      for (int d = 0; d < KD; ++d) fma4x4(acc, lds4(sKgT + d * SQ + i0), lds4(sD + d * SQ + j0), 1.0f);
 #pragma unroll
-    for (int m = 0; m < KD / 8; ++m) {
-      const int d = rg + 8 * m;
-      float acc = sGam[d] * sD[d * SP + j];
-      for (int i = 0; i < C; ++i) {
-        acc = fmaf(sQg[i * KP + d], sO[i * SP + j], acc);
-        acc = fmaf(-sW[i * KP + d], sV[i * SP + j], acc);
+      for (int r = 0; r < 4; ++r) {
+        const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
+        *reinterpret_cast<float4*>(rec + R_DVN + (i0 + r) * KD + c0 + j0) = o4;
       }
-      nd[m] = acc;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < KD / 8; ++m) sD[(rg + 8 * m) * SP + j] = nd[m];
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<float4*>(rec + R_DVNT + (c0 + j0 + cc) * C + i0) =
+            make_float4(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
+    }
+    // dS = gamma dS' + Qg^T dO - W^T dVnew: rows 8 tr .. +7, with Qg and W
+    // staged 32 rows at a time where Kg^T was.
+    const int d0 = 8 * tr;
+    float acc[8][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float gm = sGam[d0 + r];
+      const float4 s4 = lds4(sD + (d0 + r) * SQ + j0);
+      acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
+    }
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // Kg^T (or the previous half) is no longer read; dVnew is complete
+      load_rows(sQh, KP, rec + R_QG, KD, h * (C / 2), C / 2, 0, KD, tid);
+      load_rows(sWh, KP, rec + R_W, KD, h * (C / 2), C / 2, 0, KD, tid);
+      __syncthreads();
+#pragma unroll 2
+      for (int i = 0; i < C / 2; ++i) {
+        const float4 bo = lds4(sO + (h * (C / 2) + i) * SQ + j0);
+        const float4 bv = lds4(sV + (h * (C / 2) + i) * SQ + j0);
+        fma4x4(acc, lds4(sQh + i * KP + d0), bo, 1.0f);
+        fma4x4(acc + 4, lds4(sQh + i * KP + d0 + 4), bo, 1.0f);
+        fma4x4(acc, lds4(sWh + i * KP + d0), bv, -1.0f);
+        fma4x4(acc + 4, lds4(sWh + i * KP + d0 + 4), bv, -1.0f);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      *reinterpret_cast<float4*>(sD + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
     __syncthreads();
   }
   if (p.dh0)
-    for (int d = rg; d < KD; d += 8) p.dh0[(sh + d) * KD + c0 + j] = sD[d * SP + j];
+    for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+      const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
+      *reinterpret_cast<float4*>(p.dh0 + (sh + d) * KD + c0 + 4 * c4) = lds4(sD + d * SQ + 4 * c4);
+    }
 }
 
 // --------------------------------------------------------------- gradients
-// Thread t owns channel (or value column) d = t % 128 and rows
-// i = t / 128 + 2 m, m = 0..31, of every [C][128] quantity.
-constexpr int NR = C / 2;
-constexpr int GRAD_LDS = (2 * C * KP + 5 * C * CP + 2 * C + KD) * 4;
+// Register-blocked like the carries.  Every [C][128] quantity is owned in
+// 4x8 tiles: thread t holds rows 4 (t / 16) .. +3 and columns
+// 8 (t % 16) .. +7 of dq^, dk^ and dG for the whole kernel; [C][C]
+// products use 4x4 tiles (rows 4 (t / 16), columns 4 (t % 16)).  LDS holds
+// three [128][68] regions (R0-R2), one [64][132] region (R3) and one
+// [64][68] region (R4); what each holds changes by phase (below).
+constexpr int LQ = C + 4;           // row stride of [*][C] tiles
+constexpr int R0_OFF = 0;
+constexpr int R1_OFF = R0_OFF + KD * LQ;
+constexpr int R2_OFF = R1_OFF + KD * LQ;
+constexpr int R3_OFF = R2_OFF + KD * LQ;
+constexpr int R4_OFF = R3_OFF + C * KP;
+constexpr int SM_OFF = R4_OFF + C * LQ;
+constexpr int GRAD_LDS = (SM_OFF + 2 * C + KD) * 4;
 static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
-static_assert(2 * C * CP == C * KP, "A and T together alias one [C][KP] tile");
+static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ, "regions hold their alternates");
+
+// acc[4][8] += a[4] (x) b[8].
+__device__ __forceinline__ void fma4x8(float (*acc)[8], const float4 a, const float4 b0, const float4 b1) {
+  const float av[4] = {a.x, a.y, a.z, a.w};
+  const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+}
+
+__device__ __forceinline__ void ld8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void st8(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
 
 __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
-  float* sX = smem;                 // dO, then dW, then q^
-  float* sZ = sX + C * KP;          // Vnew, then dVnew, then G
-  float* sA = sZ + C * KP;          // A        } later k^ ([C][KP] over both)
-  float* sT = sA + C * CP;          // T        }
-  float* sM1 = sT + C * CP;         // dAqk
-  float* sM2 = sM1 + C * CP;        // dA, then dT, then dL
-  float* sM3 = sM2 + C * CP;        // dT T^T
-  float* sB = sM3 + C * CP;         // beta
+  float* R0 = smem + R0_OFF;
+  float* R1 = smem + R1_OFF;
+  float* R2 = smem + R2_OFF;
+  float* R3 = smem + R3_OFF;
+  float* R4 = smem + R4_OFF;
+  float* sB = smem + SM_OFF;        // beta
   float* sDB = sB + C;              // dbeta
   float* sGl = sDB + C;             // dG_last
-  float* sKn = sA;
 
   const int64_t slot = blockIdx.x;
   const int hv = blockIdx.y;
@@ -494,226 +608,323 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   seq_range(p, n, tok0, len);
   const int64_t t0 = tok0 + int64_t(c) * C;
   const int nv = min(C, len - c * C);
-  const float* rec = record(p, hv, slot);
+  float* rec = record(p, hv, slot);
   const int tid = threadIdx.x;
-  const int d = tid & (KD - 1);
-  const int hr = tid >> 7;
+  const int rb = tid >> 4, cb = tid & 15;
+  const int i0 = 4 * rb, d0 = 8 * cb, j0 = 4 * cb;   // 4x8 tile rows/cols; 4x4 tile cols
+  // This thread's dq^, dk^ (rows of the chunk's real tokens) and dG (all
+  // rows) accumulate in memory it alone touches: the per-value-head q and
+  // k gradient buffers and the record's U field (no longer read).
+  float* gdq = p.dqh + (t0 * p.HV + hv) * KD;
+  float* gdk = p.dkh + (t0 * p.HV + hv) * KD;
+  const int64_t rs = int64_t(p.HV) * KD;     // token stride of gdq, gdk
+  float* gdG = rec + R_U;
 
-  float dq[NR], dk[NR], dG[NR];
-#pragma unroll
-  for (int m = 0; m < NR; ++m) dq[m] = dk[m] = dG[m] = 0.0f;
-  float dgl = 0.0f;   // this thread's share of dG_last[d]
-
-  // dO (zero past the chunk's end) and Vnew; A, T, beta.
+  // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T, dgamma,
+  // dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T, R2 = dVnew^T
+  // ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per block.
   for (int t = tid; t < C * KD; t += NTB) {
-    const int i = t / KD, e = t - i * KD;
-    sX[i * KP + e] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + e]) : 0.0f;
+    const int i = t / KD, vv = t - i * KD;
+    R0[vv * LQ + i] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + vv]) : 0.0f;
   }
-  load_tile(sZ, rec + R_VN, tid);
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, j = t - i * C;
-    sA[i * CP + j] = rec[R_A + t];
-    sT[i * CP + j] = rec[R_T + t];
-  }
+  load_rows(R1, LQ, rec + R_VNT, C, 0, KD, 0, C, tid);
+  load_rows(R2, LQ, rec + R_DVNT, C, 0, KD, 0, C, tid);
   if (tid < C) {
     sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
     sDB[tid] = 0.0f;
   }
-  __syncthreads();
-
-  // dQg = dO S^T: dq^ += K^-1/2 dQg exp(G), dG += dQg Qg.
+  float aq[4][8] = {}, aw[4][8] = {}, akg[4][8] = {};
+  float dgam[8] = {};
+  for (int vb = 0; vb < KD / 32; ++vb) {
+    load_rows(R3, KP, rec + R_ST, KD, 32 * vb, 32, 0, KD, tid);
+    load_rows(R3 + 32 * KP, KP, rec + R_DST, KD, 32 * vb, 32, 0, KD, tid);
+    __syncthreads();
+#pragma unroll 2
+    for (int u = 0; u < 32; ++u) {
+      const int vv = 32 * vb + u;
+      const float4 bs0 = lds4(R3 + u * KP + d0), bs1 = lds4(R3 + u * KP + d0 + 4);
+      const float4 bd0 = lds4(R3 + (32 + u) * KP + d0), bd1 = lds4(R3 + (32 + u) * KP + d0 + 4);
+      fma4x8(aq, lds4(R0 + vv * LQ + i0), bs0, bs1);
+      fma4x8(aw, lds4(R2 + vv * LQ + i0), bs0, bs1);
+      fma4x8(akg, lds4(R1 + vv * LQ + i0), bd0, bd1);
+      dgam[0] = fmaf(bs0.x, bd0.x, dgam[0]); dgam[1] = fmaf(bs0.y, bd0.y, dgam[1]);
+      dgam[2] = fmaf(bs0.z, bd0.z, dgam[2]); dgam[3] = fmaf(bs0.w, bd0.w, dgam[3]);
+      dgam[4] = fmaf(bs1.x, bd1.x, dgam[4]); dgam[5] = fmaf(bs1.y, bd1.y, dgam[5]);
+      dgam[6] = fmaf(bs1.z, bd1.z, dgam[6]); dgam[7] = fmaf(bs1.w, bd1.w, dgam[7]);
+    }
+    __syncthreads();
+  }
+  // Epilogue: dq^ = K^-1/2 dQg exp(G); dG = dQg Qg - dKg Kg;
+  // dk^ = dKg exp(G_last - G); dG_last partials dKg Kg (+ dgamma gamma).
   {
-    float acc[NR];
+    float gl[8], dglp[8];
+    ld8(rec + R_G + (C - 1) * KD + d0, gl);
 #pragma unroll
-    for (int m = 0; m < NR; ++m) acc[m] = 0.0f;
-    for (int vv = 0; vv < KD; ++vv) {
-      const float s = rec[R_ST + vv * KD + d];
+    for (int cc = 0; cc < 8; ++cc) dglp[cc] = 0.0f;
+    if (rb == 0) {
+      float gm[8];
+      ld8(rec + R_GAM + d0, gm);
 #pragma unroll
-      for (int m = 0; m < NR; ++m) acc[m] = fmaf(sX[(hr + 2 * m) * KP + vv], s, acc[m]);
+      for (int cc = 0; cc < 8; ++cc) dglp[cc] = dgam[cc] * gm[cc];
     }
 #pragma unroll
-    for (int m = 0; m < NR; ++m) {
-      const int i = hr + 2 * m;
-      dq[m] = fmaf(kScale * acc[m], expf(rec[R_G + i * KD + d]), dq[m]);
-      dG[m] = fmaf(acc[m], rec[R_QG + i * KD + d], dG[m]);
-    }
-  }
-  // dAqk = tril(dO Vnew^T).
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, j = t - i * C;
-    float acc = 0.0f;
-    if (j <= i) {
-      const float* a = sX + i * KP;
-      const float* b = sZ + j * KP;
-      for (int e = 0; e < KD; ++e) acc = fmaf(a[e], b[e], acc);
-    }
-    sM1[i * CP + j] = acc;
-  }
-  // dKg = Vnew dS'^T: dk^ += dKg exp(G_last - G), dG -= dKg Kg, dG_last += dKg Kg.
-  {
-    float acc[NR];
+    for (int r = 0; r < 4; ++r) {
+      float gv[8], qg[8], kg[8];
+      ld8(rec + R_G + (i0 + r) * KD + d0, gv);
+      ld8(rec + R_QG + (i0 + r) * KD + d0, qg);
+      ld8(rec + R_KG + (i0 + r) * KD + d0, kg);
+      float vq[8], vk[8], vg[8];
 #pragma unroll
-    for (int m = 0; m < NR; ++m) acc[m] = 0.0f;
-    for (int vv = 0; vv < KD; ++vv) {
-      const float s = rec[R_DST + vv * KD + d];
-#pragma unroll
-      for (int m = 0; m < NR; ++m) acc[m] = fmaf(sZ[(hr + 2 * m) * KP + vv], s, acc[m]);
-    }
-    const float gl = rec[R_G + (C - 1) * KD + d];
-#pragma unroll
-    for (int m = 0; m < NR; ++m) {
-      const int i = hr + 2 * m;
-      const float kg = rec[R_KG + i * KD + d];
-      dk[m] = fmaf(acc[m], expf(gl - rec[R_G + i * KD + d]), dk[m]);
-      dG[m] = fmaf(-acc[m], kg, dG[m]);
-      dgl = fmaf(acc[m], kg, dgl);
-    }
-  }
-  // dgamma = rowsum(dS' * S): dG_last += dgamma gamma.
-  if (hr == 0) {
-    float acc = 0.0f;
-    for (int vv = 0; vv < KD; ++vv) acc = fmaf(rec[R_DST + vv * KD + d], rec[R_ST + vv * KD + d], acc);
-    dgl = fmaf(acc, rec[R_GAM + d], dgl);
-  }
-  __syncthreads();   // dO and Vnew are consumed
-
-  // dVnew; dW = -dVnew S^T (into sX).
-  load_tile(sZ, rec + R_DVN, tid);
-  __syncthreads();
-  {
-    float acc[NR];
-#pragma unroll
-    for (int m = 0; m < NR; ++m) acc[m] = 0.0f;
-    for (int vv = 0; vv < KD; ++vv) {
-      const float s = rec[R_ST + vv * KD + d];
-#pragma unroll
-      for (int m = 0; m < NR; ++m) acc[m] = fmaf(sZ[(hr + 2 * m) * KP + vv], s, acc[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < NR; ++m) sX[(hr + 2 * m) * KP + d] = -acc[m];
-  }
-  __syncthreads();
-  // dA = tril(dVnew v^T + dW E^T).
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, j = t - i * C;
-    float acc = 0.0f;
-    if (j <= i) {
-      const float* dvn = sZ + i * KP;
-      const float* dw = sX + i * KP;
-      const float* ej = rec + R_E + j * KD;
-      if (j < nv) {
-        const uint16_t* vj = p.v + ((t0 + j) * p.HV + hv) * KD;
-        for (int e = 0; e < KD; ++e) acc = fmaf(dvn[e], bf16f(vj[e]), acc);
+      for (int cc = 0; cc < 8; ++cc) {
+        vq[cc] = kScale * aq[r][cc] * expf(gv[cc]);
+        vg[cc] = aq[r][cc] * qg[cc] - akg[r][cc] * kg[cc];
+        vk[cc] = akg[r][cc] * expf(gl[cc] - gv[cc]);
+        dglp[cc] = fmaf(akg[r][cc], kg[cc], dglp[cc]);
       }
-      for (int e = 0; e < KD; ++e) acc = fmaf(dw[e], ej[e], acc);
+      st8(gdG + (i0 + r) * KD + d0, vg);
+      if (i0 + r < nv) {
+        st8(gdq + (i0 + r) * rs + d0, vq);
+        st8(gdk + (i0 + r) * rs + d0, vk);
+      }
     }
-    sM2[i * CP + j] = acc;
+    st8(R3 + rb * KD + d0, dglp);   // [16][128] partials (R3 is free)
   }
-  // dv = A^T dVnew; dE = A^T dW: dk^ += dE exp(G), dG += dE E.
+  // dAqk (lower triangle incl. the diagonal) into R4.
+  {
+    float acc[4][4] = {};
+#pragma unroll 4
+    for (int vv = 0; vv < KD; ++vv) fma4x4(acc, lds4(R0 + vv * LQ + i0), lds4(R1 + vv * LQ + j0), 1.0f);
 #pragma unroll
-  for (int m = 0; m < NR; ++m) {
-    const int j = hr + 2 * m;
-    float av = 0.0f, ae = 0.0f;
-    for (int i = j; i < C; ++i) {
-      const float a = sA[i * CP + j];
-      av = fmaf(a, sZ[i * KP + d], av);
-      ae = fmaf(a, sX[i * KP + d], ae);
-    }
-    if (j < nv) p.dv[((t0 + j) * p.HV + hv) * KD + d] = av;
-    dk[m] = fmaf(ae, expf(rec[R_G + j * KD + d]), dk[m]);
-    dG[m] = fmaf(ae, rec[R_E + j * KD + d], dG[m]);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) R4[(i0 + r) * LQ + j0 + cc] = (j0 + cc <= i0 + r) ? acc[r][cc] : 0.0f;
   }
   __syncthreads();
-  // dbeta_j += sum_i dA_ij T_ij; then dT = dA diag(beta).
+  if (tid < KD) {
+    float sacc = 0.0f;
+    for (int r = 0; r < C / 4; ++r) sacc += R3[r * KD + tid];
+    sGl[tid] = sacc;
+  }
+  // ---- phase 2: dA = tril(dVnew v^T + dW E^T), dv = A^T dVnew,
+  // dE = A^T dW.  R0 = dW^T [K][C]; R1 = v^T then E^T ([*][C]);
+  // R2 = dVnew^T; R3 = dW [C][K].
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+    *reinterpret_cast<float4*>(R0 + (d0 + cc) * LQ + i0) = make_float4(-aw[0][cc], -aw[1][cc], -aw[2][cc], -aw[3][cc]);
+  __syncthreads();   // sGl read R3's partials
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float w[8] = {-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3], -aw[r][4], -aw[r][5], -aw[r][6], -aw[r][7]};
+    st8(R3 + (i0 + r) * KP + d0, w);
+  }
+  for (int t = tid; t < C * KD; t += NTB) {
+    const int j = t / KD, vv = t - j * KD;
+    R1[vv * LQ + j] = j < nv ? bf16f(p.v[((t0 + j) * p.HV + hv) * KD + vv]) : 0.0f;
+  }
+  __syncthreads();
+  float da[4][4] = {};
+#pragma unroll 4
+  for (int vv = 0; vv < KD; ++vv) fma4x4(da, lds4(R2 + vv * LQ + i0), lds4(R1 + vv * LQ + j0), 1.0f);
+  __syncthreads();
+  load_rows(R1, LQ, rec + R_ET, C, 0, KD, 0, C, tid);
+  __syncthreads();
+#pragma unroll 4
+  for (int d = 0; d < KD; ++d) fma4x4(da, lds4(R0 + d * LQ + i0), lds4(R1 + d * LQ + j0), 1.0f);
+  __syncthreads();
+  // R0 = A | T ([C][LQ] each); R1 = dA | X; R2 = dVnew [C][K].
+  float* sA = R0;
+  float* sT = R0 + C * LQ;
+  float* sDA = R1;
+  float* sX = R1 + C * LQ;
+  load_rows(sA, LQ, rec + R_A, C, 0, C, 0, C, tid);
+  load_rows(sT, LQ, rec + R_T, C, 0, C, 0, C, tid);
+  load_rows(R2, KP, rec + R_DVN, KD, 0, C, 0, KD, tid);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) sDA[(i0 + r) * LQ + j0 + cc] = (j0 + cc <= i0 + r) ? da[r][cc] : 0.0f;
+  __syncthreads();
+  {
+    float av[4][8] = {}, ae[4][8] = {};
+#pragma unroll 2
+    for (int i = 0; i < C; ++i) {
+      const float4 a = lds4(sA + i * LQ + i0);   // A[i][j0 .. j0+3] over this tile's rows j
+      fma4x8(av, a, lds4(R2 + i * KP + d0), lds4(R2 + i * KP + d0 + 4));
+      fma4x8(ae, a, lds4(R3 + i * KP + d0), lds4(R3 + i * KP + d0 + 4));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = i0 + r;
+      if (j < nv) st8(p.dv + ((t0 + j) * p.HV + hv) * KD + d0, av[r]);
+      float gv[8], ev[8], vk[8], vg[8];
+      ld8(rec + R_G + j * KD + d0, gv);
+      ld8(rec + R_E + j * KD + d0, ev);
+      ld8(gdG + j * KD + d0, vg);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) vg[cc] = fmaf(ae[r][cc], ev[cc], vg[cc]);
+      st8(gdG + j * KD + d0, vg);
+      if (j < nv) {
+        ld8(gdk + j * rs + d0, vk);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) vk[cc] = fmaf(ae[r][cc], expf(gv[cc]), vk[cc]);
+        st8(gdk + j * rs + d0, vk);
+      }
+    }
+  }
+  // ---- dbeta and dL: dbeta_j += sum_i dA_ij T_ij; dT = dA diag(beta);
+  // X = dT T^T; dL = -tril_strict(T^T X) (into sDA); dbeta_i += sum_j dL_ij P_ij.
   if (tid < C) {
     const int j = tid;
     float acc = 0.0f;
-    for (int i = j; i < C; ++i) acc = fmaf(sM2[i * CP + j], sT[i * CP + j], acc);
+    for (int i = j; i < C; ++i) acc = fmaf(sDA[i * LQ + j], sT[i * LQ + j], acc);
     sDB[j] += acc;
   }
   __syncthreads();
   for (int t = tid; t < C * C; t += NTB) {
     const int i = t / C, j = t - i * C;
-    sM2[i * CP + j] *= sB[j];
+    sDA[i * LQ + j] *= sB[j];
   }
   __syncthreads();
-  // X = dT T^T (both lower triangular).
   for (int t = tid; t < C * C; t += NTB) {
     const int i = t / C, mm = t - i * C;
     float acc = 0.0f;
     const int lim = min(i, mm);
-    for (int j = 0; j <= lim; ++j) acc = fmaf(sM2[i * CP + j], sT[mm * CP + j], acc);
-    sM3[i * CP + mm] = acc;
+    for (int j = 0; j <= lim; ++j) acc = fmaf(sDA[i * LQ + j], sT[mm * LQ + j], acc);
+    sX[i * LQ + mm] = acc;
   }
   __syncthreads();
-  // dL = -tril_strict(T^T X) (into sM2).
   for (int t = tid; t < C * C; t += NTB) {
     const int a = t / C, b = t - a * C;
     float acc = 0.0f;
     if (b < a)
-      for (int i = a; i < C; ++i) acc = fmaf(sT[i * CP + a], sM3[i * CP + b], acc);
-    sM2[a * CP + b] = -acc;
+      for (int i = a; i < C; ++i) acc = fmaf(sT[i * LQ + a], sX[i * LQ + b], acc);
+    sDA[a * LQ + b] = -acc;
   }
   __syncthreads();
-  // dbeta_i += sum_j dL_ij P_ij.
   if (tid < C) {
     const int i = tid;
     float acc = 0.0f;
-    for (int j = 0; j < i; ++j) acc = fmaf(sM2[i * CP + j], rec[R_P + i * C + j], acc);
+    for (int j = 0; j < i; ++j) acc = fmaf(sDA[i * LQ + j], rec[R_P + i * C + j], acc);
     sDB[i] += acc;
   }
-  // k^, q^, G for the gated sums (k^ over A and T, which are consumed).
-  load_tile(sKn, rec + R_KN, tid);
-  load_tile(sX, rec + R_QN, tid);
-  load_tile(sZ, rec + R_G, tid);
+  // ---- phase 3: gated sums.  R0 = G, R2 = k^, R3 = q^ ([C][K]); dL in
+  // R1 (sDA), dAqk in R4.
+  load_rows(R0, KP, rec + R_G, KD, 0, C, 0, KD, tid);
+  load_rows(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
+  load_rows(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
   __syncthreads();
-  // Gated sums through P (Mk = diag(beta) dL) and Aqk (Mq = K^-1/2 dAqk).
+  {
+    float gi[4][8];
 #pragma unroll
-  for (int m = 0; m < NR; ++m) {
-    const int i = hr + 2 * m;
-    const float gi = sZ[i * KP + d];
-    const float ki = sKn[i * KP + d];
-    const float qi = sX[i * KP + d];
-    const float bi = sB[i];
-    float rk = 0.0f, rq = 0.0f;
-    for (int j = 0; j <= i; ++j) {   // row forms
-      const float e = expf(gi - sZ[j * KP + d]) * sKn[j * KP + d];
-      rk = fmaf(bi * sM2[i * CP + j], e, rk);
-      rq = fmaf(kScale * sM1[i * CP + j], e, rq);
+    for (int r = 0; r < 4; ++r) ld8(R0 + (i0 + r) * KP + d0, gi[r]);
+    // Row forms: j <= i over this tile's rows i.
+    {
+      float rk[4][8] = {}, rq[4][8] = {};
+      for (int j = 0; j <= i0 + 3; ++j) {
+        float gj[8], kj[8];
+        ld8(R0 + j * KP + d0, gj);
+        ld8(R2 + j * KP + d0, kj);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          const float mk = j <= i ? sB[i] * sDA[i * LQ + j] : 0.0f;
+          const float mq = j <= i ? kScale * R4[i * LQ + j] : 0.0f;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float e = j <= i ? expf(gi[r][cc] - gj[cc]) * kj[cc] : 0.0f;
+            rk[r][cc] = fmaf(mk, e, rk[r][cc]);
+            rq[r][cc] = fmaf(mq, e, rq[r][cc]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        float ki[8], qi[8], vg[8];
+        ld8(R2 + i * KP + d0, ki);
+        ld8(R3 + i * KP + d0, qi);
+        ld8(gdG + i * KD + d0, vg);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) vg[cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
+        st8(gdG + i * KD + d0, vg);
+        if (i < nv) {
+          float vq[8], vk[8];
+          ld8(gdq + i * rs + d0, vq);
+          ld8(gdk + i * rs + d0, vk);
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            vq[cc] += rq[r][cc];
+            vk[cc] += rk[r][cc];
+          }
+          st8(gdq + i * rs + d0, vq);
+          st8(gdk + i * rs + d0, vk);
+        }
+      }
     }
-    float ck = 0.0f, cq = 0.0f;
-    for (int r = i; r < C; ++r) {     // column forms (row i as the column index)
-      const float e = expf(sZ[r * KP + d] - gi);
-      ck = fmaf(sB[r] * sM2[r * CP + i], sKn[r * KP + d] * e, ck);
-      cq = fmaf(kScale * sM1[r * CP + i], sX[r * KP + d] * e, cq);
+    // Column forms: i >= j over this tile's rows j (as the column index).
+    {
+      float ck[4][8] = {}, cq[4][8] = {};
+      for (int i = i0; i < C; ++i) {
+        float gr[8], kr[8], qr[8];
+        ld8(R0 + i * KP + d0, gr);
+        ld8(R2 + i * KP + d0, kr);
+        ld8(R3 + i * KP + d0, qr);
+        const float4 dl4 = lds4(sDA + i * LQ + i0);
+        const float4 aq4 = lds4(R4 + i * LQ + i0);
+        const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float aqv[4] = {aq4.x, aq4.y, aq4.z, aq4.w};
+        const float bi = sB[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = i0 + r;
+          const float mk = i >= j ? bi * dl[r] : 0.0f;
+          const float mq = i >= j ? kScale * aqv[r] : 0.0f;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float e = i >= j ? expf(gr[cc] - gi[r][cc]) : 0.0f;
+            ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
+            cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        float ki[8], vg[8];
+        ld8(R2 + i * KP + d0, ki);
+        ld8(gdG + i * KD + d0, vg);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) vg[cc] -= ki[cc] * (ck[r][cc] + cq[r][cc]);
+        if (i == C - 1)
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) vg[cc] += sGl[d0 + cc];
+        st8(gdG + i * KD + d0, vg);
+        if (i < nv) {
+          float vk[8];
+          ld8(gdk + i * rs + d0, vk);
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) vk[cc] += ck[r][cc] + cq[r][cc];
+          st8(gdk + i * rs + d0, vk);
+        }
+      }
     }
-    dk[m] += rk + ck + cq;
-    dq[m] += rq;
-    dG[m] += ki * rk + qi * rq - ki * ck - ki * cq;
   }
-  // dG_last onto the last row, then dg as the reverse prefix of dG.
-  __syncthreads();
-  if (hr == 1) sGl[d] = dgl;
-  __syncthreads();
-  if (hr == 0) sGl[d] += dgl;
+  // ---- outputs: dg as the reverse prefix of dG over the chunk's rows
+  // (dG_last was added to the last row); dbeta.  Each thread reads back
+  // only the dG entries it wrote.
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < NR; ++m) {
-    const int i = hr + 2 * m;
-    float v = dG[m];
-    if (i == C - 1) v += sGl[d];
-    sX[i * KP + d] = v;
-    if (i < nv) {
-      p.dqh[((t0 + i) * p.HV + hv) * KD + d] = dq[m];
-      p.dkh[((t0 + i) * p.HV + hv) * KD + d] = dk[m];
-    }
+  for (int r = 0; r < 4; ++r) {
+    float vg[8];
+    ld8(gdG + (i0 + r) * KD + d0, vg);
+    st8(R0 + (i0 + r) * KP + d0, vg);
   }
   __syncthreads();
-  if (hr == 0) {
+  if (tid < KD) {
     float acc = 0.0f;
     for (int i = C - 1; i >= 0; --i) {
-      acc += sX[i * KP + d];
-      if (i < nv) p.dg[((t0 + i) * p.HV + hv) * KD + d] = acc;
+      acc += R0[i * KP + tid];
+      if (i < nv) p.dg[((t0 + i) * p.HV + hv) * KD + tid] = acc;
     }
   }
   if (tid < nv) p.dbeta[(t0 + tid) * p.HV + hv] = sDB[tid];
@@ -801,7 +1012,8 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
     return KDA_ERR_NULL;
   if (!kda::aligned16(q) || !kda::aligned16(k) || !kda::aligned16(v) || !kda::aligned16(g) ||
       !kda::aligned16(d_out) || !kda::aligned16(dq) || !kda::aligned16(dk) || !kda::aligned16(dv) ||
-      !kda::aligned16(dg) || !kda::aligned16(workspace))
+      !kda::aligned16(dg) || !kda::aligned16(workspace) || !kda::aligned16(initial_state) ||
+      !kda::aligned16(d_final_state) || !kda::aligned16(d_initial_state))
     return KDA_ERR_ALIGN;
   const size_t need = kda_chunk_backward_workspace_size(B, T, H, HV, Kd, Vd, int32_t(nseq));
   if (!workspace) return KDA_ERR_NULL;

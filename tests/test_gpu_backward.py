@@ -117,3 +117,29 @@ def test_backward_beta_zero(gpu_lib):
     got, ref = _run(gpu_lib, inp, d_out, d_final)
     assert np.all(got[2] == 0), "beta = 0: v must get exactly zero gradient"
     _check(got, ref, "beta0")
+
+
+def test_backward_full_size_sampled_head(gpu_lib):
+    """The bench workload (B=1, H=HV=96, T=8192, zero initial state) in one
+    call; heads are independent (H == HV), so one sampled head is checked
+    against the oracle run on that head alone (37 s of CPU), and every
+    output is checked to be finite."""
+    inp = synth.config2()
+    d_out, d_final = synth.upstream_grads(inp)
+    say(f"backward full size {inp.name}")
+    dev = "cuda"
+    got = gpu_lib.chunk_backward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                                 inp.beta.to(dev), inp.initial_state.to(dev), d_out.to(dev),
+                                 d_final.to(dev))
+    torch.cuda.synchronize()
+    for name, x in zip(NAMES, got):
+        assert bool(torch.isfinite(x).all()), f"full size: {name} non-finite"
+    h = 37
+    sl = lambda t: t[:, :, h:h + 1].float().numpy()
+    ref = oracle.recurrent_backward(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta),
+                                    inp.initial_state[:, h:h + 1].numpy(), sl(d_out),
+                                    d_final[:, h:h + 1].numpy())
+    mine = [x[:, :, h:h + 1] if x.dim() >= 3 and name != "dh0" else x[:, h:h + 1]
+            for name, x in zip(NAMES, got)]
+    mine = [x.cpu().numpy().astype(np.float64) for x in mine]
+    _check(mine, ref, f"full size head {h}")
