@@ -57,16 +57,21 @@ constexpr int C = 64;             // chunk size
 constexpr int KD = kda::kHead;    // K == V == 128
 constexpr int NTB = 256;          // threads per workgroup
 constexpr int KP = KD + 4;        // LDS row stride of [C][KD] fp32 tiles (16-byte aligned rows)
-constexpr int CP = C + 2;         // LDS row stride of [C][C] fp32 tiles
 constexpr int NCOL = 64;          // state columns per carry workgroup
 constexpr float kScale = 0.08838834764831845f;   // 128^-1/2
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x by the hardware instruction (results below 2^-126 flush to zero;
+// they only ever scale terms of sums, so the loss is below 1e-38 absolute).
+// G is kept in log2 units (G log2 e), so exp(G_i - G_j) = 2^(G2_i - G2_j).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Per-chunk record in the workspace (float offsets), one per (value head,
 // chunk slot), slots numbered as in the forward: chunk c of sequence n is
 // slot floor(first_token(n) / 64) + n + c.
 constexpr int R_QN = 0;                     // [C][K] q^ (bf16 values)
 constexpr int R_KN = R_QN + C * KD;         // [C][K] k^
-constexpr int R_G = R_KN + C * KD;          // [C][K] G, inclusive prefix of g
+constexpr int R_G = R_KN + C * KD;          // [C][K] G log2(e), G the inclusive prefix of g
 constexpr int R_E = R_G + C * KD;           // [C][K] exp(G) k^
 constexpr int R_W = R_E + C * KD;           // [C][K] A E
 constexpr int R_U = R_W + C * KD;           // [C][V] A v
@@ -167,178 +172,8 @@ __device__ __forceinline__ void load_tile(float* dst, const float* src, int tid)
   }
 }
 
-// --------------------------------------------------------------- prep
-constexpr int PREP_LDS = (3 * C * KP + 2 * C * CP + C) * 4;
-
-__global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
-  extern __shared__ __align__(16) float smem[];
-  float* sQ = smem;                 // q^, later E
-  float* sK = sQ + C * KP;          // k^, later v
-  float* sG = sK + C * KP;          // G
-  float* sP = sG + C * KP;          // P, later A
-  float* sT = sP + C * CP;          // T
-  float* sB = sT + C * CP;          // beta
-
-  const int64_t slot = blockIdx.x;
-  const int hv = blockIdx.y;
-  int c;
-  const int n = slot_owner(p, slot, c);
-  if (n < 0) return;
-  int64_t tok0;
-  int len;
-  seq_range(p, n, tok0, len);
-  const int64_t t0 = tok0 + int64_t(c) * C;
-  const int nv = min(C, len - c * C);
-  const int hq = hv / (p.HV / p.H);
-  float* rec = record(p, hv, slot);
-  const int tid = threadIdx.x;
-
-  // q^ and k^: 16 rows per pass (16 lanes per row, 8 elements per lane);
-  // rows 0..63 are q, 64..127 are k; rows past the chunk's end are zero.
-  for (int pass = 0; pass < 2 * C / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
-    const int l16 = tid & 15;
-    const bool isk = r >= C;
-    const int tr = r & (C - 1);
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (tr < nv)
-      x = *reinterpret_cast<const uint4*>((isk ? p.k : p.q) + ((t0 + tr) * p.H + hq) * KD + 8 * l16);
-    const uint4 y = kda::l2norm_row16(x);
-    const uint32_t w[4] = {y.x, y.y, y.z, y.w};
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = kda::bf16lo(w[e]);
-      f[2 * e + 1] = kda::bf16hi(w[e]);
-    }
-    float* dl = (isk ? sK : sQ) + tr * KP + 8 * l16;
-    float* dgl = rec + (isk ? R_KN : R_QN) + tr * KD + 8 * l16;
-    *reinterpret_cast<float4*>(dl) = make_float4(f[0], f[1], f[2], f[3]);
-    *reinterpret_cast<float4*>(dl + 4) = make_float4(f[4], f[5], f[6], f[7]);
-    *reinterpret_cast<float4*>(dgl) = make_float4(f[0], f[1], f[2], f[3]);
-    *reinterpret_cast<float4*>(dgl + 4) = make_float4(f[4], f[5], f[6], f[7]);
-  }
-  // G: inclusive prefix over the chunk's tokens (padding has g = 0).
-  if (tid < KD) {
-    float acc = 0.0f;
-    for (int t = 0; t < C; ++t) {
-      if (t < nv) acc += p.g[((t0 + t) * p.HV + hv) * KD + tid];
-      sG[t * KP + tid] = acc;
-      rec[R_G + t * KD + tid] = acc;
-    }
-  }
-  if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
-  __syncthreads();
-
-  // P and Aqk over the lower triangle; zeros above it.
-  for (int t = tid; t < kPairs; t += NTB) {
-    int i, j;
-    tri_pair(t, i, j);
-    const float* ki = sK + i * KP;
-    const float* kj = sK + j * KP;
-    const float* qi = sQ + i * KP;
-    const float* gi = sG + i * KP;
-    const float* gj = sG + j * KP;
-    float pk = 0.0f, pq = 0.0f;
-    for (int d = 0; d < KD; ++d) {
-      const float e = expf(gi[d] - gj[d]);
-      const float kje = kj[d] * e;
-      pk = fmaf(ki[d], kje, pk);
-      pq = fmaf(qi[d], kje, pq);
-    }
-    const float pv = j < i ? pk : 0.0f;
-    sP[i * CP + j] = pv;
-    rec[R_P + i * C + j] = pv;
-    rec[R_AQK + i * C + j] = kScale * pq;
-  }
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, j = t - i * C;
-    if (j > i) {
-      sP[i * CP + j] = 0.0f;
-      rec[R_P + t] = 0.0f;
-      rec[R_AQK + t] = 0.0f;
-    }
-  }
-  __syncthreads();
-
-  // T = (I + diag(beta) P)^-1 by forward substitution, one column per thread.
-  if (tid < C) {
-    const int j = tid;
-    for (int i = 0; i < C; ++i) {
-      float tv;
-      if (i < j) {
-        tv = 0.0f;
-      } else if (i == j) {
-        tv = 1.0f;
-      } else {
-        float acc = 0.0f;
-        for (int m = j; m < i; ++m) acc = fmaf(sP[i * CP + m], sT[m * CP + j], acc);
-        tv = -sB[i] * acc;
-      }
-      sT[i * CP + j] = tv;
-    }
-  }
-  __syncthreads();
-  // A = T diag(beta) (into sP); T and A to the record.
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, j = t - i * C;
-    const float tv = sT[i * CP + j];
-    const float a = tv * sB[j];
-    rec[R_T + t] = tv;
-    rec[R_A + t] = a;
-    sP[i * CP + j] = a;
-  }
-  if (tid < KD) rec[R_GAM + tid] = expf(sG[(C - 1) * KP + tid]);
-  // Qg, Kg, E (E replaces q^ in LDS).
-  for (int t = tid; t < C * KD; t += NTB) {
-    const int i = t / KD, d = t - i * KD;
-    const float gv = sG[i * KP + d];
-    const float eg = expf(gv);
-    const float kv = sK[i * KP + d];
-    rec[R_QG + t] = kScale * sQ[i * KP + d] * eg;
-    const float kg = kv * expf(sG[(C - 1) * KP + d] - gv);
-    rec[R_KG + t] = kg;
-    rec[R_KGT + d * C + i] = kg;
-    const float ev = eg * kv;
-    rec[R_E + t] = ev;
-    rec[R_ET + d * C + i] = ev;
-    sQ[i * KP + d] = ev;
-  }
-  __syncthreads();
-  // v (zero past the chunk's end) replaces k^ in LDS.
-  for (int t = tid; t < C * KD; t += NTB) {
-    const int i = t / KD, d = t - i * KD;
-    sK[i * KP + d] = i < nv ? bf16f(p.v[((t0 + i) * p.HV + hv) * KD + d]) : 0.0f;
-  }
-  __syncthreads();
-  // W = A E and U = A v (A lower triangular).
-  {
-    const int d = tid & (KD - 1);
-    for (int i = tid >> 7; i < C; i += 2) {
-      float w = 0.0f, u = 0.0f;
-      for (int j = 0; j <= i; ++j) {
-        const float a = sP[i * CP + j];
-        w = fmaf(a, sQ[j * KP + d], w);
-        u = fmaf(a, sK[j * KP + d], u);
-      }
-      rec[R_W + i * KD + d] = w;
-      rec[R_WT + d * C + i] = w;
-      rec[R_U + i * KD + d] = u;
-    }
-  }
-}
-
-// --------------------------------------------------------------- carries
-// Workgroup (column group cg, value head hv, sequence n) owns state columns
-// 64 cg .. 64 cg + 63.  Every product is register-blocked: thread t
-// computes a 4x4 or 8x4 tile (rows from t / 16, columns 4 (t % 16) ..+3)
-// from 16-byte LDS reads of operands stored contraction-index-major, so
-// one pair of reads feeds 16 or 32 fused multiply-adds.
-constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
-constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ) * 4;
-constexpr int REV_LDS = (2 * KD * SQ + 3 * C * SQ + KD) * 4;
-static_assert(FWD_LDS <= 160 * 1024 && REV_LDS <= 160 * 1024, "LDS budget");
-static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where Kg^T was");
+// --------------------------------------------------------------- helpers
+constexpr int LQ = C + 4;         // LDS row stride of [*][C] fp32 tiles (16-byte aligned rows)
 
 // Copy rows [r0, r0 + rows) of a [*][cols] fp32 record matrix, columns
 // [c0, c0 + w), into LDS with row stride ld (all multiples of 4).
@@ -363,6 +198,260 @@ __device__ __forceinline__ void fma4x4(float (*acc)[4], const float4 a, const fl
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
 }
+
+// acc[4][8] += a[4] (x) b[8].
+__device__ __forceinline__ void fma4x8(float (*acc)[8], const float4 a, const float4 b0, const float4 b1) {
+  const float av[4] = {a.x, a.y, a.z, a.w};
+  const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+}
+
+__device__ __forceinline__ void ld8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void st8(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// --------------------------------------------------------------- prep
+// Thread tiles as in the gradient kernel: [C][128] results in 4x8 tiles
+// (rows 4 (t / 16), columns 8 (t % 16)); P and Aqk in 4x4 blocks of
+// (i, j) pairs, one lower-triangle block per thread for the first 136
+// threads (the other 120 threads write the zero blocks above it).
+constexpr int PREP_LDS = (3 * C * KP + 2 * C * LQ + C) * 4;
+constexpr int kTriBlocks = (C / 4) * (C / 4 + 1) / 2;   // 136
+static_assert(NTB - kTriBlocks == (C / 4) * (C / 4 - 1) / 2, "one thread per 4x4 block of the square");
+
+__global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
+  extern __shared__ __align__(16) float smem[];
+  float* sQ = smem;                 // q^, later E
+  float* sK = sQ + C * KP;          // k^, later v
+  float* sG = sK + C * KP;          // G
+  float* sP = sG + C * KP;          // P [C][LQ]
+  float* sAT = sP + C * LQ;         // A^T [C][LQ]
+  float* sB = sAT + C * LQ;         // beta
+
+  const int64_t slot = blockIdx.x;
+  const int hv = blockIdx.y;
+  int c;
+  const int n = slot_owner(p, slot, c);
+  if (n < 0) return;
+  int64_t tok0;
+  int len;
+  seq_range(p, n, tok0, len);
+  const int64_t t0 = tok0 + int64_t(c) * C;
+  const int nv = min(C, len - c * C);
+  const int hq = hv / (p.HV / p.H);
+  float* rec = record(p, hv, slot);
+  const int tid = threadIdx.x;
+  const int rb = tid >> 4, cb = tid & 15;
+  const int i0 = 4 * rb, d0 = 8 * cb;
+
+  // q^ and k^: 16 rows per pass (16 lanes per row, 8 elements per lane);
+  // rows 0..63 are q, 64..127 are k; rows past the chunk's end are zero.
+  for (int pass = 0; pass < 2 * C / 16; ++pass) {
+    const int r = pass * 16 + (tid >> 4);
+    const int l16 = tid & 15;
+    const bool isk = r >= C;
+    const int tr = r & (C - 1);
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (tr < nv)
+      x = *reinterpret_cast<const uint4*>((isk ? p.k : p.q) + ((t0 + tr) * p.H + hq) * KD + 8 * l16);
+    const uint4 y = kda::l2norm_row16(x);
+    const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = kda::bf16lo(w[e]);
+      f[2 * e + 1] = kda::bf16hi(w[e]);
+    }
+    st8((isk ? sK : sQ) + tr * KP + 8 * l16, f);
+    st8(rec + (isk ? R_KN : R_QN) + tr * KD + 8 * l16, f);
+  }
+  // G: inclusive prefix over the chunk's tokens (padding has g = 0), kept
+  // in log2 units.
+  if (tid < KD) {
+    float acc = 0.0f;
+    for (int t = 0; t < C; ++t) {
+      if (t < nv) acc += p.g[((t0 + t) * p.HV + hv) * KD + tid];
+      const float g2 = acc * kLog2e;
+      sG[t * KP + tid] = g2;
+      rec[R_G + t * KD + tid] = g2;
+    }
+  }
+  if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
+  __syncthreads();
+
+  // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.
+  {
+    int bi, bj;
+    const bool lower = tid < kTriBlocks;
+    if (lower) {
+      tri_pair(tid, bi, bj);
+    } else {   // the strictly-upper blocks, numbered the same way transposed
+      tri_pair(tid - kTriBlocks, bj, bi);
+      ++bj;    // tri_pair over a triangle one smaller, shifted past the diagonal
+    }
+    const int a0 = 4 * bi, b0 = 4 * bj;
+    float pk[4][4] = {}, pq[4][4] = {};
+    if (lower) {
+      for (int d = 0; d < KD; d += 4) {
+        float4 gi[4], gj[4], ki[4], kj[4], qi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gi[r] = lds4(sG + (a0 + r) * KP + d);
+          gj[r] = lds4(sG + (b0 + r) * KP + d);
+          ki[r] = lds4(sK + (a0 + r) * KP + d);
+          kj[r] = lds4(sK + (b0 + r) * KP + d);
+          qi[r] = lds4(sQ + (a0 + r) * KP + d);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool ok = b0 + q <= a0 + r;   // no positive exponent is formed
+            const float e0 = ok ? ex2(gi[r].x - gj[q].x) : 0.0f;
+            const float e1 = ok ? ex2(gi[r].y - gj[q].y) : 0.0f;
+            const float e2 = ok ? ex2(gi[r].z - gj[q].z) : 0.0f;
+            const float e3 = ok ? ex2(gi[r].w - gj[q].w) : 0.0f;
+            const float k0 = kj[q].x * e0, k1 = kj[q].y * e1, k2 = kj[q].z * e2, k3 = kj[q].w * e3;
+            pk[r][q] = fmaf(ki[r].x, k0, fmaf(ki[r].y, k1, fmaf(ki[r].z, k2, fmaf(ki[r].w, k3, pk[r][q]))));
+            pq[r][q] = fmaf(qi[r].x, k0, fmaf(qi[r].y, k1, fmaf(qi[r].z, k2, fmaf(qi[r].w, k3, pq[r][q]))));
+          }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = a0 + r;
+      float pv[4], av[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = b0 + q;
+        pv[q] = j < i ? pk[r][q] : 0.0f;
+        av[q] = j <= i ? kScale * pq[r][q] : 0.0f;
+      }
+      const float4 p4 = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      *reinterpret_cast<float4*>(sP + i * LQ + b0) = p4;
+      *reinterpret_cast<float4*>(rec + R_P + i * C + b0) = p4;
+      *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
+    }
+  }
+  __syncthreads();
+
+  // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
+  // 4j .. 4j+3 own column j, lane part holding T[16 part + m][j] (m < 16)
+  // in registers; row i's sum over the column is split by part and
+  // completed across the four lanes.  (P is strictly lower and T starts at
+  // zero, so the sums need no bounds.)
+  {
+    const int j = tid >> 2, part = tid & 3;
+    float tc[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) tc[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 pr = lds4(sP + i * LQ + 16 * part + 4 * q);
+        acc = fmaf(pr.x, tc[4 * q], acc);
+        acc = fmaf(pr.y, tc[4 * q + 1], acc);
+        acc = fmaf(pr.z, tc[4 * q + 2], acc);
+        acc = fmaf(pr.w, tc[4 * q + 3], acc);
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      const float tv = i == j ? 1.0f : -sB[i] * acc;
+      if (part == i / 16) tc[i % 16] = tv;
+    }
+    // T and A = T diag(beta) to the record; A^T to LDS.
+    const float bj = sB[j];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int i = 16 * part + m;
+      rec[R_T + i * C + j] = tc[m];
+      rec[R_A + i * C + j] = tc[m] * bj;
+      sAT[j * LQ + i] = tc[m] * bj;
+    }
+  }
+  if (tid < KD) rec[R_GAM + tid] = ex2(sG[(C - 1) * KP + tid]);
+  // Qg, Kg, E over this thread's 4x8 tile (E replaces q^ in LDS; the
+  // transposed copies are written four rows at a time).
+  {
+    float gl[8];
+    ld8(sG + (C - 1) * KP + d0, gl);
+    float kgt[8][4], et[8][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r;
+      float gv[8], kv[8], qv[8], qg[8], kg[8], ev[8];
+      ld8(sG + i * KP + d0, gv);
+      ld8(sK + i * KP + d0, kv);
+      ld8(sQ + i * KP + d0, qv);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const float eg = ex2(gv[cc]);
+        qg[cc] = kScale * qv[cc] * eg;
+        kg[cc] = kv[cc] * ex2(gl[cc] - gv[cc]);
+        ev[cc] = eg * kv[cc];
+        kgt[cc][r] = kg[cc];
+        et[cc][r] = ev[cc];
+      }
+      st8(rec + R_QG + i * KD + d0, qg);
+      st8(rec + R_KG + i * KD + d0, kg);
+      st8(rec + R_E + i * KD + d0, ev);
+      st8(sQ + i * KP + d0, ev);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      *reinterpret_cast<float4*>(rec + R_KGT + (d0 + cc) * C + i0) = make_float4(kgt[cc][0], kgt[cc][1], kgt[cc][2], kgt[cc][3]);
+      *reinterpret_cast<float4*>(rec + R_ET + (d0 + cc) * C + i0) = make_float4(et[cc][0], et[cc][1], et[cc][2], et[cc][3]);
+    }
+  }
+  __syncthreads();
+  // v (zero past the chunk's end) replaces k^ in LDS.
+  for (int t = tid; t < C * KD; t += NTB) {
+    const int i = t / KD, d = t - i * KD;
+    sK[i * KP + d] = i < nv ? bf16f(p.v[((t0 + i) * p.HV + hv) * KD + d]) : 0.0f;
+  }
+  __syncthreads();
+  // W = A E and U = A v (A lower triangular: j <= i0 + 3 suffices).
+  {
+    float w[4][8] = {}, u[4][8] = {};
+    for (int j = 0; j <= i0 + 3; ++j) {
+      const float4 a = lds4(sAT + j * LQ + i0);
+      fma4x8(w, a, lds4(sQ + j * KP + d0), lds4(sQ + j * KP + d0 + 4));
+      fma4x8(u, a, lds4(sK + j * KP + d0), lds4(sK + j * KP + d0 + 4));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st8(rec + R_W + (i0 + r) * KD + d0, w[r]);
+      st8(rec + R_U + (i0 + r) * KD + d0, u[r]);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      *reinterpret_cast<float4*>(rec + R_WT + (d0 + cc) * C + i0) = make_float4(w[0][cc], w[1][cc], w[2][cc], w[3][cc]);
+  }
+}
+
+// --------------------------------------------------------------- carries
+// Workgroup (column group cg, value head hv, sequence n) owns state columns
+// 64 cg .. 64 cg + 63.  Every product is register-blocked: thread t
+// computes a 4x4 or 8x4 tile (rows from t / 16, columns 4 (t % 16) ..+3)
+// from 16-byte LDS reads of operands stored contraction-index-major, so
+// one pair of reads feeds 16 or 32 fused multiply-adds.
+constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
+constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ) * 4;
+constexpr int REV_LDS = (2 * KD * SQ + 3 * C * SQ + KD) * 4;
+static_assert(FWD_LDS <= 160 * 1024 && REV_LDS <= 160 * 1024, "LDS budget");
+static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where Kg^T was");
 
 __global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -555,7 +644,6 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
 // products use 4x4 tiles (rows 4 (t / 16), columns 4 (t % 16)).  LDS holds
 // three [128][68] regions (R0-R2), one [64][132] region (R3) and one
 // [64][68] region (R4); what each holds changes by phase (below).
-constexpr int LQ = C + 4;           // row stride of [*][C] tiles
 constexpr int R0_OFF = 0;
 constexpr int R1_OFF = R0_OFF + KD * LQ;
 constexpr int R2_OFF = R1_OFF + KD * LQ;
@@ -565,27 +653,6 @@ constexpr int SM_OFF = R4_OFF + C * LQ;
 constexpr int GRAD_LDS = (SM_OFF + 2 * C + KD) * 4;
 static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ, "regions hold their alternates");
-
-// acc[4][8] += a[4] (x) b[8].
-__device__ __forceinline__ void fma4x8(float (*acc)[8], const float4 a, const float4 b0, const float4 b1) {
-  const float av[4] = {a.x, a.y, a.z, a.w};
-  const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-}
-
-__device__ __forceinline__ void ld8(const float* p, float* v) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-__device__ __forceinline__ void st8(float* p, const float* v) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
 
 __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -676,9 +743,9 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
       float vq[8], vk[8], vg[8];
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        vq[cc] = kScale * aq[r][cc] * expf(gv[cc]);
+        vq[cc] = kScale * aq[r][cc] * ex2(gv[cc]);
         vg[cc] = aq[r][cc] * qg[cc] - akg[r][cc] * kg[cc];
-        vk[cc] = akg[r][cc] * expf(gl[cc] - gv[cc]);
+        vk[cc] = akg[r][cc] * ex2(gl[cc] - gv[cc]);
         dglp[cc] = fmaf(akg[r][cc], kg[cc], dglp[cc]);
       }
       st8(gdG + (i0 + r) * KD + d0, vg);
@@ -766,7 +833,7 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
       if (j < nv) {
         ld8(gdk + j * rs + d0, vk);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) vk[cc] = fmaf(ae[r][cc], expf(gv[cc]), vk[cc]);
+        for (int cc = 0; cc < 8; ++cc) vk[cc] = fmaf(ae[r][cc], ex2(gv[cc]), vk[cc]);
         st8(gdk + j * rs + d0, vk);
       }
     }
@@ -831,7 +898,7 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
           const float mq = j <= i ? kScale * R4[i * LQ + j] : 0.0f;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            const float e = j <= i ? expf(gi[r][cc] - gj[cc]) * kj[cc] : 0.0f;
+            const float e = j <= i ? ex2(gi[r][cc] - gj[cc]) * kj[cc] : 0.0f;
             rk[r][cc] = fmaf(mk, e, rk[r][cc]);
             rq[r][cc] = fmaf(mq, e, rq[r][cc]);
           }
@@ -881,7 +948,7 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
           const float mq = i >= j ? kScale * aqv[r] : 0.0f;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            const float e = i >= j ? expf(gr[cc] - gi[r][cc]) : 0.0f;
+            const float e = i >= j ? ex2(gr[cc] - gi[r][cc]) : 0.0f;
             ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
             cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
           }
