@@ -177,10 +177,11 @@ constexpr int LQ = C + 4;         // LDS row stride of [*][C] fp32 tiles (16-byt
 
 // Copy rows [r0, r0 + rows) of a [*][cols] fp32 record matrix, columns
 // [c0, c0 + w), into LDS with row stride ld (all multiples of 4).
+template <int NTH = NTB>
 __device__ __forceinline__ void load_rows(float* dst, int ld, const float* src, int cols, int r0, int rows, int c0,
                                           int w, int tid) {
   const int q4 = w / 4;
-  for (int u = tid; u < rows * q4; u += NTB) {
+  for (int u = tid; u < rows * q4; u += NTH) {
     const int r = u / q4, c4 = u - r * q4;
     *reinterpret_cast<float4*>(dst + r * ld + 4 * c4) =
         *reinterpret_cast<const float4*>(src + (r0 + r) * cols + c0 + 4 * c4);
@@ -638,12 +639,15 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
 }
 
 // --------------------------------------------------------------- gradients
-// Register-blocked like the carries.  Every [C][128] quantity is owned in
-// 4x8 tiles: thread t holds rows 4 (t / 16) .. +3 and columns
-// 8 (t % 16) .. +7 of dq^, dk^ and dG for the whole kernel; [C][C]
-// products use 4x4 tiles (rows 4 (t / 16), columns 4 (t % 16)).  LDS holds
-// three [128][68] regions (R0-R2), one [64][132] region (R3) and one
-// [64][68] region (R4); what each holds changes by phase (below).
+// 512 threads (two waves per SIMD: the LDS footprint allows one workgroup
+// per compute unit, and the second wave hides the first one's latency).
+// Every [C][128] quantity is owned in 4x4 tiles: thread t holds rows
+// 4 (t / 32) .. +3 and columns 4 (t % 32) .. +3; [C][C] products use 2x4
+// tiles (rows 2 (t / 16) .. +1, columns 4 (t % 16) .. +3).  dq^, dk^ and dG
+// accumulate in memory only the owning thread touches.  LDS holds three
+// [128][68] regions (R0-R2), one [64][132] region (R3) and one [64][68]
+// region (R4); what each holds changes by phase (below).
+constexpr int NTG = 512;
 constexpr int R0_OFF = 0;
 constexpr int R1_OFF = R0_OFF + KD * LQ;
 constexpr int R2_OFF = R1_OFF + KD * LQ;
@@ -652,9 +656,31 @@ constexpr int R4_OFF = R3_OFF + C * KP;
 constexpr int SM_OFF = R4_OFF + C * LQ;
 constexpr int GRAD_LDS = (SM_OFF + 2 * C + KD) * 4;
 static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
-static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ, "regions hold their alternates");
+static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ && C * LQ <= C * KP, "regions hold their alternates");
+static_assert((C / 4) * KD <= C * KP, "dG_last partials fit in R3");
 
-__global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
+__device__ __forceinline__ float2 lds2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+
+// acc[2][4] += a[2] (x) b[4].
+__device__ __forceinline__ void fma2x4(float (*acc)[4], const float2 a, const float4 b) {
+  const float av[2] = {a.x, a.y};
+  const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+}
+
+__device__ __forceinline__ void ld4(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
+__device__ __forceinline__ void st4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
   float* R0 = smem + R0_OFF;
   float* R1 = smem + R1_OFF;
@@ -677,94 +703,88 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   const int nv = min(C, len - c * C);
   float* rec = record(p, hv, slot);
   const int tid = threadIdx.x;
-  const int rb = tid >> 4, cb = tid & 15;
-  const int i0 = 4 * rb, d0 = 8 * cb, j0 = 4 * cb;   // 4x8 tile rows/cols; 4x4 tile cols
-  // This thread's dq^, dk^ (rows of the chunk's real tokens) and dG (all
-  // rows) accumulate in memory it alone touches: the per-value-head q and
-  // k gradient buffers and the record's U field (no longer read).
+  const int rb = tid >> 5;
+  const int i0 = 4 * rb, d0 = 4 * (tid & 31);          // 4x4 tile of a [C][128] quantity
+  const int s0r = 2 * (tid >> 4), s0c = 4 * (tid & 15);  // 2x4 tile of a [C][C] product
   float* gdq = p.dqh + (t0 * p.HV + hv) * KD;
   float* gdk = p.dkh + (t0 * p.HV + hv) * KD;
   const int64_t rs = int64_t(p.HV) * KD;     // token stride of gdq, gdk
-  float* gdG = rec + R_U;
+  float* gdG = rec + R_U;                    // the record's U field is no longer read
 
   // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T, dgamma,
   // dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T, R2 = dVnew^T
   // ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per block.
-  for (int t = tid; t < C * KD; t += NTB) {
+  for (int t = tid; t < C * KD; t += NTG) {
     const int i = t / KD, vv = t - i * KD;
     R0[vv * LQ + i] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + vv]) : 0.0f;
   }
-  load_rows(R1, LQ, rec + R_VNT, C, 0, KD, 0, C, tid);
-  load_rows(R2, LQ, rec + R_DVNT, C, 0, KD, 0, C, tid);
+  load_rows<NTG>(R1, LQ, rec + R_VNT, C, 0, KD, 0, C, tid);
+  load_rows<NTG>(R2, LQ, rec + R_DVNT, C, 0, KD, 0, C, tid);
   if (tid < C) {
     sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
     sDB[tid] = 0.0f;
   }
-  float aq[4][8] = {}, aw[4][8] = {}, akg[4][8] = {};
-  float dgam[8] = {};
+  float aq[4][4] = {}, aw[4][4] = {}, akg[4][4] = {};
+  float dgam[4] = {};
   for (int vb = 0; vb < KD / 32; ++vb) {
-    load_rows(R3, KP, rec + R_ST, KD, 32 * vb, 32, 0, KD, tid);
-    load_rows(R3 + 32 * KP, KP, rec + R_DST, KD, 32 * vb, 32, 0, KD, tid);
+    load_rows<NTG>(R3, KP, rec + R_ST, KD, 32 * vb, 32, 0, KD, tid);
+    load_rows<NTG>(R3 + 32 * KP, KP, rec + R_DST, KD, 32 * vb, 32, 0, KD, tid);
     __syncthreads();
-#pragma unroll 2
+#pragma unroll 4
     for (int u = 0; u < 32; ++u) {
       const int vv = 32 * vb + u;
-      const float4 bs0 = lds4(R3 + u * KP + d0), bs1 = lds4(R3 + u * KP + d0 + 4);
-      const float4 bd0 = lds4(R3 + (32 + u) * KP + d0), bd1 = lds4(R3 + (32 + u) * KP + d0 + 4);
-      fma4x8(aq, lds4(R0 + vv * LQ + i0), bs0, bs1);
-      fma4x8(aw, lds4(R2 + vv * LQ + i0), bs0, bs1);
-      fma4x8(akg, lds4(R1 + vv * LQ + i0), bd0, bd1);
-      dgam[0] = fmaf(bs0.x, bd0.x, dgam[0]); dgam[1] = fmaf(bs0.y, bd0.y, dgam[1]);
-      dgam[2] = fmaf(bs0.z, bd0.z, dgam[2]); dgam[3] = fmaf(bs0.w, bd0.w, dgam[3]);
-      dgam[4] = fmaf(bs1.x, bd1.x, dgam[4]); dgam[5] = fmaf(bs1.y, bd1.y, dgam[5]);
-      dgam[6] = fmaf(bs1.z, bd1.z, dgam[6]); dgam[7] = fmaf(bs1.w, bd1.w, dgam[7]);
+      const float4 bs = lds4(R3 + u * KP + d0);
+      const float4 bd = lds4(R3 + (32 + u) * KP + d0);
+      fma4x4(aq, lds4(R0 + vv * LQ + i0), bs, 1.0f);
+      fma4x4(aw, lds4(R2 + vv * LQ + i0), bs, 1.0f);
+      fma4x4(akg, lds4(R1 + vv * LQ + i0), bd, 1.0f);
+      dgam[0] = fmaf(bs.x, bd.x, dgam[0]); dgam[1] = fmaf(bs.y, bd.y, dgam[1]);
+      dgam[2] = fmaf(bs.z, bd.z, dgam[2]); dgam[3] = fmaf(bs.w, bd.w, dgam[3]);
     }
     __syncthreads();
   }
   // Epilogue: dq^ = K^-1/2 dQg exp(G); dG = dQg Qg - dKg Kg;
   // dk^ = dKg exp(G_last - G); dG_last partials dKg Kg (+ dgamma gamma).
   {
-    float gl[8], dglp[8];
-    ld8(rec + R_G + (C - 1) * KD + d0, gl);
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) dglp[cc] = 0.0f;
+    float gl[4], dglp[4] = {};
+    ld4(rec + R_G + (C - 1) * KD + d0, gl);
     if (rb == 0) {
-      float gm[8];
-      ld8(rec + R_GAM + d0, gm);
+      float gm[4];
+      ld4(rec + R_GAM + d0, gm);
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) dglp[cc] = dgam[cc] * gm[cc];
+      for (int cc = 0; cc < 4; ++cc) dglp[cc] = dgam[cc] * gm[cc];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float gv[8], qg[8], kg[8];
-      ld8(rec + R_G + (i0 + r) * KD + d0, gv);
-      ld8(rec + R_QG + (i0 + r) * KD + d0, qg);
-      ld8(rec + R_KG + (i0 + r) * KD + d0, kg);
-      float vq[8], vk[8], vg[8];
+      const int i = i0 + r;
+      float gv[4], qg[4], kg[4], vq[4], vk[4], vg[4];
+      ld4(rec + R_G + i * KD + d0, gv);
+      ld4(rec + R_QG + i * KD + d0, qg);
+      ld4(rec + R_KG + i * KD + d0, kg);
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
+      for (int cc = 0; cc < 4; ++cc) {
         vq[cc] = kScale * aq[r][cc] * ex2(gv[cc]);
         vg[cc] = aq[r][cc] * qg[cc] - akg[r][cc] * kg[cc];
         vk[cc] = akg[r][cc] * ex2(gl[cc] - gv[cc]);
         dglp[cc] = fmaf(akg[r][cc], kg[cc], dglp[cc]);
       }
-      st8(gdG + (i0 + r) * KD + d0, vg);
-      if (i0 + r < nv) {
-        st8(gdq + (i0 + r) * rs + d0, vq);
-        st8(gdk + (i0 + r) * rs + d0, vk);
+      st4(gdG + i * KD + d0, vg);
+      if (i < nv) {
+        st4(gdq + i * rs + d0, vq);
+        st4(gdk + i * rs + d0, vk);
       }
     }
-    st8(R3 + rb * KD + d0, dglp);   // [16][128] partials (R3 is free)
+    st4(R3 + rb * KD + d0, dglp);   // [16][128] partials (R3 is free)
   }
   // dAqk (lower triangle incl. the diagonal) into R4.
   {
-    float acc[4][4] = {};
+    float acc[2][4] = {};
 #pragma unroll 4
-    for (int vv = 0; vv < KD; ++vv) fma4x4(acc, lds4(R0 + vv * LQ + i0), lds4(R1 + vv * LQ + j0), 1.0f);
+    for (int vv = 0; vv < KD; ++vv) fma2x4(acc, lds2(R0 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) R4[(i0 + r) * LQ + j0 + cc] = (j0 + cc <= i0 + r) ? acc[r][cc] : 0.0f;
+      for (int cc = 0; cc < 4; ++cc) R4[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? acc[r][cc] : 0.0f;
   }
   __syncthreads();
   if (tid < KD) {
@@ -776,65 +796,64 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   // dE = A^T dW.  R0 = dW^T [K][C]; R1 = v^T then E^T ([*][C]);
   // R2 = dVnew^T; R3 = dW [C][K].
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc)
+  for (int cc = 0; cc < 4; ++cc)
     *reinterpret_cast<float4*>(R0 + (d0 + cc) * LQ + i0) = make_float4(-aw[0][cc], -aw[1][cc], -aw[2][cc], -aw[3][cc]);
-  __syncthreads();   // sGl read R3's partials
+  __syncthreads();   // sGl has read R3's partials
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float w[8] = {-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3], -aw[r][4], -aw[r][5], -aw[r][6], -aw[r][7]};
-    st8(R3 + (i0 + r) * KP + d0, w);
-  }
-  for (int t = tid; t < C * KD; t += NTB) {
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<float4*>(R3 + (i0 + r) * KP + d0) = make_float4(-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3]);
+  for (int t = tid; t < C * KD; t += NTG) {
     const int j = t / KD, vv = t - j * KD;
     R1[vv * LQ + j] = j < nv ? bf16f(p.v[((t0 + j) * p.HV + hv) * KD + vv]) : 0.0f;
   }
   __syncthreads();
-  float da[4][4] = {};
+  float da[2][4] = {};
 #pragma unroll 4
-  for (int vv = 0; vv < KD; ++vv) fma4x4(da, lds4(R2 + vv * LQ + i0), lds4(R1 + vv * LQ + j0), 1.0f);
+  for (int vv = 0; vv < KD; ++vv) fma2x4(da, lds2(R2 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
   __syncthreads();
-  load_rows(R1, LQ, rec + R_ET, C, 0, KD, 0, C, tid);
+  load_rows<NTG>(R1, LQ, rec + R_ET, C, 0, KD, 0, C, tid);
   __syncthreads();
 #pragma unroll 4
-  for (int d = 0; d < KD; ++d) fma4x4(da, lds4(R0 + d * LQ + i0), lds4(R1 + d * LQ + j0), 1.0f);
+  for (int d = 0; d < KD; ++d) fma2x4(da, lds2(R0 + d * LQ + s0r), lds4(R1 + d * LQ + s0c));
   __syncthreads();
   // R0 = A | T ([C][LQ] each); R1 = dA | X; R2 = dVnew [C][K].
   float* sA = R0;
   float* sT = R0 + C * LQ;
   float* sDA = R1;
   float* sX = R1 + C * LQ;
-  load_rows(sA, LQ, rec + R_A, C, 0, C, 0, C, tid);
-  load_rows(sT, LQ, rec + R_T, C, 0, C, 0, C, tid);
-  load_rows(R2, KP, rec + R_DVN, KD, 0, C, 0, KD, tid);
+  load_rows<NTG>(sA, LQ, rec + R_A, C, 0, C, 0, C, tid);
+  load_rows<NTG>(sT, LQ, rec + R_T, C, 0, C, 0, C, tid);
+  load_rows<NTG>(R2, KP, rec + R_DVN, KD, 0, C, 0, KD, tid);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) sDA[(i0 + r) * LQ + j0 + cc] = (j0 + cc <= i0 + r) ? da[r][cc] : 0.0f;
+    for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? da[r][cc] : 0.0f;
   __syncthreads();
   {
-    float av[4][8] = {}, ae[4][8] = {};
-#pragma unroll 2
+    float av[4][4] = {}, ae[4][4] = {};
+#pragma unroll 4
     for (int i = 0; i < C; ++i) {
-      const float4 a = lds4(sA + i * LQ + i0);   // A[i][j0 .. j0+3] over this tile's rows j
-      fma4x8(av, a, lds4(R2 + i * KP + d0), lds4(R2 + i * KP + d0 + 4));
-      fma4x8(ae, a, lds4(R3 + i * KP + d0), lds4(R3 + i * KP + d0 + 4));
+      const float4 a = lds4(sA + i * LQ + i0);   // A[i][j] for this tile's rows j
+      fma4x4(av, a, lds4(R2 + i * KP + d0), 1.0f);
+      fma4x4(ae, a, lds4(R3 + i * KP + d0), 1.0f);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = i0 + r;
-      if (j < nv) st8(p.dv + ((t0 + j) * p.HV + hv) * KD + d0, av[r]);
-      float gv[8], ev[8], vk[8], vg[8];
-      ld8(rec + R_G + j * KD + d0, gv);
-      ld8(rec + R_E + j * KD + d0, ev);
-      ld8(gdG + j * KD + d0, vg);
+      if (j < nv) st4(p.dv + ((t0 + j) * p.HV + hv) * KD + d0, av[r]);
+      float gv[4], ev[4], vg[4];
+      ld4(rec + R_G + j * KD + d0, gv);
+      ld4(rec + R_E + j * KD + d0, ev);
+      ld4(gdG + j * KD + d0, vg);
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) vg[cc] = fmaf(ae[r][cc], ev[cc], vg[cc]);
-      st8(gdG + j * KD + d0, vg);
+      for (int cc = 0; cc < 4; ++cc) vg[cc] = fmaf(ae[r][cc], ev[cc], vg[cc]);
+      st4(gdG + j * KD + d0, vg);
       if (j < nv) {
-        ld8(gdk + j * rs + d0, vk);
+        float vk[4];
+        ld4(gdk + j * rs + d0, vk);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) vk[cc] = fmaf(ae[r][cc], ex2(gv[cc]), vk[cc]);
-        st8(gdk + j * rs + d0, vk);
+        for (int cc = 0; cc < 4; ++cc) vk[cc] = fmaf(ae[r][cc], ex2(gv[cc]), vk[cc]);
+        st4(gdk + j * rs + d0, vk);
       }
     }
   }
@@ -847,57 +866,76 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
     sDB[j] += acc;
   }
   __syncthreads();
-  for (int t = tid; t < C * C; t += NTB) {
+  for (int t = tid; t < C * C; t += NTG) {
     const int i = t / C, j = t - i * C;
     sDA[i * LQ + j] *= sB[j];
   }
   __syncthreads();
-  for (int t = tid; t < C * C; t += NTB) {
-    const int i = t / C, mm = t - i * C;
-    float acc = 0.0f;
-    const int lim = min(i, mm);
-    for (int j = 0; j <= lim; ++j) acc = fmaf(sDA[i * LQ + j], sT[mm * LQ + j], acc);
-    sX[i * LQ + mm] = acc;
+  // dT^T and T^T (R2 and R3 are free: dv and dE are done) and P.
+  float* sDTT = R2;
+  float* sTT = R2 + C * LQ;
+  float* sP = R3;
+  for (int t = tid; t < C * C; t += NTG) {
+    const int i = t / C, j = t - i * C;
+    sDTT[j * LQ + i] = sDA[i * LQ + j];
+    sTT[j * LQ + i] = sT[i * LQ + j];
+  }
+  load_rows<NTG>(sP, LQ, rec + R_P, C, 0, C, 0, C, tid);
+  __syncthreads();
+  // X = dT T^T: X[i][m] = sum_j dT[i][j] T[m][j] (j <= min(i, m)).
+  {
+    float acc[2][4] = {};
+    const int lim = min(s0r + 1, s0c + 3);
+#pragma unroll 4
+    for (int j = 0; j <= lim; ++j) fma2x4(acc, lds2(sDTT + j * LQ + s0r), lds4(sTT + j * LQ + s0c));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      *reinterpret_cast<float4*>(sX + (s0r + r) * LQ + s0c) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
   }
   __syncthreads();
-  for (int t = tid; t < C * C; t += NTB) {
-    const int a = t / C, b = t - a * C;
-    float acc = 0.0f;
-    if (b < a)
-      for (int i = a; i < C; ++i) acc = fmaf(sT[i * LQ + a], sX[i * LQ + b], acc);
-    sDA[a * LQ + b] = -acc;
+  // dL = -tril_strict(T^T X): dL[a][b] = -sum_{i >= a} T[i][a] X[i][b] (into sDA).
+  {
+    float acc[2][4] = {};
+#pragma unroll 4
+    for (int i = s0r; i < C; ++i) fma2x4(acc, lds2(sT + i * LQ + s0r), lds4(sX + i * LQ + s0c));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc < s0r + r) ? -acc[r][cc] : 0.0f;
   }
   __syncthreads();
   if (tid < C) {
     const int i = tid;
     float acc = 0.0f;
-    for (int j = 0; j < i; ++j) acc = fmaf(sDA[i * LQ + j], rec[R_P + i * C + j], acc);
+    for (int j = 0; j < i; ++j) acc = fmaf(sDA[i * LQ + j], sP[i * LQ + j], acc);
     sDB[i] += acc;
   }
+  __syncthreads();   // R2 and R3 are reloaded below
   // ---- phase 3: gated sums.  R0 = G, R2 = k^, R3 = q^ ([C][K]); dL in
   // R1 (sDA), dAqk in R4.
-  load_rows(R0, KP, rec + R_G, KD, 0, C, 0, KD, tid);
-  load_rows(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
-  load_rows(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
+  load_rows<NTG>(R0, KP, rec + R_G, KD, 0, C, 0, KD, tid);
+  load_rows<NTG>(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
+  load_rows<NTG>(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
   __syncthreads();
   {
-    float gi[4][8];
+    float gi[4][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ld8(R0 + (i0 + r) * KP + d0, gi[r]);
+    for (int r = 0; r < 4; ++r) ld4(R0 + (i0 + r) * KP + d0, gi[r]);
     // Row forms: j <= i over this tile's rows i.
     {
-      float rk[4][8] = {}, rq[4][8] = {};
+      float rk[4][4] = {}, rq[4][4] = {};
+#pragma unroll 2
       for (int j = 0; j <= i0 + 3; ++j) {
-        float gj[8], kj[8];
-        ld8(R0 + j * KP + d0, gj);
-        ld8(R2 + j * KP + d0, kj);
+        float gj[4], kj[4];
+        ld4(R0 + j * KP + d0, gj);
+        ld4(R2 + j * KP + d0, kj);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
           const float mk = j <= i ? sB[i] * sDA[i * LQ + j] : 0.0f;
           const float mq = j <= i ? kScale * R4[i * LQ + j] : 0.0f;
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
+          for (int cc = 0; cc < 4; ++cc) {
             const float e = j <= i ? ex2(gi[r][cc] - gj[cc]) * kj[cc] : 0.0f;
             rk[r][cc] = fmaf(mk, e, rk[r][cc]);
             rq[r][cc] = fmaf(mq, e, rq[r][cc]);
@@ -907,35 +945,36 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        float ki[8], qi[8], vg[8];
-        ld8(R2 + i * KP + d0, ki);
-        ld8(R3 + i * KP + d0, qi);
-        ld8(gdG + i * KD + d0, vg);
+        float ki[4], qi[4], vg[4];
+        ld4(R2 + i * KP + d0, ki);
+        ld4(R3 + i * KP + d0, qi);
+        ld4(gdG + i * KD + d0, vg);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) vg[cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
-        st8(gdG + i * KD + d0, vg);
+        for (int cc = 0; cc < 4; ++cc) vg[cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
+        st4(gdG + i * KD + d0, vg);
         if (i < nv) {
-          float vq[8], vk[8];
-          ld8(gdq + i * rs + d0, vq);
-          ld8(gdk + i * rs + d0, vk);
+          float vq[4], vk[4];
+          ld4(gdq + i * rs + d0, vq);
+          ld4(gdk + i * rs + d0, vk);
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
+          for (int cc = 0; cc < 4; ++cc) {
             vq[cc] += rq[r][cc];
             vk[cc] += rk[r][cc];
           }
-          st8(gdq + i * rs + d0, vq);
-          st8(gdk + i * rs + d0, vk);
+          st4(gdq + i * rs + d0, vq);
+          st4(gdk + i * rs + d0, vk);
         }
       }
     }
     // Column forms: i >= j over this tile's rows j (as the column index).
     {
-      float ck[4][8] = {}, cq[4][8] = {};
+      float ck[4][4] = {}, cq[4][4] = {};
+#pragma unroll 2
       for (int i = i0; i < C; ++i) {
-        float gr[8], kr[8], qr[8];
-        ld8(R0 + i * KP + d0, gr);
-        ld8(R2 + i * KP + d0, kr);
-        ld8(R3 + i * KP + d0, qr);
+        float gr[4], kr[4], qr[4];
+        ld4(R0 + i * KP + d0, gr);
+        ld4(R2 + i * KP + d0, kr);
+        ld4(R3 + i * KP + d0, qr);
         const float4 dl4 = lds4(sDA + i * LQ + i0);
         const float4 aq4 = lds4(R4 + i * LQ + i0);
         const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
@@ -947,7 +986,7 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
           const float mk = i >= j ? bi * dl[r] : 0.0f;
           const float mq = i >= j ? kScale * aqv[r] : 0.0f;
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
+          for (int cc = 0; cc < 4; ++cc) {
             const float e = i >= j ? ex2(gr[cc] - gi[r][cc]) : 0.0f;
             ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
             cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
@@ -957,21 +996,21 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        float ki[8], vg[8];
-        ld8(R2 + i * KP + d0, ki);
-        ld8(gdG + i * KD + d0, vg);
+        float ki[4], vg[4];
+        ld4(R2 + i * KP + d0, ki);
+        ld4(gdG + i * KD + d0, vg);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) vg[cc] -= ki[cc] * (ck[r][cc] + cq[r][cc]);
+        for (int cc = 0; cc < 4; ++cc) vg[cc] -= ki[cc] * (ck[r][cc] + cq[r][cc]);
         if (i == C - 1)
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) vg[cc] += sGl[d0 + cc];
-        st8(gdG + i * KD + d0, vg);
+          for (int cc = 0; cc < 4; ++cc) vg[cc] += sGl[d0 + cc];
+        st4(gdG + i * KD + d0, vg);
         if (i < nv) {
-          float vk[8];
-          ld8(gdk + i * rs + d0, vk);
+          float vk[4];
+          ld4(gdk + i * rs + d0, vk);
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) vk[cc] += ck[r][cc] + cq[r][cc];
-          st8(gdk + i * rs + d0, vk);
+          for (int cc = 0; cc < 4; ++cc) vk[cc] += ck[r][cc] + cq[r][cc];
+          st4(gdk + i * rs + d0, vk);
         }
       }
     }
@@ -982,9 +1021,9 @@ __global__ __launch_bounds__(NTB) void bwd_grad_kernel(BParams p) {
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float vg[8];
-    ld8(gdG + (i0 + r) * KD + d0, vg);
-    st8(R0 + (i0 + r) * KP + d0, vg);
+    float vg[4];
+    ld4(gdG + (i0 + r) * KD + d0, vg);
+    st4(R0 + (i0 + r) * KP + d0, vg);
   }
   __syncthreads();
   if (tid < KD) {
@@ -1135,7 +1174,7 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
   st = kda::launch_status();
   if (st != KDA_OK) return st;
   if (tokens == 0) return KDA_OK;
-  hipLaunchKernelGGL(bwd_grad_kernel, chunks, dim3(NTB), GRAD_LDS, s, p);
+  hipLaunchKernelGGL(bwd_grad_kernel, chunks, dim3(NTG), GRAD_LDS, s, p);
   st = kda::launch_status();
   if (st != KDA_OK) return st;
   const int64_t rows = 2 * tokens * H;
