@@ -221,20 +221,42 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+__device__ __forceinline__ float2 lds2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+
+// acc[2][4] += a[2] (x) b[4].
+__device__ __forceinline__ void fma2x4(float (*acc)[4], const float2 a, const float4 b, float sign = 1.0f) {
+  const float av[2] = {sign * a.x, sign * a.y};
+  const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+}
+
+__device__ __forceinline__ void ld4(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
+__device__ __forceinline__ void st4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // --------------------------------------------------------------- prep
-// Thread tiles as in the gradient kernel: [C][128] results in 4x8 tiles
-// (rows 4 (t / 16), columns 8 (t % 16)); P and Aqk in 4x4 blocks of
-// (i, j) pairs, one lower-triangle block per thread for the first 136
-// threads (the other 120 threads write the zero blocks above it).
+// 512 threads.  [C][128] results in 4x4 tiles (rows 4 (t / 32), columns
+// 4 (t % 32)); P and Aqk in 4x4 blocks of (i, j) pairs, each block taken by
+// two adjacent lanes that split the channels (lanes 0..271 cover the 136
+// lower-triangle blocks, lanes 272..511 write the 120 zero blocks above).
+constexpr int NTP = 512;
 constexpr int PREP_LDS = (3 * C * KP + 2 * C * LQ + C) * 4;
 constexpr int kTriBlocks = (C / 4) * (C / 4 + 1) / 2;   // 136
-static_assert(NTB - kTriBlocks == (C / 4) * (C / 4 - 1) / 2, "one thread per 4x4 block of the square");
+static_assert(NTP / 2 - kTriBlocks == (C / 4) * (C / 4 - 1) / 2, "one lane pair per 4x4 block of the square");
 
-__global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
+__global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
   float* sQ = smem;                 // q^, later E
   float* sK = sQ + C * KP;          // k^, later v
-  float* sG = sK + C * KP;          // G
+  float* sG = sK + C * KP;          // G (log2 units)
   float* sP = sG + C * KP;          // P [C][LQ]
   float* sAT = sP + C * LQ;         // A^T [C][LQ]
   float* sB = sAT + C * LQ;         // beta
@@ -252,13 +274,12 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
   const int hq = hv / (p.HV / p.H);
   float* rec = record(p, hv, slot);
   const int tid = threadIdx.x;
-  const int rb = tid >> 4, cb = tid & 15;
-  const int i0 = 4 * rb, d0 = 8 * cb;
+  const int i0 = 4 * (tid >> 5), d0 = 4 * (tid & 31);
 
-  // q^ and k^: 16 rows per pass (16 lanes per row, 8 elements per lane);
+  // q^ and k^: 32 rows per pass (16 lanes per row, 8 elements per lane);
   // rows 0..63 are q, 64..127 are k; rows past the chunk's end are zero.
-  for (int pass = 0; pass < 2 * C / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
+  for (int pass = 0; pass < 2 * C / 32; ++pass) {
+    const int r = pass * 32 + (tid >> 4);
     const int l16 = tid & 15;
     const bool isk = r >= C;
     const int tr = r & (C - 1);
@@ -292,18 +313,19 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
 
   // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.
   {
+    const int blk = tid >> 1, half = tid & 1;
     int bi, bj;
-    const bool lower = tid < kTriBlocks;
+    const bool lower = blk < kTriBlocks;
     if (lower) {
-      tri_pair(tid, bi, bj);
+      tri_pair(blk, bi, bj);
     } else {   // the strictly-upper blocks, numbered the same way transposed
-      tri_pair(tid - kTriBlocks, bj, bi);
+      tri_pair(blk - kTriBlocks, bj, bi);
       ++bj;    // tri_pair over a triangle one smaller, shifted past the diagonal
     }
     const int a0 = 4 * bi, b0 = 4 * bj;
     float pk[4][4] = {}, pq[4][4] = {};
     if (lower) {
-      for (int d = 0; d < KD; d += 4) {
+      for (int d = (KD / 2) * half; d < (KD / 2) * (half + 1); d += 4) {
         float4 gi[4], gj[4], ki[4], kj[4], qi[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -329,75 +351,86 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = a0 + r;
-      float pv[4], av[4];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = b0 + q;
-        pv[q] = j < i ? pk[r][q] : 0.0f;
-        av[q] = j <= i ? kScale * pq[r][q] : 0.0f;
+        pk[r][q] += __shfl_xor(pk[r][q], 1, 64);
+        pq[r][q] += __shfl_xor(pq[r][q], 1, 64);
       }
-      const float4 p4 = make_float4(pv[0], pv[1], pv[2], pv[3]);
-      *reinterpret_cast<float4*>(sP + i * LQ + b0) = p4;
-      *reinterpret_cast<float4*>(rec + R_P + i * C + b0) = p4;
-      *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
+    if (half == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = a0 + r;
+        float pv[4], av[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = b0 + q;
+          pv[q] = j < i ? pk[r][q] : 0.0f;
+          av[q] = j <= i ? kScale * pq[r][q] : 0.0f;
+        }
+        const float4 p4 = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *reinterpret_cast<float4*>(sP + i * LQ + b0) = p4;
+        *reinterpret_cast<float4*>(rec + R_P + i * C + b0) = p4;
+        *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
+      }
     }
   }
   __syncthreads();
 
   // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
-  // 4j .. 4j+3 own column j, lane part holding T[16 part + m][j] (m < 16)
-  // in registers; row i's sum over the column is split by part and
-  // completed across the four lanes.  (P is strictly lower and T starts at
-  // zero, so the sums need no bounds.)
+  // 8j .. 8j+7 own column j, lane part holding T[8 part + m][j] (m < 8) in
+  // registers; row i's sum over the column is split by part and completed
+  // across the eight lanes.  (P is strictly lower and T starts at zero, so
+  // the sums need no bounds.)
   {
-    const int j = tid >> 2, part = tid & 3;
-    float tc[16];
+    const int j = tid >> 3, part = tid & 7;
+    float tc[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) tc[m] = 0.0f;
+    for (int m = 0; m < 8; ++m) tc[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 pr = lds4(sP + i * LQ + 16 * part + 4 * q);
-        acc = fmaf(pr.x, tc[4 * q], acc);
-        acc = fmaf(pr.y, tc[4 * q + 1], acc);
-        acc = fmaf(pr.z, tc[4 * q + 2], acc);
-        acc = fmaf(pr.w, tc[4 * q + 3], acc);
-      }
+      const float4 pa = lds4(sP + i * LQ + 8 * part);
+      const float4 pb = lds4(sP + i * LQ + 8 * part + 4);
+      float acc = pa.x * tc[0];
+      acc = fmaf(pa.y, tc[1], acc);
+      acc = fmaf(pa.z, tc[2], acc);
+      acc = fmaf(pa.w, tc[3], acc);
+      acc = fmaf(pb.x, tc[4], acc);
+      acc = fmaf(pb.y, tc[5], acc);
+      acc = fmaf(pb.z, tc[6], acc);
+      acc = fmaf(pb.w, tc[7], acc);
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
       const float tv = i == j ? 1.0f : -sB[i] * acc;
-      if (part == i / 16) tc[i % 16] = tv;
+      if (part == i / 8) tc[i % 8] = tv;
     }
     // T and A = T diag(beta) to the record; A^T to LDS.
     const float bj = sB[j];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int i = 16 * part + m;
+    for (int m = 0; m < 8; ++m) {
+      const int i = 8 * part + m;
       rec[R_T + i * C + j] = tc[m];
       rec[R_A + i * C + j] = tc[m] * bj;
       sAT[j * LQ + i] = tc[m] * bj;
     }
   }
   if (tid < KD) rec[R_GAM + tid] = ex2(sG[(C - 1) * KP + tid]);
-  // Qg, Kg, E over this thread's 4x8 tile (E replaces q^ in LDS; the
+  // Qg, Kg, E over this thread's 4x4 tile (E replaces q^ in LDS; the
   // transposed copies are written four rows at a time).
   {
-    float gl[8];
-    ld8(sG + (C - 1) * KP + d0, gl);
-    float kgt[8][4], et[8][4];
+    float gl[4];
+    ld4(sG + (C - 1) * KP + d0, gl);
+    float kgt[4][4], et[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r;
-      float gv[8], kv[8], qv[8], qg[8], kg[8], ev[8];
-      ld8(sG + i * KP + d0, gv);
-      ld8(sK + i * KP + d0, kv);
-      ld8(sQ + i * KP + d0, qv);
+      float gv[4], kv[4], qv[4], qg[4], kg[4], ev[4];
+      ld4(sG + i * KP + d0, gv);
+      ld4(sK + i * KP + d0, kv);
+      ld4(sQ + i * KP + d0, qv);
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
+      for (int cc = 0; cc < 4; ++cc) {
         const float eg = ex2(gv[cc]);
         qg[cc] = kScale * qv[cc] * eg;
         kg[cc] = kv[cc] * ex2(gl[cc] - gv[cc]);
@@ -405,56 +438,58 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BParams p) {
         kgt[cc][r] = kg[cc];
         et[cc][r] = ev[cc];
       }
-      st8(rec + R_QG + i * KD + d0, qg);
-      st8(rec + R_KG + i * KD + d0, kg);
-      st8(rec + R_E + i * KD + d0, ev);
-      st8(sQ + i * KP + d0, ev);
+      st4(rec + R_QG + i * KD + d0, qg);
+      st4(rec + R_KG + i * KD + d0, kg);
+      st4(rec + R_E + i * KD + d0, ev);
+      st4(sQ + i * KP + d0, ev);
     }
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      *reinterpret_cast<float4*>(rec + R_KGT + (d0 + cc) * C + i0) = make_float4(kgt[cc][0], kgt[cc][1], kgt[cc][2], kgt[cc][3]);
-      *reinterpret_cast<float4*>(rec + R_ET + (d0 + cc) * C + i0) = make_float4(et[cc][0], et[cc][1], et[cc][2], et[cc][3]);
+    for (int cc = 0; cc < 4; ++cc) {
+      st4(rec + R_KGT + (d0 + cc) * C + i0, kgt[cc]);
+      st4(rec + R_ET + (d0 + cc) * C + i0, et[cc]);
     }
   }
   __syncthreads();
   // v (zero past the chunk's end) replaces k^ in LDS.
-  for (int t = tid; t < C * KD; t += NTB) {
+  for (int t = tid; t < C * KD; t += NTP) {
     const int i = t / KD, d = t - i * KD;
     sK[i * KP + d] = i < nv ? bf16f(p.v[((t0 + i) * p.HV + hv) * KD + d]) : 0.0f;
   }
   __syncthreads();
   // W = A E and U = A v (A lower triangular: j <= i0 + 3 suffices).
   {
-    float w[4][8] = {}, u[4][8] = {};
+    float w[4][4] = {}, u[4][4] = {};
     for (int j = 0; j <= i0 + 3; ++j) {
       const float4 a = lds4(sAT + j * LQ + i0);
-      fma4x8(w, a, lds4(sQ + j * KP + d0), lds4(sQ + j * KP + d0 + 4));
-      fma4x8(u, a, lds4(sK + j * KP + d0), lds4(sK + j * KP + d0 + 4));
+      fma4x4(w, a, lds4(sQ + j * KP + d0), 1.0f);
+      fma4x4(u, a, lds4(sK + j * KP + d0), 1.0f);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      st8(rec + R_W + (i0 + r) * KD + d0, w[r]);
-      st8(rec + R_U + (i0 + r) * KD + d0, u[r]);
+      st4(rec + R_W + (i0 + r) * KD + d0, w[r]);
+      st4(rec + R_U + (i0 + r) * KD + d0, u[r]);
     }
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
+    for (int cc = 0; cc < 4; ++cc)
       *reinterpret_cast<float4*>(rec + R_WT + (d0 + cc) * C + i0) = make_float4(w[0][cc], w[1][cc], w[2][cc], w[3][cc]);
   }
 }
 
 // --------------------------------------------------------------- carries
 // Workgroup (column group cg, value head hv, sequence n) owns state columns
-// 64 cg .. 64 cg + 63.  Every product is register-blocked: thread t
-// computes a 4x4 or 8x4 tile (rows from t / 16, columns 4 (t % 16) ..+3)
-// from 16-byte LDS reads of operands stored contraction-index-major, so
-// one pair of reads feeds 16 or 32 fused multiply-adds.
+// 64 cg .. 64 cg + 63, with 512 threads (two waves per SIMD).  Every
+// product is register-blocked: thread t computes a 2x4 or 4x4 tile (rows
+// from t / 16, columns 4 (t % 16) ..+3) from 8- and 16-byte LDS reads of
+// operands stored contraction-index-major, so one pair of reads feeds 8 or
+// 16 fused multiply-adds.
 constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
+constexpr int NTC = 512;          // threads per carry workgroup
 constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ) * 4;
 constexpr int REV_LDS = (2 * KD * SQ + 3 * C * SQ + KD) * 4;
 static_assert(FWD_LDS <= 160 * 1024 && REV_LDS <= 160 * 1024, "LDS budget");
 static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where Kg^T was");
 
-__global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
+__global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
   float* sS = smem;                 // [K][64] state slice
   float* sWT = sS + KD * SQ;        // [K][C] W^T
@@ -472,7 +507,7 @@ __global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
   const int64_t sb = slot_base(p, n);
   const int64_t sh = (int64_t(n) * p.HV + hv) * KD;
 
-  for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+  for (int u = tid; u < KD * NCOL / 4; u += NTC) {
     const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
     *reinterpret_cast<float4*>(sS + d * SQ + 4 * c4) =
         p.s0 ? *reinterpret_cast<const float4*>(p.s0 + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -482,62 +517,57 @@ __global__ __launch_bounds__(NTB) void bwd_carry_fwd_kernel(BParams p) {
   for (int c = 0; c < nch; ++c) {
     float* rec = record(p, hv, sb + c);
     // Entering state, transposed: ST[v][d] for this group's columns v.
-    for (int t = tid; t < NCOL * KD; t += NTB) {
+    for (int t = tid; t < NCOL * KD; t += NTC) {
       const int vv = t / KD, d = t - vv * KD;
       rec[R_ST + (c0 + vv) * KD + d] = sS[d * SQ + vv];
     }
-    load_rows(sWT, SQ, rec + R_WT, C, 0, KD, 0, C, tid);
-    load_rows(sKg, KP, rec + R_KG, KD, 0, C, 0, KD, tid);
-    load_rows(sV, SQ, rec + R_U, KD, 0, C, c0, NCOL, tid);
+    load_rows<NTC>(sWT, SQ, rec + R_WT, C, 0, KD, 0, C, tid);
+    load_rows<NTC>(sKg, KP, rec + R_KG, KD, 0, C, 0, KD, tid);
+    load_rows<NTC>(sV, SQ, rec + R_U, KD, 0, C, c0, NCOL, tid);
     __syncthreads();
-    // Vnew = U - W S: rows 4 tr .. +3.
+    // Vnew = U - W S: rows 2 tr .. +1.
     {
-      const int i0 = 4 * tr;
-      float acc[4][4];
+      const int i0 = 2 * tr;
+      float acc[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 2; ++r) {
         const float4 u = lds4(sV + (i0 + r) * SQ + j0);
         acc[r][0] = u.x; acc[r][1] = u.y; acc[r][2] = u.z; acc[r][3] = u.w;
       }
 #pragma unroll 4
-      for (int d = 0; d < KD; ++d) fma4x4(acc, lds4(sWT + d * SQ + i0), lds4(sS + d * SQ + j0), -1.0f);
+      for (int d = 0; d < KD; ++d) fma2x4(acc, lds2(sWT + d * SQ + i0), lds4(sS + d * SQ + j0), -1.0f);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 2; ++r) {
         const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
         *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
         *reinterpret_cast<float4*>(rec + R_VN + (i0 + r) * KD + c0 + j0) = o4;
       }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
-        *reinterpret_cast<float4*>(rec + R_VNT + (c0 + j0 + cc) * C + i0) =
-            make_float4(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
+        *reinterpret_cast<float2*>(rec + R_VNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
     }
     __syncthreads();
-    // S = gamma S + Kg^T Vnew: rows 8 tr .. +7.
+    // S = gamma S + Kg^T Vnew: rows 4 tr .. +3.
     {
-      const int d0 = 8 * tr;
-      float acc[8][4];
+      const int d0 = 4 * tr;
+      float acc[4][4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const float gm = rec[R_GAM + d0 + r];
         const float4 s4 = lds4(sS + (d0 + r) * SQ + j0);
         acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
       }
 #pragma unroll 4
-      for (int i = 0; i < C; ++i) {
-        const float4 b = lds4(sV + i * SQ + j0);
-        fma4x4(acc, lds4(sKg + i * KP + d0), b, 1.0f);
-        fma4x4(acc + 4, lds4(sKg + i * KP + d0 + 4), b, 1.0f);
-      }
+      for (int i = 0; i < C; ++i) fma4x4(acc, lds4(sKg + i * KP + d0), lds4(sV + i * SQ + j0), 1.0f);
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int r = 0; r < 4; ++r)
         *reinterpret_cast<float4*>(sS + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
     }
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
+__global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
   float* sD = smem;                 // [K][64] dS' slice
   float* sKgT = sD + KD * SQ;       // [K][C] Kg^T; later half tiles of Qg and W
@@ -559,7 +589,7 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
   const int64_t sb = slot_base(p, n);
   const int64_t sh = (int64_t(n) * p.HV + hv) * KD;
 
-  for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+  for (int u = tid; u < KD * NCOL / 4; u += NTC) {
     const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
     *reinterpret_cast<float4*>(sD + d * SQ + 4 * c4) =
         p.dht ? *reinterpret_cast<const float4*>(p.dht + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -570,69 +600,64 @@ __global__ __launch_bounds__(NTB) void bwd_carry_rev_kernel(BParams p) {
     float* rec = record(p, hv, sb + c);
     const int nv = min(C, len - c * C);
     const int64_t t0 = tok0 + int64_t(c) * C;
-    for (int t = tid; t < NCOL * KD; t += NTB) {
+    for (int t = tid; t < NCOL * KD; t += NTC) {
       const int vv = t / KD, d = t - vv * KD;
       rec[R_DST + (c0 + vv) * KD + d] = sD[d * SQ + vv];
     }
-    load_rows(sKgT, SQ, rec + R_KGT, C, 0, KD, 0, C, tid);
-    load_rows(sAqk, SQ, rec + R_AQK, C, 0, C, 0, C, tid);
-    for (int t = tid; t < C * NCOL; t += NTB) {
+    load_rows<NTC>(sKgT, SQ, rec + R_KGT, C, 0, KD, 0, C, tid);
+    load_rows<NTC>(sAqk, SQ, rec + R_AQK, C, 0, C, 0, C, tid);
+    for (int t = tid; t < C * NCOL; t += NTC) {
       const int i = t / NCOL, jj = t - i * NCOL;
       sO[i * SQ + jj] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + c0 + jj]) : 0.0f;
     }
     if (tid < KD) sGam[tid] = rec[R_GAM + tid];
     __syncthreads();
-    // dVnew = Aqk^T dO + Kg dS': rows 4 tr .. +3 (Aqk[m][i] = 0 for m < i).
+    // dVnew = Aqk^T dO + Kg dS': rows 2 tr .. +1 (Aqk[m][i] = 0 for m < i).
     {
-      const int i0 = 4 * tr;
-      float acc[4][4] = {};
+      const int i0 = 2 * tr;
+      float acc[2][4] = {};
 #pragma unroll 4
-      for (int m = i0; m < C; ++m) fma4x4(acc, lds4(sAqk + m * SQ + i0), lds4(sO + m * SQ + j0), 1.0f);
+      for (int m = i0; m < C; ++m) fma2x4(acc, lds2(sAqk + m * SQ + i0), lds4(sO + m * SQ + j0));
 #pragma unroll 4
-      for (int d = 0; d < KD; ++d) fma4x4(acc, lds4(sKgT + d * SQ + i0), lds4(sD + d * SQ + j0), 1.0f);
+      for (int d = 0; d < KD; ++d) fma2x4(acc, lds2(sKgT + d * SQ + i0), lds4(sD + d * SQ + j0));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 2; ++r) {
         const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
         *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
         *reinterpret_cast<float4*>(rec + R_DVN + (i0 + r) * KD + c0 + j0) = o4;
       }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
-        *reinterpret_cast<float4*>(rec + R_DVNT + (c0 + j0 + cc) * C + i0) =
-            make_float4(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
+        *reinterpret_cast<float2*>(rec + R_DVNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
     }
-    // dS = gamma dS' + Qg^T dO - W^T dVnew: rows 8 tr .. +7, with Qg and W
+    // dS = gamma dS' + Qg^T dO - W^T dVnew: rows 4 tr .. +3, with Qg and W
     // staged 32 rows at a time where Kg^T was.
-    const int d0 = 8 * tr;
-    float acc[8][4];
+    const int d0 = 4 * tr;
+    float acc[4][4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const float gm = sGam[d0 + r];
       const float4 s4 = lds4(sD + (d0 + r) * SQ + j0);
       acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
     }
     for (int h = 0; h < 2; ++h) {
       __syncthreads();   // Kg^T (or the previous half) is no longer read; dVnew is complete
-      load_rows(sQh, KP, rec + R_QG, KD, h * (C / 2), C / 2, 0, KD, tid);
-      load_rows(sWh, KP, rec + R_W, KD, h * (C / 2), C / 2, 0, KD, tid);
+      load_rows<NTC>(sQh, KP, rec + R_QG, KD, h * (C / 2), C / 2, 0, KD, tid);
+      load_rows<NTC>(sWh, KP, rec + R_W, KD, h * (C / 2), C / 2, 0, KD, tid);
       __syncthreads();
-#pragma unroll 2
+#pragma unroll 4
       for (int i = 0; i < C / 2; ++i) {
-        const float4 bo = lds4(sO + (h * (C / 2) + i) * SQ + j0);
-        const float4 bv = lds4(sV + (h * (C / 2) + i) * SQ + j0);
-        fma4x4(acc, lds4(sQh + i * KP + d0), bo, 1.0f);
-        fma4x4(acc + 4, lds4(sQh + i * KP + d0 + 4), bo, 1.0f);
-        fma4x4(acc, lds4(sWh + i * KP + d0), bv, -1.0f);
-        fma4x4(acc + 4, lds4(sWh + i * KP + d0 + 4), bv, -1.0f);
+        fma4x4(acc, lds4(sQh + i * KP + d0), lds4(sO + (h * (C / 2) + i) * SQ + j0), 1.0f);
+        fma4x4(acc, lds4(sWh + i * KP + d0), lds4(sV + (h * (C / 2) + i) * SQ + j0), -1.0f);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < 4; ++r)
       *reinterpret_cast<float4*>(sD + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
     __syncthreads();
   }
   if (p.dh0)
-    for (int u = tid; u < KD * NCOL / 4; u += NTB) {
+    for (int u = tid; u < KD * NCOL / 4; u += NTC) {
       const int d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
       *reinterpret_cast<float4*>(p.dh0 + (sh + d) * KD + c0 + 4 * c4) = lds4(sD + d * SQ + 4 * c4);
     }
@@ -658,27 +683,6 @@ constexpr int GRAD_LDS = (SM_OFF + 2 * C + KD) * 4;
 static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ && C * LQ <= C * KP, "regions hold their alternates");
 static_assert((C / 4) * KD <= C * KP, "dG_last partials fit in R3");
-
-__device__ __forceinline__ float2 lds2(const float* p) { return *reinterpret_cast<const float2*>(p); }
-
-// acc[2][4] += a[2] (x) b[4].
-__device__ __forceinline__ void fma2x4(float (*acc)[4], const float2 a, const float4 b) {
-  const float av[2] = {a.x, a.y};
-  const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-}
-
-__device__ __forceinline__ void ld4(const float* p, float* v) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-}
-
-__device__ __forceinline__ void st4(float* p, const float* v) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
 
 __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -1164,13 +1168,13 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
   hipStream_t s = kda::as_stream(stream);
   const dim3 chunks = dim3(unsigned(nslots), unsigned(HV));
   const dim3 carries = dim3(KD / NCOL, unsigned(HV), unsigned(nseq));
-  hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(NTB), PREP_LDS, s, p);
+  hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(NTP), PREP_LDS, s, p);
   int st = kda::launch_status();
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(bwd_carry_fwd_kernel, carries, dim3(NTB), FWD_LDS, s, p);
+  hipLaunchKernelGGL(bwd_carry_fwd_kernel, carries, dim3(NTC), FWD_LDS, s, p);
   st = kda::launch_status();
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(bwd_carry_rev_kernel, carries, dim3(NTB), REV_LDS, s, p);
+  hipLaunchKernelGGL(bwd_carry_rev_kernel, carries, dim3(NTC), REV_LDS, s, p);
   st = kda::launch_status();
   if (st != KDA_OK) return st;
   if (tokens == 0) return KDA_OK;
