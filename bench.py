@@ -248,6 +248,45 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
     print(json.dumps(rec), flush=True)
 
 
+def measure_backward(torch, synth, kda, pin, inputs, stream, steps, warmup):
+    """Mean call time of kda_chunk_backward on the prefill workload (random
+    upstream gradients), with its float32 ALU roofline: gradients of
+    sum(o * d_out) + sum(final_state * d_final_state)."""
+    print("[bench] backward", file=sys.stderr, flush=True)
+    q, k, v, g, beta, s0 = inputs
+    B, T, H, _ = pin.q.shape
+    HV = pin.v.shape[2]
+    dev = q.device
+    d_out, d_final = synth.upstream_grads(pin)
+    d_out, d_final = d_out.to(dev), d_final.to(dev)
+    bws = torch.empty(kda.backward_workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
+    evs = []
+    for i in range(warmup + steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kda.chunk_backward(q, k, v, g, beta, s0, d_out, d_final, workspace=bws)
+        e1.record(stream)
+        if i >= warmup:
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    bw_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    n_ch = B * ((T + C - 1) // C) * HV
+    bw_flops = backward_alg_flops(n_ch)
+    bw_bytes = backward_alg_bytes(B * T, H, HV, B, s0 is not None, True)
+    del bws, d_out, d_final
+    return {
+        "workload": f"B={B} H=HV={HV} T={T}, float32",
+        "call_us_mean": bw_us,
+        "calls": steps,
+        "tokens_per_s": B * T / (bw_us * 1e-6),
+        "alg_flops": bw_flops,
+        "alg_bytes": bw_bytes,
+        "roofline": {"bound": "alu", "achieved": bw_flops / (bw_us * 1e-6) / 1e12, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": bw_flops / (bw_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS},
+        "hbm_frac": bw_bytes / (bw_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +297,8 @@ def main():
     ap.add_argument("--decode-B", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=8, help="value heads in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the backward of the prefill workload (for profiling)")
     ap.add_argument("--only-steps", action="store_true",
                     help="time only the steps (prefill + decode); skip the handoff, packed decode and "
                          "partition measurements (for profiler runs that average per kernel name)")
@@ -299,6 +340,12 @@ def main():
     o = torch.empty(B, T, HV, V, dtype=torch.bfloat16, device=dev)
     sf = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev)
     ws = torch.empty(kda.workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
+    if args.only_backward:
+        torch.cuda.synchronize()
+        bw = measure_backward(torch, synth, kda, pin, (q, k, v, g, beta, s0), torch.cuda.current_stream(),
+                              args.steps, args.warmup)
+        print(json.dumps({"backward": bw}), flush=True)
+        return
 
     din = synth.decode_config(args.decode_B)
     dq, dk, dv, dg, db = (t.to(dev) for t in (din.q, din.k, din.v, din.g, din.beta))
@@ -523,28 +570,8 @@ def main():
     }
     del c4a, o4, sf4, ws4
     result["prefill_partitions"] = partitions
-    # Backward of the bench workload: gradients of sum(o * d_out) +
-    # sum(final_state * d_final_state) for random upstream gradients.
-    print("[bench] backward", file=sys.stderr, flush=True)
-    d_out, d_final = synth.upstream_grads(pin)
-    d_out, d_final = d_out.to(dev), d_final.to(dev)
-    bws = torch.empty(kda.backward_workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
-    bw_us = time_calls(lambda: kda.chunk_backward(q, k, v, g, beta, s0, d_out, d_final, workspace=bws),
-                       max(3, args.steps // 2))
-    n_ch = B * ((T + C - 1) // C) * HV
-    bw_flops = backward_alg_flops(n_ch)
-    bw_bytes = backward_alg_bytes(B * T, H, HV, B, True, True)
-    result["backward"] = {
-        "workload": f"B={B} H=HV={HV} T={T}, float32",
-        "call_us_mean": bw_us,
-        "tokens_per_s": B * T / (bw_us * 1e-6),
-        "alg_flops": bw_flops,
-        "alg_bytes": bw_bytes,
-        "roofline": {"bound": "alu", "achieved": bw_flops / (bw_us * 1e-6) / 1e12, "peak": FP32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": bw_flops / (bw_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS},
-        "hbm_frac": bw_bytes / (bw_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-    }
-    del bws, d_out, d_final
+    result["backward"] = measure_backward(torch, synth, kda, pin, (q, k, v, g, beta, s0), stream,
+                                          max(3, args.steps // 2), args.warmup)
     if args.cpu_heads > 0:
         print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)
