@@ -13,6 +13,10 @@
 // the normalised q and k passes gradients through unchanged: dq and dk are
 // the gradients of x / sqrt(sum(x*x) + 1e-6).
 //
+// Workgroup barriers order LDS only (kda::lds_barrier): no data crosses
+// threads through global memory inside a kernel, and the plain barrier
+// would also wait for every outstanding global load and store.
+//
 // Everything runs in float32.  Five kernels, split where the method splits
 // (chunk-local work is chunk-parallel, the carries are sequential per
 // (sequence, value head) and column-parallel, since column v of the state
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
     }
   }
   if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
-  __syncthreads();
+  kda::lds_barrier();
 
   // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.
   {
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
       }
     }
   }
-  __syncthreads();
+  kda::lds_barrier();
 
   // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
   // 8j .. 8j+7 own column j, lane part holding T[8 part + m][j] (m < 8) in
@@ -449,13 +453,13 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
       st4(rec + R_ET + (d0 + cc) * C + i0, et[cc]);
     }
   }
-  __syncthreads();
+  kda::lds_barrier();
   // v (zero past the chunk's end) replaces k^ in LDS.
   for (int t = tid; t < C * KD; t += NTP) {
     const int i = t / KD, d = t - i * KD;
     sK[i * KP + d] = i < nv ? bf16f(p.v[((t0 + i) * p.HV + hv) * KD + d]) : 0.0f;
   }
-  __syncthreads();
+  kda::lds_barrier();
   // W = A E and U = A v (A lower triangular: j <= i0 + 3 suffices).
   {
     float w[4][4] = {}, u[4][4] = {};
@@ -484,10 +488,19 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
 // 16 fused multiply-adds.
 constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
 constexpr int NTC = 512;          // threads per carry workgroup
-constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ) * 4;
+constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ + KD) * 4;
 constexpr int REV_LDS = (2 * KD * SQ + 3 * C * SQ + KD) * 4;
 static_assert(FWD_LDS <= 160 * 1024 && REV_LDS <= 160 * 1024, "LDS budget");
 static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where Kg^T was");
+
+// Both carries load the operands of the next chunk step into registers
+// while the current step computes, so that their latency overlaps the
+// products.  Thread t carries the 16-byte pieces t, t + 512, ... of each
+// matrix in row-major order (as native vectors, which stay in registers).
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f ldg4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+__device__ __forceinline__ void sts4(float* p, v4f v) { *reinterpret_cast<v4f*>(p) = v; }
 
 __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -495,6 +508,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
   float* sWT = sS + KD * SQ;        // [K][C] W^T
   float* sKg = sWT + KD * SQ;       // [C][K] Kg
   float* sV = sKg + C * KP;         // [C][64] U, then Vnew
+  float* sGam = sV + C * SQ;        // [K]
 
   const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
   const int c0 = cg * NCOL;
@@ -512,7 +526,23 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
     *reinterpret_cast<float4*>(sS + d * SQ + 4 * c4) =
         p.s0 ? *reinterpret_cast<const float4*>(p.s0 + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  __syncthreads();
+  v4f pwt[4], pkg[4], pu[2];      // W^T [K][C], Kg [C][K], U [C][64 columns]
+  float pgam;                     // exp(G_last)[t % K]
+  auto fetch = [&](const float* r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      pwt[k] = ldg4(r + R_WT + 4 * (tid + NTC * k));
+      pkg[k] = ldg4(r + R_KG + 4 * (tid + NTC * k));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + NTC * k, rr = u / (NCOL / 4), c4 = u - rr * (NCOL / 4);
+      pu[k] = ldg4(r + R_U + rr * KD + c0 + 4 * c4);
+    }
+    pgam = r[R_GAM + (tid & (KD - 1))];
+  };
+  if (nch > 0) fetch(record(p, hv, sb));
+  kda::lds_barrier();
 
   for (int c = 0; c < nch; ++c) {
     float* rec = record(p, hv, sb + c);
@@ -521,10 +551,22 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
       const int vv = t / KD, d = t - vv * KD;
       rec[R_ST + (c0 + vv) * KD + d] = sS[d * SQ + vv];
     }
-    load_rows<NTC>(sWT, SQ, rec + R_WT, C, 0, KD, 0, C, tid);
-    load_rows<NTC>(sKg, KP, rec + R_KG, KD, 0, C, 0, KD, tid);
-    load_rows<NTC>(sV, SQ, rec + R_U, KD, 0, C, c0, NCOL, tid);
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = tid + NTC * k;
+      const int rw = u / (C / 4), cw = u - rw * (C / 4);
+      sts4(sWT + rw * SQ + 4 * cw, pwt[k]);
+      const int rk = u / (KD / 4), ck = u - rk * (KD / 4);
+      sts4(sKg + rk * KP + 4 * ck, pkg[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + NTC * k, r = u / (NCOL / 4), c4 = u - r * (NCOL / 4);
+      sts4(sV + r * SQ + 4 * c4, pu[k]);
+    }
+    if (tid < KD) sGam[tid] = pgam;
+    kda::lds_barrier();
+    fetch(record(p, hv, sb + min(c + 1, nch - 1)));   // next step (the last re-reads its own)
     // Vnew = U - W S: rows 2 tr .. +1.
     {
       const int i0 = 2 * tr;
@@ -536,6 +578,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
       }
 #pragma unroll 4
       for (int d = 0; d < KD; ++d) fma2x4(acc, lds2(sWT + d * SQ + i0), lds4(sS + d * SQ + j0), -1.0f);
+      kda::lds_barrier();   // every thread has read its U rows before Vnew overwrites them
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
@@ -546,14 +589,14 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
       for (int cc = 0; cc < 4; ++cc)
         *reinterpret_cast<float2*>(rec + R_VNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
     }
-    __syncthreads();
+    kda::lds_barrier();
     // S = gamma S + Kg^T Vnew: rows 4 tr .. +3.
     {
       const int d0 = 4 * tr;
       float acc[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float gm = rec[R_GAM + d0 + r];
+        const float gm = sGam[d0 + r];
         const float4 s4 = lds4(sS + (d0 + r) * SQ + j0);
         acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
       }
@@ -563,7 +606,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
       for (int r = 0; r < 4; ++r)
         *reinterpret_cast<float4*>(sS + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
     }
-    __syncthreads();
+    kda::lds_barrier();
   }
 }
 
@@ -594,24 +637,67 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
     *reinterpret_cast<float4*>(sD + d * SQ + 4 * c4) =
         p.dht ? *reinterpret_cast<const float4*>(p.dht + (sh + d) * KD + c0 + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  __syncthreads();
+  v4f pkgt[4], paqk[2], pqg[4], pw[4];      // Kg^T [K][C], Aqk [C][C], Qg and W [C][K]
+  v4u pdo;                                   // d_out: row t / 8, 8 bf16 of this group's columns
+  float pgam;
+  // Rows past the chunk's end are clamped here and zeroed when stored to LDS.
+  auto fetch_a = [&](const float* r, int64_t t0, int nv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pkgt[k] = ldg4(r + R_KGT + 4 * (tid + NTC * k));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) paqk[k] = ldg4(r + R_AQK + 4 * (tid + NTC * k));
+    const int rr = min(tid >> 3, nv - 1), c8 = tid & 7;
+    pdo = *reinterpret_cast<const v4u*>(p.dout + ((t0 + rr) * p.HV + hv) * KD + c0 + 8 * c8);
+    pgam = r[R_GAM + (tid & (KD - 1))];
+  };
+  auto fetch_b = [&](const float* r, int h) __attribute__((always_inline)) {   // pieces 2h, 2h + 1: rows 32h .. 32h + 31
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      pqg[2 * h + k] = ldg4(r + R_QG + 4 * (tid + NTC * (2 * h + k)));
+      pw[2 * h + k] = ldg4(r + R_W + 4 * (tid + NTC * (2 * h + k)));
+    }
+  };
+  if (nch > 0) {
+    const float* r0 = record(p, hv, sb + nch - 1);
+    fetch_a(r0, tok0 + int64_t(nch - 1) * C, len - (nch - 1) * C);
+    fetch_b(r0, 0);
+    fetch_b(r0, 1);
+  }
+  kda::lds_barrier();
 
   for (int c = nch - 1; c >= 0; --c) {
     float* rec = record(p, hv, sb + c);
     const int nv = min(C, len - c * C);
-    const int64_t t0 = tok0 + int64_t(c) * C;
+    const int cn = max(c - 1, 0);     // next step (the first chunk re-reads its own)
+    const float* recn = record(p, hv, sb + cn);
     for (int t = tid; t < NCOL * KD; t += NTC) {
       const int vv = t / KD, d = t - vv * KD;
       rec[R_DST + (c0 + vv) * KD + d] = sD[d * SQ + vv];
     }
-    load_rows<NTC>(sKgT, SQ, rec + R_KGT, C, 0, KD, 0, C, tid);
-    load_rows<NTC>(sAqk, SQ, rec + R_AQK, C, 0, C, 0, C, tid);
-    for (int t = tid; t < C * NCOL; t += NTC) {
-      const int i = t / NCOL, jj = t - i * NCOL;
-      sO[i * SQ + jj] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + c0 + jj]) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = tid + NTC * k, rr = u / (C / 4), cc = u - rr * (C / 4);
+      sts4(sKgT + rr * SQ + 4 * cc, pkgt[k]);
     }
-    if (tid < KD) sGam[tid] = rec[R_GAM + tid];
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + NTC * k, rr = u / (C / 4), cc = u - rr * (C / 4);
+      sts4(sAqk + rr * SQ + 4 * cc, paqk[k]);
+    }
+    {
+      const int r = tid >> 3, c8 = tid & 7;
+      const uint32_t w[4] = {pdo.x, pdo.y, pdo.z, pdo.w};
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = r < nv ? kda::bf16lo(w[e]) : 0.0f;
+        f[2 * e + 1] = r < nv ? kda::bf16hi(w[e]) : 0.0f;
+      }
+      st8(sO + r * SQ + 8 * c8, f);
+    }
+    if (tid < KD) sGam[tid] = pgam;
+    kda::lds_barrier();
+    fetch_a(recn, tok0 + int64_t(cn) * C, min(C, len - cn * C));
     // dVnew = Aqk^T dO + Kg dS': rows 2 tr .. +1 (Aqk[m][i] = 0 for m < i).
     {
       const int i0 = 2 * tr;
@@ -631,7 +717,8 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
         *reinterpret_cast<float2*>(rec + R_DVNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
     }
     // dS = gamma dS' + Qg^T dO - W^T dVnew: rows 4 tr .. +3, with Qg and W
-    // staged 32 rows at a time where Kg^T was.
+    // staged 32 rows at a time where Kg^T was (pieces k = 2h, 2h+1 of each
+    // thread are rows 32h .. 32h+31).
     const int d0 = 4 * tr;
     float acc[4][4];
 #pragma unroll
@@ -640,21 +727,29 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
       const float4 s4 = lds4(sD + (d0 + r) * SQ + j0);
       acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
     }
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
-      __syncthreads();   // Kg^T (or the previous half) is no longer read; dVnew is complete
-      load_rows<NTC>(sQh, KP, rec + R_QG, KD, h * (C / 2), C / 2, 0, KD, tid);
-      load_rows<NTC>(sWh, KP, rec + R_W, KD, h * (C / 2), C / 2, 0, KD, tid);
-      __syncthreads();
+      kda::lds_barrier();   // Kg^T (or the previous half) is no longer read; dVnew is complete
+#pragma unroll
+      for (int k = 2 * h; k < 2 * h + 2; ++k) {
+        const int u = tid + NTC * k - h * (C / 2) * (KD / 4);
+        const int rr = u / (KD / 4), cc = u - rr * (KD / 4);
+        sts4(sQh + rr * KP + 4 * cc, pqg[k]);
+        sts4(sWh + rr * KP + 4 * cc, pw[k]);
+      }
+      fetch_b(recn, h);
+      kda::lds_barrier();
 #pragma unroll 4
       for (int i = 0; i < C / 2; ++i) {
         fma4x4(acc, lds4(sQh + i * KP + d0), lds4(sO + (h * (C / 2) + i) * SQ + j0), 1.0f);
         fma4x4(acc, lds4(sWh + i * KP + d0), lds4(sV + (h * (C / 2) + i) * SQ + j0), -1.0f);
       }
     }
+    kda::lds_barrier();   // every thread has read its dS' rows (and the halves) before dS overwrites them
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       *reinterpret_cast<float4*>(sD + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-    __syncthreads();
+    kda::lds_barrier();
   }
   if (p.dh0)
     for (int u = tid; u < KD * NCOL / 4; u += NTC) {
@@ -733,7 +828,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   for (int vb = 0; vb < KD / 32; ++vb) {
     load_rows<NTG>(R3, KP, rec + R_ST, KD, 32 * vb, 32, 0, KD, tid);
     load_rows<NTG>(R3 + 32 * KP, KP, rec + R_DST, KD, 32 * vb, 32, 0, KD, tid);
-    __syncthreads();
+    kda::lds_barrier();
 #pragma unroll 4
     for (int u = 0; u < 32; ++u) {
       const int vv = 32 * vb + u;
@@ -745,7 +840,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       dgam[0] = fmaf(bs.x, bd.x, dgam[0]); dgam[1] = fmaf(bs.y, bd.y, dgam[1]);
       dgam[2] = fmaf(bs.z, bd.z, dgam[2]); dgam[3] = fmaf(bs.w, bd.w, dgam[3]);
     }
-    __syncthreads();
+    kda::lds_barrier();
   }
   // Epilogue: dq^ = K^-1/2 dQg exp(G); dG = dQg Qg - dKg Kg;
   // dk^ = dKg exp(G_last - G); dG_last partials dKg Kg (+ dgamma gamma).
@@ -790,7 +885,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) R4[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? acc[r][cc] : 0.0f;
   }
-  __syncthreads();
+  kda::lds_barrier();
   if (tid < KD) {
     float sacc = 0.0f;
     for (int r = 0; r < C / 4; ++r) sacc += R3[r * KD + tid];
@@ -802,7 +897,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc)
     *reinterpret_cast<float4*>(R0 + (d0 + cc) * LQ + i0) = make_float4(-aw[0][cc], -aw[1][cc], -aw[2][cc], -aw[3][cc]);
-  __syncthreads();   // sGl has read R3's partials
+  kda::lds_barrier();   // sGl has read R3's partials
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     *reinterpret_cast<float4*>(R3 + (i0 + r) * KP + d0) = make_float4(-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3]);
@@ -810,16 +905,16 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     const int j = t / KD, vv = t - j * KD;
     R1[vv * LQ + j] = j < nv ? bf16f(p.v[((t0 + j) * p.HV + hv) * KD + vv]) : 0.0f;
   }
-  __syncthreads();
+  kda::lds_barrier();
   float da[2][4] = {};
 #pragma unroll 4
   for (int vv = 0; vv < KD; ++vv) fma2x4(da, lds2(R2 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
-  __syncthreads();
+  kda::lds_barrier();
   load_rows<NTG>(R1, LQ, rec + R_ET, C, 0, KD, 0, C, tid);
-  __syncthreads();
+  kda::lds_barrier();
 #pragma unroll 4
   for (int d = 0; d < KD; ++d) fma2x4(da, lds2(R0 + d * LQ + s0r), lds4(R1 + d * LQ + s0c));
-  __syncthreads();
+  kda::lds_barrier();
   // R0 = A | T ([C][LQ] each); R1 = dA | X; R2 = dVnew [C][K].
   float* sA = R0;
   float* sT = R0 + C * LQ;
@@ -832,7 +927,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? da[r][cc] : 0.0f;
-  __syncthreads();
+  kda::lds_barrier();
   {
     float av[4][4] = {}, ae[4][4] = {};
 #pragma unroll 4
@@ -869,12 +964,12 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int i = j; i < C; ++i) acc = fmaf(sDA[i * LQ + j], sT[i * LQ + j], acc);
     sDB[j] += acc;
   }
-  __syncthreads();
+  kda::lds_barrier();
   for (int t = tid; t < C * C; t += NTG) {
     const int i = t / C, j = t - i * C;
     sDA[i * LQ + j] *= sB[j];
   }
-  __syncthreads();
+  kda::lds_barrier();
   // dT^T and T^T (R2 and R3 are free: dv and dE are done) and P.
   float* sDTT = R2;
   float* sTT = R2 + C * LQ;
@@ -885,7 +980,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sTT[j * LQ + i] = sT[i * LQ + j];
   }
   load_rows<NTG>(sP, LQ, rec + R_P, C, 0, C, 0, C, tid);
-  __syncthreads();
+  kda::lds_barrier();
   // X = dT T^T: X[i][m] = sum_j dT[i][j] T[m][j] (j <= min(i, m)).
   {
     float acc[2][4] = {};
@@ -896,7 +991,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int r = 0; r < 2; ++r)
       *reinterpret_cast<float4*>(sX + (s0r + r) * LQ + s0c) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
   }
-  __syncthreads();
+  kda::lds_barrier();
   // dL = -tril_strict(T^T X): dL[a][b] = -sum_{i >= a} T[i][a] X[i][b] (into sDA).
   {
     float acc[2][4] = {};
@@ -907,20 +1002,20 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc < s0r + r) ? -acc[r][cc] : 0.0f;
   }
-  __syncthreads();
+  kda::lds_barrier();
   if (tid < C) {
     const int i = tid;
     float acc = 0.0f;
     for (int j = 0; j < i; ++j) acc = fmaf(sDA[i * LQ + j], sP[i * LQ + j], acc);
     sDB[i] += acc;
   }
-  __syncthreads();   // R2 and R3 are reloaded below
+  kda::lds_barrier();   // R2 and R3 are reloaded below
   // ---- phase 3: gated sums.  R0 = G, R2 = k^, R3 = q^ ([C][K]); dL in
   // R1 (sDA), dAqk in R4.
   load_rows<NTG>(R0, KP, rec + R_G, KD, 0, C, 0, KD, tid);
   load_rows<NTG>(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
   load_rows<NTG>(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
-  __syncthreads();
+  kda::lds_barrier();
   {
     float gi[4][4];
 #pragma unroll
@@ -1022,14 +1117,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   // ---- outputs: dg as the reverse prefix of dG over the chunk's rows
   // (dG_last was added to the last row); dbeta.  Each thread reads back
   // only the dG entries it wrote.
-  __syncthreads();
+  kda::lds_barrier();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float vg[4];
     ld4(gdG + (i0 + r) * KD + d0, vg);
     st4(R0 + (i0 + r) * KP + d0, vg);
   }
-  __syncthreads();
+  kda::lds_barrier();
   if (tid < KD) {
     float acc = 0.0f;
     for (int i = C - 1; i >= 0; --i) {
