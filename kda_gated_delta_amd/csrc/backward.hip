@@ -812,7 +812,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 
   // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T, dgamma,
   // dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T, R2 = dVnew^T
-  // ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per block.
+  // ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per block, the
+  // next block loaded into registers while the current one is used.
+  v4f pst[2], pdst[2];
+  auto fetch_blk = [&](int vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+      pst[k] = ldg4(rec + R_ST + (32 * vb + row) * KD + 4 * c4);
+      pdst[k] = ldg4(rec + R_DST + (32 * vb + row) * KD + 4 * c4);
+    }
+  };
+  fetch_blk(0);
   for (int t = tid; t < C * KD; t += NTG) {
     const int i = t / KD, vv = t - i * KD;
     R0[vv * LQ + i] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + vv]) : 0.0f;
@@ -826,9 +837,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   float aq[4][4] = {}, aw[4][4] = {}, akg[4][4] = {};
   float dgam[4] = {};
   for (int vb = 0; vb < KD / 32; ++vb) {
-    load_rows<NTG>(R3, KP, rec + R_ST, KD, 32 * vb, 32, 0, KD, tid);
-    load_rows<NTG>(R3 + 32 * KP, KP, rec + R_DST, KD, 32 * vb, 32, 0, KD, tid);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+      sts4(R3 + row * KP + 4 * c4, pst[k]);
+      sts4(R3 + (32 + row) * KP + 4 * c4, pdst[k]);
+    }
     kda::lds_barrier();
+    if (vb + 1 < KD / 32) fetch_blk(vb + 1);
 #pragma unroll 4
     for (int u = 0; u < 32; ++u) {
       const int vv = 32 * vb + u;
@@ -1016,26 +1032,63 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   load_rows<NTG>(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
   load_rows<NTG>(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
   kda::lds_barrier();
+  float dgt[4][4];   // this tile's final dG (written to LDS once all of phase 3 is done)
   {
     float gi[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ld4(R0 + (i0 + r) * KP + d0, gi[r]);
-    // Row forms: j <= i over this tile's rows i.
+    // Row forms: j <= i over this tile's rows i.  Below the tile's first
+    // row i0 the factor splits around it, exp(G_i - G_j) =
+    // exp(G_i - G_i0) exp(G_i0 - G_j), both <= 1, so each j needs 4
+    // exponentials instead of 16; the tile's own 4x4 diagonal block is
+    // formed directly (j <= i only).
     {
       float rk[4][4] = {}, rq[4][4] = {};
+      float fr[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) fr[r][cc] = ex2(gi[r][cc] - gi[0][cc]);
+      float mkb[4], mqb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mkb[r] = sB[i0 + r];
+        mqb[r] = kScale;
+      }
 #pragma unroll 2
-      for (int j = 0; j <= i0 + 3; ++j) {
+      for (int j = 0; j < i0; ++j) {
+        float gj[4], kj[4], fc[4];
+        ld4(R0 + j * KP + d0, gj);
+        ld4(R2 + j * KP + d0, kj);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) fc[cc] = ex2(gi[0][cc] - gj[cc]) * kj[cc];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          const float mk = mkb[r] * sDA[i * LQ + j];
+          const float mq = mqb[r] * R4[i * LQ + j];
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const float e = fr[r][cc] * fc[cc];
+            rk[r][cc] = fmaf(mk, e, rk[r][cc]);
+            rq[r][cc] = fmaf(mq, e, rq[r][cc]);
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = i0 + jj;
         float gj[4], kj[4];
         ld4(R0 + j * KP + d0, gj);
         ld4(R2 + j * KP + d0, kj);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = jj; r < 4; ++r) {
           const int i = i0 + r;
-          const float mk = j <= i ? sB[i] * sDA[i * LQ + j] : 0.0f;
-          const float mq = j <= i ? kScale * R4[i * LQ + j] : 0.0f;
+          const float mk = mkb[r] * sDA[i * LQ + j];
+          const float mq = mqb[r] * R4[i * LQ + j];
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            const float e = j <= i ? ex2(gi[r][cc] - gj[cc]) * kj[cc] : 0.0f;
+            const float e = ex2(gi[r][cc] - gj[cc]) * kj[cc];
             rk[r][cc] = fmaf(mk, e, rk[r][cc]);
             rq[r][cc] = fmaf(mq, e, rq[r][cc]);
           }
@@ -1044,13 +1097,12 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        float ki[4], qi[4], vg[4];
+        float ki[4], qi[4];
         ld4(R2 + i * KP + d0, ki);
         ld4(R3 + i * KP + d0, qi);
-        ld4(gdG + i * KD + d0, vg);
+        ld4(gdG + i * KD + d0, dgt[r]);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) vg[cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
-        st4(gdG + i * KD + d0, vg);
+        for (int cc = 0; cc < 4; ++cc) dgt[r][cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
         if (i < nv) {
           float vq[4], vk[4];
           ld4(gdq + i * rs + d0, vq);
@@ -1066,11 +1118,38 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       }
     }
     // Column forms: i >= j over this tile's rows j (as the column index).
+    // Past the tile's last row i0 + 3 the factor splits around it, both
+    // parts <= 1; the diagonal block is formed directly (i >= j only).
     {
       float ck[4][4] = {}, cq[4][4] = {};
-#pragma unroll 2
-      for (int i = i0; i < C; ++i) {
+      float fj[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) fj[r][cc] = ex2(gi[3][cc] - gi[r][cc]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = i0 + ii;
         float gr[4], kr[4], qr[4];
+        ld4(R0 + i * KP + d0, gr);
+        ld4(R2 + i * KP + d0, kr);
+        ld4(R3 + i * KP + d0, qr);
+        const float bi = sB[i];
+#pragma unroll
+        for (int r = 0; r <= ii; ++r) {
+          const float mk = bi * sDA[i * LQ + i0 + r];
+          const float mq = kScale * R4[i * LQ + i0 + r];
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const float e = ex2(gr[cc] - gi[r][cc]);
+            ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
+            cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
+          }
+        }
+      }
+#pragma unroll 2
+      for (int i = i0 + 4; i < C; ++i) {
+        float gr[4], kr[4], qr[4], fi[4];
         ld4(R0 + i * KP + d0, gr);
         ld4(R2 + i * KP + d0, kr);
         ld4(R3 + i * KP + d0, qr);
@@ -1080,13 +1159,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
         const float aqv[4] = {aq4.x, aq4.y, aq4.z, aq4.w};
         const float bi = sB[i];
 #pragma unroll
+        for (int cc = 0; cc < 4; ++cc) fi[cc] = ex2(gr[cc] - gi[3][cc]);
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = i0 + r;
-          const float mk = i >= j ? bi * dl[r] : 0.0f;
-          const float mq = i >= j ? kScale * aqv[r] : 0.0f;
+          const float mk = bi * dl[r];
+          const float mq = kScale * aqv[r];
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            const float e = i >= j ? ex2(gr[cc] - gi[r][cc]) : 0.0f;
+            const float e = fi[cc] * fj[r][cc];
             ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
             cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
           }
@@ -1095,15 +1175,13 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        float ki[4], vg[4];
+        float ki[4];
         ld4(R2 + i * KP + d0, ki);
-        ld4(gdG + i * KD + d0, vg);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) vg[cc] -= ki[cc] * (ck[r][cc] + cq[r][cc]);
+        for (int cc = 0; cc < 4; ++cc) dgt[r][cc] -= ki[cc] * (ck[r][cc] + cq[r][cc]);
         if (i == C - 1)
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) vg[cc] += sGl[d0 + cc];
-        st4(gdG + i * KD + d0, vg);
+          for (int cc = 0; cc < 4; ++cc) dgt[r][cc] += sGl[d0 + cc];
         if (i < nv) {
           float vk[4];
           ld4(gdk + i * rs + d0, vk);
@@ -1115,21 +1193,27 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
   }
   // ---- outputs: dg as the reverse prefix of dG over the chunk's rows
-  // (dG_last was added to the last row); dbeta.  Each thread reads back
-  // only the dG entries it wrote.
+  // (dG_last was added to the last row), in four 16-row blocks per column:
+  // suffix sums within each block, then the totals of the later blocks.
   kda::lds_barrier();
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float vg[4];
-    ld4(gdG + (i0 + r) * KD + d0, vg);
-    st4(R0 + (i0 + r) * KP + d0, vg);
-  }
+  for (int r = 0; r < 4; ++r) st4(R0 + (i0 + r) * KP + d0, dgt[r]);
   kda::lds_barrier();
-  if (tid < KD) {
+  {
+    const int d = tid & (KD - 1), blk = tid >> 7;
     float acc = 0.0f;
-    for (int i = C - 1; i >= 0; --i) {
-      acc += R0[i * KP + tid];
-      if (i < nv) p.dg[((t0 + i) * p.HV + hv) * KD + tid] = acc;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      acc += R0[(16 * blk + r) * KP + d];
+      R0[(16 * blk + r) * KP + d] = acc;
+    }
+    kda::lds_barrier();
+    float later = 0.0f;
+    for (int b = blk + 1; b < C / 16; ++b) later += R0[16 * b * KP + d];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 16 * blk + r;
+      if (i < nv) p.dg[((t0 + i) * p.HV + hv) * KD + d] = R0[i * KP + d] + later;
     }
   }
   if (tid < nv) p.dbeta[(t0 + tid) * p.HV + hv] = sDB[tid];
