@@ -179,6 +179,13 @@ __device__ __forceinline__ void load_tile(float* dst, const float* src, int tid)
 // --------------------------------------------------------------- helpers
 constexpr int LQ = C + 4;         // LDS row stride of [*][C] fp32 tiles (16-byte aligned rows)
 
+// 16-byte values kept across phases are native vectors: locals of HIP's
+// float4 struct type in arrays were not promoted to registers.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f ldg4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+__device__ __forceinline__ void sts4(float* p, v4f v) { *reinterpret_cast<v4f*>(p) = v; }
+
 // Copy rows [r0, r0 + rows) of a [*][cols] fp32 record matrix, columns
 // [c0, c0 + w), into LDS with row stride ld (all multiples of 4).
 template <int NTH = NTB>
@@ -280,17 +287,32 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   const int tid = threadIdx.x;
   const int i0 = 4 * (tid >> 5), d0 = 4 * (tid & 31);
 
-  // q^ and k^: 32 rows per pass (16 lanes per row, 8 elements per lane);
-  // rows 0..63 are q, 64..127 are k; rows past the chunk's end are zero.
+  // Raw inputs first, all loads in flight together: the q and k rows of
+  // the four normalisation passes (32 rows per pass, 16 lanes per row, 8
+  // elements per lane; rows 0..63 are q, 64..127 are k) and this thread's
+  // four 16-byte pieces of g.  Rows past the chunk's end are zero.
+  uint4 xr[2 * C / 32];
+#pragma unroll
+  for (int pass = 0; pass < 2 * C / 32; ++pass) {
+    const int r = pass * 32 + (tid >> 4);
+    const int tr = r & (C - 1);
+    xr[pass] = make_uint4(0u, 0u, 0u, 0u);
+    if (tr < nv)
+      xr[pass] = *reinterpret_cast<const uint4*>((r >= C ? p.k : p.q) + ((t0 + tr) * p.H + hq) * KD + 8 * (tid & 15));
+  }
+  v4f graw[C * KD / 4 / NTP];
+#pragma unroll
+  for (int k = 0; k < C * KD / 4 / NTP; ++k) {
+    const int u = tid + NTP * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+    graw[k] = row < nv ? ldg4(p.g + ((t0 + row) * p.HV + hv) * KD + 4 * c4) : v4f{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
   for (int pass = 0; pass < 2 * C / 32; ++pass) {
     const int r = pass * 32 + (tid >> 4);
     const int l16 = tid & 15;
     const bool isk = r >= C;
     const int tr = r & (C - 1);
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (tr < nv)
-      x = *reinterpret_cast<const uint4*>((isk ? p.k : p.q) + ((t0 + tr) * p.H + hq) * KD + 8 * l16);
-    const uint4 y = kda::l2norm_row16(x);
+    const uint4 y = kda::l2norm_row16(xr[pass]);
     const uint32_t w[4] = {y.x, y.y, y.z, y.w};
     float f[8];
 #pragma unroll
@@ -301,15 +323,35 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
     st8((isk ? sK : sQ) + tr * KP + 8 * l16, f);
     st8(rec + (isk ? R_KN : R_QN) + tr * KD + 8 * l16, f);
   }
-  // G: inclusive prefix over the chunk's tokens (padding has g = 0), kept
-  // in log2 units.
-  if (tid < KD) {
+  // G: inclusive prefix of g over the chunk's tokens (padding has g = 0),
+  // kept in log2 units: prefixes within four 16-row blocks per channel,
+  // then the totals of the earlier blocks.
+#pragma unroll
+  for (int k = 0; k < C * KD / 4 / NTP; ++k) {
+    const int u = tid + NTP * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+    sts4(sG + row * KP + 4 * c4, graw[k]);
+  }
+  kda::lds_barrier();
+  {
+    const int d = tid & (KD - 1), blk = tid >> 7;
+    float pre[16];
     float acc = 0.0f;
-    for (int t = 0; t < C; ++t) {
-      if (t < nv) acc += p.g[((t0 + t) * p.HV + hv) * KD + tid];
-      const float g2 = acc * kLog2e;
-      sG[t * KP + tid] = g2;
-      rec[R_G + t * KD + tid] = g2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc += sG[(16 * blk + r) * KP + d];
+      pre[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sG[(16 * blk + r) * KP + d] = pre[r];
+    kda::lds_barrier();
+    float off = 0.0f;
+    for (int b = 0; b < blk; ++b) off += sG[(16 * b + 15) * KP + d];
+    kda::lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float g2 = (pre[r] + off) * kLog2e;
+      sG[(16 * blk + r) * KP + d] = g2;
+      rec[R_G + (16 * blk + r) * KD + d] = g2;
     }
   }
   if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
@@ -496,11 +538,7 @@ static_assert(KD * SQ >= 2 * (C / 2) * KP, "two half tiles of Qg and W fit where
 // Both carries load the operands of the next chunk step into registers
 // while the current step computes, so that their latency overlaps the
 // products.  Thread t carries the 16-byte pieces t, t + 512, ... of each
-// matrix in row-major order (as native vectors, which stay in registers).
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4f ldg4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
-__device__ __forceinline__ void sts4(float* p, v4f v) { *reinterpret_cast<v4f*>(p) = v; }
+// matrix in row-major order.
 
 __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
