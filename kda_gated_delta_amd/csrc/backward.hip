@@ -896,6 +896,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     kda::lds_barrier();
   }
+  // Phase 2's global operands, loaded now so that they arrive during the
+  // epilogue and dAqk: v (bf16; row u / 16, 8 values from column
+  // 8 (u % 16), for u = t, t + 512) and E^T.
+  v4u pv[2];
+  v4f pet[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + NTG * k, j = u >> 4, c8 = u & 15;
+    pv[k] = j < nv ? *reinterpret_cast<const v4u*>(p.v + ((t0 + j) * p.HV + hv) * KD + 8 * c8) : v4u{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pet[k] = ldg4(rec + R_ET + 4 * (tid + NTG * k));
   // Epilogue: dq^ = K^-1/2 dQg exp(G); dG = dQg Qg - dKg Kg;
   // dk^ = dKg exp(G_last - G); dG_last partials dKg Kg (+ dgamma gamma).
   {
@@ -955,16 +967,35 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     *reinterpret_cast<float4*>(R3 + (i0 + r) * KP + d0) = make_float4(-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3]);
-  for (int t = tid; t < C * KD; t += NTG) {
-    const int j = t / KD, vv = t - j * KD;
-    R1[vv * LQ + j] = j < nv ? bf16f(p.v[((t0 + j) * p.HV + hv) * KD + vv]) : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + NTG * k, j = u >> 4, c8 = u & 15;
+    const uint32_t w[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      R1[(8 * c8 + 2 * e) * LQ + j] = kda::bf16lo(w[e]);
+      R1[(8 * c8 + 2 * e + 1) * LQ + j] = kda::bf16hi(w[e]);
+    }
   }
   kda::lds_barrier();
   float da[2][4] = {};
 #pragma unroll 4
   for (int vv = 0; vv < KD; ++vv) fma2x4(da, lds2(R2 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
   kda::lds_barrier();
-  load_rows<NTG>(R1, LQ, rec + R_ET, C, 0, KD, 0, C, tid);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = tid + NTG * k, row = u / (C / 4), c4 = u - row * (C / 4);
+    sts4(R1 + row * LQ + 4 * c4, pet[k]);
+  }
+  // The dv / dE operands, loaded during the second half of dA.
+  v4f pa[2], ptt[2], pdv[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    pa[k] = ldg4(rec + R_A + 4 * (tid + NTG * k));
+    ptt[k] = ldg4(rec + R_T + 4 * (tid + NTG * k));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pdv[k] = ldg4(rec + R_DVN + 4 * (tid + NTG * k));
   kda::lds_barrier();
 #pragma unroll 4
   for (int d = 0; d < KD; ++d) fma2x4(da, lds2(R0 + d * LQ + s0r), lds4(R1 + d * LQ + s0c));
@@ -974,9 +1005,17 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   float* sT = R0 + C * LQ;
   float* sDA = R1;
   float* sX = R1 + C * LQ;
-  load_rows<NTG>(sA, LQ, rec + R_A, C, 0, C, 0, C, tid);
-  load_rows<NTG>(sT, LQ, rec + R_T, C, 0, C, 0, C, tid);
-  load_rows<NTG>(R2, KP, rec + R_DVN, KD, 0, C, 0, KD, tid);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + NTG * k, row = u / (C / 4), c4 = u - row * (C / 4);
+    sts4(sA + row * LQ + 4 * c4, pa[k]);
+    sts4(sT + row * LQ + 4 * c4, ptt[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+    sts4(R2 + row * KP + 4 * c4, pdv[k]);
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -1024,6 +1063,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sDA[i * LQ + j] *= sB[j];
   }
   kda::lds_barrier();
+  // Phase 3's operands (G, k^, q^), loaded while dbeta, X and dL run.
+  v4f pg3[4], pk3[4], pq3[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pg3[k] = ldg4(rec + R_G + 4 * (tid + NTG * k));
+    pk3[k] = ldg4(rec + R_KN + 4 * (tid + NTG * k));
+    pq3[k] = ldg4(rec + R_QN + 4 * (tid + NTG * k));
+  }
   // dT^T and T^T (R2 and R3 are free: dv and dE are done) and P.
   float* sDTT = R2;
   float* sTT = R2 + C * LQ;
@@ -1066,9 +1113,13 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   kda::lds_barrier();   // R2 and R3 are reloaded below
   // ---- phase 3: gated sums.  R0 = G, R2 = k^, R3 = q^ ([C][K]); dL in
   // R1 (sDA), dAqk in R4.
-  load_rows<NTG>(R0, KP, rec + R_G, KD, 0, C, 0, KD, tid);
-  load_rows<NTG>(R2, KP, rec + R_KN, KD, 0, C, 0, KD, tid);
-  load_rows<NTG>(R3, KP, rec + R_QN, KD, 0, C, 0, KD, tid);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
+    sts4(R0 + row * KP + 4 * c4, pg3[k]);
+    sts4(R2 + row * KP + 4 * c4, pk3[k]);
+    sts4(R3 + row * KP + 4 * c4, pq3[k]);
+  }
   kda::lds_barrier();
   float dgt[4][4];   // this tile's final dG (written to LDS once all of phase 3 is done)
   {
