@@ -255,13 +255,9 @@ __device__ __forceinline__ void st4(float* p, const float* v) {
 
 // --------------------------------------------------------------- prep
 // 512 threads.  [C][128] results in 4x4 tiles (rows 4 (t / 32), columns
-// 4 (t % 32)); P and Aqk in 4x4 blocks of (i, j) pairs, each block taken by
-// two adjacent lanes that split the channels (lanes 0..271 cover the 136
-// lower-triangle blocks, lanes 272..511 write the 120 zero blocks above).
+// 4 (t % 32)); P and Aqk in 4x4 blocks of (i, j) pairs (below).
 constexpr int NTP = 512;
 constexpr int PREP_LDS = (3 * C * KP + 2 * C * LQ + C) * 4;
-constexpr int kTriBlocks = (C / 4) * (C / 4 + 1) / 2;   // 136
-static_assert(NTP / 2 - kTriBlocks == (C / 4) * (C / 4 - 1) / 2, "one lane pair per 4x4 block of the square");
 
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -299,6 +295,13 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
     xr[pass] = make_uint4(0u, 0u, 0u, 0u);
     if (tr < nv)
       xr[pass] = *reinterpret_cast<const uint4*>((r >= C ? p.k : p.q) + ((t0 + tr) * p.H + hq) * KD + 8 * (tid & 15));
+  }
+  v4u vraw[C * KD / 8 / NTP];   // v: row u / 16, 8 values from column 8 (u % 16)
+#pragma unroll
+  for (int k = 0; k < C * KD / 8 / NTP; ++k) {
+    const int u = tid + NTP * k, row = u >> 4, c8 = u & 15;
+    vraw[k] = row < nv ? *reinterpret_cast<const v4u*>(p.v + ((t0 + row) * p.HV + hv) * KD + 8 * c8)
+                       : v4u{0u, 0u, 0u, 0u};
   }
   v4f graw[C * KD / 4 / NTP];
 #pragma unroll
@@ -357,21 +360,32 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
   kda::lds_barrier();
 
-  // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.
+  // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.  Lanes 0..479 take
+  // the 120 blocks strictly below the diagonal, four lanes per block (one
+  // quarter of the channels each), where exp(G_i - G_j) splits around the
+  // block's first row a0 as exp(G_i - G_a0) exp(G_a0 - G_j) (both <= 1):
+  // 8 exponentials per channel instead of 16.  Lanes 480..511 take the 16
+  // diagonal blocks, two lanes per block (channel halves), formed directly
+  // (j <= i only).  Partial sums are combined with register-only DPP moves.
   {
-    const int blk = tid >> 1, half = tid & 1;
-    int bi, bj;
-    const bool lower = blk < kTriBlocks;
-    if (lower) {
-      tri_pair(blk, bi, bj);
-    } else {   // the strictly-upper blocks, numbered the same way transposed
-      tri_pair(blk - kTriBlocks, bj, bi);
-      ++bj;    // tri_pair over a triangle one smaller, shifted past the diagonal
+    constexpr int kBelow = (C / 4) * (C / 4 - 1) / 2;   // 120
+    static_assert(4 * kBelow + 2 * (C / 4) == NTP, "lanes cover the lower triangle exactly");
+    const bool below = tid < 4 * kBelow;
+    int bi, bj, d_lo, d_hi;
+    if (below) {
+      tri_pair(tid >> 2, bi, bj);
+      ++bi;    // strictly lower: row block bi + 1 over column blocks 0 .. bi
+      d_lo = (KD / 4) * (tid & 3);
+      d_hi = d_lo + KD / 4;
+    } else {
+      bi = bj = (tid - 4 * kBelow) >> 1;
+      d_lo = (KD / 2) * (tid & 1);
+      d_hi = d_lo + KD / 2;
     }
     const int a0 = 4 * bi, b0 = 4 * bj;
     float pk[4][4] = {}, pq[4][4] = {};
-    if (lower) {
-      for (int d = (KD / 2) * half; d < (KD / 2) * (half + 1); d += 4) {
+    if (below) {
+      for (int d = d_lo; d < d_hi; d += 4) {
         float4 gi[4], gj[4], ki[4], kj[4], qi[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -381,29 +395,62 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
           kj[r] = lds4(sK + (b0 + r) * KP + d);
           qi[r] = lds4(sQ + (a0 + r) * KP + d);
         }
+        float4 fr[4], fc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          fr[r] = make_float4(ex2(gi[r].x - gi[0].x), ex2(gi[r].y - gi[0].y), ex2(gi[r].z - gi[0].z),
+                              ex2(gi[r].w - gi[0].w));
+          fc[r] = make_float4(ex2(gi[0].x - gj[r].x) * kj[r].x, ex2(gi[0].y - gj[r].y) * kj[r].y,
+                              ex2(gi[0].z - gj[r].z) * kj[r].z, ex2(gi[0].w - gj[r].w) * kj[r].w);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 a = make_float4(ki[r].x * fr[r].x, ki[r].y * fr[r].y, ki[r].z * fr[r].z, ki[r].w * fr[r].w);
+          const float4 b = make_float4(qi[r].x * fr[r].x, qi[r].y * fr[r].y, qi[r].z * fr[r].z, qi[r].w * fr[r].w);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pk[r][q] = fmaf(a.x, fc[q].x, fmaf(a.y, fc[q].y, fmaf(a.z, fc[q].z, fmaf(a.w, fc[q].w, pk[r][q]))));
+            pq[r][q] = fmaf(b.x, fc[q].x, fmaf(b.y, fc[q].y, fmaf(b.z, fc[q].z, fmaf(b.w, fc[q].w, pq[r][q]))));
+          }
+        }
+      }
+    } else {
+      for (int d = d_lo; d < d_hi; d += 4) {
+        float4 gi[4], ki[4], qi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gi[r] = lds4(sG + (a0 + r) * KP + d);
+          ki[r] = lds4(sK + (a0 + r) * KP + d);
+          qi[r] = lds4(sQ + (a0 + r) * KP + d);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool ok = b0 + q <= a0 + r;   // no positive exponent is formed
-            const float e0 = ok ? ex2(gi[r].x - gj[q].x) : 0.0f;
-            const float e1 = ok ? ex2(gi[r].y - gj[q].y) : 0.0f;
-            const float e2 = ok ? ex2(gi[r].z - gj[q].z) : 0.0f;
-            const float e3 = ok ? ex2(gi[r].w - gj[q].w) : 0.0f;
-            const float k0 = kj[q].x * e0, k1 = kj[q].y * e1, k2 = kj[q].z * e2, k3 = kj[q].w * e3;
+          for (int q = 0; q <= r; ++q) {   // no positive exponent is formed
+            const float k0 = ki[q].x * ex2(gi[r].x - gi[q].x), k1 = ki[q].y * ex2(gi[r].y - gi[q].y);
+            const float k2 = ki[q].z * ex2(gi[r].z - gi[q].z), k3 = ki[q].w * ex2(gi[r].w - gi[q].w);
             pk[r][q] = fmaf(ki[r].x, k0, fmaf(ki[r].y, k1, fmaf(ki[r].z, k2, fmaf(ki[r].w, k3, pk[r][q]))));
             pq[r][q] = fmaf(qi[r].x, k0, fmaf(qi[r].y, k1, fmaf(qi[r].z, k2, fmaf(qi[r].w, k3, pq[r][q]))));
           }
       }
     }
+    // Sum over the block's lanes: xor 1 everywhere, xor 2 only within the
+    // four-lane groups (the diagonal lanes' partner at xor 2 belongs to
+    // another block, so its value is not added there).
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        pk[r][q] += __shfl_xor(pk[r][q], 1, 64);
-        pq[r][q] += __shfl_xor(pq[r][q], 1, 64);
+        pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pk[r][q])));
+        pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pq[r][q])));
+        const float pk2 = __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pk[r][q])));
+        const float pq2 = __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pq[r][q])));
+        if (below) {
+          pk[r][q] += pk2;
+          pq[r][q] += pq2;
+        }
       }
-    if (half == 0) {
+    if ((tid & (below ? 3 : 1)) == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = a0 + r;
@@ -420,42 +467,54 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
         *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
       }
     }
+    // The 120 blocks above the diagonal are zero: one row of one block per
+    // lane.
+    for (int t = tid; t < 4 * kBelow; t += NTP) {
+      int ui, uj;
+      tri_pair(t >> 2, uj, ui);
+      ++uj;
+      const int i = 4 * ui + (t & 3), j0u = 4 * uj;
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(sP + i * LQ + j0u) = z;
+      *reinterpret_cast<float4*>(rec + R_P + i * C + j0u) = z;
+      *reinterpret_cast<float4*>(rec + R_AQK + i * C + j0u) = z;
+    }
   }
   kda::lds_barrier();
 
   // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
-  // 8j .. 8j+7 own column j, lane part holding T[8 part + m][j] (m < 8) in
-  // registers; row i's sum over the column is split by part and completed
-  // across the eight lanes.  (P is strictly lower and T starts at zero, so
-  // the sums need no bounds.)
-  {
-    const int j = tid >> 3, part = tid & 7;
-    float tc[8];
+  // 4j .. 4j+3 (the first 256 threads) own column j, lane part holding
+  // T[16 part + m][j] (m < 16) in registers; row i's sum over the column is
+  // split by part and completed across the four lanes with register-only
+  // DPP moves.  (P is strictly lower and T starts at zero, so the sums
+  // need no bounds.)
+  if (tid < 4 * C) {
+    const int j = tid >> 2, part = tid & 3;
+    float tc[16];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) tc[m] = 0.0f;
+    for (int m = 0; m < 16; ++m) tc[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      const float4 pa = lds4(sP + i * LQ + 8 * part);
-      const float4 pb = lds4(sP + i * LQ + 8 * part + 4);
-      float acc = pa.x * tc[0];
-      acc = fmaf(pa.y, tc[1], acc);
-      acc = fmaf(pa.z, tc[2], acc);
-      acc = fmaf(pa.w, tc[3], acc);
-      acc = fmaf(pb.x, tc[4], acc);
-      acc = fmaf(pb.y, tc[5], acc);
-      acc = fmaf(pb.z, tc[6], acc);
-      acc = fmaf(pb.w, tc[7], acc);
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 pr = lds4(sP + i * LQ + 16 * part + 4 * q);
+        acc0 = fmaf(pr.x, tc[4 * q], acc0);
+        acc1 = fmaf(pr.y, tc[4 * q + 1], acc1);
+        acc0 = fmaf(pr.z, tc[4 * q + 2], acc0);
+        acc1 = fmaf(pr.w, tc[4 * q + 3], acc1);
+      }
+      float acc = acc0 + acc1;
+      acc += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(acc)));
+      acc += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(acc)));
       const float tv = i == j ? 1.0f : -sB[i] * acc;
-      if (part == i / 8) tc[i % 8] = tv;
+      if (part == i / 16) tc[i % 16] = tv;
     }
     // T and A = T diag(beta) to the record; A^T to LDS.
     const float bj = sB[j];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int i = 8 * part + m;
+    for (int m = 0; m < 16; ++m) {
+      const int i = 16 * part + m;
       rec[R_T + i * C + j] = tc[m];
       rec[R_A + i * C + j] = tc[m] * bj;
       sAT[j * LQ + i] = tc[m] * bj;
@@ -497,9 +556,17 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   }
   kda::lds_barrier();
   // v (zero past the chunk's end) replaces k^ in LDS.
-  for (int t = tid; t < C * KD; t += NTP) {
-    const int i = t / KD, d = t - i * KD;
-    sK[i * KP + d] = i < nv ? bf16f(p.v[((t0 + i) * p.HV + hv) * KD + d]) : 0.0f;
+#pragma unroll
+  for (int k = 0; k < C * KD / 8 / NTP; ++k) {
+    const int u = tid + NTP * k, row = u >> 4, c8 = u & 15;
+    const uint32_t w[4] = {vraw[k].x, vraw[k].y, vraw[k].z, vraw[k].w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = kda::bf16lo(w[e]);
+      f[2 * e + 1] = kda::bf16hi(w[e]);
+    }
+    st8(sK + row * KP + 8 * c8, f);
   }
   kda::lds_barrier();
   // W = A E and U = A v (A lower triangular: j <= i0 + 3 suffices).
