@@ -483,38 +483,39 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   kda::lds_barrier();
 
   // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
-  // 4j .. 4j+3 (the first 256 threads) own column j, lane part holding
-  // T[16 part + m][j] (m < 16) in registers; row i's sum over the column is
-  // split by part and completed across the four lanes with register-only
-  // DPP moves.  (P is strictly lower and T starts at zero, so the sums
-  // need no bounds.)
-  if (tid < 4 * C) {
-    const int j = tid >> 2, part = tid & 3;
-    float tc[16];
+  // 8j .. 8j+7 own column j, lane part holding T[8 part + m][j] (m < 8) in
+  // registers; row i's sum over the column is split by part and completed
+  // across the eight lanes with register-only DPP moves (neighbour swap,
+  // pair swap, half-row mirror).  (P is strictly lower and T starts at
+  // zero, so the sums need no bounds.)
+  {
+    const int j = tid >> 3, part = tid & 7;
+    float tc[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) tc[m] = 0.0f;
+    for (int m = 0; m < 8; ++m) tc[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 pr = lds4(sP + i * LQ + 16 * part + 4 * q);
-        acc0 = fmaf(pr.x, tc[4 * q], acc0);
-        acc1 = fmaf(pr.y, tc[4 * q + 1], acc1);
-        acc0 = fmaf(pr.z, tc[4 * q + 2], acc0);
-        acc1 = fmaf(pr.w, tc[4 * q + 3], acc1);
-      }
+      const float4 pa = lds4(sP + i * LQ + 8 * part);
+      const float4 pb = lds4(sP + i * LQ + 8 * part + 4);
+      float acc0 = pa.x * tc[0], acc1 = pa.y * tc[1];
+      acc0 = fmaf(pa.z, tc[2], acc0);
+      acc1 = fmaf(pa.w, tc[3], acc1);
+      acc0 = fmaf(pb.x, tc[4], acc0);
+      acc1 = fmaf(pb.y, tc[5], acc1);
+      acc0 = fmaf(pb.z, tc[6], acc0);
+      acc1 = fmaf(pb.w, tc[7], acc1);
       float acc = acc0 + acc1;
       acc += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(acc)));
       acc += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(acc)));
+      acc += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(acc)));
       const float tv = i == j ? 1.0f : -sB[i] * acc;
-      if (part == i / 16) tc[i % 16] = tv;
+      if (part == i / 8) tc[i % 8] = tv;
     }
     // T and A = T diag(beta) to the record; A^T to LDS.
     const float bj = sB[j];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int i = 16 * part + m;
+    for (int m = 0; m < 8; ++m) {
+      const int i = 8 * part + m;
       rec[R_T + i * C + j] = tc[m];
       rec[R_A + i * C + j] = tc[m] * bj;
       sAT[j * LQ + i] = tc[m] * bj;
