@@ -143,3 +143,35 @@ def test_backward_full_size_sampled_head(gpu_lib):
             for name, x in zip(NAMES, got)]
     mine = [x.cpu().numpy().astype(np.float64) for x in mine]
     _check(mine, ref, f"full size head {h}")
+
+
+def test_backward_varlen_gqa_full_size_sampled(gpu_lib):
+    """The 16-sequence varlen GQA batch (H=16, HV=32, about 37.5k tokens)
+    in one call; the longest sequence's Q/K head 3 with its two value heads
+    is checked against the oracle run on that sequence and head group."""
+    inp = synth.config3()
+    d_out, d_final = synth.upstream_grads(inp, 77)
+    cu = inp.cu_seqlens
+    say(f"backward full size {inp.name}")
+    dev = "cuda"
+    got = gpu_lib.chunk_backward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                                 inp.beta.to(dev), inp.initial_state.to(dev), d_out.to(dev),
+                                 d_final.to(dev), cu_seqlens=cu.to(dev))
+    torch.cuda.synchronize()
+    for name, x in zip(NAMES, got):
+        assert bool(torch.isfinite(x).all()), f"varlen full size: {name} non-finite"
+    lens = (cu[1:] - cu[:-1]).tolist()
+    n = int(np.argmax(lens))
+    t0, t1 = int(cu[n]), int(cu[n + 1])
+    h = 3
+    hv0, hv1 = 2 * h, 2 * h + 2
+    qk = lambda t: t[:, t0:t1, h:h + 1].float().numpy()
+    vh = lambda t: t[:, t0:t1, hv0:hv1].float().numpy()
+    ref = oracle.recurrent_backward(qk(inp.q), qk(inp.k), vh(inp.v), vh(inp.g), vh(inp.beta),
+                                    inp.initial_state[n:n + 1, hv0:hv1].numpy(), vh(d_out),
+                                    d_final[n:n + 1, hv0:hv1].numpy())
+    dq, dk, dv, dg, db, dh0 = got
+    mine = [dq[:, t0:t1, h:h + 1], dk[:, t0:t1, h:h + 1], dv[:, t0:t1, hv0:hv1], dg[:, t0:t1, hv0:hv1],
+            db[:, t0:t1, hv0:hv1], dh0[n:n + 1, hv0:hv1]]
+    mine = [x.cpu().numpy().astype(np.float64) for x in mine]
+    _check(mine, ref, f"varlen full size sequence {n} ({t1 - t0} tokens) head {h}")
