@@ -253,6 +253,14 @@ __device__ __forceinline__ void st4(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// fp32 MFMA (v_mfma_f32_16x16x4_f32), twice the rate of plain fp32 VALU code
+// here: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and holds
+// D[4 (l / 16) + r][l % 16] in register r (checked on the chip).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // --------------------------------------------------------------- prep
 // 512 threads.  [C][128] results in 4x4 tiles (rows 4 (t / 32), columns
 // 4 (t % 32)); P and Aqk in 4x4 blocks of (i, j) pairs (below).
@@ -592,10 +600,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
 // --------------------------------------------------------------- carries
 // Workgroup (column group cg, value head hv, sequence n) owns state columns
 // 64 cg .. 64 cg + 63, with 512 threads (two waves per SIMD).  Every
-// product is register-blocked: thread t computes a 2x4 or 4x4 tile (rows
-// from t / 16, columns 4 (t % 16) ..+3) from 8- and 16-byte LDS reads of
-// operands stored contraction-index-major, so one pair of reads feeds 8 or
-// 16 fused multiply-adds.
+// product runs on fp32 MFMA in 16x16 output tiles, several tiles per wave
+// sharing their A operand, with operands read from LDS layouts whose
+// 16-lane groups touch consecutive words.
 constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
 constexpr int NTC = 512;          // threads per carry workgroup
 constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ + KD) * 4;
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
   const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
   const int c0 = cg * NCOL;
   const int tid = threadIdx.x;
-  const int tr = tid >> 4, j0 = 4 * (tid & 15);
+  const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;   // MFMA lane roles
   int64_t tok0;
   int len;
   seq_range(p, n, tok0, len);
@@ -673,44 +680,59 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
     if (tid < KD) sGam[tid] = pgam;
     kda::lds_barrier();
     fetch(record(p, hv, sb + min(c + 1, nch - 1)));   // next step (the last re-reads its own)
-    // Vnew = U - W S: rows 2 tr .. +1.
+    // Vnew = U - W S on MFMA: wave w owns token block ib = w / 2 and column
+    // blocks 2 (w % 2), 2 (w % 2) + 1 (two 16x16 tiles sharing A = W).
     {
-      const int i0 = 2 * tr;
-      float acc[2][4];
+      const int ib = wave >> 1, jb0 = 2 * (wave & 1);
+      f32x4v acc[2];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float4 u = lds4(sV + (i0 + r) * SQ + j0);
-        acc[r][0] = u.x; acc[r][1] = u.y; acc[r][2] = u.z; acc[r][3] = u.w;
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = sV[(16 * ib + 4 * lg + r) * SQ + 16 * (jb0 + t) + l16];
 #pragma unroll 4
-      for (int d = 0; d < KD; ++d) fma2x4(acc, lds2(sWT + d * SQ + i0), lds4(sS + d * SQ + j0), -1.0f);
-      kda::lds_barrier();   // every thread has read its U rows before Vnew overwrites them
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-        *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
-        *reinterpret_cast<float4*>(rec + R_VN + (i0 + r) * KD + c0 + j0) = o4;
+      for (int ks = 0; ks < KD / 4; ++ks) {
+        const int d = 4 * ks + lg;
+        const float a = -sWT[d * SQ + 16 * ib + l16];
+        acc[0] = mfma4(a, sS[d * SQ + 16 * jb0 + l16], acc[0]);
+        acc[1] = mfma4(a, sS[d * SQ + 16 * (jb0 + 1) + l16], acc[1]);
       }
+      kda::lds_barrier();   // every wave has read its U tiles before Vnew overwrites them
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        *reinterpret_cast<float2*>(rec + R_VNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
+      for (int t = 0; t < 2; ++t) {
+        const int j = 16 * (jb0 + t) + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * lg + r;
+          sV[i * SQ + j] = acc[t][r];
+          rec[R_VN + i * KD + c0 + j] = acc[t][r];
+        }
+        *reinterpret_cast<f32x4v*>(rec + R_VNT + (c0 + j) * C + 16 * ib + 4 * lg) = acc[t];
+      }
     }
     kda::lds_barrier();
-    // S = gamma S + Kg^T Vnew: rows 4 tr .. +3.
+    // S = gamma S + Kg^T Vnew on MFMA: wave w owns state rows 16 w .. +15,
+    // all four column blocks (A = Kg^T shared).
     {
-      const int d0 = 4 * tr;
-      float acc[4][4];
+      f32x4v acc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float gm = sGam[d0 + r];
-        const float4 s4 = lds4(sS + (d0 + r) * SQ + j0);
-        acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
-      }
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 16 * wave + 4 * lg + r;
+          acc[t][r] = sGam[d] * sS[d * SQ + 16 * t + l16];
+        }
 #pragma unroll 4
-      for (int i = 0; i < C; ++i) fma4x4(acc, lds4(sKg + i * KP + d0), lds4(sV + i * SQ + j0), 1.0f);
+      for (int ks = 0; ks < C / 4; ++ks) {
+        const int i = 4 * ks + lg;
+        const float a = sKg[i * KP + 16 * wave + l16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<float4*>(sS + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        for (int t = 0; t < 4; ++t) acc[t] = mfma4(a, sV[i * SQ + 16 * t + l16], acc[t]);
+      }
+      kda::lds_barrier();   // every wave has read S before it is overwritten
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[(16 * wave + 4 * lg + r) * SQ + 16 * t + l16] = acc[t][r];
     }
     kda::lds_barrier();
   }
@@ -730,7 +752,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
   const int cg = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
   const int c0 = cg * NCOL;
   const int tid = threadIdx.x;
-  const int tr = tid >> 4, j0 = 4 * (tid & 15);
+  const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;   // MFMA lane roles
   int64_t tok0;
   int len;
   seq_range(p, n, tok0, len);
@@ -804,35 +826,50 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
     if (tid < KD) sGam[tid] = pgam;
     kda::lds_barrier();
     fetch_a(recn, tok0 + int64_t(cn) * C, min(C, len - cn * C));
-    // dVnew = Aqk^T dO + Kg dS': rows 2 tr .. +1 (Aqk[m][i] = 0 for m < i).
+    // dVnew = Aqk^T dO + Kg dS' on MFMA: wave w owns token block ib = w / 2
+    // and column blocks 2 (w % 2), +1 (two tiles sharing A).  Aqk[m][i] = 0
+    // for m < i, so the first product starts at m = 16 ib.
     {
-      const int i0 = 2 * tr;
-      float acc[2][4] = {};
+      const int ib = wave >> 1, jb0 = 2 * (wave & 1);
+      f32x4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 2
+      for (int ks = 4 * ib; ks < C / 4; ++ks) {
+        const int m = 4 * ks + lg;
+        const float a = sAqk[m * SQ + 16 * ib + l16];
+        acc[0] = mfma4(a, sO[m * SQ + 16 * jb0 + l16], acc[0]);
+        acc[1] = mfma4(a, sO[m * SQ + 16 * (jb0 + 1) + l16], acc[1]);
+      }
 #pragma unroll 4
-      for (int m = i0; m < C; ++m) fma2x4(acc, lds2(sAqk + m * SQ + i0), lds4(sO + m * SQ + j0));
-#pragma unroll 4
-      for (int d = 0; d < KD; ++d) fma2x4(acc, lds2(sKgT + d * SQ + i0), lds4(sD + d * SQ + j0));
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float4 o4 = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-        *reinterpret_cast<float4*>(sV + (i0 + r) * SQ + j0) = o4;
-        *reinterpret_cast<float4*>(rec + R_DVN + (i0 + r) * KD + c0 + j0) = o4;
+      for (int ks = 0; ks < KD / 4; ++ks) {
+        const int d = 4 * ks + lg;
+        const float a = sKgT[d * SQ + 16 * ib + l16];
+        acc[0] = mfma4(a, sD[d * SQ + 16 * jb0 + l16], acc[0]);
+        acc[1] = mfma4(a, sD[d * SQ + 16 * (jb0 + 1) + l16], acc[1]);
       }
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        *reinterpret_cast<float2*>(rec + R_DVNT + (c0 + j0 + cc) * C + i0) = make_float2(acc[0][cc], acc[1][cc]);
-    }
-    // dS = gamma dS' + Qg^T dO - W^T dVnew: rows 4 tr .. +3, with Qg and W
-    // staged 32 rows at a time where Kg^T was (pieces k = 2h, 2h+1 of each
-    // thread are rows 32h .. 32h+31).
-    const int d0 = 4 * tr;
-    float acc[4][4];
+      for (int t = 0; t < 2; ++t) {
+        const int j = 16 * (jb0 + t) + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gm = sGam[d0 + r];
-      const float4 s4 = lds4(sD + (d0 + r) * SQ + j0);
-      acc[r][0] = gm * s4.x; acc[r][1] = gm * s4.y; acc[r][2] = gm * s4.z; acc[r][3] = gm * s4.w;
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * lg + r;
+          sV[i * SQ + j] = acc[t][r];
+          rec[R_DVN + i * KD + c0 + j] = acc[t][r];
+        }
+        *reinterpret_cast<f32x4v*>(rec + R_DVNT + (c0 + j) * C + 16 * ib + 4 * lg) = acc[t];
+      }
     }
+    // dS = gamma dS' + Qg^T dO - W^T dVnew on MFMA: wave w owns state rows
+    // 16 w .. +15 and all four column blocks, with Qg and W staged 32 rows
+    // at a time where Kg^T was (pieces k = 2h, 2h+1 of each thread are rows
+    // 32h .. 32h+31).
+    f32x4v acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * wave + 4 * lg + r;
+        acc[t][r] = sGam[d] * sD[d * SQ + 16 * t + l16];
+      }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       kda::lds_barrier();   // Kg^T (or the previous half) is no longer read; dVnew is complete
@@ -845,16 +882,24 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
       }
       fetch_b(recn, h);
       kda::lds_barrier();
-#pragma unroll 4
-      for (int i = 0; i < C / 2; ++i) {
-        fma4x4(acc, lds4(sQh + i * KP + d0), lds4(sO + (h * (C / 2) + i) * SQ + j0), 1.0f);
-        fma4x4(acc, lds4(sWh + i * KP + d0), lds4(sV + (h * (C / 2) + i) * SQ + j0), -1.0f);
+#pragma unroll 2
+      for (int ks = 0; ks < C / 8; ++ks) {
+        const int i = 4 * ks + lg;                 // row within the half
+        const int ig = h * (C / 2) + i;            // token
+        const float aq = sQh[i * KP + 16 * wave + l16];
+        const float aw = -sWh[i * KP + 16 * wave + l16];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[t] = mfma4(aq, sO[ig * SQ + 16 * t + l16], acc[t]);
+          acc[t] = mfma4(aw, sV[ig * SQ + 16 * t + l16], acc[t]);
+        }
       }
     }
-    kda::lds_barrier();   // every thread has read its dS' rows (and the halves) before dS overwrites them
+    kda::lds_barrier();   // every wave has read dS' (and the halves) before dS overwrites it
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<float4*>(sD + (d0 + r) * SQ + j0) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sD[(16 * wave + 4 * lg + r) * SQ + 16 * t + l16] = acc[t][r];
     kda::lds_barrier();
   }
   if (p.dh0)
