@@ -166,15 +166,6 @@ __device__ __forceinline__ void tri_pair(int t, int& i, int& j) {
   i = r;
   j = t - r * (r + 1) / 2;
 }
-constexpr int kPairs = C * (C + 1) / 2;
-
-// Copy a [C][KD] fp32 tile from the record into LDS (row stride KP).
-__device__ __forceinline__ void load_tile(float* dst, const float* src, int tid) {
-  for (int u = tid; u < C * KD / 4; u += NTB) {
-    const int r = u / (KD / 4), c4 = u - r * (KD / 4);
-    *reinterpret_cast<float4*>(dst + r * KP + 4 * c4) = reinterpret_cast<const float4*>(src)[u];
-  }
-}
 
 // --------------------------------------------------------------- helpers
 constexpr int LQ = C + 4;         // LDS row stride of [*][C] fp32 tiles (16-byte aligned rows)
@@ -209,22 +200,6 @@ __device__ __forceinline__ void fma4x4(float (*acc)[4], const float4 a, const fl
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-}
-
-// acc[4][8] += a[4] (x) b[8].
-__device__ __forceinline__ void fma4x8(float (*acc)[8], const float4 a, const float4 b0, const float4 b1) {
-  const float av[4] = {a.x, a.y, a.z, a.w};
-  const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-}
-
-__device__ __forceinline__ void ld8(const float* p, float* v) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 __device__ __forceinline__ void st8(float* p, const float* v) {
