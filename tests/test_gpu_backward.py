@@ -175,3 +175,34 @@ def test_backward_varlen_gqa_full_size_sampled(gpu_lib):
             db[:, t0:t1, hv0:hv1], dh0[n:n + 1, hv0:hv1]]
     mine = [x.cpu().numpy().astype(np.float64) for x in mine]
     _check(mine, ref, f"varlen full size sequence {n} ({t1 - t0} tokens) head {h}")
+
+
+def test_backward_empty_sequence_axis(gpu_lib):
+    """T = 0: nothing flows through the recurrence, so d_initial_state is
+    d_final_state exactly and the token gradients are empty."""
+    dev = "cuda"
+    B, H, HV = 2, 1, 2
+    inp = synth.prefill_basic(40, B, 0, H, HV, init="normal0.1", name="t0")
+    d_out, d_final = synth.upstream_grads(inp, 140)
+    got = gpu_lib.chunk_backward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                                 inp.beta.to(dev), inp.initial_state.to(dev), d_out.to(dev), d_final.to(dev))
+    torch.cuda.synchronize()
+    assert all(x.numel() == 0 for x in got[:5])
+    assert torch.equal(got[5].cpu(), d_final)
+
+
+def test_backward_deterministic_and_inputs_untouched(gpu_lib):
+    """Two calls give bitwise equal gradients (no atomics: every sum has a
+    fixed order) and leave every input unchanged."""
+    dev = "cuda"
+    inp = synth.prefill_basic(41, 1, 300, 2, 4, init="normal0.1", name="det")
+    d_out, d_final = synth.upstream_grads(inp, 141)
+    args = [t.to(dev) for t in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.initial_state, d_out, d_final)]
+    before = [t.clone() for t in args]
+    a = gpu_lib.chunk_backward(*args)
+    b = gpu_lib.chunk_backward(*args)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    for x, y in zip(args, before):
+        assert torch.equal(x, y)
