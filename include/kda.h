@@ -1,10 +1,11 @@
 /*
- * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
  *
  * The operation is the KDA forward hot path specified on the page
  * "KDA Chunk Prefill on Ascend A3" (sections "Function and tensor contract"
  * and "Mathematical definition") and, for single-token decode, on the page
- * "flashinfer.kda_decode.packed_kda_decode" (section "Parameters").
+ * "flashinfer.kda_decode.packed_kda_decode" (section "Parameters"), plus
+ * the prefill's optional backward (kda_chunk_backward).
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
