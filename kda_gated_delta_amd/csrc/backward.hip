@@ -1139,11 +1139,20 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   }
   // ---- dbeta and dL: dbeta_j += sum_i dA_ij T_ij; dT = dA diag(beta);
   // X = dT T^T; dL = -tril_strict(T^T X) (into sDA); dbeta_i += sum_j dL_ij P_ij.
-  if (tid < C) {
-    const int j = tid;
+  // Eight lanes per column (rows p, p + 8, ...), summed across the lanes by DPP.
+  static_assert(NTG == 8 * C, "one 8-lane group per row or column of the chunk");
+  {
+    const int j = tid >> 3, p = tid & 7;
     float acc = 0.0f;
-    for (int i = j; i < C; ++i) acc = fmaf(sDA[i * LQ + j], sT[i * LQ + j], acc);
-    sDB[j] += acc;
+#pragma unroll
+    for (int m = 0; m < C / 8; ++m) {
+      const int i = p + 8 * m;
+      if (i >= j) acc = fmaf(sDA[i * LQ + j], sT[i * LQ + j], acc);
+    }
+    acc += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(acc)));
+    acc += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(acc)));
+    acc += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(acc)));
+    if (p == 0) sDB[j] += acc;
   }
   kda::lds_barrier();
   for (int t = tid; t < C * C; t += NTG) {
@@ -1192,11 +1201,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc < s0r + r) ? -acc[r][cc] : 0.0f;
   }
   kda::lds_barrier();
-  if (tid < C) {
-    const int i = tid;
+  {
+    const int i = tid >> 3, p = tid & 7;
     float acc = 0.0f;
-    for (int j = 0; j < i; ++j) acc = fmaf(sDA[i * LQ + j], sP[i * LQ + j], acc);
-    sDB[i] += acc;
+#pragma unroll
+    for (int m = 0; m < C / 8; ++m) {
+      const int j = p + 8 * m;
+      if (j < i) acc = fmaf(sDA[i * LQ + j], sP[i * LQ + j], acc);
+    }
+    acc += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(acc)));
+    acc += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(acc)));
+    acc += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(acc)));
+    if (p == 0) sDB[i] += acc;
   }
   kda::lds_barrier();   // R2 and R3 are reloaded below
   // ---- phase 3: gated sums.  R0 = G, R2 = k^, R3 = q^ ([C][K]); dL in
@@ -1216,40 +1232,43 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int r = 0; r < 4; ++r) ld4(R0 + (i0 + r) * KP + d0, gi[r]);
     // Row forms: j <= i over this tile's rows i.  Below the tile's first
     // row i0 the factor splits around it, exp(G_i - G_j) =
-    // exp(G_i - G_i0) exp(G_i0 - G_j), both <= 1, so each j needs 4
-    // exponentials instead of 16; the tile's own 4x4 diagonal block is
-    // formed directly (j <= i only).
+    // exp(G_i - G_i0) exp(G_i0 - G_j), both <= 1.  The first part (with
+    // beta_i and the scale) does not depend on j, so the loop sums the
+    // second part only and the first is applied once after it; the tile's
+    // own 4x4 diagonal block is formed directly (j <= i only).
     {
       float rk[4][4] = {}, rq[4][4] = {};
-      float fr[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) fr[r][cc] = ex2(gi[r][cc] - gi[0][cc]);
-      float mkb[4], mqb[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mkb[r] = sB[i0 + r];
-        mqb[r] = kScale;
-      }
-#pragma unroll 2
-      for (int j = 0; j < i0; ++j) {
-        float gj[4], kj[4], fc[4];
-        ld4(R0 + j * KP + d0, gj);
-        ld4(R2 + j * KP + d0, kj);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) fc[cc] = ex2(gi[0][cc] - gj[cc]) * kj[cc];
+      for (int j4 = 0; j4 < i0; j4 += 4) {
+        float dl[4][4], aq[4][4];   // [row r][column j4 + jj]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          const float mk = mkb[r] * sDA[i * LQ + j];
-          const float mq = mqb[r] * R4[i * LQ + j];
+          ld4(sDA + (i0 + r) * LQ + j4, dl[r]);
+          ld4(R4 + (i0 + r) * LQ + j4, aq[r]);
+        }
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const float e = fr[r][cc] * fc[cc];
-            rk[r][cc] = fmaf(mk, e, rk[r][cc]);
-            rq[r][cc] = fmaf(mq, e, rq[r][cc]);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          float gj[4], kj[4], fc[4];
+          ld4(R0 + (j4 + jj) * KP + d0, gj);
+          ld4(R2 + (j4 + jj) * KP + d0, kj);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) fc[cc] = ex2(gi[0][cc] - gj[cc]) * kj[cc];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+              rk[r][cc] = fmaf(dl[r][jj], fc[cc], rk[r][cc]);
+              rq[r][cc] = fmaf(aq[r][jj], fc[cc], rq[r][cc]);
+            }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float bi = sB[i0 + r];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const float f = ex2(gi[r][cc] - gi[0][cc]);
+          rk[r][cc] *= bi * f;
+          rq[r][cc] *= kScale * f;
         }
       }
 #pragma unroll
@@ -1261,8 +1280,8 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
         for (int r = jj; r < 4; ++r) {
           const int i = i0 + r;
-          const float mk = mkb[r] * sDA[i * LQ + j];
-          const float mq = mqb[r] * R4[i * LQ + j];
+          const float mk = sB[i] * sDA[i * LQ + j];
+          const float mq = kScale * R4[i * LQ + j];
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             const float e = ex2(gi[r][cc] - gj[cc]) * kj[cc];
@@ -1296,14 +1315,43 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     // Column forms: i >= j over this tile's rows j (as the column index).
     // Past the tile's last row i0 + 3 the factor splits around it, both
-    // parts <= 1; the diagonal block is formed directly (i >= j only).
+    // parts <= 1; the part exp(G_{i0+3} - G_j) does not depend on i and is
+    // applied once after the loop (the scale of the q form with it).  The
+    // diagonal block is formed directly (i >= j only).
     {
       float ck[4][4] = {}, cq[4][4] = {};
-      float fj[4][4];
+#pragma unroll 2
+      for (int i = i0 + 4; i < C; ++i) {
+        float gr[4], kr[4], qr[4], dl[4], aqv[4];
+        ld4(R0 + i * KP + d0, gr);
+        ld4(R2 + i * KP + d0, kr);
+        ld4(R3 + i * KP + d0, qr);
+        ld4(sDA + i * LQ + i0, dl);
+        ld4(R4 + i * LQ + i0, aqv);
+        const float bi = sB[i];
+        float kf[4], qf[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const float fi = ex2(gr[cc] - gi[3][cc]);
+          kf[cc] = bi * kr[cc] * fi;
+          qf[cc] = qr[cc] * fi;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            ck[r][cc] = fmaf(dl[r], kf[cc], ck[r][cc]);
+            cq[r][cc] = fmaf(aqv[r], qf[cc], cq[r][cc]);
+          }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) fj[r][cc] = ex2(gi[3][cc] - gi[r][cc]);
+        for (int cc = 0; cc < 4; ++cc) {
+          const float f = ex2(gi[3][cc] - gi[r][cc]);
+          ck[r][cc] *= f;
+          cq[r][cc] *= kScale * f;
+        }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = i0 + ii;
@@ -1319,31 +1367,6 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             const float e = ex2(gr[cc] - gi[r][cc]);
-            ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
-            cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
-          }
-        }
-      }
-#pragma unroll 2
-      for (int i = i0 + 4; i < C; ++i) {
-        float gr[4], kr[4], qr[4], fi[4];
-        ld4(R0 + i * KP + d0, gr);
-        ld4(R2 + i * KP + d0, kr);
-        ld4(R3 + i * KP + d0, qr);
-        const float4 dl4 = lds4(sDA + i * LQ + i0);
-        const float4 aq4 = lds4(R4 + i * LQ + i0);
-        const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-        const float aqv[4] = {aq4.x, aq4.y, aq4.z, aq4.w};
-        const float bi = sB[i];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) fi[cc] = ex2(gr[cc] - gi[3][cc]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float mk = bi * dl[r];
-          const float mq = kScale * aqv[r];
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const float e = fi[cc] * fj[r][cc];
             ck[r][cc] = fmaf(mk, kr[cc] * e, ck[r][cc]);
             cq[r][cc] = fmaf(mq, qr[cc] * e, cq[r][cc]);
           }
