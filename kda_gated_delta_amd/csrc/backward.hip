@@ -936,10 +936,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   const int64_t rs = int64_t(p.HV) * KD;     // token stride of gdq, gdk
   float* gdG = rec + R_U;                    // the record's U field is no longer read
 
-  // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T, dgamma,
-  // dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T, R2 = dVnew^T
-  // ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per block, the
-  // next block loaded into registers while the current one is used.
+  // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T (on
+  // MFMA), dgamma, then dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T,
+  // R2 = dVnew^T ([V][C]); R3 = 32 rows of S^T then 32 rows of dS'^T per
+  // block, the next block loaded into registers while the current one is
+  // used.  Wave w owns token tiles 2 (w % 2) .. +1 and state-row tiles
+  // 2 (w / 2) .. +1 (16x16 each) of all three products.  In k-step s of a
+  // 16-row block of v, lane group g takes v = s + 4 g: the operand rows'
+  // strides are 4 mod 64 words, so the four groups read disjoint banks.
   v4f pst[2], pdst[2];
   auto fetch_blk = [&](int vb) __attribute__((always_inline)) {
 #pragma unroll
@@ -949,19 +953,51 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       pdst[k] = ldg4(rec + R_DST + (32 * vb + row) * KD + 4 * c4);
     }
   };
-  fetch_blk(0);
-  for (int t = tid; t < C * KD; t += NTG) {
-    const int i = t / KD, vv = t - i * KD;
-    R0[vv * LQ + i] = i < nv ? bf16f(p.dout[((t0 + i) * p.HV + hv) * KD + vv]) : 0.0f;
+  // Every load of the prologue is issued before the first is used: dO
+  // (bf16; row u / 16, 8 values from column 8 (u % 16)), Vnew^T, dVnew^T
+  // ([V][C]) and the first block of S^T / dS'^T.
+  v4u pdo[C * KD / 8 / NTG];
+  v4f pvn[KD * C / 4 / NTG], pdvn[KD * C / 4 / NTG];
+#pragma unroll
+  for (int k = 0; k < C * KD / 8 / NTG; ++k) {
+    const int u = tid + NTG * k, j = u >> 4, c8 = u & 15;
+    pdo[k] = j < nv ? *reinterpret_cast<const v4u*>(p.dout + ((t0 + j) * p.HV + hv) * KD + 8 * c8) : v4u{0u, 0u, 0u, 0u};
   }
-  load_rows<NTG>(R1, LQ, rec + R_VNT, C, 0, KD, 0, C, tid);
-  load_rows<NTG>(R2, LQ, rec + R_DVNT, C, 0, KD, 0, C, tid);
+#pragma unroll
+  for (int k = 0; k < KD * C / 4 / NTG; ++k) {
+    pvn[k] = ldg4(rec + R_VNT + 4 * (tid + NTG * k));
+    pdvn[k] = ldg4(rec + R_DVNT + 4 * (tid + NTG * k));
+  }
+  fetch_blk(0);
+  const float beta_t = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
+#pragma unroll
+  for (int k = 0; k < C * KD / 8 / NTG; ++k) {
+    const int u = tid + NTG * k, j = u >> 4, c8 = u & 15;
+    const uint32_t w[4] = {pdo[k].x, pdo[k].y, pdo[k].z, pdo[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      R0[(8 * c8 + 2 * e) * LQ + j] = kda::bf16lo(w[e]);
+      R0[(8 * c8 + 2 * e + 1) * LQ + j] = kda::bf16hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KD * C / 4 / NTG; ++k) {
+    const int u = tid + NTG * k, row = u / (C / 4), c4 = u - row * (C / 4);
+    sts4(R1 + row * LQ + 4 * c4, pvn[k]);
+    sts4(R2 + row * LQ + 4 * c4, pdvn[k]);
+  }
   if (tid < C) {
-    sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
+    sB[tid] = beta_t;
     sDB[tid] = 0.0f;
   }
-  float aq[4][4] = {}, aw[4][4] = {}, akg[4][4] = {};
-  float dgam[4] = {};
+  const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;   // MFMA lane roles
+  const int it0 = 2 * (wave & 1), dt0 = 2 * (wave >> 1);
+  f32x4v mq[2][2], mw[2][2], mk[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) mq[a][b] = mw[a][b] = mk[a][b] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  float dgp = 0.0f;   // dgamma partial: state row tid % 128, rows 8 (tid / 128) .. +7 of each block
   for (int vb = 0; vb < KD / 32; ++vb) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -971,19 +1007,57 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     kda::lds_barrier();
     if (vb + 1 < KD / 32) fetch_blk(vb + 1);
-#pragma unroll 4
-    for (int u = 0; u < 32; ++u) {
-      const int vv = 32 * vb + u;
-      const float4 bs = lds4(R3 + u * KP + d0);
-      const float4 bd = lds4(R3 + (32 + u) * KP + d0);
-      fma4x4(aq, lds4(R0 + vv * LQ + i0), bs, 1.0f);
-      fma4x4(aw, lds4(R2 + vv * LQ + i0), bs, 1.0f);
-      fma4x4(akg, lds4(R1 + vv * LQ + i0), bd, 1.0f);
-      dgam[0] = fmaf(bs.x, bd.x, dgam[0]); dgam[1] = fmaf(bs.y, bd.y, dgam[1]);
-      dgam[2] = fmaf(bs.z, bd.z, dgam[2]); dgam[3] = fmaf(bs.w, bd.w, dgam[3]);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int vl = 16 * (ks >> 2) + (ks & 3) + 4 * lg;   // row of the block
+      const int vv = 32 * vb + vl;
+      float bs[2], bd[2], ao[2], av[2], adv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bs[t] = R3[vl * KP + 16 * (dt0 + t) + l16];
+        bd[t] = R3[(32 + vl) * KP + 16 * (dt0 + t) + l16];
+        ao[t] = R0[vv * LQ + 16 * (it0 + t) + l16];
+        av[t] = R1[vv * LQ + 16 * (it0 + t) + l16];
+        adv[t] = R2[vv * LQ + 16 * (it0 + t) + l16];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          mq[a][b] = mfma4(ao[a], bs[b], mq[a][b]);
+          mw[a][b] = mfma4(adv[a], bs[b], mw[a][b]);
+          mk[a][b] = mfma4(av[a], bd[b], mk[a][b]);
+        }
+    }
+    {
+      const int d = tid & (KD - 1), v8 = 8 * (tid >> 7);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dgp = fmaf(R3[(v8 + u) * KP + d], R3[(32 + v8 + u) * KP + d], dgp);
     }
     kda::lds_barrier();
   }
+  // dgamma partials into R4 ([4][128]); dQg and dKg to this thread's 4x4
+  // tiles through R3 (dW stays in MFMA order until phase 2).
+  R4[(tid >> 7) * KD + (tid & (KD - 1))] = dgp;
+  float aq[4][4], akg[4][4];
+  auto to_tiles = [&](const f32x4v (&m)[2][2], float (&o)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R3[(16 * (it0 + a) + 4 * lg + r) * KP + 16 * (dt0 + b) + l16] = m[a][b][r];
+    kda::lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ld4(R3 + (i0 + r) * KP + d0, o[r]);
+    kda::lds_barrier();
+  };
+  to_tiles(mq, aq);
+  float dgam[4] = {};   // read before the next barriers (R4 takes dAqk below)
+  if (rb == 0)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) dgam[cc] = R4[d0 + cc] + R4[KD + d0 + cc] + R4[2 * KD + d0 + cc] + R4[3 * KD + d0 + cc];
+  to_tiles(mk, akg);
   // Phase 2's global operands, loaded now so that they arrive during the
   // epilogue and dAqk: v (bf16; row u / 16, 8 values from column
   // 8 (u % 16), for u = t, t + 512) and E^T.
@@ -1049,12 +1123,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   // dE = A^T dW.  R0 = dW^T [K][C]; R1 = v^T then E^T ([*][C]);
   // R2 = dVnew^T; R3 = dW [C][K].
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-    *reinterpret_cast<float4*>(R0 + (d0 + cc) * LQ + i0) = make_float4(-aw[0][cc], -aw[1][cc], -aw[2][cc], -aw[3][cc]);
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R0[(16 * (dt0 + b) + l16) * LQ + 16 * (it0 + a) + 4 * lg + r] = -mw[a][b][r];
   kda::lds_barrier();   // sGl has read R3's partials
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    *reinterpret_cast<float4*>(R3 + (i0 + r) * KP + d0) = make_float4(-aw[r][0], -aw[r][1], -aw[r][2], -aw[r][3]);
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R3[(16 * (it0 + a) + 4 * lg + r) * KP + 16 * (dt0 + b) + l16] = -mw[a][b][r];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int u = tid + NTG * k, j = u >> 4, c8 = u & 15;
