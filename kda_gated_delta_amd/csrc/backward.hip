@@ -1036,6 +1036,17 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     kda::lds_barrier();
   }
+  // The epilogue's global operands (G, Qg, Kg rows of this thread's tile,
+  // G_last, gamma), issued now so that they arrive during the round trips.
+  v4f egv[4], eqg[4], ekg[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    egv[r] = ldg4(rec + R_G + (i0 + r) * KD + d0);
+    eqg[r] = ldg4(rec + R_QG + (i0 + r) * KD + d0);
+    ekg[r] = ldg4(rec + R_KG + (i0 + r) * KD + d0);
+  }
+  const v4f egl = ldg4(rec + R_G + (C - 1) * KD + d0);
+  const v4f egm = rb == 0 ? ldg4(rec + R_GAM + d0) : v4f{0.f, 0.f, 0.f, 0.f};
   // dgamma partials into R4 ([4][128]); dQg and dKg to this thread's 4x4
   // tiles through R3 (dW stays in MFMA order until phase 2).
   R4[(tid >> 7) * KD + (tid & (KD - 1))] = dgp;
@@ -1073,27 +1084,19 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   // Epilogue: dq^ = K^-1/2 dQg exp(G); dG = dQg Qg - dKg Kg;
   // dk^ = dKg exp(G_last - G); dG_last partials dKg Kg (+ dgamma gamma).
   {
-    float gl[4], dglp[4] = {};
-    ld4(rec + R_G + (C - 1) * KD + d0, gl);
-    if (rb == 0) {
-      float gm[4];
-      ld4(rec + R_GAM + d0, gm);
+    float dglp[4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) dglp[cc] = dgam[cc] * gm[cc];
-    }
+    for (int cc = 0; cc < 4; ++cc) dglp[cc] = dgam[cc] * egm[cc];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r;
-      float gv[4], qg[4], kg[4], vq[4], vk[4], vg[4];
-      ld4(rec + R_G + i * KD + d0, gv);
-      ld4(rec + R_QG + i * KD + d0, qg);
-      ld4(rec + R_KG + i * KD + d0, kg);
+      float vq[4], vk[4], vg[4];
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        vq[cc] = kScale * aq[r][cc] * ex2(gv[cc]);
-        vg[cc] = aq[r][cc] * qg[cc] - akg[r][cc] * kg[cc];
-        vk[cc] = akg[r][cc] * ex2(gl[cc] - gv[cc]);
-        dglp[cc] = fmaf(akg[r][cc], kg[cc], dglp[cc]);
+        vq[cc] = kScale * aq[r][cc] * ex2(egv[r][cc]);
+        vg[cc] = aq[r][cc] * eqg[r][cc] - akg[r][cc] * ekg[r][cc];
+        vk[cc] = akg[r][cc] * ex2(egl[cc] - egv[r][cc]);
+        dglp[cc] = fmaf(akg[r][cc], ekg[r][cc], dglp[cc]);
       }
       st4(gdG + i * KD + d0, vg);
       if (i < nv) {
@@ -1156,11 +1159,12 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sts4(R1 + row * LQ + 4 * c4, pet[k]);
   }
   // The dv / dE operands, loaded during the second half of dA.
-  v4f pa[2], ptt[2], pdv[4];
+  v4f pa[2], ptt[2], pdv[4], pp[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     pa[k] = ldg4(rec + R_A + 4 * (tid + NTG * k));
     ptt[k] = ldg4(rec + R_T + 4 * (tid + NTG * k));
+    pp[k] = ldg4(rec + R_P + 4 * (tid + NTG * k));
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) pdv[k] = ldg4(rec + R_DVN + 4 * (tid + NTG * k));
@@ -1190,6 +1194,16 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? da[r][cc] : 0.0f;
   kda::lds_barrier();
   {
+    // G, E and this tile's own dG and dk^ partials, issued before the products.
+    v4f xg[4], xe[4], xdg[4], xdk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = i0 + r;
+      xg[r] = ldg4(rec + R_G + j * KD + d0);
+      xe[r] = ldg4(rec + R_E + j * KD + d0);
+      xdg[r] = ldg4(gdG + j * KD + d0);
+      xdk[r] = j < nv ? ldg4(gdk + j * rs + d0) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
     float av[4][4] = {}, ae[4][4] = {};
 #pragma unroll 4
     for (int i = 0; i < C; ++i) {
@@ -1201,20 +1215,14 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int r = 0; r < 4; ++r) {
       const int j = i0 + r;
       if (j < nv) st4(p.dv + ((t0 + j) * p.HV + hv) * KD + d0, av[r]);
-      float gv[4], ev[4], vg[4];
-      ld4(rec + R_G + j * KD + d0, gv);
-      ld4(rec + R_E + j * KD + d0, ev);
-      ld4(gdG + j * KD + d0, vg);
+      float vg[4], vk[4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) vg[cc] = fmaf(ae[r][cc], ev[cc], vg[cc]);
-      st4(gdG + j * KD + d0, vg);
-      if (j < nv) {
-        float vk[4];
-        ld4(gdk + j * rs + d0, vk);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) vk[cc] = fmaf(ae[r][cc], ex2(gv[cc]), vk[cc]);
-        st4(gdk + j * rs + d0, vk);
+      for (int cc = 0; cc < 4; ++cc) {
+        vg[cc] = fmaf(ae[r][cc], xe[r][cc], xdg[r][cc]);
+        vk[cc] = fmaf(ae[r][cc], ex2(xg[r][cc]), xdk[r][cc]);
       }
+      st4(gdG + j * KD + d0, vg);
+      if (j < nv) st4(gdk + j * rs + d0, vk);
     }
   }
   // ---- dbeta and dL: dbeta_j += sum_i dA_ij T_ij; dT = dA diag(beta);
@@ -1257,7 +1265,11 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sDTT[j * LQ + i] = sDA[i * LQ + j];
     sTT[j * LQ + i] = sT[i * LQ + j];
   }
-  load_rows<NTG>(sP, LQ, rec + R_P, C, 0, C, 0, C, tid);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + NTG * k, row = u / (C / 4), c4 = u - row * (C / 4);
+    sts4(sP + row * LQ + 4 * c4, pp[k]);
+  }
   kda::lds_barrier();
   // X = dT T^T: X[i][m] = sum_j dT[i][j] T[m][j] (j <= min(i, m)).
   {
@@ -1341,6 +1353,16 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
             }
         }
       }
+      // This tile's dG, dq^ and dk^ so far (phase 2 stored their last
+      // parts), all four rows loaded before any is stored.
+      v4f zdg[4], zdq[4], zdk[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        zdg[r] = ldg4(gdG + i * KD + d0);
+        zdq[r] = i < nv ? ldg4(gdq + i * rs + d0) : v4f{0.f, 0.f, 0.f, 0.f};
+        zdk[r] = i < nv ? ldg4(gdk + i * rs + d0) : v4f{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float bi = sB[i0 + r];
@@ -1373,23 +1395,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        float ki[4], qi[4];
+        float ki[4], qi[4], vq[4];
         ld4(R2 + i * KP + d0, ki);
         ld4(R3 + i * KP + d0, qi);
-        ld4(gdG + i * KD + d0, dgt[r]);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) dgt[r][cc] += ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
+        for (int cc = 0; cc < 4; ++cc) {
+          dgt[r][cc] = zdg[r][cc] + ki[cc] * rk[r][cc] + qi[cc] * rq[r][cc];
+          vq[cc] = zdq[r][cc] + rq[r][cc];
+          zdk[r][cc] += rk[r][cc];
+        }
         if (i < nv) {
-          float vq[4], vk[4];
-          ld4(gdq + i * rs + d0, vq);
-          ld4(gdk + i * rs + d0, vk);
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            vq[cc] += rq[r][cc];
-            vk[cc] += rk[r][cc];
-          }
           st4(gdq + i * rs + d0, vq);
-          st4(gdk + i * rs + d0, vk);
+          *reinterpret_cast<v4f*>(gdk + i * rs + d0) = zdk[r];
         }
       }
     }
@@ -1452,6 +1469,9 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
           }
         }
       }
+      v4f yk[4];   // dk^ as the row forms left it, all four rows loaded first
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yk[r] = i0 + r < nv ? ldg4(gdk + (i0 + r) * rs + d0) : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
@@ -1464,9 +1484,8 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
           for (int cc = 0; cc < 4; ++cc) dgt[r][cc] += sGl[d0 + cc];
         if (i < nv) {
           float vk[4];
-          ld4(gdk + i * rs + d0, vk);
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) vk[cc] += ck[r][cc] + cq[r][cc];
+          for (int cc = 0; cc < 4; ++cc) vk[cc] = yk[r][cc] + ck[r][cc] + cq[r][cc];
           st4(gdk + i * rs + d0, vk);
         }
       }
