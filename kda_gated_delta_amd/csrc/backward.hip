@@ -905,6 +905,54 @@ static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ && C * LQ <= C * KP, "regions hold their alternates");
 static_assert((C / 4) * KD <= C * KP, "dG_last partials fit in R3");
 
+// Lower 16x16 tiles (J <= I) of a [C][C] product X Y^T on MFMA, with both
+// operands stored transposed in LDS ([k][C], row stride ld): wave w takes
+// tiles w and w + 8 (when below 10) in the order (0,0) (1,0) (1,1) (2,0) ...
+// In k-step s of each 16-wide block, lane group g takes k = s + 4 g (row
+// strides are 4 mod 64 words, so the groups read disjoint banks).
+__device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
+  I = (t >= 1) + (t >= 3) + (t >= 6);
+  J = t - I * (I + 1) / 2;
+}
+__device__ __forceinline__ void tri_mfma(f32x4v (&acc)[2], const float* xt, const float* yt, int ld, int K,
+                                         int wave, int lg, int l16) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = wave + 8 * h;
+    if (t >= 10) break;
+    int I, J;
+    tri_tile(t, I, J);
+#pragma unroll 4
+    for (int kb = 0; kb < K; kb += 16)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k = kb + s + 4 * lg;
+        acc[h] = mfma4(xt[k * ld + 16 * I + l16], yt[k * ld + 16 * J + l16], acc[h]);
+      }
+  }
+}
+// Writes the tiles tri_mfma computed into out ([C][C], stride ld), keeping
+// column <= row on the diagonal tiles, and zeroes the tiles above them.
+__device__ __forceinline__ void tri_store(float* out, int ld, const f32x4v (&acc)[2], int wave, int lg, int l16,
+                                          int tid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = wave + 8 * h;
+    if (t >= 10) break;
+    int I, J;
+    tri_tile(t, I, J);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
+      out[i * ld + j] = (j <= i) ? acc[h][r] : 0.0f;
+    }
+  }
+  for (int u = tid; u < C * C; u += NTG) {
+    const int i = u / C, j = u - i * C;
+    if ((j >> 4) > (i >> 4)) out[i * ld + j] = 0.0f;
+  }
+}
+
 __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
   float* R0 = smem + R0_OFF;
@@ -1106,15 +1154,11 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     st4(R3 + rb * KD + d0, dglp);   // [16][128] partials (R3 is free)
   }
-  // dAqk (lower triangle incl. the diagonal) into R4.
+  // dAqk (lower triangle incl. the diagonal) into R4, on MFMA.
   {
-    float acc[2][4] = {};
-#pragma unroll 4
-    for (int vv = 0; vv < KD; ++vv) fma2x4(acc, lds2(R0 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) R4[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? acc[r][cc] : 0.0f;
+    f32x4v acc[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
+    tri_mfma(acc, R0, R1, LQ, KD, wave, lg, l16);
+    tri_store(R4, LQ, acc, wave, lg, l16, tid);
   }
   kda::lds_barrier();
   if (tid < KD) {
@@ -1149,9 +1193,8 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
   }
   kda::lds_barrier();
-  float da[2][4] = {};
-#pragma unroll 4
-  for (int vv = 0; vv < KD; ++vv) fma2x4(da, lds2(R2 + vv * LQ + s0r), lds4(R1 + vv * LQ + s0c));
+  f32x4v da[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // dA's lower tiles, on MFMA
+  tri_mfma(da, R2, R1, LQ, KD, wave, lg, l16);
   kda::lds_barrier();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -1169,8 +1212,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) pdv[k] = ldg4(rec + R_DVN + 4 * (tid + NTG * k));
   kda::lds_barrier();
-#pragma unroll 4
-  for (int d = 0; d < KD; ++d) fma2x4(da, lds2(R0 + d * LQ + s0r), lds4(R1 + d * LQ + s0c));
+  tri_mfma(da, R0, R1, LQ, KD, wave, lg, l16);
   kda::lds_barrier();
   // R0 = A | T ([C][LQ] each); R1 = dA | X; R2 = dVnew [C][K].
   float* sA = R0;
@@ -1188,10 +1230,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
     sts4(R2 + row * KP + 4 * c4, pdv[k]);
   }
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc <= s0r + r) ? da[r][cc] : 0.0f;
+  tri_store(sDA, LQ, da, wave, lg, l16, tid);
   kda::lds_barrier();
   {
     // G, E and this tile's own dG and dk^ partials, issued before the products.
