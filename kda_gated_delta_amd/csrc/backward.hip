@@ -931,6 +931,18 @@ __device__ __forceinline__ void tri_mfma(f32x4v (&acc)[2], const float* xt, cons
       }
   }
 }
+// One 16x16 tile (I, J) of X Y^T on MFMA over k in [k0, k1) (multiples of
+// 16), operands stored transposed as in tri_mfma.
+__device__ __forceinline__ f32x4v tile_mfma(f32x4v acc, const float* xt, const float* yt, int ld, int I, int J,
+                                            int k0, int k1, int lg, int l16) {
+  for (int kb = k0; kb < k1; kb += 16)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kb + s + 4 * lg;
+      acc = mfma4(xt[k * ld + 16 * I + l16], yt[k * ld + 16 * J + l16], acc);
+    }
+  return acc;
+}
 // Writes the tiles tri_mfma computed into out ([C][C], stride ld), keeping
 // column <= row on the diagonal tiles, and zeroes the tiles above them.
 __device__ __forceinline__ void tri_store(float* out, int ld, const f32x4v (&acc)[2], int wave, int lg, int l16,
@@ -1310,26 +1322,32 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sts4(sP + row * LQ + 4 * c4, pp[k]);
   }
   kda::lds_barrier();
-  // X = dT T^T: X[i][m] = sum_j dT[i][j] T[m][j] (j <= min(i, m)).
-  {
-    float acc[2][4] = {};
-    const int lim = min(s0r + 1, s0c + 3);
-#pragma unroll 4
-    for (int j = 0; j <= lim; ++j) fma2x4(acc, lds2(sDTT + j * LQ + s0r), lds4(sTT + j * LQ + s0c));
+  // X = dT T^T on MFMA: X[i][m] = sum_j dT[i][j] T[m][j] (j <= min(i, m),
+  // so tile (I, J) stops at k = 16 (min(I, J) + 1)); wave w takes tiles w
+  // and w + 8 of the 4x4 grid.
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      *reinterpret_cast<float4*>(sX + (s0r + r) * LQ + s0c) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+  for (int h = 0; h < 2; ++h) {
+    const int t = wave + 8 * h, I = t >> 2, J = t & 3;
+    const f32x4v acc = tile_mfma(f32x4v{0.f, 0.f, 0.f, 0.f}, sDTT, sTT, LQ, I, J, 0, 16 * (min(I, J) + 1), lg, l16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sX[(16 * I + 4 * lg + r) * LQ + 16 * J + l16] = acc[r];
   }
   kda::lds_barrier();
-  // dL = -tril_strict(T^T X): dL[a][b] = -sum_{i >= a} T[i][a] X[i][b] (into sDA).
-  {
-    float acc[2][4] = {};
-#pragma unroll 4
-    for (int i = s0r; i < C; ++i) fma2x4(acc, lds2(sT + i * LQ + s0r), lds4(sX + i * LQ + s0c));
+  // dL = -tril_strict(T^T X) on MFMA: dL[a][b] = -sum_{i >= a} T[i][a] X[i][b]
+  // (T stored row-major is T^T stored transposed), lower tiles into sDA;
+  // the tiles above hold dT's zeros already.
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+  for (int h = 0; h < 2; ++h) {
+    const int t = wave + 8 * h;
+    if (t >= 10) break;
+    int I, J;
+    tri_tile(t, I, J);
+    const f32x4v acc = tile_mfma(f32x4v{0.f, 0.f, 0.f, 0.f}, sT, sX, LQ, I, J, 16 * I, C, lg, l16);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) sDA[(s0r + r) * LQ + s0c + cc] = (s0c + cc < s0r + r) ? -acc[r][cc] : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int a = 16 * I + 4 * lg + r, b = 16 * J + l16;
+      sDA[a * LQ + b] = (b < a) ? -acc[r] : 0.0f;
+    }
   }
   kda::lds_barrier();
   {
