@@ -905,11 +905,45 @@ static_assert(GRAD_LDS <= 160 * 1024, "LDS budget");
 static_assert(C * KP <= KD * LQ && 2 * C * LQ <= KD * LQ && C * LQ <= C * KP, "regions hold their alternates");
 static_assert((C / 4) * KD <= C * KP, "dG_last partials fit in R3");
 
-// Lower 16x16 tiles (J <= I) of a [C][C] product X Y^T on MFMA, with both
-// operands stored transposed in LDS ([k][C], row stride ld): wave w takes
-// tiles w and w + 8 (when below 10) in the order (0,0) (1,0) (1,1) (2,0) ...
-// In k-step s of each 16-wide block, lane group g takes k = s + 4 g (row
-// strides are 4 mod 64 words, so the groups read disjoint banks).
+// One 16x16 tile (I, J) of X Y^T on MFMA over k in [k0, k1) (multiples of
+// 16, k1 > k0), with both operands stored transposed in LDS ([k][*], row
+// stride ld).  In k-step s of each 16-wide block, lane group g takes
+// k = s + 4 g (row strides are 4 mod 64 words, so the groups read disjoint
+// banks); the next block's operands are loaded while the current one's
+// four products run.
+__device__ __forceinline__ f32x4v tile_mfma(f32x4v acc, const float* xt, const float* yt, int ld, int I, int J,
+                                            int k0, int k1, int lg, int l16) {
+  const float* xp = xt + (k0 + 4 * lg) * ld + 16 * I + l16;
+  const float* yp = yt + (k0 + 4 * lg) * ld + 16 * J + l16;
+  float xa[4], ya[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    xa[s] = xp[s * ld];
+    ya[s] = yp[s * ld];
+  }
+  for (int kb = k0; kb < k1; kb += 16) {
+    const int step = kb + 16 < k1 ? 16 * ld : 0;   // the last block re-reads itself
+    xp += step;
+    yp += step;
+    float xb[4], yb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      xb[s] = xp[s * ld];
+      yb[s] = yp[s * ld];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma4(xa[s], ya[s], acc);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      xa[s] = xb[s];
+      ya[s] = yb[s];
+    }
+  }
+  return acc;
+}
+// Lower 16x16 tiles (J <= I) of a [C][C] product X Y^T over k in [0, K):
+// wave w takes tiles w and w + 8 (when below 10) in the order (0,0) (1,0)
+// (1,1) (2,0) ...
 __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
   I = (t >= 1) + (t >= 3) + (t >= 6);
   J = t - I * (I + 1) / 2;
@@ -919,29 +953,12 @@ __device__ __forceinline__ void tri_mfma(f32x4v (&acc)[2], const float* xt, cons
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = wave + 8 * h;
-    if (t >= 10) break;
-    int I, J;
-    tri_tile(t, I, J);
-#pragma unroll 4
-    for (int kb = 0; kb < K; kb += 16)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k = kb + s + 4 * lg;
-        acc[h] = mfma4(xt[k * ld + 16 * I + l16], yt[k * ld + 16 * J + l16], acc[h]);
-      }
-  }
-}
-// One 16x16 tile (I, J) of X Y^T on MFMA over k in [k0, k1) (multiples of
-// 16), operands stored transposed as in tri_mfma.
-__device__ __forceinline__ f32x4v tile_mfma(f32x4v acc, const float* xt, const float* yt, int ld, int I, int J,
-                                            int k0, int k1, int lg, int l16) {
-  for (int kb = k0; kb < k1; kb += 16)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = kb + s + 4 * lg;
-      acc = mfma4(xt[k * ld + 16 * I + l16], yt[k * ld + 16 * J + l16], acc);
+    if (t < 10) {
+      int I, J;
+      tri_tile(t, I, J);
+      acc[h] = tile_mfma(acc[h], xt, yt, ld, I, J, 0, K, lg, l16);
     }
-  return acc;
+  }
 }
 // Writes the tiles tri_mfma computed into out ([C][C], stride ld), keeping
 // column <= row on the diagonal tiles, and zeroes the tiles above them.
