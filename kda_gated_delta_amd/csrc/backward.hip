@@ -343,115 +343,158 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   if (tid < C) sB[tid] = tid < nv ? bf16f(p.beta[(t0 + tid) * p.HV + hv]) : 0.0f;
   kda::lds_barrier();
 
-  // P (j < i) and Aqk (j <= i) in 4x4 blocks of pairs.  Lanes 0..479 take
-  // the 120 blocks strictly below the diagonal, four lanes per block (one
-  // quarter of the channels each), where exp(G_i - G_j) splits around the
-  // block's first row a0 as exp(G_i - G_a0) exp(G_a0 - G_j) (both <= 1):
-  // 8 exponentials per channel instead of 16.  Lanes 480..511 take the 16
-  // diagonal blocks, two lanes per block (channel halves), formed directly
-  // (j <= i only).  Partial sums are combined with register-only DPP moves.
+  // P (j < i) and Aqk (j <= i).  The six 16x16 tiles below the diagonal
+  // run on MFMA in waves 0-3 (tiles w and w + 4 in the order (1,0) (2,0)
+  // (2,1) (3,0) ...): with r the tile's first row, exp(G_i - G_j) =
+  // exp(G_i - G_r) exp(G_r - G_j), both <= 1, so P's tile is the product of
+  // k^_i exp(G_i - G_r) and k^_j exp(G_r - G_j) over the channels (Aqk's with
+  // q^_i), each lane forming its operand values from LDS; in k-step s of a
+  // 16-channel block, lane group g takes channel 4 s + g (rows 4 mod 64
+  // words apart, so the groups read disjoint banks).  The four diagonal
+  // tiles run on VALU in waves 4-7, in 4x4 blocks of pairs: lanes 256..351
+  // take the 24 blocks below their diagonals, four lanes per block (channel
+  // quarters), split around the block's first row a0 as above; lanes
+  // 384..511 take the 16 blocks on the diagonal, eight lanes per block
+  // (channel eighths), formed directly (j <= i only).  Partial sums are
+  // combined with register-only DPP moves.
   {
-    constexpr int kBelow = (C / 4) * (C / 4 - 1) / 2;   // 120
-    static_assert(4 * kBelow + 2 * (C / 4) == NTP, "lanes cover the lower triangle exactly");
-    const bool below = tid < 4 * kBelow;
-    int bi, bj, d_lo, d_hi;
-    if (below) {
-      tri_pair(tid >> 2, bi, bj);
-      ++bi;    // strictly lower: row block bi + 1 over column blocks 0 .. bi
-      d_lo = (KD / 4) * (tid & 3);
-      d_hi = d_lo + KD / 4;
-    } else {
-      bi = bj = (tid - 4 * kBelow) >> 1;
-      d_lo = (KD / 2) * (tid & 1);
-      d_hi = d_lo + KD / 2;
-    }
-    const int a0 = 4 * bi, b0 = 4 * bj;
-    float pk[4][4] = {}, pq[4][4] = {};
-    if (below) {
-      for (int d = d_lo; d < d_hi; d += 4) {
-        float4 gi[4], gj[4], ki[4], kj[4], qi[4];
+    if (tid < 256) {
+      const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gi[r] = lds4(sG + (a0 + r) * KP + d);
-          gj[r] = lds4(sG + (b0 + r) * KP + d);
-          ki[r] = lds4(sK + (a0 + r) * KP + d);
-          kj[r] = lds4(sK + (b0 + r) * KP + d);
-          qi[r] = lds4(sQ + (a0 + r) * KP + d);
-        }
-        float4 fr[4], fc[4];
+      for (int h = 0; h < 2; ++h) {
+        const int t = wave + 4 * h;
+        if (t < 6) {
+          int I, J;
+          tri_pair(t, I, J);
+          ++I;
+          const int r0 = 16 * I, i = r0 + l16, j = 16 * J + l16;
+          f32x4v ap = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+          for (int kb = 0; kb < KD; kb += 16)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          fr[r] = make_float4(ex2(gi[r].x - gi[0].x), ex2(gi[r].y - gi[0].y), ex2(gi[r].z - gi[0].z),
-                              ex2(gi[r].w - gi[0].w));
-          fc[r] = make_float4(ex2(gi[0].x - gj[r].x) * kj[r].x, ex2(gi[0].y - gj[r].y) * kj[r].y,
-                              ex2(gi[0].z - gj[r].z) * kj[r].z, ex2(gi[0].w - gj[r].w) * kj[r].w);
-        }
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int d = kb + 4 * s4 + lg;
+              const float gr = sG[r0 * KP + d];
+              const float fi = ex2(sG[i * KP + d] - gr);
+              const float bk = sK[j * KP + d] * ex2(gr - sG[j * KP + d]);
+              ap = mfma4(sK[i * KP + d] * fi, bk, ap);
+              aq = mfma4(sQ[i * KP + d] * fi, bk, aq);
+            }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 a = make_float4(ki[r].x * fr[r].x, ki[r].y * fr[r].y, ki[r].z * fr[r].z, ki[r].w * fr[r].w);
-          const float4 b = make_float4(qi[r].x * fr[r].x, qi[r].y * fr[r].y, qi[r].z * fr[r].z, qi[r].w * fr[r].w);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            pk[r][q] = fmaf(a.x, fc[q].x, fmaf(a.y, fc[q].y, fmaf(a.z, fc[q].z, fmaf(a.w, fc[q].w, pk[r][q]))));
-            pq[r][q] = fmaf(b.x, fc[q].x, fmaf(b.y, fc[q].y, fmaf(b.z, fc[q].z, fmaf(b.w, fc[q].w, pq[r][q]))));
+          for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 4 * lg + r;
+            sP[row * LQ + j] = ap[r];
+            rec[R_P + row * C + j] = ap[r];
+            rec[R_AQK + row * C + j] = kScale * aq[r];
           }
         }
       }
     } else {
-      for (int d = d_lo; d < d_hi; d += 4) {
-        float4 gi[4], ki[4], qi[4];
+      const int u = tid - 256;
+      const bool below = u < 96, diag = u >= 128;
+      int bi = 0, bj = 0, d_lo = 0, d_hi = 0;
+      if (below) {
+        tri_pair((u >> 2) % 6, bi, bj);
+        ++bi;
+        bi += 4 * ((u >> 2) / 6);
+        bj += 4 * ((u >> 2) / 6);
+        d_lo = (KD / 4) * (u & 3);
+        d_hi = d_lo + KD / 4;
+      } else if (diag) {
+        bi = bj = (u - 128) >> 3;
+        d_lo = (KD / 8) * (u & 7);
+        d_hi = d_lo + KD / 8;
+      }
+      const int a0 = 4 * bi, b0 = 4 * bj;
+      float pk[4][4] = {}, pq[4][4] = {};
+      if (below) {
+        for (int d = d_lo; d < d_hi; d += 4) {
+          float4 gi[4], gj[4], ki[4], kj[4], qi[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gi[r] = lds4(sG + (a0 + r) * KP + d);
-          ki[r] = lds4(sK + (a0 + r) * KP + d);
-          qi[r] = lds4(sQ + (a0 + r) * KP + d);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int q = 0; q <= r; ++q) {   // no positive exponent is formed
-            const float k0 = ki[q].x * ex2(gi[r].x - gi[q].x), k1 = ki[q].y * ex2(gi[r].y - gi[q].y);
-            const float k2 = ki[q].z * ex2(gi[r].z - gi[q].z), k3 = ki[q].w * ex2(gi[r].w - gi[q].w);
-            pk[r][q] = fmaf(ki[r].x, k0, fmaf(ki[r].y, k1, fmaf(ki[r].z, k2, fmaf(ki[r].w, k3, pk[r][q]))));
-            pq[r][q] = fmaf(qi[r].x, k0, fmaf(qi[r].y, k1, fmaf(qi[r].z, k2, fmaf(qi[r].w, k3, pq[r][q]))));
+          for (int r = 0; r < 4; ++r) {
+            gi[r] = lds4(sG + (a0 + r) * KP + d);
+            gj[r] = lds4(sG + (b0 + r) * KP + d);
+            ki[r] = lds4(sK + (a0 + r) * KP + d);
+            kj[r] = lds4(sK + (b0 + r) * KP + d);
+            qi[r] = lds4(sQ + (a0 + r) * KP + d);
           }
-      }
-    }
-    // Sum over the block's lanes: xor 1 everywhere, xor 2 only within the
-    // four-lane groups (the diagonal lanes' partner at xor 2 belongs to
-    // another block, so its value is not added there).
+          float4 fr[4], fc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r) {
+            fr[r] = make_float4(ex2(gi[r].x - gi[0].x), ex2(gi[r].y - gi[0].y), ex2(gi[r].z - gi[0].z),
+                                ex2(gi[r].w - gi[0].w));
+            fc[r] = make_float4(ex2(gi[0].x - gj[r].x) * kj[r].x, ex2(gi[0].y - gj[r].y) * kj[r].y,
+                                ex2(gi[0].z - gj[r].z) * kj[r].z, ex2(gi[0].w - gj[r].w) * kj[r].w);
+          }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pk[r][q])));
-        pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pq[r][q])));
-        const float pk2 = __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pk[r][q])));
-        const float pq2 = __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pq[r][q])));
-        if (below) {
-          pk[r][q] += pk2;
-          pq[r][q] += pq2;
+          for (int r = 0; r < 4; ++r) {
+            const float4 a = make_float4(ki[r].x * fr[r].x, ki[r].y * fr[r].y, ki[r].z * fr[r].z, ki[r].w * fr[r].w);
+            const float4 b = make_float4(qi[r].x * fr[r].x, qi[r].y * fr[r].y, qi[r].z * fr[r].z, qi[r].w * fr[r].w);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              pk[r][q] = fmaf(a.x, fc[q].x, fmaf(a.y, fc[q].y, fmaf(a.z, fc[q].z, fmaf(a.w, fc[q].w, pk[r][q]))));
+              pq[r][q] = fmaf(b.x, fc[q].x, fmaf(b.y, fc[q].y, fmaf(b.z, fc[q].z, fmaf(b.w, fc[q].w, pq[r][q]))));
+            }
+          }
+        }
+      } else if (diag) {
+        for (int d = d_lo; d < d_hi; d += 4) {
+          float4 gi[4], ki[4], qi[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            gi[r] = lds4(sG + (a0 + r) * KP + d);
+            ki[r] = lds4(sK + (a0 + r) * KP + d);
+            qi[r] = lds4(sQ + (a0 + r) * KP + d);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q = 0; q <= r; ++q) {   // no positive exponent is formed
+              const float k0 = ki[q].x * ex2(gi[r].x - gi[q].x), k1 = ki[q].y * ex2(gi[r].y - gi[q].y);
+              const float k2 = ki[q].z * ex2(gi[r].z - gi[q].z), k3 = ki[q].w * ex2(gi[r].w - gi[q].w);
+              pk[r][q] = fmaf(ki[r].x, k0, fmaf(ki[r].y, k1, fmaf(ki[r].z, k2, fmaf(ki[r].w, k3, pk[r][q]))));
+              pq[r][q] = fmaf(qi[r].x, k0, fmaf(qi[r].y, k1, fmaf(qi[r].z, k2, fmaf(qi[r].w, k3, pq[r][q]))));
+            }
         }
       }
-    if ((tid & (below ? 3 : 1)) == 0) {
+      // Sum over each block's lanes: xor 1 and xor 2 (four-lane groups),
+      // then the mirrored quad for the eight-lane groups of the diagonal.
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = a0 + r;
-        float pv[4], av[4];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int j = b0 + q;
-          pv[q] = j < i ? pk[r][q] : 0.0f;
-          av[q] = j <= i ? kScale * pq[r][q] : 0.0f;
+          pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pk[r][q])));
+          pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pq[r][q])));
+          pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pk[r][q])));
+          pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pq[r][q])));
+          const float pk4 = __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pk[r][q])));
+          const float pq4 = __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pq[r][q])));
+          if (diag) {
+            pk[r][q] += pk4;
+            pq[r][q] += pq4;
+          }
         }
-        const float4 p4 = make_float4(pv[0], pv[1], pv[2], pv[3]);
-        *reinterpret_cast<float4*>(sP + i * LQ + b0) = p4;
-        *reinterpret_cast<float4*>(rec + R_P + i * C + b0) = p4;
-        *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
+      if ((below && (u & 3) == 0) || (diag && (u & 7) == 0)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = a0 + r;
+          float pv[4], av[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = b0 + q;
+            pv[q] = j < i ? pk[r][q] : 0.0f;
+            av[q] = j <= i ? kScale * pq[r][q] : 0.0f;
+          }
+          const float4 p4 = make_float4(pv[0], pv[1], pv[2], pv[3]);
+          *reinterpret_cast<float4*>(sP + i * LQ + b0) = p4;
+          *reinterpret_cast<float4*>(rec + R_P + i * C + b0) = p4;
+          *reinterpret_cast<float4*>(rec + R_AQK + i * C + b0) = make_float4(av[0], av[1], av[2], av[3]);
+        }
       }
     }
-    // The 120 blocks above the diagonal are zero: one row of one block per
-    // lane.
+    // The 120 4x4 blocks above the diagonal are zero: one row of one block
+    // per lane.
+    constexpr int kBelow = (C / 4) * (C / 4 - 1) / 2;
     for (int t = tid; t < 4 * kBelow; t += NTP) {
       int ui, uj;
       tri_pair(t >> 2, uj, ui);
