@@ -344,67 +344,67 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   kda::lds_barrier();
 
   // P (j < i) and Aqk (j <= i).  The six 16x16 tiles below the diagonal
-  // run on MFMA in waves 0-3 (tiles w and w + 4 in the order (1,0) (2,0)
-  // (2,1) (3,0) ...): with r the tile's first row, exp(G_i - G_j) =
+  // run on MFMA in waves 0-2, two tiles each ((1,0) (3,2); (2,0) (2,1);
+  // (3,0) (3,1)): with r the first row of tile row I, exp(G_i - G_j) =
   // exp(G_i - G_r) exp(G_r - G_j), both <= 1, so P's tile is the product of
   // k^_i exp(G_i - G_r) and k^_j exp(G_r - G_j) over the channels (Aqk's with
-  // q^_i), each lane forming its operand values from LDS; in k-step s of a
-  // 16-channel block, lane group g takes channel 4 s + g (rows 4 mod 64
-  // words apart, so the groups read disjoint banks).  The four diagonal
-  // tiles run on VALU in waves 4-7, in 4x4 blocks of pairs: lanes 256..351
-  // take the 24 blocks below their diagonals, four lanes per block (channel
-  // quarters), split around the block's first row a0 as above; lanes
-  // 384..511 take the 16 blocks on the diagonal, eight lanes per block
-  // (channel eighths), formed directly (j <= i only).  Partial sums are
-  // combined with register-only DPP moves.
+  // q^_i), each lane forming its operand values from LDS (shared by the two
+  // tiles when they share I); in k-step s of a 16-channel block, lane group
+  // g takes channel 4 s + g (rows 4 mod 64 words apart, so the groups read
+  // disjoint banks).  The four diagonal tiles run on VALU in waves 3-7, in
+  // 4x4 blocks of pairs with eight lanes per block (channel eighths): lanes
+  // 192..383 take the 24 blocks below their diagonals, split around the
+  // block's first row a0 as above; lanes 384..511 take the 16 blocks on the
+  // diagonal, formed directly (j <= i only).  Partial sums are combined
+  // with register-only DPP moves.
   {
-    if (tid < 256) {
+    if (tid < 192) {
       const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = wave + 4 * h;
-        if (t < 6) {
-          int I, J;
-          tri_pair(t, I, J);
-          ++I;
-          const int r0 = 16 * I, i = r0 + l16, j = 16 * J + l16;
-          f32x4v ap = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+      const int I0 = wave == 0 ? 1 : wave + 1, J0 = 0;
+      const int I1 = wave == 0 ? 3 : wave + 1, J1 = wave == 0 ? 2 : 1;
+      const bool share = I0 == I1;
+      const int ra = 16 * I0, rb = 16 * I1;
+      f32x4v ap0 = {0.f, 0.f, 0.f, 0.f}, aq0 = ap0, ap1 = ap0, aq1 = ap0;
 #pragma unroll 2
-          for (int kb = 0; kb < KD; kb += 16)
+      for (int kb = 0; kb < KD; kb += 16)
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-              const int d = kb + 4 * s4 + lg;
-              const float gr = sG[r0 * KP + d];
-              const float fi = ex2(sG[i * KP + d] - gr);
-              const float bk = sK[j * KP + d] * ex2(gr - sG[j * KP + d]);
-              ap = mfma4(sK[i * KP + d] * fi, bk, ap);
-              aq = mfma4(sQ[i * KP + d] * fi, bk, aq);
-            }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = r0 + 4 * lg + r;
-            sP[row * LQ + j] = ap[r];
-            rec[R_P + row * C + j] = ap[r];
-            rec[R_AQK + row * C + j] = kScale * aq[r];
-          }
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int d = kb + 4 * s4 + lg;
+          const float ga = sG[ra * KP + d];
+          const float fa = ex2(sG[(ra + l16) * KP + d] - ga);
+          const float gb = share ? ga : sG[rb * KP + d];
+          const float fb = share ? fa : ex2(sG[(rb + l16) * KP + d] - gb);
+          const float b0 = sK[(16 * J0 + l16) * KP + d] * ex2(ga - sG[(16 * J0 + l16) * KP + d]);
+          const float b1 = sK[(16 * J1 + l16) * KP + d] * ex2(gb - sG[(16 * J1 + l16) * KP + d]);
+          ap0 = mfma4(sK[(ra + l16) * KP + d] * fa, b0, ap0);
+          aq0 = mfma4(sQ[(ra + l16) * KP + d] * fa, b0, aq0);
+          ap1 = mfma4(sK[(rb + l16) * KP + d] * fb, b1, ap1);
+          aq1 = mfma4(sQ[(rb + l16) * KP + d] * fb, b1, aq1);
         }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row0 = ra + 4 * lg + r, row1 = rb + 4 * lg + r;
+        const int j0 = 16 * J0 + l16, j1 = 16 * J1 + l16;
+        sP[row0 * LQ + j0] = ap0[r];
+        rec[R_P + row0 * C + j0] = ap0[r];
+        rec[R_AQK + row0 * C + j0] = kScale * aq0[r];
+        sP[row1 * LQ + j1] = ap1[r];
+        rec[R_P + row1 * C + j1] = ap1[r];
+        rec[R_AQK + row1 * C + j1] = kScale * aq1[r];
       }
     } else {
-      const int u = tid - 256;
-      const bool below = u < 96, diag = u >= 128;
-      int bi = 0, bj = 0, d_lo = 0, d_hi = 0;
+      const int u = tid - 192;
+      const bool below = u < 192, diag = !below;
+      int bi, bj;
       if (below) {
-        tri_pair((u >> 2) % 6, bi, bj);
+        tri_pair((u >> 3) % 6, bi, bj);
         ++bi;
-        bi += 4 * ((u >> 2) / 6);
-        bj += 4 * ((u >> 2) / 6);
-        d_lo = (KD / 4) * (u & 3);
-        d_hi = d_lo + KD / 4;
-      } else if (diag) {
-        bi = bj = (u - 128) >> 3;
-        d_lo = (KD / 8) * (u & 7);
-        d_hi = d_lo + KD / 8;
+        bi += 4 * ((u >> 3) / 6);
+        bj += 4 * ((u >> 3) / 6);
+      } else {
+        bi = bj = (u - 192) >> 3;
       }
+      const int d_lo = (KD / 8) * (u & 7), d_hi = d_lo + KD / 8;
       const int a0 = 4 * bi, b0 = 4 * bj;
       float pk[4][4] = {}, pq[4][4] = {};
       if (below) {
@@ -419,10 +419,12 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
             qi[r] = lds4(sQ + (a0 + r) * KP + d);
           }
           float4 fr[4], fc[4];
+          fr[0] = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            fr[r] = make_float4(ex2(gi[r].x - gi[0].x), ex2(gi[r].y - gi[0].y), ex2(gi[r].z - gi[0].z),
-                                ex2(gi[r].w - gi[0].w));
+            if (r > 0)
+              fr[r] = make_float4(ex2(gi[r].x - gi[0].x), ex2(gi[r].y - gi[0].y), ex2(gi[r].z - gi[0].z),
+                                  ex2(gi[r].w - gi[0].w));
             fc[r] = make_float4(ex2(gi[0].x - gj[r].x) * kj[r].x, ex2(gi[0].y - gj[r].y) * kj[r].y,
                                 ex2(gi[0].z - gj[r].z) * kj[r].z, ex2(gi[0].w - gj[r].w) * kj[r].w);
           }
@@ -457,8 +459,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
             }
         }
       }
-      // Sum over each block's lanes: xor 1 and xor 2 (four-lane groups),
-      // then the mirrored quad for the eight-lane groups of the diagonal.
+      // Sum over each block's eight lanes: neighbours, pairs, mirrored quads.
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -467,14 +468,10 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
           pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(pq[r][q])));
           pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pk[r][q])));
           pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(pq[r][q])));
-          const float pk4 = __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pk[r][q])));
-          const float pq4 = __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pq[r][q])));
-          if (diag) {
-            pk[r][q] += pk4;
-            pq[r][q] += pq4;
-          }
+          pk[r][q] += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pk[r][q])));
+          pq[r][q] += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(pq[r][q])));
         }
-      if ((below && (u & 3) == 0) || (diag && (u & 7) == 0)) {
+      if ((u & 7) == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = a0 + r;
