@@ -17,7 +17,8 @@
 // threads through global memory inside a kernel, and the plain barrier
 // would also wait for every outstanding global load and store.
 //
-// Everything runs in float32.  Five kernels, split where the method splits
+// Everything runs in float32.  Five kernels (four when every Q/K head has
+// one value head), split where the method splits
 // (chunk-local work is chunk-parallel, the carries are sequential per
 // (sequence, value head) and column-parallel, since column v of the state
 // only ever meets column v of the values):
@@ -26,7 +27,7 @@
 //   normalisation), G, P (L = diag(beta) P), Aqk, T = (I+L)^-1, A = T
 //   diag(beta), E = exp(G) k^, W = A E, U = A v, Qg, Kg, gamma = exp(G_last),
 //   written to the chunk's record in the workspace.
-// bwd_carry_fwd_kernel -- per (sequence, value head, 32 state columns), in
+// bwd_carry_fwd_kernel -- per (sequence, value head, 64 state columns), in
 //   chunk order: stores each chunk's entering state S (transposed) and
 //   Vnew = U - W S, then S = gamma S + Kg^T Vnew.
 // bwd_carry_rev_kernel -- same split, chunks in reverse, with dS' the
@@ -38,10 +39,12 @@
 //   dA = tril(dVnew v^T + dW E^T), dv = A^T dVnew, dE = A^T dW,
 //   dT = dA diag(beta), dL = -tril_strict(T^T dT T^T), dbeta from A and L,
 //   then the gated sums through P and Aqk, dq^, dk^ and dG, and dg as the
-//   reverse cumulative sum of dG within the chunk.
-// bwd_norm_kernel -- per (token, Q/K head): dq^, dk^ summed over the value
-//   heads that share the Q/K head (GQA), then through the L2 norm:
-//   dx = dy / n - x (x . dy) / n^3 with n^2 = sum(x*x) + 1e-6.
+//   reverse cumulative sum of dG within the chunk; with one value head per
+//   Q/K head, also the L2 norm's backward below on its own dq^ and dk^.
+// bwd_norm_kernel -- per (token, Q/K head), only when Q/K heads are shared
+//   (GQA): dq^, dk^ summed over the value heads that share the Q/K head,
+//   then through the L2 norm: dx = dy / n - x (x . dy) / n^3 with
+//   n^2 = sum(x*x) + 1e-6.
 //
 // Gated sums: with Gam_ij[d] = exp(G_id - G_jd) (j <= i, so <= 1 for
 // non-positive gates), Mk = diag(beta) dL and Mq = K^-1/2 dAqk,
@@ -1052,6 +1055,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   float* gdk = p.dkh + (t0 * p.HV + hv) * KD;
   const int64_t rs = int64_t(p.HV) * KD;     // token stride of gdq, gdk
   float* gdG = rec + R_U;                    // the record's U field is no longer read
+  const bool fused = p.H == p.HV;            // normalisation backward at the end of this kernel
 
   // ---- phase 1: dQg = dO S^T, dW = -dVnew S^T, dKg = Vnew dS'^T (on
   // MFMA), dgamma, then dAqk = tril(dO Vnew^T).  R0 = dO^T, R1 = Vnew^T,
@@ -1432,6 +1436,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   }
   kda::lds_barrier();
   float dgt[4][4];   // this tile's final dG (written to LDS once all of phase 3 is done)
+  float fk[4][4];    // this tile's final dk^
   {
     float gi[4][4];
 #pragma unroll
@@ -1596,12 +1601,9 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
         if (i == C - 1)
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) dgt[r][cc] += sGl[d0 + cc];
-        if (i < nv) {
-          float vk[4];
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) vk[cc] = yk[r][cc] + ck[r][cc] + cq[r][cc];
-          st4(gdk + i * rs + d0, vk);
-        }
+        for (int cc = 0; cc < 4; ++cc) fk[r][cc] = yk[r][cc] + ck[r][cc] + cq[r][cc];
+        if (i < nv && !fused) st4(gdk + i * rs + d0, fk[r]);
       }
     }
   }
@@ -1609,6 +1611,21 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   // (dG_last was added to the last row), in four 16-row blocks per column:
   // suffix sums within each block, then the totals of the later blocks.
   kda::lds_barrier();
+  // With one value head per Q/K head the normalisation's backward runs here
+  // too (below): this tile's raw q and k and its final dq^, loaded now.
+  uint2 xq[4], xk[4];
+  v4f fq[4];
+  if (fused) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r;
+      const bool ok = i < nv;
+      const int64_t xo = ((t0 + i) * p.H + hv) * KD + d0;
+      xq[r] = ok ? *reinterpret_cast<const uint2*>(p.q + xo) : make_uint2(0u, 0u);
+      xk[r] = ok ? *reinterpret_cast<const uint2*>(p.k + xo) : make_uint2(0u, 0u);
+      fq[r] = ok ? ldg4(gdq + i * rs + d0) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) st4(R0 + (i0 + r) * KP + d0, dgt[r]);
   kda::lds_barrier();
@@ -1630,6 +1647,45 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
   }
   if (tid < nv) p.dbeta[(t0 + tid) * p.HV + hv] = sDB[tid];
+  // Normalisation backward (one value head per Q/K head): for x the raw row,
+  // n = sqrt(sum x^2 + 1e-6), dx = dy / n - x (x . dy) / n^3; the sums over
+  // a row's 128 channels run across the 32 lanes that hold it.
+  if (fused) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float xqv[4] = {kda::bf16lo(xq[r].x), kda::bf16hi(xq[r].x), kda::bf16lo(xq[r].y), kda::bf16hi(xq[r].y)};
+      const float xkv[4] = {kda::bf16lo(xk[r].x), kda::bf16hi(xk[r].x), kda::bf16lo(xk[r].y), kda::bf16hi(xk[r].y)};
+      float sq = 0.f, dq_ = 0.f, sk = 0.f, dk_ = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        sq = fmaf(xqv[cc], xqv[cc], sq);
+        dq_ = fmaf(xqv[cc], fq[r][cc], dq_);
+        sk = fmaf(xkv[cc], xkv[cc], sk);
+        dk_ = fmaf(xkv[cc], fk[r][cc], dk_);
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) {
+        sq += __shfl_xor(sq, off, 32);
+        dq_ += __shfl_xor(dq_, off, 32);
+        sk += __shfl_xor(sk, off, 32);
+        dk_ += __shfl_xor(dk_, off, 32);
+      }
+      const int i = i0 + r;
+      if (i < nv) {
+        const float iq = 1.0f / sqrtf(sq + 1e-6f), ik = 1.0f / sqrtf(sk + 1e-6f);
+        const float cq3 = dq_ * iq * iq * iq, ck3 = dk_ * ik * ik * ik;
+        float oq[4], ok[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          oq[cc] = fq[r][cc] * iq - xqv[cc] * cq3;
+          ok[cc] = fk[r][cc] * ik - xkv[cc] * ck3;
+        }
+        const int64_t o = ((t0 + i) * p.H + hv) * KD + d0;
+        st4(p.dq + o, oq);
+        st4(p.dk + o, ok);
+      }
+    }
+  }
 }
 
 // --------------------------------------------------------------- norm
@@ -1773,6 +1829,7 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
   hipLaunchKernelGGL(bwd_grad_kernel, chunks, dim3(NTG), GRAD_LDS, s, p);
   st = kda::launch_status();
   if (st != KDA_OK) return st;
+  if (H == HV) return KDA_OK;   // the gradient kernel ran the normalisation backward
   const int64_t rows = 2 * tokens * H;
   hipLaunchKernelGGL(bwd_norm_kernel, dim3(unsigned((rows + NTB / 64 - 1) / (NTB / 64))), dim3(NTB), 0, s, p);
   return kda::launch_status();
