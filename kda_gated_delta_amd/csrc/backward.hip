@@ -620,7 +620,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
 // 64 cg .. 64 cg + 63, with 512 threads (two waves per SIMD).  Every
 // product runs on fp32 MFMA in 16x16 output tiles, several tiles per wave
 // sharing their A operand, with operands read from LDS layouts whose
-// 16-lane groups touch consecutive words.
+// 16-lane groups touch consecutive words; in k-step s of each 16-wide
+// block of the contraction, lane group g takes k = s + 4 g, so that with
+// row strides of 4 mod 64 words the four groups read disjoint banks.
 constexpr int SQ = NCOL + 4;      // LDS row stride of [rows][64-column] tiles
 constexpr int NTC = 512;          // threads per carry workgroup
 constexpr int FWD_LDS = (2 * KD * SQ + C * KP + C * SQ + KD) * 4;
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
         for (int r = 0; r < 4; ++r) acc[t][r] = sV[(16 * ib + 4 * lg + r) * SQ + 16 * (jb0 + t) + l16];
 #pragma unroll 4
       for (int ks = 0; ks < KD / 4; ++ks) {
-        const int d = 4 * ks + lg;
+        const int d = 16 * (ks >> 2) + (ks & 3) + 4 * lg;   // lane groups on disjoint banks
         const float a = -sWT[d * SQ + 16 * ib + l16];
         acc[0] = mfma4(a, sS[d * SQ + 16 * jb0 + l16], acc[0]);
         acc[1] = mfma4(a, sS[d * SQ + 16 * (jb0 + 1) + l16], acc[1]);
@@ -741,7 +743,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
         }
 #pragma unroll 4
       for (int ks = 0; ks < C / 4; ++ks) {
-        const int i = 4 * ks + lg;
+        const int i = 16 * (ks >> 2) + (ks & 3) + 4 * lg;
         const float a = sKg[i * KP + 16 * wave + l16];
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = mfma4(a, sV[i * SQ + 16 * t + l16], acc[t]);
@@ -852,14 +854,14 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
       f32x4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
       for (int ks = 4 * ib; ks < C / 4; ++ks) {
-        const int m = 4 * ks + lg;
+        const int m = 16 * (ks >> 2) + (ks & 3) + 4 * lg;
         const float a = sAqk[m * SQ + 16 * ib + l16];
         acc[0] = mfma4(a, sO[m * SQ + 16 * jb0 + l16], acc[0]);
         acc[1] = mfma4(a, sO[m * SQ + 16 * (jb0 + 1) + l16], acc[1]);
       }
 #pragma unroll 4
       for (int ks = 0; ks < KD / 4; ++ks) {
-        const int d = 4 * ks + lg;
+        const int d = 16 * (ks >> 2) + (ks & 3) + 4 * lg;   // lane groups on disjoint banks
         const float a = sKgT[d * SQ + 16 * ib + l16];
         acc[0] = mfma4(a, sD[d * SQ + 16 * jb0 + l16], acc[0]);
         acc[1] = mfma4(a, sD[d * SQ + 16 * (jb0 + 1) + l16], acc[1]);
@@ -902,7 +904,7 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
       kda::lds_barrier();
 #pragma unroll 2
       for (int ks = 0; ks < C / 8; ++ks) {
-        const int i = 4 * ks + lg;                 // row within the half
+        const int i = 16 * (ks >> 2) + (ks & 3) + 4 * lg;   // row within the half
         const int ig = h * (C / 2) + i;            // token
         const float aq = sQh[i * KP + 16 * wave + l16];
         const float aw = -sWh[i * KP + 16 * wave + l16];
