@@ -243,7 +243,8 @@ __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
 // 512 threads.  [C][128] results in 4x4 tiles (rows 4 (t / 32), columns
 // 4 (t % 32)); P and Aqk in 4x4 blocks of (i, j) pairs (below).
 constexpr int NTP = 512;
-constexpr int PREP_LDS = (3 * C * KP + 2 * C * LQ + C) * 4;
+constexpr int XS = 20;            // row stride of the T solve's [16][16] X tiles
+constexpr int PREP_LDS = (3 * C * KP + 2 * C * LQ + C + 3 * 16 * XS) * 4;
 
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   extern __shared__ __align__(16) float smem[];
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   float* sP = sG + C * KP;          // P [C][LQ]
   float* sAT = sP + C * LQ;         // A^T [C][LQ]
   float* sB = sAT + C * LQ;         // beta
+  float* sXs = sB + C;              // three [16][XS] tiles for the T solve
 
   const int64_t slot = blockIdx.x;
   const int hv = blockIdx.y;
@@ -508,43 +510,89 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
   }
   kda::lds_barrier();
 
-  // T = (I + diag(beta) P)^-1 by forward substitution over rows i: lanes
-  // 8j .. 8j+7 own column j, lane part holding T[8 part + m][j] (m < 8) in
-  // registers; row i's sum over the column is split by part and completed
-  // across the eight lanes with register-only DPP moves (neighbour swap,
-  // pair swap, half-row mirror).  (P is strictly lower and T starts at
-  // zero, so the sums need no bounds.)
+  // T = (I + L)^-1 with L = diag(beta) P (strictly lower), blocked by 16
+  // rows: the four diagonal blocks by forward substitution, then the blocks
+  // below one block diagonal at a time, T_IJ = -T_II X with
+  // X = diag(beta_I) sum_{J <= K < I} P_IK T_KJ, both products on MFMA.
+  // T is kept transposed in sAT; at the end it goes to the record as T and
+  // A = T diag(beta), and sAT is scaled to A^T.
   {
-    const int j = tid >> 3, part = tid & 7;
-    float tc[8];
+    // Diagonal blocks: lanes 8j .. 8j+7 own column j (block D = j / 16),
+    // lane part p holding the block's local rows 2p and 2p+1; row i's sum
+    // over the block's earlier rows is split by part and completed across
+    // the eight lanes with register-only DPP moves.  (P is strictly lower
+    // and T starts at zero, so the sums need no bounds.)
+    const int j = tid >> 3, part = tid & 7, rb = 16 * (j >> 4), jl = j & 15;
+    float t0v = 0.0f, t1v = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) tc[m] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const float4 pa = lds4(sP + i * LQ + 8 * part);
-      const float4 pb = lds4(sP + i * LQ + 8 * part + 4);
-      float acc0 = pa.x * tc[0], acc1 = pa.y * tc[1];
-      acc0 = fmaf(pa.z, tc[2], acc0);
-      acc1 = fmaf(pa.w, tc[3], acc1);
-      acc0 = fmaf(pb.x, tc[4], acc0);
-      acc1 = fmaf(pb.y, tc[5], acc1);
-      acc0 = fmaf(pb.z, tc[6], acc0);
-      acc1 = fmaf(pb.w, tc[7], acc1);
-      float acc = acc0 + acc1;
+    for (int i = 0; i < 16; ++i) {
+      const float2 pp = lds2(sP + (rb + i) * LQ + rb + 2 * part);
+      float acc = fmaf(pp.y, t1v, pp.x * t0v);
       acc += __uint_as_float(kda::dpp32<kda::kDppXor1>(__float_as_uint(acc)));
       acc += __uint_as_float(kda::dpp32<kda::kDppXor2>(__float_as_uint(acc)));
       acc += __uint_as_float(kda::dpp32<kda::kDppHalfMirror>(__float_as_uint(acc)));
-      const float tv = i == j ? 1.0f : -sB[i] * acc;
-      if (part == i / 8) tc[i % 8] = tv;
+      const float tv = i == jl ? 1.0f : -sB[rb + i] * acc;
+      if (part == (i >> 1)) {
+        if (i & 1)
+          t1v = tv;
+        else
+          t0v = tv;
+      }
     }
-    // T and A = T diag(beta) to the record; A^T to LDS.
-    const float bj = sB[j];
+    *reinterpret_cast<float2*>(sAT + j * LQ + rb + 2 * part) = make_float2(t0v, t1v);
+    for (int u = tid; u < C * C; u += NTP) {   // T above its diagonal blocks is zero
+      const int jj = u / C, ii = u - jj * C;
+      if ((ii >> 4) < (jj >> 4)) sAT[jj * LQ + ii] = 0.0f;
+    }
+    kda::lds_barrier();
+    // Blocks (J + lev, J): wave J takes one.  X's k-step s of a 16-block
+    // takes k = 4 s + g in lane group g (P rows and T^T rows are read along
+    // k); T_II X's takes k = s + 4 g (T^T and X read across k).  Either way
+    // the four groups read disjoint banks.
+    const int wave = tid >> 6, lg = (tid >> 4) & 3, l16 = tid & 15;
+    for (int lev = 1; lev < 4; ++lev) {
+      const bool act = wave < 4 - lev;
+      const int J = wave, I = wave + lev;
+      if (act) {
+        f32x4v x = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 16 * J; kb < 16 * I; kb += 16)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int i = 8 * part + m;
-      rec[R_T + i * C + j] = tc[m];
-      rec[R_A + i * C + j] = tc[m] * bj;
-      sAT[j * LQ + i] = tc[m] * bj;
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int k = kb + 4 * s4 + lg;
+            x = mfma4(sP[(16 * I + l16) * LQ + k], sAT[(16 * J + l16) * LQ + k], x);
+          }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sXs[(16 * J + 4 * lg + r) * XS + l16] = sB[16 * I + 4 * lg + r] * x[r];
+      }
+      kda::lds_barrier();
+      if (act) {
+        f32x4v y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int k = s4 + 4 * lg;
+          y = mfma4(sAT[(16 * I + k) * LQ + 16 * I + l16], sXs[(16 * J + k) * XS + l16], y);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sAT[(16 * J + l16) * LQ + 16 * I + 4 * lg + r] = -y[r];
+      }
+      kda::lds_barrier();
+    }
+    // T and A = T diag(beta) to the record, row by row from T^T.
+    {
+      const int i = tid >> 3, j8 = 8 * (tid & 7);
+      float tv[8], av[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tv[e] = sAT[(j8 + e) * LQ + i];
+        av[e] = tv[e] * sB[j8 + e];
+      }
+      st8(rec + R_T + i * C + j8, tv);
+      st8(rec + R_A + i * C + j8, av);
+    }
+    kda::lds_barrier();
+    for (int u = tid; u < C * C; u += NTP) {   // A^T = diag(beta) T^T
+      const int jj = u / C, ii = u - jj * C;
+      sAT[jj * LQ + ii] *= sB[jj];
     }
   }
   if (tid < KD) rec[R_GAM + tid] = ex2(sG[(C - 1) * KP + tid]);
