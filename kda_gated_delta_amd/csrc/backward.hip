@@ -76,9 +76,9 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // Per-chunk record in the workspace (float offsets), one per (value head,
 // chunk slot), slots numbered as in the forward: chunk c of sequence n is
 // slot floor(first_token(n) / 64) + n + c.
-constexpr int R_QN = 0;                     // [C][K] q^ (bf16 values)
-constexpr int R_KN = R_QN + C * KD;         // [C][K] k^
-constexpr int R_G = R_KN + C * KD;          // [C][K] G log2(e), G the inclusive prefix of g
+constexpr int R_QN = 0;                     // [C][K] q^ as bf16 (two per float slot)
+constexpr int R_KN = R_QN + C * KD / 2;     // [C][K] k^ as bf16
+constexpr int R_G = R_KN + C * KD / 2;      // [C][K] G log2(e), G the inclusive prefix of g
 constexpr int R_E = R_G + C * KD;           // [C][K] exp(G) k^
 constexpr int R_W = R_E + C * KD;           // [C][K] A E
 constexpr int R_U = R_W + C * KD;           // [C][V] A v
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
       f[2 * e + 1] = kda::bf16hi(w[e]);
     }
     st8((isk ? sK : sQ) + tr * KP + 8 * l16, f);
-    st8(rec + (isk ? R_KN : R_QN) + tr * KD + 8 * l16, f);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(rec + (isk ? R_KN : R_QN)) + tr * KD + 8 * l16) = y;
   }
   // G: inclusive prefix of g over the chunk's tokens (padding has g = 0),
   // kept in log2 units: prefixes within four 16-row blocks per channel,
@@ -1411,12 +1411,13 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   }
   kda::lds_barrier();
   // Phase 3's operands (G, k^, q^), loaded while dbeta, X and dL run.
-  v4f pg3[4], pk3[4], pq3[4];
+  v4f pg3[4];
+  uint2 pk3[4], pq3[4];   // bf16 k^ and q^, four per piece
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     pg3[k] = ldg4(rec + R_G + 4 * (tid + NTG * k));
-    pk3[k] = ldg4(rec + R_KN + 4 * (tid + NTG * k));
-    pq3[k] = ldg4(rec + R_QN + 4 * (tid + NTG * k));
+    pk3[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(rec + R_KN) + 4 * (tid + NTG * k));
+    pq3[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(rec + R_QN) + 4 * (tid + NTG * k));
   }
   // dT^T and T^T (R2 and R3 are free: dv and dE are done) and P.
   float* sDTT = R2;
@@ -1481,8 +1482,8 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   for (int k = 0; k < 4; ++k) {
     const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
     sts4(R0 + row * KP + 4 * c4, pg3[k]);
-    sts4(R2 + row * KP + 4 * c4, pk3[k]);
-    sts4(R3 + row * KP + 4 * c4, pq3[k]);
+    sts4(R2 + row * KP + 4 * c4, v4f{kda::bf16lo(pk3[k].x), kda::bf16hi(pk3[k].x), kda::bf16lo(pk3[k].y), kda::bf16hi(pk3[k].y)});
+    sts4(R3 + row * KP + 4 * c4, v4f{kda::bf16lo(pq3[k].x), kda::bf16hi(pq3[k].x), kda::bf16lo(pq3[k].y), kda::bf16hi(pq3[k].y)});
   }
   kda::lds_barrier();
   float dgt[4][4];   // this tile's final dG (written to LDS once all of phase 3 is done)
