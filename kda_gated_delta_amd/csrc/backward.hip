@@ -90,8 +90,7 @@ constexpr int R_T = R_AQK + C * C;          // [C][C] (I + diag(beta) P)^-1
 constexpr int R_A = R_T + C * C;            // [C][C] T diag(beta)
 constexpr int R_GAM = R_A + C * C;          // [K] exp(G_last)
 constexpr int R_ST = R_GAM + KD;            // [V][K] entering state, transposed
-constexpr int R_VN = R_ST + KD * KD;        // [C][V] Vnew
-constexpr int R_DST = R_VN + C * KD;        // [V][K] gradient of the exiting state, transposed
+constexpr int R_DST = R_ST + KD * KD;       // [V][K] gradient of the exiting state, transposed
 constexpr int R_DVN = R_DST + KD * KD;      // [C][V] dVnew
 constexpr int R_WT = R_DVN + C * KD;        // [K][C] W transposed
 constexpr int R_KGT = R_WT + KD * C;        // [K][C] Kg transposed
@@ -772,7 +771,6 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ib + 4 * lg + r;
           sV[i * SQ + j] = acc[t][r];
-          rec[R_VN + i * KD + c0 + j] = acc[t][r];
         }
         *reinterpret_cast<f32x4v*>(rec + R_VNT + (c0 + j) * C + 16 * ib + 4 * lg) = acc[t];
       }
