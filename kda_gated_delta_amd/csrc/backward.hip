@@ -211,15 +211,6 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
 
 __device__ __forceinline__ float2 lds2(const float* p) { return *reinterpret_cast<const float2*>(p); }
 
-// acc[2][4] += a[2] (x) b[4].
-__device__ __forceinline__ void fma2x4(float (*acc)[4], const float2 a, const float4 b, float sign = 1.0f) {
-  const float av[2] = {sign * a.x, sign * a.y};
-  const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-}
 
 __device__ __forceinline__ void ld4(const float* p, float* v) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -979,9 +970,10 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
 // 512 threads (two waves per SIMD: the LDS footprint allows one workgroup
 // per compute unit, and the second wave hides the first one's latency).
 // Every [C][128] quantity is owned in 4x4 tiles: thread t holds rows
-// 4 (t / 32) .. +3 and columns 4 (t % 32) .. +3; [C][C] products use 2x4
-// tiles (rows 2 (t / 16) .. +1, columns 4 (t % 16) .. +3).  dq^, dk^ and dG
-// accumulate in memory only the owning thread touches.  LDS holds three
+// 4 (t / 32) .. +3 and columns 4 (t % 32) .. +3; the dense products run on
+// fp32 MFMA in 16x16 tiles and come back to those 4x4 tiles through LDS
+// where elementwise work follows.  dq^, dk^ and dG accumulate in memory
+// only the owning thread touches.  LDS holds three
 // [128][68] regions (R0-R2), one [64][132] region (R3) and one [64][68]
 // region (R4); what each holds changes by phase (below).
 constexpr int NTG = 512;
@@ -1098,7 +1090,6 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   const int tid = threadIdx.x;
   const int rb = tid >> 5;
   const int i0 = 4 * rb, d0 = 4 * (tid & 31);          // 4x4 tile of a [C][128] quantity
-  const int s0r = 2 * (tid >> 4), s0c = 4 * (tid & 15);  // 2x4 tile of a [C][C] product
   float* gdq = p.dqh + (t0 * p.HV + hv) * KD;
   float* gdk = p.dkh + (t0 * p.HV + hv) * KD;
   const int64_t rs = int64_t(p.HV) * KD;     // token stride of gdq, gdk
