@@ -89,8 +89,8 @@ constexpr int R_AQK = R_P + C * C;          // [C][C] Aqk (j <= i)
 constexpr int R_T = R_AQK + C * C;          // [C][C] (I + diag(beta) P)^-1
 constexpr int R_A = R_T + C * C;            // [C][C] T diag(beta)
 constexpr int R_GAM = R_A + C * C;          // [K] exp(G_last)
-constexpr int R_ST = R_GAM + KD;            // [V][K] entering state, transposed
-constexpr int R_DST = R_ST + KD * KD;       // [V][K] gradient of the exiting state, transposed
+constexpr int R_ST = R_GAM + KD;            // [K][V] entering state
+constexpr int R_DST = R_ST + KD * KD;       // [K][V] gradient of the exiting state
 constexpr int R_DVN = R_DST + KD * KD;      // [C][V] dVnew
 constexpr int R_WT = R_DVN + C * KD;        // [K][C] W transposed
 constexpr int R_KGT = R_WT + KD * C;        // [K][C] Kg transposed
@@ -717,10 +717,11 @@ __global__ __launch_bounds__(NTC) void bwd_carry_fwd_kernel(BParams p) {
 
   for (int c = 0; c < nch; ++c) {
     float* rec = record(p, hv, sb + c);
-    // Entering state, transposed: ST[v][d] for this group's columns v.
-    for (int t = tid; t < NCOL * KD; t += NTC) {
-      const int vv = t / KD, d = t - vv * KD;
-      rec[R_ST + (c0 + vv) * KD + d] = sS[d * SQ + vv];
+    // Entering state, this group's columns, 16 bytes per store.
+#pragma unroll
+    for (int k = 0; k < KD * NCOL / 4 / NTC; ++k) {
+      const int u = tid + NTC * k, d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
+      *reinterpret_cast<float4*>(rec + R_ST + d * KD + c0 + 4 * c4) = lds4(sS + d * SQ + 4 * c4);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -855,9 +856,10 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
     const int nv = min(C, len - c * C);
     const int cn = max(c - 1, 0);     // next step (the first chunk re-reads its own)
     const float* recn = record(p, hv, sb + cn);
-    for (int t = tid; t < NCOL * KD; t += NTC) {
-      const int vv = t / KD, d = t - vv * KD;
-      rec[R_DST + (c0 + vv) * KD + d] = sD[d * SQ + vv];
+#pragma unroll
+    for (int k = 0; k < KD * NCOL / 4 / NTC; ++k) {   // dS', this group's columns
+      const int u = tid + NTC * k, d = u / (NCOL / 4), c4 = u - d * (NCOL / 4);
+      *reinterpret_cast<float4*>(rec + R_DST + d * KD + c0 + 4 * c4) = lds4(sD + d * SQ + 4 * c4);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1104,13 +1106,16 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   // 2 (w / 2) .. +1 (16x16 each) of all three products.  In k-step s of a
   // 16-row block of v, lane group g takes v = s + 4 g: the operand rows'
   // strides are 4 mod 64 words, so the four groups read disjoint banks.
+  // Block vb of S and dS' is their columns 32 vb .. +31 (stored [K][V]),
+  // transposed into R3 as it is staged: thread piece u is row d = u / 8,
+  // columns 4 (u % 8) .. +3 of the block.
   v4f pst[2], pdst[2];
   auto fetch_blk = [&](int vb) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
-      pst[k] = ldg4(rec + R_ST + (32 * vb + row) * KD + 4 * c4);
-      pdst[k] = ldg4(rec + R_DST + (32 * vb + row) * KD + 4 * c4);
+      const int u = tid + NTG * k, d = u >> 3, c4 = u & 7;
+      pst[k] = ldg4(rec + R_ST + d * KD + 32 * vb + 4 * c4);
+      pdst[k] = ldg4(rec + R_DST + d * KD + 32 * vb + 4 * c4);
     }
   };
   // Every load of the prologue is issued before the first is used: dO
@@ -1161,9 +1166,12 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   for (int vb = 0; vb < KD / 32; ++vb) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
-      sts4(R3 + row * KP + 4 * c4, pst[k]);
-      sts4(R3 + (32 + row) * KP + 4 * c4, pdst[k]);
+      const int u = tid + NTG * k, d = u >> 3, c4 = u & 7;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        R3[(4 * c4 + e) * KP + d] = pst[k][e];
+        R3[(32 + 4 * c4 + e) * KP + d] = pdst[k][e];
+      }
     }
     kda::lds_barrier();
     if (vb + 1 < KD / 32) fetch_blk(vb + 1);
