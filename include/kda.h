@@ -314,8 +314,8 @@ int kda_chunk_backward(const void* q, const void* k, const void* v,
 /*
  * kda_chunk_backward_workspace_size -- bytes of workspace kda_chunk_backward
  * needs (num_seqs as for kda_chunk_prefill; 0 when cu_seqlens is NULL);
- * 0 for sizes it rejects.  About 10.8 KB per token and value head: one
- * 623,104-byte record per 64-token chunk slot (floor(B*T/64) + N + 1
+ * 0 for sizes it rejects.  About 10.2 KB per token and value head: one
+ * 590,336-byte record per 64-token chunk slot (floor(B*T/64) + N + 1
  * slots per value head) plus 1 KB per token and value head for the
  * per-value-head q and k gradients before the GQA sum.
  */

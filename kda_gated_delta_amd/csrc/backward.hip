@@ -91,8 +91,7 @@ constexpr int R_A = R_T + C * C;            // [C][C] T diag(beta)
 constexpr int R_GAM = R_A + C * C;          // [K] exp(G_last)
 constexpr int R_ST = R_GAM + KD;            // [K][V] entering state
 constexpr int R_DST = R_ST + KD * KD;       // [K][V] gradient of the exiting state
-constexpr int R_DVN = R_DST + KD * KD;      // [C][V] dVnew
-constexpr int R_WT = R_DVN + C * KD;        // [K][C] W transposed
+constexpr int R_WT = R_DST + KD * KD;       // [K][C] W transposed
 constexpr int R_KGT = R_WT + KD * C;        // [K][C] Kg transposed
 constexpr int R_ET = R_KGT + KD * C;        // [K][C] E transposed
 constexpr int R_VNT = R_ET + KD * C;        // [V][C] Vnew transposed
@@ -912,7 +911,6 @@ __global__ __launch_bounds__(NTC) void bwd_carry_rev_kernel(BParams p) {
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ib + 4 * lg + r;
           sV[i * SQ + j] = acc[t][r];
-          rec[R_DVN + i * KD + c0 + j] = acc[t][r];
         }
         *reinterpret_cast<f32x4v*>(rec + R_DVNT + (c0 + j) * C + 16 * ib + 4 * lg) = acc[t];
       }
@@ -1330,7 +1328,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     pp[k] = ldg4(rec + R_P + 4 * (tid + NTG * k));
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) pdv[k] = ldg4(rec + R_DVN + 4 * (tid + NTG * k));
+  for (int k = 0; k < 4; ++k) pdv[k] = ldg4(rec + R_DVNT + 4 * (tid + NTG * k));   // dVnew^T [V][C]
   kda::lds_barrier();
   tri_mfma(da, R0, R1, LQ, KD, wave, lg, l16);
   kda::lds_barrier();
@@ -1346,9 +1344,10 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     sts4(sT + row * LQ + 4 * c4, ptt[k]);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int u = tid + NTG * k, row = u / (KD / 4), c4 = u - row * (KD / 4);
-    sts4(R2 + row * KP + 4 * c4, pdv[k]);
+  for (int k = 0; k < 4; ++k) {   // dVnew [C][K] from its transpose: piece u is row v = u / 16, tokens 4 (u % 16) ..
+    const int u = tid + NTG * k, v = u / (C / 4), c4 = u - v * (C / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R2[(4 * c4 + e) * KP + v] = pdv[k][e];
   }
   tri_store(sDA, LQ, da, wave, lg, l16, tid);
   kda::lds_barrier();

@@ -203,7 +203,7 @@ def test_backward_metadata_errors():
 
 def test_backward_workspace_size_formula():
     lib = kda.load()
-    rec = 155776 * 4     # record per chunk slot (float32, q^ and k^ as bf16)
+    rec = 147584 * 4     # record per chunk slot (float32, q^ and k^ as bf16)
     # floor(B*T/64) + N + 1 slots per value head, plus two float32 [tokens, HV, 128] buffers
     assert lib.kda_chunk_backward_workspace_size(1, 8192, 96, 96, 128, 128, 0) == \
         (128 + 1 + 1) * 96 * rec + 8192 * 96 * 128 * 4 * 2
