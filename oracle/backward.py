@@ -12,7 +12,7 @@ Definition.  With upstream gradients do (shape of o) and dht (shape of
 final_state), the gradients are those of the scalar
     sum(o * do) + sum(final_state * dht)
 through the same recurrence as recurrent.recurrent, in float64.  Reading
-(listed in the design doc): the normalised q^, k^ enter the recurrence rounded to
+(the page gives no backward formula): the normalised q^, k^ enter the recurrence rounded to
 bf16 exactly as in the forward, and the rounding passes gradients through
 unchanged (its derivative is taken as the identity), so dq and dk are the
 gradients of the unrounded x / sqrt(sum(x*x) + 1e-6).  The pins in

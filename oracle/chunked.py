@@ -1,30 +1,44 @@
-"""Chunk construction of the KDA recurrence in float64 (oracle form 2).
+"""Chunk-parallel form of the KDA recurrence in float64 (oracle form 2).
 
 TEST INFRASTRUCTURE ONLY -- see the package docstring.
 
-Source: "KDA Chunk Prefill on Ascend A3", section "Mathematical definition",
-the equivalent construction for a chunk of C tokens (zero-based indices,
-ordered by token position), for one value head:
+Source: "KDA Chunk Prefill on Ascend A3", section "Mathematical definition".
+The page states the token recurrence and says an equivalent chunk-local
+construction with an inter-chunk state carry computes the same result; the
+golden uses 64-token chunks with the last partial chunk zero-padded (q, k, v,
+g and beta all zero), the output trimmed and the state kept.  This module
+does not restate the page's construction.  It derives the chunk form afresh
+from the recurrence, as follows, and computes it that way.
 
-    G_i     = sum_{u <= i} g_u                                (per channel)
-    L_ij    = beta_i * sum_d k_id k_jd exp(G_id - G_jd)   for j <  i, else 0
-    A       = solve(I + L, diag(beta))
-    W       = A @ (exp(G) * k)
-    U       = A @ v
-    Qg_i    = K**-0.5 * q_i * exp(G_i)
-    Kg_i    = k_i * exp(G_last - G_i)
-    Aqk_ij  = K**-0.5 * sum_d q_id k_jd exp(G_id - G_jd)  for j <= i, else 0
-    Vnew    = U - W @ S_in
-    O       = Qg @ S_in + Aqk @ Vnew
-    S_out   = exp(G_last)[:, None] * S_in + Kg^T @ Vnew
+Derivation (one value head; state S is [K, V]; inside a chunk the tokens are
+numbered 1..C and S_0 is the state entering the chunk).  A token first
+decays every key row of the state by exp(g_t) and then writes the rank-one
+correction k_t u_t^T, where the "write" u_t = beta_t (v_t - k_t^T S') is the
+delta-rule residual against the decayed state S'.  Let P_t be the running
+per-channel decay exp(g_1 + ... + g_t) (a diagonal matrix).  Unrolling the
+recurrence,
 
-The page's golden uses C = 64 and zero-pads q, k, v, g and beta of the last
-partial chunk, trims the output and keeps the state.  This module follows
-that, with C a parameter.  It shares nothing with ``recurrent`` except the
-L2 normalisation, so agreement between the two pins both.
+    state before token i's write = P_i S_0 + sum_{j<i} P_i P_j^-1 k_j u_j^T
 
-The exponent differences G_i - G_j are formed only where j <= i (masked to
--inf elsewhere before exp), so no positive exponent is ever evaluated.
+(the product P_i P_j^-1 = exp(sum of g over tokens j+1..i) is at most 1, so
+it is evaluated as one exponential of that partial sum, never as a ratio).
+Substituting into the definition of u_i gives a unit lower-triangular system
+for the writes of the whole chunk,
+
+    u_i + beta_i sum_{j<i} M_ij u_j = beta_i (v_i - (P_i k_i)^T S_0),
+    M_ij = sum_d k_id k_jd exp(G_id - G_jd),  G = running sum of g,
+
+which is solved here by explicit forward substitution, one token at a time.
+The outputs and the exiting state then follow from the same unrolling:
+
+    o_i   = K^-1/2 [ (P_i q_i)^T S_0 + sum_{j<=i} N_ij u_j ],
+            N_ij = sum_d q_id k_jd exp(G_id - G_jd)
+    S_out = P_C S_0 + sum_j (P_C P_j^-1 k_j) u_j^T.
+
+Nothing here is shared with ``recurrent`` except the L2 normalisation and
+the sequence segmentation, so agreement between the two pins both.  The
+exponent differences are formed only for j <= i (masked to -inf before the
+exponential), so no positive exponent is ever evaluated.
 """
 
 import numpy as np
@@ -33,34 +47,29 @@ from .l2norm import l2norm_bf16
 from .recurrent import _segments
 
 
-def _chunk(qc, kc, vc, gc, bc, S, scale):
-    """One chunk for all heads. qc,kc,gc [C,HV,K]; vc [C,HV,V]; bc [C,HV];
-    S [HV,K,V].  Returns (O [C,HV,V], S_out)."""
+def _chunk(qc, kc, vc, gc, bc, S0, scale):
+    """One chunk for all value heads.  qc, kc, gc [C,HV,K]; vc [C,HV,V];
+    bc [C,HV]; S0 [HV,K,V].  Returns (o [C,HV,V], S_out [HV,K,V])."""
     C = qc.shape[0]
-    G = np.cumsum(gc, axis=0)                                  # [C,HV,K]
-    diff = G[:, None] - G[None, :]                             # [i,j,HV,K]
-    lower_incl = np.tril(np.ones((C, C), dtype=bool))          # j <= i
-    lower_strict = np.tril(np.ones((C, C), dtype=bool), -1)    # j <  i
-    E = np.exp(np.where(lower_incl[:, :, None, None], diff, -np.inf))
-    kk = np.einsum("ihd,jhd,ijhd->hij", kc, kc, E)
-    qk = np.einsum("ihd,jhd,ijhd->hij", qc, kc, E)
-    L = np.where(lower_strict[None], bc.T[:, :, None] * kk, 0.0)   # [HV,i,j]
-    Aqk = np.where(lower_incl[None], scale * qk, 0.0)
-    eye = np.eye(C)[None]
-    A = np.linalg.solve(eye + L, eye * bc.T[:, None, :])      # solve(I+L, diag(beta))
-    eG = np.exp(G).transpose(1, 0, 2)                          # [HV,C,K]
-    kT = kc.transpose(1, 0, 2)
-    qT = qc.transpose(1, 0, 2)
-    vT = vc.transpose(1, 0, 2)
-    W = A @ (eG * kT)
-    U = A @ vT
-    Qg = scale * qT * eG
-    Glast = G[-1]                                              # [HV,K]
-    Kg = kT * np.exp(Glast[:, None, :] - G.transpose(1, 0, 2))
-    Vnew = U - W @ S
-    O = Qg @ S + Aqk @ Vnew
-    S_out = np.exp(Glast)[:, :, None] * S + Kg.transpose(0, 2, 1) @ Vnew
-    return O.transpose(1, 0, 2), S_out
+    G = np.cumsum(gc, axis=0)                                    # running log-decay [C,HV,K]
+    incl = np.tril(np.ones((C, C), dtype=bool))                  # j <= i
+    # pair decay exp(G_i - G_j) per channel, only where j <= i
+    dec = np.exp(np.where(incl[:, :, None, None], G[:, None] - G[None, :], -np.inf))   # [i,j,HV,K]
+    M = np.einsum("ihd,jhd,ijhd->hij", kc, kc, dec)             # key-key decayed overlaps
+    N = np.einsum("ihd,jhd,ijhd->hij", qc, kc, dec)             # query-key decayed overlaps
+    P = np.exp(G)                                                # decay since the chunk start
+    # right-hand side: the residual of each token against the decayed entering state
+    rhs = bc[:, :, None] * (vc - np.einsum("ihk,hkv->ihv", P * kc, S0))   # [C,HV,V]
+    # forward substitution for the writes u
+    u = np.zeros_like(rhs)
+    for i in range(C):
+        acc = np.einsum("hj,jhv->hv", M[:, i, :i], u[:i]) if i else 0.0
+        u[i] = rhs[i] - bc[i][:, None] * acc
+    o = scale * (np.einsum("ihk,hkv->ihv", P * qc, S0) + np.einsum("hij,jhv->ihv", N, u))
+    # exiting state: decayed entering state plus every write, decayed to the chunk end
+    tail = np.exp(G[-1][None] - G)                               # [C,HV,K], each <= 1
+    S_out = P[-1][:, :, None] * S0 + np.einsum("jhk,jhv->hkv", tail * kc, u)
+    return o, S_out
 
 
 def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, C=64, normalize=True):

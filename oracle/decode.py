@@ -12,7 +12,7 @@ Sources:
   * "KDA Chunk Prefill on Ascend A3", section "Mathematical definition":
     the recurrent step itself and the Q/K normalisation.
 
-Readings (listed in the design doc): the pool's axes are [slot, HV, K, V] with V
+Readings where the pages are silent: the pool's axes are [slot, HV, K, V] with V
 innermost (the same [K, V] orientation as the prefill state); o is formed
 from the unrounded updated state, and the stored state is that state
 rounded once to bf16 (nearest, ties to even).  The decode front-end of the

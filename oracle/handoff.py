@@ -10,7 +10,7 @@ Sources:
     decode keeps states in a bf16 pool [slots, HV, K, V], addressed by an
     int32 slot index per row, -1 meaning no state access.
 
-Reading (listed in the design doc): handing a state to the decode stores it in
+Reading (the pages are silent here): handing a state to the decode stores it in
 its slot rounded once to bf16, nearest-even -- the rounding the decode
 itself applies when it writes a slot back.  An index outside
 [0, slots) skips its state.

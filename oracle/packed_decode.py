@@ -12,7 +12,7 @@ sigmoid on beta, and one recurrent step against the bf16 state pool (the
 step of decode.decode_step).  Shapes: mixed_qkv [B, 3*H*K] (rows may be
 padded), raw_gate [B, H*K], raw_beta [B, H], A_log [H], dt_bias [H*K].
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * the packed row is q | k | v, each [H, K] head-major;
   * the gate is g = lower_bound * sigmoid(exp(A_log[h]) * (raw_gate + dt_bias)).
     The page names the transform, its parameters and lower_bound = -5 but

@@ -3,20 +3,19 @@
 TEST INFRASTRUCTURE ONLY -- see the package docstring.
 
 Source: "KDA Chunk Prefill on Ascend A3", section "Mathematical definition",
-the recurrent semantics for one batch row and one value head, with the state
-S shaped [K, V]:
-
-    S_decay = exp(g_t)[:, None] * S_prev          (per-key-channel decay)
-    r_t     = v_t - k_t^T S_decay                 (delta-rule residual)
-    S_t     = S_decay + beta_t * k_t r_t^T        (rank-one write)
-    o_t     = (K**-0.5 * q_t)^T S_t
+the recurrent semantics for one batch row and one value head with a [K, V]
+state.  Each token first multiplies key row d of the state by exp(g_t[d]);
+it then measures the residual between its value and what the decayed state
+already returns for its key, and adds the outer product of the key with
+beta_t times that residual (the delta-rule write); its output is the scaled
+query (K**-0.5 q_t) read against the updated state.
 
 q and k enter already L2-normalised and rounded to bfloat16 (section
 "Mathematical definition": the normalised bf16 values are widened for the
 rest of the computation).  Section "Function and tensor contract": value
 head h reads Q/K head h // (HV // H).
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
   * g is [B, T, HV, K] and beta is [B, T, HV]: the gate and the write
     strength belong to the value head whose state they act on.
   * cu_seqlens (int [N+1], B == 1) packs N independent sequences along T,

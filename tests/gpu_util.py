@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-# Tolerances (spec parity bar, written here so every test uses the same):
+# Tolerances (the parity bar of the forward path, written here so every test uses the same):
 #   o:            |o_gpu - o_ref| <= 1e-2 * max(1, |o_ref|) elementwise
 #   final state:  ||S_gpu - S_ref||_F / ||S_ref||_F <= 1e-3 per (sequence, head);
 #                 an all-zero reference requires an exactly zero result
