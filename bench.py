@@ -9,22 +9,31 @@ pool's slots from the 256 MB last-level cache between decode calls, so the
 decode runs cache-cold.
 
 Prints one JSON line:
-  value        prefill tokens/s (T / mean prefill kernel time)
+  value        prefill tokens/s (T / mean prefill call time by HIP events)
   roofline     the prefill entry point -- its two kernels, intra_kernel then
                inter_kernel, timed together by HIP events on the launch
                stream -- against the HBM roofline: algorithmic bytes per
                call / mean call time.  traffic is the measured HBM bytes per
                call from the committed rocprofv3 counter summary when that
                was taken on the current kernel source, else null
+  prefill, decode  event statistics (mean, p10, median, p90), the device
+               kernel durations from the torch profiler's GPU trace (no
+               launch gaps), and the same calls after a 1 GiB cache flush
+  configs      the other workloads (the small prefills, the varlen GQA
+               batch, decode at B = 1, 8, 32, 256), each after a cache
+               flush, with its algorithmic bytes and roofline fractions
   handoff,     the prefill-to-decode handoff (256 x 12 fp32 states into the
   packed_decode  pool) and the packed-input decode (B=256, H=12), each timed
-               after the steps with a prefill before every launch, so they
-               too meet the caches the way they would in serving
+               with a prefill before every launch, so they too meet the
+               caches the way they would in serving
   prefill_partitions  mean call time of the split and the fused prefill
                partitions on this workload, on the 16-sequence varlen GQA
                batch (512 units) and on B=16 H=HV=64 T=2048 (1024 units)
+  backward     the prefill's backward on this workload (float32 ALU roofline)
+  measured_ceilings  copy / read / write bandwidth and a bf16 GEMM on this
+               box, beside the vendor peaks
   cpu_baseline the fp64 oracle (token-by-token form) on a bounded sample of
-               the same prefill workload, on this host's cores
+               the same prefill workload, on all of this host's cores
 Only --gpus 1 is supported: the library runs on one GPU.
 """
 
@@ -68,10 +77,11 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector (and fp32 MFMA)
 
 def backward_alg_bytes(T_tot, H, HV, N, has_init, has_dht):
     """Backward inputs read once (q, k, v, beta, d_out bf16; g fp32; initial
-    state and final-state gradient fp32) and float32 gradients written once
-    (dq, dk, dv, dg, dbeta, d_initial_state)."""
+    state and final-state gradient fp32) and the gradients written once in
+    their inputs' dtypes (dq, dk, dv, dbeta bf16; dg, d_initial_state
+    fp32)."""
     per_tok = H * 2 * K * 2 + HV * (V * 2 + K * 4 + 2 + V * 2)          # inputs
-    per_tok += H * 2 * K * 4 + HV * (V * 4 + K * 4 + 4)                 # gradients
+    per_tok += H * 2 * K * 2 + HV * (V * 2 + K * 4 + 2)                 # gradients
     states = N * HV * K * V * 4 * ((1 if has_init else 0) + (1 if has_dht else 0) + 1)
     return T_tot * per_tok + states
 
@@ -127,48 +137,51 @@ def traffic_from_profiles():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, heads, target_s):
+def cpu_baseline(inp, target_cpu_s):
     """Time the fp64 recurrent oracle on a bounded sample of the prefill
-    workload: the first value heads over the first tokens, sized from pilot
-    runs so that the timed run takes about `target_s` seconds.  Reported as
-    tokens/s of the full workload (all value heads)."""
-    import numpy as np
-    import oracle
-    h = slice(0, heads)
+    workload -- every value head over the first tokens -- on all of this
+    host's cores (one process per head, at most 16), sized from a pilot so
+    that the sample costs about `target_cpu_s` seconds of CPU time.
+    Reported as tokens/s of the sample (all heads of each token)."""
+    import multiprocessing as mp
+    from oracle.parallel import _task, default_workers
     T = inp.q.shape[1]
     HV = inp.v.shape[2]
+    H = inp.q.shape[2]
+    grp = HV // H
+    workers = default_workers()
 
-    def run(n):
-        q = inp.q[:, :n, h].float().numpy()
-        k = inp.k[:, :n, h].float().numpy()
-        v = inp.v[:, :n, h].float().numpy()
-        g = inp.g[:, :n, h].numpy()
-        b = inp.beta[:, :n, h].float().numpy()
-        s0 = inp.initial_state[:, h].numpy()
-        c0 = time.process_time()
+    def tasks(n):
+        out = []
+        for h in range(H):
+            hv = slice(h * grp, (h + 1) * grp)
+            out.append((inp.q[:, :n, h:h + 1].float().numpy(), inp.k[:, :n, h:h + 1].float().numpy(),
+                        inp.v[:, :n, hv].float().numpy(), inp.g[:, :n, hv].numpy(),
+                        inp.beta[:, :n, hv].float().numpy(), inp.initial_state[:, hv].numpy()))
+        return out
+
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map(_task, tasks(8)[:workers], chunksize=1)          # start-up, untimed
+        n = 256
+        c0, t0 = time.process_time(), time.perf_counter()
+        ts = tasks(n)
+        pool.map(_task, ts, chunksize=1)
+        pilot = time.perf_counter() - t0
+        # cpu seconds of the pilot = wall x busy workers (the pool's time is not in this process)
+        per_tok_cpu = pilot * min(workers, len(ts)) / n
+        n = int(min(T, max(n, target_cpu_s / max(per_tok_cpu, 1e-9))))
+        ts = tasks(n)
         t0 = time.perf_counter()
-        oracle.recurrent(q, k, v, g, b, s0)
-        return time.perf_counter() - t0, time.process_time() - c0
-
-    # Pilot on `heads` heads over all tokens (the oracle is fast enough on the
-    # hosts here), then widen the head count so the timed run lands near
-    # target_s; on a slow host shorten the token range instead.
-    n = min(T, 256)
-    w, _ = run(n)
-    n = int(min(T, max(n, n * target_s / max(w, 1e-6))))
-    if n == T:
-        w, _ = run(n)
-        heads = int(min(HV, max(heads, heads * target_s / max(w, 1e-6))))
-        h = slice(0, heads)
-    wall, cpu = run(n)
+        pool.map(_task, ts, chunksize=1)
+        wall = time.perf_counter() - t0
     return {
-        "value": n * heads / HV / wall,
+        "value": n / wall,
         "unit": "tokens/s",
-        "cores": max(1, round(cpu / wall)),
+        "cores": min(workers, len(ts)),
         "kind": "oracle",
-        "sample": f"fp64 token-by-token oracle on the prefill workload's first {heads} of {HV} value heads "
-                  f"x first {n} of {T} tokens ({wall:.1f} s wall, {cpu:.1f} s cpu); tokens/s scaled to all "
-                  f"{HV} heads; host reports {os.cpu_count()} cpus",
+        "sample": f"fp64 token-by-token oracle on the prefill workload's first {n} of {T} tokens, all {HV} "
+                  f"value heads, one process per head on {min(workers, len(ts))} worker processes "
+                  f"({wall:.1f} s wall); host reports {os.cpu_count()} cpus",
     }
 
 
@@ -287,6 +300,95 @@ def measure_backward(torch, synth, kda, pin, inputs, stream, steps, warmup):
     }
 
 
+def time_events(torch, stream, fn, n, warmup, flush=None):
+    """Per-call times (ms) of fn by HIP events recorded on the launch stream.
+    With `flush` (a callable), it runs before every call, outside the events
+    (a write of a buffer larger than the last-level cache)."""
+    evs = []
+    for i in range(warmup + n):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        if i >= warmup:
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def stats_us(ms):
+    xs = sorted(ms)
+    return {"mean": sum(xs) / len(xs) * 1e3, "p10": xs[len(xs) // 10] * 1e3, "median": xs[len(xs) // 2] * 1e3,
+            "p90": xs[(9 * len(xs)) // 10] * 1e3, "n": len(xs)}
+
+
+def device_durations(torch, fn, n):
+    """Sum of the device durations of the kernels one call of fn runs
+    (microseconds, averaged over n calls), per kernel name and in total,
+    from the torch profiler's GPU activity trace.  None if the profiler
+    records no kernels here."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        per = {}
+        for e in prof.events():
+            if str(getattr(e, "device_type", "")).endswith("CUDA") and e.name and "Memcpy" not in e.name:
+                dur = getattr(e, "device_time", None)
+                if dur is None:
+                    dur = getattr(e, "cuda_time", 0.0)
+                per.setdefault(e.name, []).append(float(dur))
+        if not per:
+            return None
+        kernels = {}
+        for name, ds in per.items():
+            short = re.sub(r"\(.*", "", name).split("<")[0].split("::")[-1].strip() or name[:40]
+            kernels[short] = {"us_per_call": sum(ds) / n, "launches_per_call": len(ds) / n}
+        return {"total_us_per_call": sum(v["us_per_call"] for v in kernels.values()), "kernels": kernels,
+                "calls": n, "source": "torch.profiler GPU activity (kernel start/end on the device)"}
+    except Exception as exc:   # the profiler is optional context, never a reason to fail the bench
+        return {"error": f"{type(exc).__name__}: {exc}"}
+
+
+def measured_ceilings(torch, dev):
+    """What the chip delivers to plain library kernels on this machine: 1 GiB
+    device copy (read + write), read-only reduction, write-only fill, and a
+    bf16 GEMM (hipBLASLt via torch.matmul), beside the vendor peaks."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    f = a.view(torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def best(fn, reps=8):
+        return min(time_events(torch, stream, fn, reps, 2)) * 1e-3
+
+    out = {}
+    t = best(lambda: b.copy_(a))
+    out["copy_gbs"] = 2 * n / t / 1e9
+    t = best(lambda: f.sum())
+    out["read_gbs"] = n / t / 1e9
+    t = best(lambda: b.fill_(3))
+    out["write_gbs"] = n / t / 1e9
+    del a, b, f
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    t = best(lambda: torch.matmul(x, y), reps=10)
+    out["bf16_gemm_tflops"] = 2 * m ** 3 / t / 1e12
+    del x, y
+    out["vendor"] = {"hbm_gbs": HBM_PEAK_GBS, "bf16_fp16_mfma_tflops": F16_PEAK_TFLOPS,
+                     "fp32_tflops": FP32_PEAK_TFLOPS}
+    out["kernels"] = "torch copy_/sum/fill_ (1 GiB, best of 8) and torch.matmul bf16 8192^3 (hipBLASLt)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,13 +397,13 @@ def main():
     ap.add_argument("--T", type=int, default=8192)
     ap.add_argument("--H", type=int, default=96)
     ap.add_argument("--decode-B", type=int, default=256)
-    ap.add_argument("--cpu-heads", type=int, default=8, help="value heads in the CPU-oracle sample (0 = skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="CPU seconds of the oracle sample for cpu_baseline (0 = skip)")
     ap.add_argument("--only-backward", action="store_true",
                     help="time only the backward of the prefill workload (for profiling)")
     ap.add_argument("--only-steps", action="store_true",
-                    help="time only the steps (prefill + decode); skip the handoff, packed decode and "
-                         "partition measurements (for profiler runs that average per kernel name)")
+                    help="time only the steps (prefill + decode); skip everything else (for profiler runs "
+                         "that average per kernel name)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -340,10 +442,10 @@ def main():
     o = torch.empty(B, T, HV, V, dtype=torch.bfloat16, device=dev)
     sf = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev)
     ws = torch.empty(kda.workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
     if args.only_backward:
         torch.cuda.synchronize()
-        bw = measure_backward(torch, synth, kda, pin, (q, k, v, g, beta, s0), torch.cuda.current_stream(),
-                              args.steps, args.warmup)
+        bw = measure_backward(torch, synth, kda, pin, (q, k, v, g, beta, s0), stream, args.steps, args.warmup)
         print(json.dumps({"backward": bw}), flush=True)
         return
 
@@ -354,15 +456,16 @@ def main():
     dout = torch.empty(args.decode_B, 1, din.v.shape[1], V, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    prefill = lambda: kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
+    decode = lambda: kda.decode(dq, dk, dv, dg, db, pool, idx, out=dout)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
+        prefill()
         if ev is not None:
             ev[1].record(stream)
-        kda.decode(dq, dk, dv, dg, db, pool, idx, out=dout)
+        decode()
         if ev is not None:
             ev[2].record(stream)
 
@@ -391,12 +494,12 @@ def main():
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
-    pre_mean = sum(pre_ms) / len(pre_ms)
-    dec_mean = sum(dec_ms) / len(dec_ms)
-    pre_sorted = sorted(pre_ms)
+    pre = stats_us(pre_ms)
+    dec = stats_us(dec_ms)
+    pre_mean = pre["mean"] * 1e-3
+    dec_mean = dec["mean"] * 1e-3
 
-    n_seq = 1
-    pbytes = prefill_alg_bytes(B * T, H, HV, n_seq, True)
+    pbytes = prefill_alg_bytes(B * T, H, HV, 1, True)
     pflops = prefill_alg_flops(B * T, HV)
     achieved_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     mfma_tflops = pflops / (pre_mean * 1e-3) / 1e12
@@ -436,10 +539,10 @@ def main():
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
         },
+        "timing": "HIP events on the launch stream around each call, back-to-back steps; the decode "
+                  "follows a prefill whose >1 GB of traffic leaves it cache-cold",
         "prefill": {
-            "kernel_us_mean": pre_mean * 1e3,
-            "kernel_us_p10": pre_sorted[len(pre_sorted) // 10] * 1e3,
-            "kernel_us_p90": pre_sorted[(9 * len(pre_sorted)) // 10] * 1e3,
+            "event_us": pre,
             "alg_bytes": pbytes,
             "alg_flops": pflops,
             "mfma_tflops": mfma_tflops,
@@ -449,16 +552,78 @@ def main():
         "decode": {
             "B": args.decode_B,
             "active_rows": n_act,
-            "kernel_us_mean": dec_mean * 1e3,
+            "event_us": dec,
             "alg_bytes": dbytes,
             "state_gbs": dec_gbs,
             "hbm_frac": dec_gbs / HBM_PEAK_GBS,
         },
     }
     if args.only_steps:
-        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds) if args.cpu_heads > 0 else None
+        if args.cpu_seconds > 0:
+            result["cpu_baseline"] = cpu_baseline(pin, args.cpu_seconds)
         print(json.dumps(result), flush=True)
         return
+
+    # Device kernel durations (no launch or inter-call gaps), and the same
+    # calls after a 1 GiB cache-flushing write.
+    print("[bench] device durations and cache-flushed timings", file=sys.stderr, flush=True)
+    n_aux = max(5, args.steps // 2)
+    result["prefill"]["device"] = device_durations(torch, prefill, n_aux)
+    result["decode"]["device"] = device_durations(torch, decode, n_aux)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(7)
+    pf = stats_us(time_events(torch, stream, prefill, n_aux, 1, flush))
+    result["prefill"]["flushed_event_us"] = pf
+    df = stats_us(time_events(torch, stream, decode, n_aux, 1, flush))
+    result["decode"]["flushed_event_us"] = df
+    result["decode"]["flushed_hbm_frac"] = dbytes / (df["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    result["cache_conditions"] = ("event_us: back-to-back steps (prefill then decode); flushed_event_us: "
+                                  "a 1 GiB fill (untimed) before every call, so each call starts with "
+                                  "L2 and the 256 MB last-level cache holding none of its inputs")
+
+    # The other workloads: each timed after a cache flush, with its
+    # algorithmic bytes and the fraction of the HBM roofline.
+    print("[bench] other workloads", file=sys.stderr, flush=True)
+    configs = {}
+
+    def prefill_line(inp, label, bound):
+        a = [t.to(dev) if t is not None else None for t in (inp.q, inp.k, inp.v, inp.g, inp.beta,
+                                                              inp.initial_state, inp.cu_seqlens)]
+        Bc, Tc, Hc, _ = inp.q.shape
+        HVc = inp.v.shape[2]
+        Nc = inp.cu_seqlens.numel() - 1 if inp.cu_seqlens is not None else Bc
+        oc = torch.empty(Bc, Tc, HVc, V, dtype=torch.bfloat16, device=dev)
+        sc = torch.empty(Nc, HVc, K, V, dtype=torch.float32, device=dev)
+        wc = torch.empty(max(16, kda.workspace_size(Bc, Tc, Hc, HVc, Nc if inp.cu_seqlens is not None else 0)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: kda.chunk_prefill(*a, out=oc, final_state=sc, workspace=wc)
+        st = stats_us(time_events(torch, stream, fn, n_aux, 2, flush))
+        nb = prefill_alg_bytes(Bc * Tc, Hc, HVc, Nc, inp.initial_state is not None)
+        nf = prefill_alg_flops(Bc * Tc, HVc)
+        configs[label] = {"bound": bound, "flushed_event_us": st, "tokens_per_s": Bc * Tc / (st["mean"] * 1e-6),
+                          "alg_bytes": nb, "hbm_frac": nb / (st["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_frac": nf / (st["mean"] * 1e-6) / 1e12 / F16_PEAK_TFLOPS}
+
+    prefill_line(synth.config0(), "prefill B=1 H=HV=1 T=128", "launch latency (0.26 MB)")
+    prefill_line(synth.config1(), "prefill B=2 H=HV=8 T=1000 harsh decay", "latency / parallelism (26.7 MB)")
+    c3 = synth.config3()
+    prefill_line(c3, f"prefill varlen N=16 H=16 HV=32 T={c3.q.shape[1]}", "hbm")
+    for Bd in (1, 8, 32, 256):
+        di = synth.decode_config(Bd)
+        da = [t.to(dev) for t in (di.q, di.k, di.v, di.g, di.beta)]
+        dp = di.pool.to(dev)
+        dx = di.state_indices.to(dev)
+        do_ = torch.empty(Bd, 1, 12, V, dtype=torch.bfloat16, device=dev)
+        st = stats_us(time_events(torch, stream, lambda: kda.decode(*da, dp, dx, out=do_), n_aux, 2, flush))
+        na = int((di.state_indices >= 0).sum())
+        nb = decode_alg_bytes(na, Bd - na, 12, 12)
+        configs[f"decode B={Bd} H=HV=12"] = {
+            "bound": "hbm" if Bd >= 256 else "launch latency",
+            "active_rows": na, "flushed_event_us": st, "alg_bytes": nb,
+            "hbm_frac": nb / (st["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del dp
+    result["configs"] = configs
+    del flush_buf
 
     # Prefill-to-decode handoff, timed on its own after the steps: the decode
     # workload's rows each hand a fresh fp32 state to their pool slot.  As
@@ -468,23 +633,14 @@ def main():
     print("[bench] handoff", file=sys.stderr, flush=True)
     hstate, _, _ = synth.handoff_config(args.decode_B, slots=args.decode_B, HV=din.v.shape[1])
     hstate = hstate.to(dev)
-    h_ev = []
-    for i in range(args.warmup + args.steps):
-        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        kda.state_to_pool(hstate, pool, idx)
-        e1.record(stream)
-        if i >= args.warmup:
-            h_ev.append((e0, e1))
-    torch.cuda.synchronize()
-    h_ms = [a.elapsed_time(b) for a, b in h_ev]
+    h_ms = time_events(torch, stream, lambda: kda.state_to_pool(hstate, pool, idx), args.steps, args.warmup,
+                       prefill)
     h_mean = sum(h_ms) / len(h_ms)
     hbytes = handoff_alg_bytes(n_act, args.decode_B, din.v.shape[1])
     result["handoff"] = {
         "states": args.decode_B,
         "active": n_act,
-        "kernel_us_mean": h_mean * 1e3,
+        "event_us": stats_us(h_ms),
         "alg_bytes": hbytes,
         "gbs": hbytes / (h_mean * 1e-3) / 1e9,
         "hbm_frac": hbytes / (h_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -496,23 +652,15 @@ def main():
     pk_pool = pk.pool.to(dev)
     pk_idx = pk.state_indices.to(dev)
     pk_out = torch.empty(args.decode_B, 1, pk.H, V, dtype=torch.bfloat16, device=dev)
-    p_ev = []
-    for i in range(args.warmup + args.steps):
-        kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf, workspace=ws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        kda.packed_decode(*pk_args, pk_pool, pk_idx, out=pk_out)
-        e1.record(stream)
-        if i >= args.warmup:
-            p_ev.append((e0, e1))
-    torch.cuda.synchronize()
-    p_mean = sum(a.elapsed_time(b) for a, b in p_ev) / len(p_ev)
+    p_ms = time_events(torch, stream, lambda: kda.packed_decode(*pk_args, pk_pool, pk_idx, out=pk_out),
+                       args.steps, args.warmup, prefill)
+    p_mean = sum(p_ms) / len(p_ms)
     pk_act = int((pk.state_indices >= 0).sum())
     pkbytes = packed_decode_alg_bytes(pk_act, args.decode_B - pk_act, pk.H)
     result["packed_decode"] = {
         "B": args.decode_B,
         "active_rows": pk_act,
-        "kernel_us_mean": p_mean * 1e3,
+        "event_us": stats_us(p_ms),
         "alg_bytes": pkbytes,
         "gbs": pkbytes / (p_mean * 1e-3) / 1e9,
         "hbm_frac": pkbytes / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -521,31 +669,21 @@ def main():
     # The two prefill partitions side by side: split (the entry point timed
     # above: chunk-parallel kernel + workspace + carry kernel) and fused (one
     # workgroup per sequence and value head, no workspace), on this workload
-    # (96 units) and on the 16-sequence varlen GQA batch (512 units).
+    # (96 units), on the 16-sequence varlen GQA batch (512 units) and on
+    # B=16 H=HV=64 T=2048 (1024 units).
     print("[bench] prefill partitions", file=sys.stderr, flush=True)
 
-    def time_calls(fn, n):
-        evs = []
-        for i in range(args.warmup + n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            if i >= args.warmup:
-                evs.append((e0, e1))
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    def mean_us(fn, n):
+        return stats_us(time_events(torch, stream, fn, n, args.warmup))["mean"]
 
     partitions = {}
     n_part = max(3, args.steps // 2)
     partitions[f"B=1 H=HV={HV} T={T}"] = {
         "units": B * HV,
-        "split_us": time_calls(lambda: kda.chunk_prefill(q, k, v, g, beta, s0, None, out=o, final_state=sf,
-                                                         workspace=ws), n_part),
-        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(q, k, v, g, beta, s0, None, out=o,
-                                                               final_state=sf), n_part),
+        "split_us": mean_us(prefill, n_part),
+        "fused_us": mean_us(lambda: kda.chunk_prefill_fused(q, k, v, g, beta, s0, None, out=o, final_state=sf),
+                            n_part),
     }
-    c3 = synth.config3()
     c3a = [t.to(dev) for t in (c3.q, c3.k, c3.v, c3.g, c3.beta, c3.initial_state, c3.cu_seqlens)]
     T3, N3, H3, HV3 = c3.q.shape[1], c3.cu_seqlens.numel() - 1, c3.q.shape[2], c3.v.shape[2]
     o3 = torch.empty(1, T3, HV3, V, dtype=torch.bfloat16, device=dev)
@@ -553,11 +691,10 @@ def main():
     ws3 = torch.empty(kda.workspace_size(1, T3, H3, HV3, N3), dtype=torch.uint8, device=dev)
     partitions[f"varlen N={N3} H={H3} HV={HV3} T={T3}"] = {
         "units": N3 * HV3,
-        "split_us": time_calls(lambda: kda.chunk_prefill(*c3a, out=o3, final_state=sf3, workspace=ws3), n_part),
-        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(*c3a, out=o3, final_state=sf3), n_part),
+        "split_us": mean_us(lambda: kda.chunk_prefill(*c3a, out=o3, final_state=sf3, workspace=ws3), n_part),
+        "fused_us": mean_us(lambda: kda.chunk_prefill_fused(*c3a, out=o3, final_state=sf3), n_part),
     }
     del c3a, o3, sf3, ws3
-    # Many equal sequences: B=16, H=HV=64, T=2048 (1024 units).
     c4 = synth.prefill_basic(5, 16, 2048, 64, 64, init="normal0.1", name="b16_h64_t2048")
     c4a = [t.to(dev) for t in (c4.q, c4.k, c4.v, c4.g, c4.beta, c4.initial_state)]
     o4 = torch.empty(16, 2048, 64, V, dtype=torch.bfloat16, device=dev)
@@ -565,16 +702,19 @@ def main():
     ws4 = torch.empty(kda.workspace_size(16, 2048, 64, 64), dtype=torch.uint8, device=dev)
     partitions["B=16 H=HV=64 T=2048"] = {
         "units": 16 * 64,
-        "split_us": time_calls(lambda: kda.chunk_prefill(*c4a, None, out=o4, final_state=sf4, workspace=ws4), n_part),
-        "fused_us": time_calls(lambda: kda.chunk_prefill_fused(*c4a, None, out=o4, final_state=sf4), n_part),
+        "split_us": mean_us(lambda: kda.chunk_prefill(*c4a, None, out=o4, final_state=sf4, workspace=ws4), n_part),
+        "fused_us": mean_us(lambda: kda.chunk_prefill_fused(*c4a, None, out=o4, final_state=sf4), n_part),
     }
     del c4a, o4, sf4, ws4
     result["prefill_partitions"] = partitions
     result["backward"] = measure_backward(torch, synth, kda, pin, (q, k, v, g, beta, s0), stream,
                                           max(3, args.steps // 2), args.warmup)
-    if args.cpu_heads > 0:
-        print(f"[bench] cpu oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_heads, args.cpu_seconds)
+    print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    del ws
+    result["measured_ceilings"] = measured_ceilings(torch, dev)
+    if args.cpu_seconds > 0:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(pin, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -41,12 +41,21 @@ typedef enum {
   KDA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
   KDA_ERR_UNSUPPORTED = 3,  /* valid request this build does not support (K, V != 128) */
   KDA_ERR_ALIGN = 4,        /* a pointer or stride is not 16-byte aligned */
-  KDA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
-  KDA_ERR_WORKSPACE = 6     /* workspace missing or smaller than required */
+  KDA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required */
+  KDA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
 } kda_status;
+
+/* Entry points return their status as an int (one of kda_status) and take
+ * the stream as void* (a hipStream_t), so the header needs no HIP include. */
 
 /* Human-readable name of a status code (static storage). */
 const char* kda_status_string(int status);
+
+/* Build identity: a hex digest of the sources and compile flags the
+ * library was built from (static storage).  Lets a caller (and the test
+ * suite) check that the loaded binary was compiled from a given source
+ * tree. */
+const char* kda_build_id(void);
 
 /*
  * kda_qk_l2norm -- bit-exact row L2 normalisation of q or k.
@@ -69,6 +78,21 @@ const char* kda_status_string(int status);
 int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream);
 
 /*
+ * Numeric domain of the prefill (kda_chunk_prefill, kda_chunk_prefill_fused
+ * and the states they carry).  The carry's matrix products take v and the
+ * running [K,V] state as fp16 operands (11-bit significand, float32
+ * accumulation), so every |v| and every |state| entry -- the initial state
+ * and every state the recurrence reaches -- must stay below 2^14 = 16384.
+ * (On the workloads this library is measured on -- v of unit scale, initial
+ * states of 0.1 -- the reached states stay below 1 in magnitude; a test
+ * runs initial states up to the bound.)  Values outside the domain are not
+ * detected (that would need a device-to-host read): they can overflow to
+ * inf/NaN in o and final_state.
+ * The decode path (kda_decode) works on float32 states and has no such
+ * bound.
+ */
+
+/*
  * kda_chunk_prefill -- KDA chunked prefill forward.
  *
  * Defined on "KDA Chunk Prefill on Ascend A3": section "Function and tensor
@@ -85,7 +109,8 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *   v              bf16 [B, T, HV, V]  magnitudes below 2^14
  *   g              fp32 [B, T, HV, K]  per-channel log decay (finite, <= 0)
  *   beta           bf16 [B, T, HV]
- *   initial_state  fp32 [N, HV, K, V]  or NULL (zeros)
+ *   initial_state  fp32 [N, HV, K, V]  or NULL (zeros); entries below 2^14
+ *                  in magnitude (see "Numeric domain" above)
  *   cu_seqlens     int32 [N + 1] device array of packed sequence offsets, or
  *                  NULL.  When given, B must be 1 and the N = num_seqs
  *                  sequences [cu[n], cu[n+1]) of the T axis are independent,
@@ -261,14 +286,23 @@ int kda_state_to_pool(const float* state, int32_t N, int32_t HV, int32_t K, int3
                       void* state_pool, int64_t slot_stride, int64_t num_slots,
                       const int32_t* state_indices, void* stream);
 
+/* Output dtypes of kda_chunk_backward's token gradients. */
+enum {
+  KDA_GRAD_FLOAT32 = 0,      /* dq, dk, dv, dbeta as float32 */
+  KDA_GRAD_INPUT_DTYPE = 1   /* dq, dk, dv, dbeta in their inputs' dtype, bf16
+                                (the float32 value rounded to nearest-even) */
+};
+
 /*
  * kda_chunk_backward -- gradients of the chunked prefill.
  *
  * Defined on "KDA Chunk Prefill on Ascend A3": section "Function and tensor
- * contract" (the optional backward: gradients with respect to q, k, v, g,
- * beta and initial_state) and section "Mathematical definition" (the
- * forward being differentiated, exactly as kda_chunk_prefill).  The page
- * gives no backward formulas.  This computes the exact gradients of
+ * contract" (the optional backward) and the closing paragraph of section
+ * "Timing and required submission" (the loss sum(o * do) + sum(final_state
+ * * dht); gradients for q, k, v, g, beta and initial_state in their
+ * corresponding dtypes, none for an absent initial state), with the forward
+ * of section "Mathematical definition" exactly as kda_chunk_prefill.  The
+ * page gives no backward formulas.  This computes the exact gradients of
  *     sum(o * d_out) + sum(final_state * d_final_state)
  * through the forward's definition, with one reading: the bf16 rounding of
  * the normalised q and k passes gradients unchanged, so dq and dk are the
@@ -283,15 +317,20 @@ int kda_state_to_pool(const float* state, int32_t N, int32_t HV, int32_t K, int3
  *   d_out            bf16 [B, T, HV, V]  gradient of o
  *   d_final_state    fp32 [N, HV, K, V]  gradient of final_state, or NULL
  *                    (zero)
- * Outputs (float32, always written unless stated; all 16-byte aligned):
- *   dq, dk           [B, T, H, K]   (summed over the value heads that share
- *                    a Q/K head)
- *   dv               [B, T, HV, V]
- *   dg               [B, T, HV, K]
- *   dbeta            [B, T, HV]
- *   d_initial_state  [N, HV, K, V], or NULL to skip it.  When initial_state
- *                    is NULL it is the gradient with respect to a zero
- *                    initial state.
+ *   grad_dtype       KDA_GRAD_INPUT_DTYPE: dq, dk, dv and dbeta are bf16,
+ *                    the dtype of q, k, v and beta (the page's contract);
+ *                    KDA_GRAD_FLOAT32: they are float32 (the values before
+ *                    that rounding).  Any other value: KDA_ERR_UNSUPPORTED.
+ * Outputs (always written unless stated; all 16-byte aligned except dbeta):
+ *   dq, dk           [B, T, H, K]   bf16 or float32 per grad_dtype (summed
+ *                    over the value heads that share a Q/K head)
+ *   dv               [B, T, HV, V]  bf16 or float32 per grad_dtype
+ *   dg               [B, T, HV, K]  float32 (the dtype of g)
+ *   dbeta            [B, T, HV]     bf16 or float32 per grad_dtype
+ *   d_initial_state  fp32 [N, HV, K, V], or NULL to skip it (the page
+ *                    returns none for an absent initial state; when
+ *                    initial_state is NULL and this is given, it is the
+ *                    gradient with respect to a zero initial state).
  *   workspace        device scratch of at least
  *                    kda_chunk_backward_workspace_size(...) bytes, owned by
  *                    the caller; contents on entry do not matter.  Calls
@@ -307,8 +346,8 @@ int kda_chunk_backward(const void* q, const void* k, const void* v,
                        int32_t B, int32_t T, int32_t H, int32_t HV,
                        int32_t K, int32_t V,
                        const void* d_out, const float* d_final_state,
-                       float* dq, float* dk, float* dv, float* dg, float* dbeta,
-                       float* d_initial_state,
+                       void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                       float* d_initial_state, int32_t grad_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -25,7 +25,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
-EXPORTS = ("kda_status_string", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
+EXPORTS = ("kda_status_string", "kda_build_id", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
            "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
            "kda_state_to_pool", "kda_chunk_backward", "kda_chunk_backward_workspace_size")
 
@@ -50,6 +50,8 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_build_id.restype = ctypes.c_char_p
+    lib.kda_build_id.argtypes = []
     lib.kda_qk_l2norm.restype = ctypes.c_int
     lib.kda_qk_l2norm.argtypes = [_vp, _vp, _i64, _i32, _vp]
     lib.kda_chunk_prefill.restype = ctypes.c_int
@@ -72,11 +74,26 @@ def load():
     lib.kda_chunk_backward.restype = ctypes.c_int
     lib.kda_chunk_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
-                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_size_t, _vp]
     lib.kda_chunk_backward_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_backward_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     _lib = lib
     return lib
+
+
+def build_id():
+    """Hash of the sources the loaded library was compiled from."""
+    return load().kda_build_id().decode()
+
+
+def check_build_matches_sources():
+    """Raise unless the loaded libkda.so was built from the source files
+    in this tree (their hash is compiled into the library)."""
+    from .build import source_hash
+    want, got = source_hash(), build_id()
+    if want != got:
+        raise KDAError(f"{LIB_PATH} was built from other sources (library {got}, tree {want}); rebuild it")
+    return got
 
 
 def status_string(code):
@@ -189,14 +206,26 @@ def backward_workspace_size(B, T, H, HV, num_seqs=0, K=128, V=128):
     return int(load().kda_chunk_backward_workspace_size(B, T, H, HV, K, V, num_seqs))
 
 
+GRAD_FLOAT32 = 0       # kda.h KDA_GRAD_FLOAT32
+GRAD_INPUT_DTYPE = 1   # kda.h KDA_GRAD_INPUT_DTYPE
+
+
 def chunk_backward(q, k, v, g, beta, initial_state, d_out, d_final_state=None, cu_seqlens=None,
-                   workspace=None, want_d_initial_state=True):
+                   workspace=None, grad_dtype="input", want_d_initial_state=False):
     """Gradients of sum(o * d_out) + sum(final_state * d_final_state) for
     the prefill with the same inputs.  d_out [B,T,HV,V] bf16; d_final_state
-    [N,HV,K,V] fp32 or None (zero).  Returns float32 (dq, dk, dv, dg,
-    dbeta, d_initial_state); d_initial_state is None when initial_state is
-    None and want_d_initial_state is False."""
+    [N,HV,K,V] fp32 or None (zero).  Returns (dq, dk, dv, dg, dbeta,
+    d_initial_state).
+
+    grad_dtype "input" (default): every gradient has its input's dtype --
+    dq, dk, dv, dbeta bf16 (the kernels round their float32 values to
+    nearest-even), dg and d_initial_state float32.  grad_dtype "float32":
+    dq, dk, dv, dbeta float32 as well.  d_initial_state is None when
+    initial_state is None, unless want_d_initial_state asks for the
+    gradient at a zero initial state."""
     lib = load()
+    if grad_dtype not in ("input", "float32"):
+        raise ValueError("grad_dtype must be 'input' or 'float32'")
     dev, (B, T, H, HV, K, V), nseq_arg, _, _ = _prefill_args(
         q, k, v, g, beta, initial_state, cu_seqlens, None, None)
     N = nseq_arg if cu_seqlens is not None else B
@@ -212,16 +241,18 @@ def chunk_backward(q, k, v, g, beta, initial_state, d_out, d_final_state=None, c
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    dq = torch.empty((B, T, H, K), **f32)
-    dk = torch.empty((B, T, H, K), **f32)
-    dv = torch.empty((B, T, HV, V), **f32)
+    tok = dict(dtype=torch.bfloat16 if grad_dtype == "input" else torch.float32, device=dev)
+    dq = torch.empty((B, T, H, K), **tok)
+    dk = torch.empty((B, T, H, K), **tok)
+    dv = torch.empty((B, T, HV, V), **tok)
     dg = torch.empty((B, T, HV, K), **f32)
-    dbeta = torch.empty((B, T, HV), **f32)
+    dbeta = torch.empty((B, T, HV), **tok)
     dh0 = torch.empty((N, HV, K, V), **f32) if (initial_state is not None or want_d_initial_state) else None
     code = lib.kda_chunk_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
                                   B, T, H, HV, K, V, _ptr(d_out), _ptr(d_final_state),
                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                  GRAD_INPUT_DTYPE if grad_dtype == "input" else GRAD_FLOAT32,
                                   _ptr(workspace), workspace.numel(), _stream())
     _check(code, "kda_chunk_backward")
     return dq, dk, dv, dg, dbeta, dh0

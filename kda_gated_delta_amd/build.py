@@ -5,6 +5,7 @@ this file.  Always rebuilds (it is the "does it build" check as well).
 """
 
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -30,6 +31,28 @@ FLAGS = [
 ]
 
 
+def source_files():
+    """Every file the library is compiled from, in a fixed order."""
+    root = os.path.dirname(HERE)
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+    return files + [os.path.join(root, "include", "kda.h")]
+
+
+def source_hash():
+    """SHA-256 (hex, first 32 digits) over the names and bytes of the
+    library's sources and its compile flags.  The build bakes it into the
+    library (kda_build_id), so a loaded binary can be matched to the
+    sources it was compiled from."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()[:32]
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -43,9 +66,10 @@ def build(verbose=False, jobs=8):
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
+    stamp = source_hash()
     for src in srcs:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc(), *FLAGS, f'-DKDA_SOURCE_HASH="{stamp}"', "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -28,11 +28,12 @@
 //   diag(beta), E = exp(G) k^, W = A E, U = A v, Qg, Kg, gamma = exp(G_last),
 //   written to the chunk's record in the workspace.
 // bwd_carry_fwd_kernel -- per (sequence, value head, 64 state columns), in
-//   chunk order: stores each chunk's entering state S (transposed) and
-//   Vnew = U - W S, then S = gamma S + Kg^T Vnew.
+//   chunk order: stores each chunk's entering state S ([K][V], as the carry
+//   holds it; the gradient kernel transposes it while staging) and
+//   Vnew = U - W S (transposed), then S = gamma S + Kg^T Vnew.
 // bwd_carry_rev_kernel -- same split, chunks in reverse, with dS' the
 //   gradient of the chunk's exiting state (starting from d_final_state):
-//   stores dS' (transposed), dVnew = Aqk^T dO + Kg dS', then
+//   stores dS' ([K][V]) and dVnew = Aqk^T dO + Kg dS' (transposed), then
 //   dS' = gamma dS' + Qg^T dO - W^T dVnew; the last one is d_initial_state.
 // bwd_grad_kernel -- per (chunk, value head): dQg = dO S^T, dAqk = tril(dO
 //   Vnew^T), dKg = Vnew dS'^T, dgamma = rowsum(dS' * S), dW = -dVnew S^T,
@@ -109,11 +110,11 @@ struct BParams {
   const int32_t* cu;        // [N+1] or null
   const uint16_t* dout;     // bf16 [tokens][HV][V]
   const float* dht;         // [N][HV][K][V] or null
-  float* dq;                // [tokens][H][K]
-  float* dk;
-  float* dv;                // [tokens][HV][V]
+  void* dq;                 // [tokens][H][K]   float32, or bf16 when obf
+  void* dk;
+  void* dv;                 // [tokens][HV][V]  float32, or bf16 when obf
   float* dg;                // [tokens][HV][K]
-  float* dbeta;             // [tokens][HV]
+  void* dbeta;              // [tokens][HV]     float32, or bf16 when obf
   float* dh0;               // [N][HV][K][V] or null
   float* ws;                // records [HV][nslots][REC]
   float* dqh;               // [tokens][HV][K] dq^ per value head
@@ -121,6 +122,7 @@ struct BParams {
   int64_t nslots;           // slots per value head
   int64_t tokens;
   int T, H, HV, N;
+  int obf;                  // dq, dk, dv, dbeta stored as bf16 (nearest-even), else float32
 };
 
 __device__ __forceinline__ void seq_range(const BParams& p, int n, int64_t& tok0, int& len) {
@@ -218,6 +220,23 @@ __device__ __forceinline__ void ld4(const float* p, float* v) {
 
 __device__ __forceinline__ void st4(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Gradient outputs that take their input's dtype: element `idx` of a
+// float32 array, or of a bf16 array (the same float32 value rounded to
+// nearest-even) when `obf` is set.  idx is a multiple of 4 for put4.
+__device__ __forceinline__ void put4(void* base, int64_t idx, const float* v, int obf) {
+  if (obf)
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+        make_uint2(kda::pack_bf16(v[0], v[1]), kda::pack_bf16(v[2], v[3]));
+  else
+    st4(static_cast<float*>(base) + idx, v);
+}
+__device__ __forceinline__ void put1(void* base, int64_t idx, float v, int obf) {
+  if (obf)
+    static_cast<uint16_t*>(base)[idx] = uint16_t(kda::pack_bf16(v, 0.0f));
+  else
+    static_cast<float*>(base)[idx] = v;
 }
 
 // fp32 MFMA (v_mfma_f32_16x16x4_f32), twice the rate of plain fp32 VALU code
@@ -1372,7 +1391,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = i0 + r;
-      if (j < nv) st4(p.dv + ((t0 + j) * p.HV + hv) * KD + d0, av[r]);
+      if (j < nv) put4(p.dv, ((t0 + j) * p.HV + hv) * KD + d0, av[r], p.obf);
       float vg[4], vk[4];
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -1693,7 +1712,7 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       if (i < nv) p.dg[((t0 + i) * p.HV + hv) * KD + d] = R0[i * KP + d] + later;
     }
   }
-  if (tid < nv) p.dbeta[(t0 + tid) * p.HV + hv] = sDB[tid];
+  if (tid < nv) put1(p.dbeta, (t0 + tid) * p.HV + hv, sDB[tid], p.obf);
   // Normalisation backward (one value head per Q/K head): for x the raw row,
   // n = sqrt(sum x^2 + 1e-6), dx = dy / n - x (x . dy) / n^3; the sums over
   // a row's 128 channels run across the 32 lanes that hold it.
@@ -1728,8 +1747,8 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
           ok[cc] = fk[r][cc] * ik - xkv[cc] * ck3;
         }
         const int64_t o = ((t0 + i) * p.H + hv) * KD + d0;
-        st4(p.dq + o, oq);
-        st4(p.dk + o, ok);
+        put4(p.dq, o, oq, p.obf);
+        put4(p.dk, o, ok, p.obf);
       }
     }
   }
@@ -1769,9 +1788,9 @@ __global__ __launch_bounds__(NTB) void bwd_norm_kernel(BParams p) {
   const float nrm = sqrtf(ss + 1e-6f);
   const float inv = 1.0f / nrm;
   const float c3 = xd * inv * inv * inv;
-  float* out = (isk ? p.dk : p.dq) + r * KD;
+  void* out = isk ? p.dk : p.dq;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) out[lane + 64 * e] = gv[e] * inv - xv[e] * c3;
+  for (int e = 0; e < 2; ++e) put1(out, r * KD + lane + 64 * e, gv[e] * inv - xv[e] * c3, p.obf);
 }
 
 // Raise a kernel's dynamic-LDS limit once per device.
@@ -1805,11 +1824,12 @@ extern "C" size_t kda_chunk_backward_workspace_size(int32_t B, int32_t T, int32_
 extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, const float* g, const void* beta,
                                   const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
                                   int32_t B, int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
-                                  const void* d_out, const float* d_final_state, float* dq, float* dk, float* dv,
-                                  float* dg, float* dbeta, float* d_initial_state, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  const void* d_out, const float* d_final_state, void* dq, void* dk, void* dv,
+                                  float* dg, void* dbeta, float* d_initial_state, int32_t grad_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
   if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
+  if (grad_dtype != KDA_GRAD_FLOAT32 && grad_dtype != KDA_GRAD_INPUT_DTYPE) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;
   const int64_t nseq = cu_seqlens ? num_seqs : B;
   const int64_t tokens = int64_t(B) * T;
@@ -1852,6 +1872,7 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
   p.H = H;
   p.HV = HV;
   p.N = int(nseq);
+  p.obf = grad_dtype == KDA_GRAD_INPUT_DTYPE;
 
   static std::atomic<bool> prep_set[kMaxDevices], fwd_set[kMaxDevices], rev_set[kMaxDevices],
       grad_set[kMaxDevices];

@@ -13,3 +13,11 @@ extern "C" const char* kda_status_string(int status) {
     default: return "unknown kda_status";
   }
 }
+
+// Hash of the sources and flags this library was compiled from (the build
+// passes it in); lets a caller check that a loaded binary matches a source
+// tree.
+#ifndef KDA_SOURCE_HASH
+#error "build with -DKDA_SOURCE_HASH=... (see build.py)"
+#endif
+extern "C" const char* kda_build_id(void) { return KDA_SOURCE_HASH; }

@@ -21,7 +21,6 @@ rounding switched off (central finite differences) and closed forms.
 """
 
 import numpy as np
-import torch
 
 from .l2norm import l2norm_bf16
 
@@ -30,6 +29,7 @@ def _norm(x, round_bf16):
     """x / sqrt(sum(x^2) + 1e-6) per row.  With round_bf16 the value is the
     canonical bf16 normalisation of the forward (l2norm_bf16) and the
     gradient is that of the unrounded expression."""
+    import torch
     n = torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)
     y = x / n
     if round_bf16:
@@ -44,6 +44,7 @@ def recurrent_backward(q, k, v, g, beta, initial_state, do, dht, cu_seqlens=None
     Returns (dq, dk, dv, dg, dbeta, dh0) as float64 arrays; dh0 is None when
     initial_state is None.
     """
+    import torch
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     q, k, v, g, beta = t(q), t(k), t(v), t(g), t(beta)
     s0 = None if initial_state is None else t(initial_state)

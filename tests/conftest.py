@@ -21,4 +21,6 @@ def gpu_lib():
         pytest.skip("no GPU")
     import kda_gated_delta_amd as kda
     kda.load()
+    # the binary under test must be the one compiled from these sources
+    print(f"libkda build {kda.check_build_matches_sources()}", flush=True)
     return kda

@@ -35,6 +35,13 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_build_id_matches_sources():
+    """The loaded library carries the hash of the sources it was built
+    from; it must be this tree's."""
+    assert kda.check_build_matches_sources() == kda.build_id()
+    assert len(kda.build_id()) == 32
+
+
 def test_status_strings():
     lib = kda.load()
     for code in range(7):
@@ -78,7 +85,7 @@ def test_prefill_metadata_errors():
     assert _prefill(lib, cu=FAKE, n=0) == 2
     assert _prefill(lib, v=MISALIGNED) == 4
     assert _prefill(lib, ws=NULL) == 1
-    assert _prefill(lib, wsb=1000) == 6                    # workspace too small
+    assert _prefill(lib, wsb=1000) == 5                    # KDA_ERR_WORKSPACE
 
 
 def test_workspace_size_formula():
@@ -179,11 +186,12 @@ def test_fused_prefill_metadata_errors():
 def _backward(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
              B=1, T=64, H=1, HV=1, K=128, V=128, do=FAKE, dht=NULL, dq=FAKE, dk=FAKE, dv=FAKE,
-             dg=FAKE, db=FAKE, dh0=NULL, ws=FAKE, wsb=1 << 30)
+             dg=FAKE, db=FAKE, dh0=NULL, gd=1, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.kda_chunk_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
                                   a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["do"], a["dht"],
-                                  a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["ws"], a["wsb"], NULL)
+                                  a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["gd"], a["ws"], a["wsb"],
+                                  NULL)
 
 
 def test_backward_metadata_errors():
@@ -198,7 +206,9 @@ def test_backward_metadata_errors():
     assert _backward(lib, cu=FAKE, n=2, B=2) == 2
     assert _backward(lib, dv=MISALIGNED) == 4
     assert _backward(lib, ws=NULL) == 1
-    assert _backward(lib, wsb=1000) == 6
+    assert _backward(lib, wsb=1000) == 5
+    assert _backward(lib, gd=2) == 3                        # unknown gradient dtype
+    assert _backward(lib, gd=-1) == 3
 
 
 def test_backward_workspace_size_formula():

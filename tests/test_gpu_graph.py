@@ -1,0 +1,81 @@
+"""The library under HIP graph capture: kda_decode (the page's -1 rows are
+"graph padding", so the decode is meant to be captured) and
+kda_chunk_prefill with a caller-owned workspace are captured once, then
+replayed on new inputs copied into the captured buffers; every replay must
+equal a direct call on the same inputs bit for bit.  Eager work and host
+synchronisations run between the replays.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def test_decode_graph_replay(gpu_lib):
+    kda = gpu_lib
+    dev = "cuda"
+    B = 32
+    base = synth.decode_config(B, N=64, seed=40)
+    static = {n: getattr(base, n).to(dev) for n in ("q", "k", "v", "g", "beta", "state_indices")}
+    pool0 = base.pool.to(dev)
+    pool = pool0.clone()
+    out = torch.empty((B, 1, 12, 128), dtype=torch.bfloat16, device=dev)
+    args = lambda d, p: (d["q"], d["k"], d["v"], d["g"], d["beta"], p, d["state_indices"])
+    kda.decode(*args(static, pool), out=out)          # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.decode(*args(static, pool), out=out)
+    torch.cuda.synchronize()
+    for r in range(4):
+        nxt = synth.decode_config(B, N=64, seed=41 + r)
+        for n in static:
+            static[n].copy_(getattr(nxt, n).to(dev))
+        pool.copy_(pool0)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_pool = pool0.clone()
+        ref_out = kda.decode(*args(static, ref_pool))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_out)), f"replay {r}: o differs"
+        assert torch.equal(_bits(pool), _bits(ref_pool)), f"replay {r}: pool differs"
+        say(f"decode graph replay {r}: identical to the direct call")
+
+
+def test_prefill_graph_replay(gpu_lib):
+    kda = gpu_lib
+    dev = "cuda"
+    B, T, H, HV = 1, 300, 2, 4
+    first = synth.prefill_basic(50, B, T, H, HV, init="normal0.1")
+    names = ("q", "k", "v", "g", "beta", "initial_state")
+    static = {n: getattr(first, n).to(dev) for n in names}
+    ws = torch.empty(kda.workspace_size(B, T, H, HV), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, HV, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, HV, 128, 128), dtype=torch.float32, device=dev)
+    call = lambda d, **kw: kda.chunk_prefill(*(d[n] for n in names), **kw)
+    call(static, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(4):
+        nxt = synth.prefill_basic(51 + r, B, T, H, HV, init="normal0.1")
+        for n in names:
+            static[n].copy_(getattr(nxt, n).to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_s = call(static)                        # its own workspace and outputs
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_o)), f"replay {r}: o differs"
+        assert torch.equal(fin, ref_s), f"replay {r}: final state differs"
+        say(f"prefill graph replay {r}: identical to the direct call")

@@ -1,9 +1,8 @@
 """kda_chunk_prefill on the GPU against the fp64 oracle.
 
-Small workloads are compared in full; the full-size workloads (H=96, T=8192
-and the packed variable-length GQA batch) run in the launch configuration
-the benchmark times and are compared on sampled heads and sequences, which
-the oracle computes independently.  Invariants that must hold bit for bit
+Every workload is compared in full, the full-size ones (H=96, T=8192 and
+the packed variable-length GQA batch) in the launch configuration the
+benchmark times, with the oracle spread over the host's cores.  Invariants that must hold bit for bit
 (determinism, GQA expansion, packing, state carry) are checked GPU vs GPU.
 """
 
@@ -14,6 +13,7 @@ import torch
 import oracle
 import synth
 from gpu_util import check_o, check_state, say
+from oracle.parallel import recurrent_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -107,40 +107,53 @@ def test_extreme_gate_fallback(gpu_lib):
     _full_check(gpu_lib, inp)
 
 
-def test_full_scale_sampled_heads(gpu_lib):
-    """H=HV=96, T=8192 as timed; heads 0, 47 and 95 against the oracle."""
+def test_full_scale_all_heads(gpu_lib):
+    """H=HV=96, T=8192 in the launch the benchmark times; every head's o
+    and final state against the oracle (run over the host's cores, one
+    process per head)."""
     inp = synth.config2()
     say("prefill cfg2 full size")
     o, s = _gpu(gpu_lib, inp)
-    for h in (0, 47, 95):
-        sub = synth.PrefillInputs(inp.q[:, :, h:h + 1], inp.k[:, :, h:h + 1], inp.v[:, :, h:h + 1],
-                                  inp.g[:, :, h:h + 1], inp.beta[:, :, h:h + 1],
-                                  inp.initial_state[:, h:h + 1], None, f"cfg2_head{h}")
-        o_ref, s_ref = _ref(sub)
-        eo = check_o(o[:, :, h:h + 1], o_ref, sub.name)
-        es = check_state(s[:, h:h + 1], s_ref, sub.name)
-        say(f"  head {h}: o_err={eo:.2e} state_err={es:.2e}")
+    a = synth.to_numpy(inp)
+    o_ref, s_ref = recurrent_parallel(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"])
+    eo = check_o(o, o_ref, inp.name)
+    es = check_state(s, s_ref, inp.name)
+    say(f"  all 96 heads: o_err={eo:.2e} state_err={es:.2e}")
 
 
-def test_varlen_gqa_sampled(gpu_lib):
-    """Packed 16-sequence batch, H=16, HV=32: sampled (sequence, Q/K head)
-    pairs against the oracle run on that sequence and head pair alone."""
+def test_varlen_gqa_all(gpu_lib):
+    """Packed 16-sequence batch, H=16, HV=32, in one call; every sequence
+    and head against the oracle (one process per sequence and Q/K head)."""
     inp = synth.config3()
     say(f"prefill {inp.name}")
     o, s = _gpu(gpu_lib, inp)
-    cu = inp.cu_seqlens.tolist()
-    lens = [cu[i + 1] - cu[i] for i in range(16)]
-    picks = [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), 5), (3, 15), (9, 7)]
-    for n, hq in picks:
-        t0, t1 = cu[n], cu[n + 1]
-        hv = slice(2 * hq, 2 * hq + 2)
-        sub = synth.PrefillInputs(inp.q[:, t0:t1, hq:hq + 1], inp.k[:, t0:t1, hq:hq + 1],
-                                  inp.v[:, t0:t1, hv], inp.g[:, t0:t1, hv], inp.beta[:, t0:t1, hv],
-                                  inp.initial_state[n:n + 1, hv], None, f"cfg3_seq{n}_qk{hq}")
-        o_ref, s_ref = _ref(sub)
-        eo = check_o(o[:, t0:t1, hv], o_ref, sub.name)
-        es = check_state(s[n:n + 1, hv], s_ref, sub.name)
-        say(f"  seq {n} (len {t1 - t0}) qk-head {hq}: o_err={eo:.2e} state_err={es:.2e}")
+    a = synth.to_numpy(inp)
+    o_ref, s_ref = recurrent_parallel(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"],
+                                      a["cu_seqlens"])
+    eo = check_o(o, o_ref, inp.name)
+    es = check_state(s, s_ref, inp.name)
+    say(f"  all sequences and heads: o_err={eo:.2e} state_err={es:.2e}")
+
+
+def test_state_near_domain_bound(gpu_lib):
+    """Initial states up to the prefill's documented bound (|state| < 2^14)
+    and values in the thousands: finite results, the final state within the
+    1e-3 relative bar, and o within 1e-2 of the oracle relative to o's
+    scale (the recurrence is linear in (v, state), so absolute errors grow
+    with them; the elementwise o bar is stated for unit-scale values)."""
+    inp = synth.prefill_basic(96, 1, 300, 2, 2, init="normal0.1", name="state_bound")
+    s0 = inp.initial_state
+    inp.initial_state = s0 * (16000.0 / float(s0.abs().max()))
+    inp.v = (inp.v.float() * 1000.0).to(torch.bfloat16)
+    o, s = _gpu(gpu_lib, inp)
+    o_ref, s_ref = _ref(inp)
+    of = o.float().cpu().numpy()
+    assert np.all(np.isfinite(of))
+    eo = float(np.abs(of - o_ref).max() / np.abs(o_ref).max())
+    es = check_state(s, s_ref, inp.name)
+    say(f"  state bound: max|S0|={float(inp.initial_state.abs().max()):.0f} max|S|={np.abs(s_ref).max():.0f} "
+        f"o_err/max|o|={eo:.2e} state_err={es:.2e}")
+    assert eo <= 1e-2
 
 
 def test_varlen_small_full(gpu_lib):

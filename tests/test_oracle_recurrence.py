@@ -265,3 +265,16 @@ def test_value_linearity(form):
     o2, S2 = form(q, k, v2, g, beta, None)
     np.testing.assert_allclose(oa, 3.0 * o1 + o2, rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(Sa, 3.0 * S1 + S2, rtol=1e-10, atol=1e-13)
+
+
+def test_parallel_runner_equals_recurrent():
+    """The multi-process runner reassembles exactly what the serial
+    recurrence computes (varlen with an empty sequence, GQA)."""
+    from oracle.parallel import recurrent_parallel
+    cu = np.array([0, 40, 40, 95, 130])
+    args, _ = _rand(21, 1, 130, 2, 4, 16, 8)
+    S0 = 0.25 * np.random.default_rng(22).standard_normal((4, 4, 16, 8))
+    o1, s1 = oracle.recurrent(*args, S0, cu)
+    o2, s2 = recurrent_parallel(*args, S0, cu, workers=3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
