@@ -149,6 +149,32 @@ size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
                                         int32_t K, int32_t V, int32_t num_seqs);
 
 /*
+ * kda_chunk_prefill_noalloc -- kda_chunk_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same operation, arguments
+ * and results, minus the workspace arguments.  The workspace is instead a
+ * static device array inside the library, KDA_NOALLOC_WORKSPACE_BYTES
+ * (64 MiB) per GPU, held from the library's first use on that GPU until
+ * the process ends.  This entry point allocates and frees nothing.
+ *
+ * Limit: sizes whose kda_chunk_prefill_workspace_size(...) exceeds
+ * KDA_NOALLOC_WORKSPACE_BYTES return KDA_ERR_WORKSPACE and enqueue nothing
+ * (64 MiB covers about 64K (token x value head) pairs, e.g. T = 8192 with
+ * HV = 7, or T = 1000 with B = 2 and HV = 8).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results.  The
+ * array needs no clearing: each call writes every part it reads.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                              const float* g, const void* beta,
+                              const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t B, int32_t T, int32_t H, int32_t HV,
+                              int32_t K, int32_t V,
+                              void* o, float* final_state, void* stream);
+
+/*
  * kda_chunk_prefill_fused -- the same operation as kda_chunk_prefill, in
  * the fused partition: one workgroup per (sequence, value head) walks that
  * sequence's chunks in order and keeps everything on chip -- the chunk-local

@@ -26,7 +26,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 EXPORTS = ("kda_status_string", "kda_build_id", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
-           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
+           "kda_chunk_prefill_noalloc", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
            "kda_state_to_pool", "kda_chunk_backward", "kda_chunk_backward_workspace_size")
 
 _lib = None
@@ -61,6 +61,9 @@ def load():
     lib.kda_chunk_prefill_fused.restype = ctypes.c_int
     lib.kda_chunk_prefill_fused.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_prefill_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                              _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.kda_decode.restype = ctypes.c_int
@@ -256,6 +259,26 @@ def chunk_backward(q, k, v, g, beta, initial_state, d_out, d_final_state=None, c
                                   _ptr(workspace), workspace.numel(), _stream())
     _check(code, "kda_chunk_backward")
     return dq, dk, dv, dg, dbeta, dh0
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20   # kda.h KDA_NOALLOC_WORKSPACE_BYTES
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None,
+                          final_state=None):
+    """kda_chunk_prefill_noalloc: the prefill with the library's static
+    64 MiB workspace (no workspace argument, nothing allocated by the
+    library).  Pass out and final_state to allocate nothing here either.
+    Sizes whose workspace exceeds the static one raise (KDA_ERR_WORKSPACE).
+    Calls that overlap on one GPU race."""
+    lib = load()
+    dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    code = lib.kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
+                                         B, T, H, HV, K, V, _ptr(out), _ptr(final_state), _stream())
+    _check(code, "kda_chunk_prefill_noalloc")
+    return out, final_state
 
 
 def chunk_prefill_fused(q, k, v, g, beta, initial_state=None, cu_seqlens=None,

@@ -1461,6 +1461,44 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
   return launch(p, as_stream(stream));
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a file-scope device array.  Its
+// name is a host-side stand-in in host code, so its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is passed to the kernels.  Every call on a device shares the
+// array: calls that overlap on one device race.  The kernels write every slot
+// they read in the same call, so nothing needs clearing between calls.
+constexpr size_t kNoAllocScratch = KDA_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+static void* scratch_address() {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = addr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    addr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+extern "C" int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                         const void* beta, const float* initial_state,
+                                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                                         int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
+                                         void* o, float* final_state, void* stream) {
+  Params p;
+  const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
+                         final_state, p);
+  if (st != KDA_OK) return st;
+  if (kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N) > kNoAllocScratch) return KDA_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return KDA_ERR_HIP;
+  p.ws = static_cast<unsigned char*>(ws);
+  return launch(p, as_stream(stream));
+}
+
 extern "C" int kda_chunk_prefill_fused(const void* q, const void* k, const void* v, const float* g,
                                        const void* beta, const float* initial_state,
                                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,

@@ -220,3 +220,19 @@ def test_backward_workspace_size_formula():
     assert lib.kda_chunk_backward_workspace_size(1, 500, 2, 4, 128, 128, 5) == \
         (7 + 5 + 1) * 4 * rec + 500 * 4 * 128 * 4 * 2
     assert lib.kda_chunk_backward_workspace_size(1, 64, 1, 1, 64, 128, 0) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_static_workspace():
+    """kda_chunk_prefill_noalloc checks the size against its 64 MiB static
+    workspace before touching the device: too large returns
+    KDA_ERR_WORKSPACE (5); metadata errors come first as usual."""
+    lib = kda.load()
+    big = dict(B=1, T=8192, H=96, HV=96)
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) > kda.NOALLOC_WORKSPACE_BYTES
+    call = lambda **kw: lib.kda_chunk_prefill_noalloc(
+        FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 0, kw.get("B", 1), kw.get("T", 64), kw.get("H", 1),
+        kw.get("HV", 1), kw.get("K", 128), 128, FAKE, FAKE, NULL)
+    assert call(**big) == 5
+    assert call(B=2, T=4096, H=8, HV=8) == 5               # 1032 slot-heads > 1016
+    assert call(K=64) == 3
+    assert call(H=3, HV=4) == 2
