@@ -185,6 +185,8 @@ struct Params {
   float* sfin;
   unsigned char* ws;
   int64_t nslots;          // slots per value head
+  int64_t w0, w1;          // slot window [w0, w1) of this launch (split form)
+  int64_t wslots;          // workspace slots per value head (the window capacity)
   int T, H, HV, N;
 };
 
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     items = (unit_len + C - 1) / C;
     stride = 1;
   } else {
-    items = int(p.nslots) * p.HV;
+    items = int(p.w1 - p.w0) * p.HV;
     stride = gridDim.x;
   }
   struct Item {
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       return it;
     }
     for (; i < items; i += stride) {
-      const int s = i / p.HV;
+      const int s = int(p.w0) + i / p.HV;
       int c;
       const int n = slot_owner(p, s, c);
       if (n < 0) continue;
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       it.trow = tok0 + int64_t(c) * C;
       it.nvalid = min(C, len - c * C);
       it.slot = s;
-      it.hv = i - s * p.HV;
+      it.hv = i - (s - int(p.w0)) * p.HV;
       it.hq = it.hv / (p.HV / p.H);
       break;
     }
@@ -1056,7 +1058,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // faster; the same hint on the input loads or on the other kernel's
     // slot, v and o traffic measured slower.
     {
-      unsigned char* dst = p.ws + (int64_t(cur.hv) * p.nslots + cur.slot) * WS_SLOT;
+      unsigned char* dst = p.ws + (int64_t(cur.hv) * p.wslots + (cur.slot - p.w0)) * WS_SLOT;
 #pragma unroll
       for (int k = 0; k < (SLOT_U4 + NT - 1) / NT; ++k) {
         const int u = min(tid + k * NT, SLOT_U4 - 1);
@@ -1158,14 +1160,26 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int len;
   seq_range(p, n, tok0, len);
   const int nch = (len + C - 1) / C;
-  const unsigned char* wsh = p.ws + (int64_t(hv) * p.nslots + slot_base(p, n)) * WS_SLOT;
+  // This launch covers the sequence's chunks whose slots lie in the window
+  // [w0, w1); the state enters from initial_state at chunk 0 and otherwise
+  // from final_state, where the previous window left it.  An empty
+  // sequence passes its state through in the first window.
+  const int64_t base = slot_base(p, n);
+  const int c_lo = int(max(int64_t(0), p.w0 - base));
+  const int c_hi = int(min(int64_t(nch), p.w1 - base));
+  if (c_lo >= c_hi && !(nch == 0 && p.w0 == 0)) return;
+  // Workspace slot of chunk c: (hv, base + c - w0).
+  auto slot_of = [&](int c) {
+    return p.ws + (int64_t(hv) * p.wslots + (base + c - p.w0)) * WS_SLOT;
+  };
   unsigned char* sv = smem + OFF_V + wave * (C * 16 * 2);
   const int c0 = half * VT + wave * 16;          // first state column of this wave
 
   const int col = c0 + l16;                      // this lane's state column
   f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
-  if (p.s0) {   // one branch around all 32 loads, so they are in flight together
-    const float* s0 = p.s0 + (int64_t(n) * p.HV + hv) * KD * KD;
+  const float* s_in = c_lo > 0 ? p.sfin : p.s0;
+  if (s_in) {   // one branch around all 32 loads, so they are in flight together
+    const float* s0 = s_in + (int64_t(n) * p.HV + hv) * KD * KD;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -1175,22 +1189,22 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int rt = 0; rt < 8; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (nch > 0) {
-    load_slot_part(smem, wsh, wave, lane, 0, BLOCKS_PER_WAVE);
-    load_v_lds(sv, p, tok0, min(C, len), hv, c0, lane);
+  if (c_lo < c_hi) {
+    load_slot_part(smem, slot_of(c_lo), wave, lane, 0, BLOCKS_PER_WAVE);
+    load_v_lds(sv, p, tok0 + int64_t(c_lo) * C, min(C, len - c_lo * C), hv, c0, lane);
   }
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);
   lds_barrier();
 
-  for (int c = 0; c < nch; ++c) {
+  for (int c = c_lo; c < c_hi; ++c) {
     const int nvalid = min(C, len - c * C);
     const int64_t trow = tok0 + int64_t(c) * C;
-    const unsigned char* cur = smem + (c & 1) * BUF_BYTES;
-    unsigned char* nbuf = smem + ((c + 1) & 1) * BUF_BYTES;   // last read in the previous chunk
-    // The next chunk's inputs, prefetched unconditionally (the last chunk
-    // re-reads its own, which nothing uses) so the body has no branches.
-    const int cn = min(c + 1, nch - 1);
-    const unsigned char* nslot = wsh + int64_t(cn) * WS_SLOT;
+    const unsigned char* cur = smem + ((c - c_lo) & 1) * BUF_BYTES;
+    unsigned char* nbuf = smem + ((c - c_lo + 1) & 1) * BUF_BYTES;   // last read in the previous chunk
+    // The next chunk's inputs, prefetched unconditionally (the window's last
+    // chunk re-reads its own, which nothing uses) so the body has no branches.
+    const int cn = min(c + 1, c_hi - 1);
+    const unsigned char* nslot = slot_of(cn);
 
     const unsigned char* sW = cur + WS_W;
     const unsigned char* sQg = cur + WS_QG;
@@ -1375,21 +1389,51 @@ int device_cus() {
   return v;
 }
 
-int launch(const Params& p, hipStream_t stream) {
+// The split form runs over windows of chunk slots: the chunk-parallel kernel
+// fills the window's slots of every value head, then the carry kernel walks
+// them, and the next window reuses the same workspace region; the state
+// crosses windows through final_state.  Windows bound the workspace (2 GiB
+// here, one window for all but very long inputs; the allocation-free entry
+// point uses its 64 MiB array).  Measured on MI355X: windows sized to stay in
+// the 256 MB last-level cache (96 MB at 96 value heads, T = 8192) made the
+// call 14% slower, the per-window ramp and tail of the two kernels costing
+// more than the cache residency saves.
+#ifndef KDA_WINDOW_BYTES
+#define KDA_WINDOW_BYTES (2048ll << 20)
+#endif
+constexpr int64_t kWindowBytes = KDA_WINDOW_BYTES;
+
+// Slots per value head in one window of at most `bytes` of workspace (at
+// least one slot; 0 if even one slot per value head does not fit).
+int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
+  const int64_t w = bytes / (HV * WS_SLOT);
+  return w < nslots ? w : nslots;
+}
+
+// Launch the split form over windows of p.wslots slots (p.ws holds
+// p.wslots slots per value head).
+int launch(Params p, hipStream_t stream) {
   static std::atomic<bool> intra_set[kMaxDevices], inter_set[kMaxDevices];
   if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
-  const int64_t items = p.nslots * p.HV;
-  if (items > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
-  const int64_t intra_blocks = items < device_cus() ? items : device_cus();
+  if (p.wslots < 1) return KDA_ERR_WORKSPACE;
+  if (p.wslots * p.HV > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t inter_blocks = 16 * ((units + 7) / 8);   // two column halves per unit
   if (inter_blocks > 0x7fffffff) return KDA_ERR_SHAPE;
-  hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
-  const int st = launch_status();
-  if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NTI), INTER_LDS, stream, p);
-  return launch_status();
+  for (int64_t w0 = 0; w0 < p.nslots; w0 += p.wslots) {
+    p.w0 = w0;
+    p.w1 = w0 + p.wslots < p.nslots ? w0 + p.wslots : p.nslots;
+    const int64_t items = (p.w1 - p.w0) * p.HV;
+    const int64_t intra_blocks = items < device_cus() ? items : device_cus();
+    hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
+    int st = launch_status();
+    if (st != KDA_OK) return st;
+    hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NTI), INTER_LDS, stream, p);
+    st = launch_status();
+    if (st != KDA_OK) return st;
+  }
+  return KDA_OK;
 }
 
 // Fused form: one workgroup per (sequence, value head); no workspace.
@@ -1426,6 +1470,9 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
   p.sfin = final_state;
   p.ws = nullptr;
   p.nslots = slots_per_head(int64_t(B) * T, nseq);
+  p.w0 = 0;
+  p.w1 = p.nslots;
+  p.wslots = p.nslots;
   p.T = T;
   p.H = H;
   p.HV = HV;
@@ -1440,7 +1487,8 @@ extern "C" size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t
   (void)H;
   if (B < 1 || T < 0 || HV < 1 || Kd != KD || Vd != KD) return 0;
   const int64_t nseq = num_seqs > 0 ? num_seqs : B;
-  return size_t(slots_per_head(int64_t(B) * T, nseq) * HV) * WS_SLOT;
+  const int64_t w = window_slots(slots_per_head(int64_t(B) * T, nseq), HV, kWindowBytes);
+  return size_t((w > 0 ? w : 1) * HV) * WS_SLOT;
 }
 
 extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -1458,6 +1506,7 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
   if (!workspace) return KDA_ERR_NULL;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
   p.ws = static_cast<unsigned char*>(workspace);
+  p.wslots = need / (int64_t(HV) * WS_SLOT);
   return launch(p, as_stream(stream));
 }
 
@@ -1467,7 +1516,9 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
 // up once per device (hipGetSymbolAddress, with that device current) and only
 // that address is passed to the kernels.  Every call on a device shares the
 // array: calls that overlap on one device race.  The kernels write every slot
-// they read in the same call, so nothing needs clearing between calls.
+// they read in the same call, so nothing needs clearing between calls.  The
+// prefill runs in windows of as many chunk slots as the array holds, so any
+// size fits whose value heads take one slot each (HV <= 1016).
 constexpr size_t kNoAllocScratch = KDA_NOALLOC_WORKSPACE_BYTES;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
 
@@ -1492,7 +1543,9 @@ extern "C" int kda_chunk_prefill_noalloc(const void* q, const void* k, const voi
   const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
                          final_state, p);
   if (st != KDA_OK) return st;
-  if (kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N) > kNoAllocScratch) return KDA_ERR_WORKSPACE;
+  // Windows of as many slots as the static workspace holds.
+  p.wslots = window_slots(p.nslots, HV, int64_t(kNoAllocScratch));
+  if (p.wslots < 1) return KDA_ERR_WORKSPACE;
   void* ws = scratch_address();
   if (!ws) return KDA_ERR_HIP;
   p.ws = static_cast<unsigned char*>(ws);

@@ -91,8 +91,10 @@ def test_prefill_metadata_errors():
 def test_workspace_size_formula():
     lib = kda.load()
     slot = 66048
-    # floor(B*T/64) + N + 1 slots per value head
+    # one window of chunk slots per value head: the window holds
+    # min(floor(B*T/64) + N + 1, floor(2 GiB / (HV * slot))) slots
     assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) == (128 + 1 + 1) * 96 * slot
+    assert lib.kda_chunk_prefill_workspace_size(1, 65536, 96, 96, 128, 128, 0) == (2**31 // (96 * slot)) * 96 * slot
     assert lib.kda_chunk_prefill_workspace_size(2, 1000, 8, 8, 128, 128, 0) == (31 + 2 + 1) * 8 * slot
     assert lib.kda_chunk_prefill_workspace_size(1, 500, 2, 4, 128, 128, 5) == (7 + 5 + 1) * 4 * slot
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 1, 1, 64, 128, 0) == 0
@@ -223,16 +225,16 @@ def test_backward_workspace_size_formula():
 
 
 def test_noalloc_rejects_sizes_beyond_its_static_workspace():
-    """kda_chunk_prefill_noalloc checks the size against its 64 MiB static
-    workspace before touching the device: too large returns
-    KDA_ERR_WORKSPACE (5); metadata errors come first as usual."""
+    """kda_chunk_prefill_noalloc runs in windows of as many chunk slots as its
+    64 MiB static workspace holds, so it takes any length; only more value
+    heads than one slot each fits (HV > 1016) returns KDA_ERR_WORKSPACE (5),
+    checked before the device is touched.  Metadata errors come first."""
     lib = kda.load()
-    big = dict(B=1, T=8192, H=96, HV=96)
-    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) > kda.NOALLOC_WORKSPACE_BYTES
     call = lambda **kw: lib.kda_chunk_prefill_noalloc(
         FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 0, kw.get("B", 1), kw.get("T", 64), kw.get("H", 1),
         kw.get("HV", 1), kw.get("K", 128), 128, FAKE, FAKE, NULL)
-    assert call(**big) == 5
-    assert call(B=2, T=4096, H=8, HV=8) == 5               # 1032 slot-heads > 1016
+    assert 1016 * 66048 <= kda.NOALLOC_WORKSPACE_BYTES < 1017 * 66048
+    assert call(H=1017, HV=1017) == 5
+    assert call(H=8, HV=2048, T=1) == 5
     assert call(K=64) == 3
     assert call(H=3, HV=4) == 2

@@ -156,6 +156,28 @@ def test_state_near_domain_bound(gpu_lib):
     assert eo <= 1e-2
 
 
+def test_many_windows_varlen(gpu_lib):
+    """512 value heads make the allocation-free entry point's slot windows
+    (64 MiB) one slot long, so sequences span many windows (the state
+    crossing them through final_state) and empty and one-token sequences
+    sit inside later windows; compared in full against the oracle, and
+    bitwise against the single-window call."""
+    lens = [100, 0, 1, 64, 200, 0, 37]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    inp = synth.prefill_basic(97, 1, int(cu[-1]), 256, 512, init="normal0.1", cu_seqlens=cu,
+                              name="varlen_512heads")
+    dev = "cuda"
+    a = [t.to(dev) for t in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.initial_state, inp.cu_seqlens)]
+    o, s = gpu_lib.chunk_prefill_noalloc(*a)
+    o1, s1 = gpu_lib.chunk_prefill(*a)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o1.view(torch.int16)) and torch.equal(s, s1)
+    o_ref, s_ref = _ref(inp)
+    eo = check_o(o, o_ref, inp.name)
+    es = check_state(s, s_ref, inp.name)
+    say(f"  512 heads, one-slot windows: o_err={eo:.2e} state_err={es:.2e}")
+
+
 def test_varlen_small_full(gpu_lib):
     lens = [70, 0, 1, 129, 64, 33]
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
