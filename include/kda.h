@@ -142,8 +142,10 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
  * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill
  * needs for these sizes (num_seqs as for kda_chunk_prefill; pass 0 when
  * cu_seqlens is NULL).  Returns 0 for sizes kda_chunk_prefill rejects.
- * It is about 1 KB per token and value head: one 66048-byte block per
- * 64-token chunk slot, with floor(B*T/64) + N + 1 slots per value head.
+ * It is one 66048-byte block per 64-token chunk slot and value head, for
+ * one window of min(floor(B*T/64) + N + 1, floor(2^31 / (HV * 66048)))
+ * slots (about 1 KB per token and value head, at most about 2 GiB): the
+ * prefill runs window by window over the slots and reuses the workspace.
  */
 size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t HV,
                                         int32_t K, int32_t V, int32_t num_seqs);
@@ -152,15 +154,15 @@ size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
  * kda_chunk_prefill_noalloc -- kda_chunk_prefill for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): the same operation, arguments
- * and results, minus the workspace arguments.  The workspace is instead a
- * static device array inside the library, KDA_NOALLOC_WORKSPACE_BYTES
- * (64 MiB) per GPU, held from the library's first use on that GPU until
- * the process ends.  This entry point allocates and frees nothing.
+ * and results (bit for bit), minus the workspace arguments.  The workspace
+ * is instead a static device array inside the library,
+ * KDA_NOALLOC_WORKSPACE_BYTES (64 MiB) per GPU, held from the library's
+ * first use on that GPU until the process ends, and the prefill runs in
+ * windows of as many chunk slots as it holds.  This entry point allocates
+ * and frees nothing.
  *
- * Limit: sizes whose kda_chunk_prefill_workspace_size(...) exceeds
- * KDA_NOALLOC_WORKSPACE_BYTES return KDA_ERR_WORKSPACE and enqueue nothing
- * (64 MiB covers about 64K (token x value head) pairs, e.g. T = 8192 with
- * HV = 7, or T = 1000 with B = 2 and HV = 8).
+ * Limit: any B, T and N; HV <= 1016 (one 66048-byte slot per value head
+ * must fit).  More value heads return KDA_ERR_WORKSPACE and enqueue nothing.
  * Every call on a GPU shares that GPU's array: calls that overlap on one
  * GPU (other streams, other threads) race and give undefined results.  The
  * array needs no clearing: each call writes every part it reads.
