@@ -355,7 +355,8 @@ def device_durations(torch, fn, n):
             return None
         kernels = {}
         for name, ds in per.items():
-            short = re.sub(r"\(.*", "", name).split("<")[0].split("::")[-1].strip() or name[:40]
+            short = re.sub(r"\(anonymous namespace\)::", "", name)
+            short = re.sub(r"\(.*", "", short).replace("void ", "").strip() or name[:40]
             kernels[short] = {"us_per_call": sum(ds) / n, "launches_per_call": len(ds) / n}
         return {"total_us_per_call": sum(v["us_per_call"] for v in kernels.values()), "kernels": kernels,
                 "calls": n, "source": "torch.profiler GPU activity (kernel start/end on the device)"}
@@ -576,12 +577,18 @@ def main():
     # calls after a 1 GiB cache-flushing write.
     print("[bench] device durations and cache-flushed timings", file=sys.stderr, flush=True)
     n_aux = max(5, args.steps // 2)
-    result["prefill"]["device"] = device_durations(torch, prefill, n_aux)
-    result["decode"]["device"] = device_durations(torch, decode, n_aux)
-    for key, nbytes in (("prefill", pbytes), ("decode", dbytes)):
-        dv = result[key]["device"]
-        if dv and "total_us_per_call" in dv:
-            dv["hbm_frac"] = nbytes / (dv["total_us_per_call"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    # Device durations of the step's kernels in the serving order (prefill,
+    # then decode), so each meets the caches as in the timed steps.
+    dsteps = device_durations(torch, step, n_aux)
+    if dsteps and "kernels" in dsteps:
+        for key, names, nbytes in (("prefill", ("intra", "inter"), pbytes), ("decode", ("decode",), dbytes)):
+            ks = {k: v for k, v in dsteps["kernels"].items() if any(n in k for n in names)}
+            us = sum(v["us_per_call"] for v in ks.values())
+            result[key]["device"] = {"us_per_call": us, "kernels": ks, "calls": dsteps["calls"],
+                                     "source": dsteps["source"] + ", over prefill + decode steps",
+                                     "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None}
+    else:
+        result["prefill"]["device"] = result["decode"]["device"] = dsteps
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.view(torch.float32).sum()
     pf = stats_us(time_events(torch, stream, prefill, n_aux, 1, flush))
