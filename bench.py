@@ -17,8 +17,10 @@ Prints one JSON line:
                call from the committed rocprofv3 counter summary when that
                was taken on the current kernel source, else null
   prefill, decode  event statistics (mean, p10, median, p90), the device
-               kernel durations from the torch profiler's GPU trace (no
-               launch gaps), and the same calls after a 1 GiB cache flush
+               kernel durations (no launch gaps) from the committed
+               rocprofv3 kernel trace of these steps when it was taken on
+               the current kernel sources, and the same calls after a 1 GiB
+               cache-flushing read
   configs      the other workloads (the small prefills, the varlen GQA
                batch, decode at B = 1, 8, 32, 256), each after a cache
                flush, with its algorithmic bytes and roofline fractions
@@ -120,6 +122,45 @@ def source_hash(name):
     lines = [re.sub(r"//.*", "", line).rstrip() for line in text.splitlines()]
     code = "\n".join(line for line in lines if line.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+KTRACE_PATH = os.path.join(ROOT, "profiles", "kernel_trace_h96_t8192.json")
+
+
+def kernel_trace_summary(stats_csv, out_path):
+    """Average device durations per kernel from a rocprofv3 --kernel-trace
+    --stats run of `bench.py --only-steps` (run_kernel_stats.csv), recorded
+    with the hashes of the kernel sources they were measured on."""
+    import csv
+    rec = {"workload": "prefill B=1 H=HV=96 T=8192 then decode B=256 H=HV=12, back-to-back steps",
+           "source": "rocprofv3 --kernel-trace --stats (kernel start to end on the device)",
+           "prefill_code_sha256_16": source_hash("prefill.hip"),
+           "decode_code_sha256_16": source_hash("decode.hip"), "kernels_us": {}}
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            name = row["Name"]
+            for key in ("intra_kernel", "inter_kernel", "decode_kernel"):
+                if key in name and ("decode" not in key or "SplitInputs" in name):
+                    rec["kernels_us"][key] = float(row["AverageNs"]) / 1e3
+    with open(out_path, "w") as fo:
+        json.dump(rec, fo, indent=1)
+        fo.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
+def kernel_trace_from_profiles():
+    """The committed rocprofv3 kernel averages, if taken on the current
+    kernel sources (else None)."""
+    if not os.path.exists(KTRACE_PATH):
+        return None
+    try:
+        rec = json.load(open(KTRACE_PATH))
+    except ValueError:
+        return None
+    if rec.get("prefill_code_sha256_16") != source_hash("prefill.hip") or \
+            rec.get("decode_code_sha256_16") != source_hash("decode.hip"):
+        return None
+    return rec
 
 
 def traffic_from_profiles():
@@ -324,46 +365,6 @@ def stats_us(ms):
             "p90": xs[(9 * len(xs)) // 10] * 1e3, "n": len(xs)}
 
 
-def device_durations(torch, fn, n):
-    """Sum of the device durations of the kernels one call of fn runs
-    (microseconds, averaged over n calls), per kernel name and in total,
-    from the torch profiler's GPU activity trace.  None if the profiler
-    records no kernels here."""
-    try:
-        from torch.profiler import ProfilerActivity, profile
-        torch.cuda.synchronize()
-        # A first, discarded session: the tracer's start-up slows the first
-        # kernels it records (measured: the prefill's persistent kernel read
-        # 585 us in a process's first session, 496 us in later ones and in
-        # rocprofv3's trace).
-        with profile(activities=[ProfilerActivity.CUDA]):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-        with profile(activities=[ProfilerActivity.CUDA]) as prof:
-            for _ in range(n):
-                fn()
-            torch.cuda.synchronize()
-        per = {}
-        for e in prof.events():
-            if str(getattr(e, "device_type", "")).endswith("CUDA") and e.name and "Memcpy" not in e.name:
-                dur = getattr(e, "device_time", None)
-                if dur is None:
-                    dur = getattr(e, "cuda_time", 0.0)
-                per.setdefault(e.name, []).append(float(dur))
-        if not per:
-            return None
-        kernels = {}
-        for name, ds in per.items():
-            short = re.sub(r"\(anonymous namespace\)::", "", name)
-            short = re.sub(r"\(.*", "", short).replace("void ", "").strip() or name[:40]
-            kernels[short] = {"us_per_call": sum(ds) / n, "launches_per_call": len(ds) / n}
-        return {"total_us_per_call": sum(v["us_per_call"] for v in kernels.values()), "kernels": kernels,
-                "calls": n, "source": "torch.profiler GPU activity (kernel start/end on the device)"}
-    except Exception as exc:   # the profiler is optional context, never a reason to fail the bench
-        return {"error": f"{type(exc).__name__}: {exc}"}
-
-
 def measured_ceilings(torch, dev):
     """What the chip delivers to plain library kernels on this machine: 1 GiB
     device copy (read + write), read-only reduction, write-only fill, and a
@@ -415,10 +416,15 @@ def main():
                          "that average per kernel name)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_JSON"),
+                    help="only summarise a rocprofv3 kernel-trace stats file into the kernel-time record")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                            "COPY_WRITE_CSV", "COPY_BYTES", "OUT_JSON"),
                     help="only summarise rocprofv3 counter files into the traffic record")
     args = ap.parse_args()
+    if args.trace_summary:
+        kernel_trace_summary(args.trace_summary[0], args.trace_summary[1])
+        return
     if args.traffic_summary:
         a = args.traffic_summary
         traffic_summary(a[0], a[1], a[2], a[3], int(a[4]), a[5])
@@ -577,18 +583,20 @@ def main():
     # calls after a 1 GiB cache-flushing write.
     print("[bench] device durations and cache-flushed timings", file=sys.stderr, flush=True)
     n_aux = max(5, args.steps // 2)
-    # Device durations of the step's kernels in the serving order (prefill,
-    # then decode), so each meets the caches as in the timed steps.
-    dsteps = device_durations(torch, step, n_aux)
-    if dsteps and "kernels" in dsteps:
-        for key, names, nbytes in (("prefill", ("intra", "inter"), pbytes), ("decode", ("decode",), dbytes)):
-            ks = {k: v for k, v in dsteps["kernels"].items() if any(n in k for n in names)}
-            us = sum(v["us_per_call"] for v in ks.values())
-            result[key]["device"] = {"us_per_call": us, "kernels": ks, "calls": dsteps["calls"],
-                                     "source": dsteps["source"] + ", over prefill + decode steps",
-                                     "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None}
+    # Device kernel durations (no launch or inter-call gaps) of the same
+    # steps, from the committed rocprofv3 kernel trace when it was taken on
+    # the current kernel sources.
+    kt = kernel_trace_from_profiles()
+    if kt:
+        ku = kt["kernels_us"]
+        for key, names, nbytes in (("prefill", ("intra_kernel", "inter_kernel"), pbytes),
+                                   ("decode", ("decode_kernel",), dbytes)):
+            us = sum(ku.get(n, 0.0) for n in names)
+            result[key]["device_trace_us"] = {"us_per_call": us, "kernels": {n: ku.get(n) for n in names},
+                                              "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None,
+                                              "source": "profiles/kernel_trace_h96_t8192.json (" + kt["source"] + ")"}
     else:
-        result["prefill"]["device"] = result["decode"]["device"] = dsteps
+        result["prefill"]["device_trace_us"] = result["decode"]["device_trace_us"] = None
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.view(torch.float32).sum()
     pf = stats_us(time_events(torch, stream, prefill, n_aux, 1, flush))
