@@ -30,7 +30,8 @@ Prints one JSON line:
                caches the way they would in serving
   prefill_partitions  mean call time of the split and the fused prefill
                partitions on this workload, on the 16-sequence varlen GQA
-               batch (512 units) and on B=16 H=HV=64 T=2048 (1024 units)
+               batch (512 units) and on B=16 H=HV=64 T=2048 (1024 units),
+               with the one kda_chunk_prefill picks ("auto")
   backward     the prefill's backward on this workload (float32 ALU roofline)
   measured_ceilings  copy / read / write bandwidth and a bf16 GEMM on this
                box, beside the vendor peaks
@@ -627,7 +628,9 @@ def main():
         st = stats_us(time_events(torch, stream, fn, n_aux, 2, flush))
         nb = prefill_alg_bytes(Bc * Tc, Hc, HVc, Nc, inp.initial_state is not None)
         nf = prefill_alg_flops(Bc * Tc, HVc)
-        configs[label] = {"bound": bound, "flushed_event_us": st, "tokens_per_s": Bc * Tc / (st["mean"] * 1e-6),
+        part = kda.prefill_partition(Bc, HVc, Nc if inp.cu_seqlens is not None else 0)
+        configs[label] = {"bound": bound, "partition": part, "flushed_event_us": st,
+                          "tokens_per_s": Bc * Tc / (st["mean"] * 1e-6),
                           "alg_bytes": nb, "hbm_frac": nb / (st["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                           "mfma_frac": nf / (st["mean"] * 1e-6) / 1e12 / F16_PEAK_TFLOPS}
 
@@ -693,11 +696,11 @@ def main():
         "hbm_frac": pkbytes / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     del pk_pool
-    # The two prefill partitions side by side: split (the entry point timed
-    # above: chunk-parallel kernel + workspace + carry kernel) and fused (one
-    # workgroup per sequence and value head, no workspace), on this workload
-    # (96 units), on the 16-sequence varlen GQA batch (512 units) and on
-    # B=16 H=HV=64 T=2048 (1024 units).
+    # The two prefill partitions side by side: split (chunk-parallel kernel +
+    # workspace + carry kernel) and fused (one workgroup per sequence and
+    # value head, no workspace), on this workload (96 units), on the
+    # 16-sequence varlen GQA batch (512 units) and on B=16 H=HV=64 T=2048
+    # (1024 units); "auto" names the one kda_chunk_prefill runs.
     print("[bench] prefill partitions", file=sys.stderr, flush=True)
 
     def mean_us(fn, n):
@@ -707,7 +710,9 @@ def main():
     n_part = max(3, args.steps // 2)
     partitions[f"B=1 H=HV={HV} T={T}"] = {
         "units": B * HV,
-        "split_us": mean_us(prefill, n_part),
+        "auto": kda.prefill_partition(B, HV),
+        "split_us": mean_us(lambda: kda.chunk_prefill_split(q, k, v, g, beta, s0, None, out=o, final_state=sf,
+                                                            workspace=ws), n_part),
         "fused_us": mean_us(lambda: kda.chunk_prefill_fused(q, k, v, g, beta, s0, None, out=o, final_state=sf),
                             n_part),
     }
@@ -718,7 +723,8 @@ def main():
     ws3 = torch.empty(kda.workspace_size(1, T3, H3, HV3, N3), dtype=torch.uint8, device=dev)
     partitions[f"varlen N={N3} H={H3} HV={HV3} T={T3}"] = {
         "units": N3 * HV3,
-        "split_us": mean_us(lambda: kda.chunk_prefill(*c3a, out=o3, final_state=sf3, workspace=ws3), n_part),
+        "auto": kda.prefill_partition(1, HV3, N3),
+        "split_us": mean_us(lambda: kda.chunk_prefill_split(*c3a, out=o3, final_state=sf3, workspace=ws3), n_part),
         "fused_us": mean_us(lambda: kda.chunk_prefill_fused(*c3a, out=o3, final_state=sf3), n_part),
     }
     del c3a, o3, sf3, ws3
@@ -729,7 +735,9 @@ def main():
     ws4 = torch.empty(kda.workspace_size(16, 2048, 64, 64), dtype=torch.uint8, device=dev)
     partitions["B=16 H=HV=64 T=2048"] = {
         "units": 16 * 64,
-        "split_us": mean_us(lambda: kda.chunk_prefill(*c4a, None, out=o4, final_state=sf4, workspace=ws4), n_part),
+        "auto": kda.prefill_partition(16, 64),
+        "split_us": mean_us(lambda: kda.chunk_prefill_split(*c4a, None, out=o4, final_state=sf4, workspace=ws4),
+                            n_part),
         "fused_us": mean_us(lambda: kda.chunk_prefill_fused(*c4a, None, out=o4, final_state=sf4), n_part),
     }
     del c4a, o4, sf4, ws4

@@ -78,7 +78,7 @@ const char* kda_build_id(void);
 int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream);
 
 /*
- * Numeric domain of the prefill (kda_chunk_prefill, kda_chunk_prefill_fused
+ * Numeric domain of the prefill (every kda_chunk_prefill* entry point
  * and the states they carry).  The carry's matrix products take v and the
  * running [K,V] state as fp16 operands (11-bit significand, float32
  * accumulation), so every |v| and every |state| entry -- the initial state
@@ -105,6 +105,19 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  * The last partial chunk of each sequence behaves as if zero-padded, as
  * the page's golden does; o is written only for real tokens.
  *
+ * Partition.  The page's design weighs two ways to spread this work, and
+ * both are built: the split form (kda_chunk_prefill_split: a chip-wide
+ * kernel writes each chunk's local matrices to the workspace, a second
+ * kernel carries the state through them) and the fused form
+ * (kda_chunk_prefill_fused: one workgroup per sequence and value head, no
+ * workspace traffic).  They give the same results bit for bit.  This entry
+ * point runs the fused form when N * HV (sequences times value heads) is at
+ * least 3/4 of the device's compute units (192 on MI355X) and the split
+ * form otherwise; kda_chunk_prefill_partition reports the choice.  Measured
+ * on MI355X: the fused form takes 0.74-0.93 of the split form's time from
+ * 192 units up and 1.7-2x at 96 units.  The workspace is checked either
+ * way, so the errors a call returns do not depend on the device.
+ *
  *   q, k           bf16 [B, T, H, K]   raw (unnormalised) queries and keys
  *   v              bf16 [B, T, HV, V]  magnitudes below 2^14
  *   g              fp32 [B, T, HV, K]  per-channel log decay (finite, <= 0)
@@ -120,15 +133,21 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *   num_seqs       N when cu_seqlens is given (>= 1); ignored otherwise
  *   o              bf16 [B, T, HV, V]  output
  *   final_state    fp32 [N, HV, K, V]  output, always written
- *   workspace      device scratch of at least
- *                  kda_chunk_prefill_workspace_size(...) bytes, owned by the
- *                  caller; its contents on entry do not matter and are
- *                  overwritten (the chunk-local matrices of every chunk).
+ *   workspace      device scratch owned by the caller, of
+ *                  workspace_bytes >= HV * KDA_PREFILL_SLOT_BYTES (one
+ *                  chunk slot per value head; fewer returns
+ *                  KDA_ERR_WORKSPACE).  The split form runs in windows of
+ *                  as many chunk slots as it holds, so
+ *                  kda_chunk_prefill_workspace_size(...) bytes (one window)
+ *                  is the fastest and a smaller workspace trades speed for
+ *                  memory; bytes beyond that size are not used.  Its
+ *                  contents on entry do not matter and are overwritten.
  *                  Calls that share a workspace must not overlap.
  * Sizes: B, T, H, HV >= 1 (T == 0 is accepted, may pass NULL token tensors,
  * and only writes final_state), HV % H == 0, K == V == 128.  q, k, v, g,
  * beta, o and the workspace must not alias.
  */
+#define KDA_PREFILL_SLOT_BYTES 66048
 int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* g, const void* beta,
                       const float* initial_state,
@@ -139,9 +158,37 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill
- * needs for these sizes (num_seqs as for kda_chunk_prefill; pass 0 when
- * cu_seqlens is NULL).  Returns 0 for sizes kda_chunk_prefill rejects.
+ * kda_chunk_prefill_split -- kda_chunk_prefill in the split form whatever
+ * the unit count (same arguments, workspace rules and results).  For
+ * callers that want the workspace-backed form explicitly, and for
+ * measuring the two forms side by side.
+ */
+int kda_chunk_prefill_split(const void* q, const void* k, const void* v,
+                            const float* g, const void* beta,
+                            const float* initial_state,
+                            const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t B, int32_t T, int32_t H, int32_t HV,
+                            int32_t K, int32_t V,
+                            void* o, float* final_state,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill_partition -- the form kda_chunk_prefill (and
+ * kda_chunk_prefill_noalloc) runs for these sizes on the current device:
+ * KDA_PARTITION_SPLIT or KDA_PARTITION_FUSED (num_seqs as for
+ * kda_chunk_prefill_workspace_size).  Returns -KDA_ERR_SHAPE for B or
+ * HV < 1.  Host query; enqueues nothing.  When the runtime reports no
+ * current device it answers for 256 compute units (MI355X).
+ */
+#define KDA_PARTITION_SPLIT 0
+#define KDA_PARTITION_FUSED 1
+int kda_chunk_prefill_partition(int32_t B, int32_t HV, int32_t num_seqs);
+
+/*
+ * kda_chunk_prefill_workspace_size -- bytes of workspace with which
+ * kda_chunk_prefill runs fastest for these sizes (num_seqs as for
+ * kda_chunk_prefill; pass 0 when cu_seqlens is NULL).  Returns 0 for sizes
+ * kda_chunk_prefill rejects.
  * It is one 66048-byte block per 64-token chunk slot and value head, for
  * one window of min(floor(B*T/64) + N + 1, floor(2^31 / (HV * 66048)))
  * slots (about 1 KB per token and value head, at most about 2 GiB): the
@@ -157,9 +204,10 @@ size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
  * and results (bit for bit), minus the workspace arguments.  The workspace
  * is instead a static device array inside the library,
  * KDA_NOALLOC_WORKSPACE_BYTES (64 MiB) per GPU, held from the library's
- * first use on that GPU until the process ends, and the prefill runs in
- * windows of as many chunk slots as it holds.  This entry point allocates
- * and frees nothing.
+ * first use on that GPU until the process ends, and the split form runs in
+ * windows of as many chunk slots as it holds.  It picks the partition as
+ * kda_chunk_prefill does (the fused form does not touch the array).  This
+ * entry point allocates and frees nothing.
  *
  * Limit: any B, T and N; HV <= 1016 (one 66048-byte slot per value head
  * must fit).  More value heads return KDA_ERR_WORKSPACE and enqueue nothing.
@@ -185,17 +233,12 @@ int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
  *
  * Defined on "KDA Chunk Prefill on Ascend A3", sections "Function and
  * tensor contract" and "Mathematical definition", exactly as
- * kda_chunk_prefill (same arguments minus the workspace, same results up
- * to floating-point rounding: both use the same per-chunk arithmetic and
- * operand precisions).  The page's design discussion weighs the two
- * partitions; this export lets them be measured side by side.  It
- * parallelises over N * HV (sequence, value head) units only, so it fills
- * the chip only when N * HV is at least the number of compute units.
- * Measured on MI355X (256 compute units): 2.0x slower than
- * kda_chunk_prefill at 96 units (B=1, HV=96, T=8192), even at 512 units
- * (16 variable-length sequences, HV=32) and 1.3x faster at 1024 units
- * (B=16, HV=64, T=2048) -- it saves the workspace round trip once the
- * units alone fill the chip twice over.
+ * kda_chunk_prefill (same arguments minus the workspace; the same results
+ * as the split form bit for bit: both use the same per-chunk
+ * arithmetic, operand precisions and accumulation orders).  It runs
+ * whatever the unit count; it parallelises over N * HV (sequence, value
+ * head) units only, so below about 3/4 of the compute units it leaves part
+ * of the chip idle (see "Partition" under kda_chunk_prefill).
  */
 int kda_chunk_prefill_fused(const void* q, const void* k, const void* v,
                             const float* g, const void* beta,
@@ -236,6 +279,11 @@ int kda_chunk_prefill_fused(const void* q, const void* k, const void* v,
  *   o              bf16 [B, HV, V]  (the [B, 1, HV, V] output)
  * Sizes: B >= 0 (0 enqueues nothing), H, HV >= 1, HV % H == 0,
  * K == V == 128.  Rows with the same active index race (undefined result).
+ * Batch invariance: a row's output and new state are the same bits
+ * whatever the batch it is decoded in.  (Two kernels serve different batch
+ * sizes -- column quarters of each (row, head) while 4 * B * HV is at most
+ * the device's compute units, whole (row, head) pairs above -- and both
+ * take the same arithmetic in the same order.)
  */
 int kda_decode(const void* q, const void* k, const void* v,
                const float* g, const void* beta,
@@ -273,7 +321,8 @@ int kda_decode(const void* q, const void* k, const void* v,
  *   state_pool, slot_stride, num_slots, state_indices   as kda_decode (HV = H)
  *   o              bf16 [B, H, V]  (the [B, 1, H, V] output)
  * Sizes: B >= 0 (0 enqueues nothing), H >= 1 (the page's operator is
- * specialised to H = 12), K == V == 128.
+ * specialised to H = 12), K == V == 128.  Batch invariant as kda_decode
+ * (the same two kernels, chosen the same way).
  */
 int kda_packed_decode(const void* mixed_qkv, int64_t qkv_row_stride,
                       const void* raw_gate, const void* raw_beta,

@@ -11,7 +11,10 @@ Entry points (same names as the C ABI, without the ``kda_`` prefix):
   qk_l2norm(x)                                    -> y
   chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
                                                   -> (o, final_state)
+  chunk_prefill_split(...same...)                 -> (o, final_state)
   chunk_prefill_fused(...same...)                 -> (o, final_state)
+  chunk_prefill_noalloc(...same...)               -> (o, final_state)
+  prefill_partition(B, HV, num_seqs=0)            -> "split" | "fused"
   decode(q, k, v, g, beta, state_pool, state_indices)   -> o
   packed_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool,
                 state_indices)                    -> o
@@ -25,8 +28,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
-EXPORTS = ("kda_status_string", "kda_build_id", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_fused",
-           "kda_chunk_prefill_noalloc", "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
+EXPORTS = ("kda_status_string", "kda_build_id", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_split",
+           "kda_chunk_prefill_fused", "kda_chunk_prefill_noalloc", "kda_chunk_prefill_partition",
+           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
            "kda_state_to_pool", "kda_chunk_backward", "kda_chunk_backward_workspace_size")
 
 _lib = None
@@ -58,6 +62,10 @@ def load():
     lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                       _vp, ctypes.c_size_t, _vp]
+    lib.kda_chunk_prefill_split.restype = ctypes.c_int
+    lib.kda_chunk_prefill_split.argtypes = lib.kda_chunk_prefill.argtypes
+    lib.kda_chunk_prefill_partition.restype = ctypes.c_int
+    lib.kda_chunk_prefill_partition.argtypes = [_i32, _i32, _i32]
     lib.kda_chunk_prefill_fused.restype = ctypes.c_int
     lib.kda_chunk_prefill_fused.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
@@ -182,26 +190,54 @@ def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     return dev, (B, T, H, HV, K, V), nseq_arg, out, final_state
 
 
+PREFILL_SLOT_BYTES = 66048   # kda.h KDA_PREFILL_SLOT_BYTES: the smallest workspace is HV of these
+
+
+def prefill_partition(B, HV, num_seqs=0):
+    """The form chunk_prefill runs for these sizes on the current device:
+    "split" or "fused" (num_seqs = 0 without cu_seqlens)."""
+    code = int(load().kda_chunk_prefill_partition(B, HV, num_seqs))
+    if code < 0:
+        _check(-code, "kda_chunk_prefill_partition")
+    return ("split", "fused")[code]
+
+
+def _prefill_with_workspace(entry, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, workspace):
+    lib = load()
+    dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(B, T, H, HV, nseq_arg, K, V), 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    code = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
+                               B, T, H, HV, K, V, _ptr(out), _ptr(final_state),
+                               _ptr(workspace), workspace.numel(), _stream())
+    _check(code, entry)
+    return out, final_state
+
+
 def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                   out=None, final_state=None, workspace=None):
     """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
     fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
     cu_seqlens int32 [N+1] (with B == 1) or None; workspace: a uint8 GPU
-    tensor of at least workspace_size(...) bytes, or None to allocate one.
+    tensor, or None to allocate workspace_size(...) bytes (the fastest
+    size; any size from HV * PREFILL_SLOT_BYTES up is accepted, the split
+    form then running in more windows).  The library picks the split or the
+    fused form (prefill_partition); both give the same result bit for bit.
     Returns (o, final_state)."""
-    lib = load()
-    dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
-        q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
-    need = workspace_size(B, T, H, HV, nseq_arg, K, V)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, 1, dev)
-    code = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
-                                 B, T, H, HV, K, V, _ptr(out), _ptr(final_state),
-                                 _ptr(workspace), workspace.numel(), _stream())
-    _check(code, "kda_chunk_prefill")
-    return out, final_state
+    return _prefill_with_workspace("kda_chunk_prefill", q, k, v, g, beta, initial_state, cu_seqlens,
+                                   out, final_state, workspace)
+
+
+def chunk_prefill_split(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                        out=None, final_state=None, workspace=None):
+    """chunk_prefill in the split form whatever the sizes (workspace-backed
+    chunk-parallel kernel plus carry kernel).  Arguments and result as
+    chunk_prefill."""
+    return _prefill_with_workspace("kda_chunk_prefill_split", q, k, v, g, beta, initial_state, cu_seqlens,
+                                   out, final_state, workspace)
 
 
 def backward_workspace_size(B, T, H, HV, num_seqs=0, K=128, V=128):

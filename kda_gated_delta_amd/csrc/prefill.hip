@@ -116,6 +116,7 @@ constexpr int WS_AQK = WS_KGT + KD * C * 2;
 constexpr int WS_A = WS_AQK + C * C * 2;
 constexpr int WS_GAM = WS_A + C * C * 2;
 constexpr int WS_SLOT = WS_GAM + KD * 4;          // 66048 bytes
+static_assert(WS_SLOT == KDA_PREFILL_SLOT_BYTES, "workspace slot size differs from the header's");
 static_assert(WS_SLOT % 16 == 0, "slots stay 16-byte aligned");
 
 // LDS row strides (elements).  Row strides of 68 or 36 words put eight
@@ -1377,17 +1378,7 @@ int set_lds(Kern kern, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
 
 int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq + 1; }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
+using kda::device_cus;
 
 // The split form runs over windows of chunk slots: the chunk-parallel kernel
 // fills the window's slots of every value head, then the carry kernel walks
@@ -1491,6 +1482,32 @@ extern "C" size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t
   return size_t((w > 0 ? w : 1) * HV) * WS_SLOT;
 }
 
+// The partition kda_chunk_prefill runs.  The fused form walks each
+// (sequence, value head) unit's chunks on one compute unit with no workspace;
+// the split form spreads the chunk-local work over the whole chip and pays
+// the workspace round trip and a second, latency-bound kernel.  Measured on
+// MI355X (256 compute units, T = 1024 to 8192): the fused form takes 0.74 to
+// 0.93 of the split form's time from 192 units up, and 2x at 96 units, so it
+// is chosen from 3/4 as many units as compute units.  Both give the same
+// results bit for bit.
+bool use_fused(int64_t units) { return units * 4 >= int64_t(device_cus()) * 3; }
+
+// Checks the caller's workspace and points p at it: windows of as many slots
+// as it holds, up to the one window kda_chunk_prefill_workspace_size sizes.
+// Both the split and the automatic entry point check it, so a call's errors
+// do not depend on the partition the device picks.
+int take_workspace(Params& p, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
+                   void* workspace, size_t workspace_bytes) {
+  if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+  if (!workspace) return KDA_ERR_NULL;
+  const size_t per = size_t(HV) * WS_SLOT;
+  if (workspace_bytes < per) return KDA_ERR_WORKSPACE;
+  const size_t full = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N);
+  p.ws = static_cast<unsigned char*>(workspace);
+  p.wslots = int64_t((workspace_bytes < full ? workspace_bytes : full) / per);
+  return KDA_OK;
+}
+
 extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
                                  const void* beta, const float* initial_state,
                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
@@ -1501,12 +1518,29 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
   const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
                          final_state, p);
   if (st != KDA_OK) return st;
-  if (!aligned16(workspace)) return KDA_ERR_ALIGN;
-  const size_t need = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N);
-  if (!workspace) return KDA_ERR_NULL;
-  if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
-  p.ws = static_cast<unsigned char*>(workspace);
-  p.wslots = need / (int64_t(HV) * WS_SLOT);
+  const int wst = take_workspace(p, B, T, H, HV, Kd, Vd, workspace, workspace_bytes);
+  if (wst != KDA_OK) return wst;
+  return use_fused(int64_t(p.N) * HV) ? launch_fused(p, as_stream(stream)) : launch(p, as_stream(stream));
+}
+
+extern "C" int kda_chunk_prefill_partition(int32_t B, int32_t HV, int32_t num_seqs) {
+  if (B < 1 || HV < 1) return -KDA_ERR_SHAPE;
+  const int64_t nseq = num_seqs > 0 ? num_seqs : B;
+  return use_fused(nseq * HV) ? KDA_PARTITION_FUSED : KDA_PARTITION_SPLIT;
+}
+
+extern "C" int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const float* g,
+                                       const void* beta, const float* initial_state,
+                                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                                       int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd,
+                                       void* o, float* final_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  Params p;
+  const int st = prepare(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, HV, Kd, Vd, o,
+                         final_state, p);
+  if (st != KDA_OK) return st;
+  const int wst = take_workspace(p, B, T, H, HV, Kd, Vd, workspace, workspace_bytes);
+  if (wst != KDA_OK) return wst;
   return launch(p, as_stream(stream));
 }
 
@@ -1546,6 +1580,7 @@ extern "C" int kda_chunk_prefill_noalloc(const void* q, const void* k, const voi
   // Windows of as many slots as the static workspace holds.
   p.wslots = window_slots(p.nslots, HV, int64_t(kNoAllocScratch));
   if (p.wslots < 1) return KDA_ERR_WORKSPACE;
+  if (use_fused(int64_t(p.N) * HV)) return launch_fused(p, as_stream(stream));   // the array is not touched
   void* ws = scratch_address();
   if (!ws) return KDA_ERR_HIP;
   p.ws = static_cast<unsigned char*>(ws);

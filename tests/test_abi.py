@@ -1,8 +1,10 @@
 """The C-ABI library loads on the host and exports every entry point that
 include/kda.h declares; metadata errors are reported without touching a GPU
-(each failing call returns before any HIP runtime call)."""
+(each failing call returns before any HIP runtime call).  The partition
+query only asks the HIP runtime for the device's compute-unit count."""
 
 import ctypes
+import functools
 import os
 import re
 
@@ -21,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_prefill", "kda_chunk_prefill_fused", "kda_chunk_prefill_workspace_size", "kda_decode",
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_split", "kda_chunk_prefill_fused",
+              "kda_chunk_prefill_partition", "kda_chunk_prefill_workspace_size", "kda_decode",
               "kda_qk_l2norm",
               "kda_packed_decode", "kda_state_to_pool", "kda_status_string",
               "kda_chunk_backward", "kda_chunk_backward_workspace_size"):
@@ -63,17 +66,19 @@ def test_l2norm_metadata_errors():
     assert lib.kda_qk_l2norm(MISALIGNED, FAKE, 4, 128, NULL) == 4
 
 
-def _prefill(lib, **kw):
+def _prefill(lib, entry="kda_chunk_prefill", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=NULL, cu=NULL, n=0,
              B=1, T=64, H=1, HV=1, K=128, V=128, o=FAKE, fs=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.kda_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
-                                 a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"],
-                                 a["ws"], a["wsb"], NULL)
+    return getattr(lib, entry)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"],
+                               a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["o"], a["fs"],
+                               a["ws"], a["wsb"], NULL)
 
 
-def test_prefill_metadata_errors():
+@pytest.mark.parametrize("entry", ["kda_chunk_prefill", "kda_chunk_prefill_split"])
+def test_prefill_metadata_errors(entry):
     lib = kda.load()
+    _prefill = functools.partial(globals()["_prefill"], entry=entry)
     assert _prefill(lib, q=NULL) == 1
     assert _prefill(lib, fs=NULL) == 1
     assert _prefill(lib, H=3, HV=4) == 2
@@ -86,6 +91,27 @@ def test_prefill_metadata_errors():
     assert _prefill(lib, v=MISALIGNED) == 4
     assert _prefill(lib, ws=NULL) == 1
     assert _prefill(lib, wsb=1000) == 5                    # KDA_ERR_WORKSPACE
+    # the smallest workspace is one 66048-byte chunk slot per value head,
+    # whatever the unit count (so the errors do not depend on the partition)
+    assert kda.PREFILL_SLOT_BYTES == 66048
+    assert _prefill(lib, H=2, HV=4, wsb=4 * 66048 - 16) == 5
+    assert _prefill(lib, B=64, H=64, HV=64, wsb=64 * 66048 - 16) == 5
+
+
+def test_partition_query():
+    """kda_chunk_prefill runs the fused form from 3/4 as many (sequence,
+    value head) units as compute units; without a device the query takes
+    MI355X's 256, which is also the count on the MI355X."""
+    lib = kda.load()
+    assert lib.kda_chunk_prefill_partition(1, 96, 0) == 0           # 96 units: split
+    assert lib.kda_chunk_prefill_partition(1, 191, 0) == 0
+    assert lib.kda_chunk_prefill_partition(1, 192, 0) == 1          # 192 = 3/4 of 256: fused
+    assert lib.kda_chunk_prefill_partition(16, 64, 0) == 1
+    assert lib.kda_chunk_prefill_partition(1, 32, 16) == 1          # 16 packed sequences x 32 heads
+    assert lib.kda_chunk_prefill_partition(1, 32, 5) == 0
+    assert lib.kda_chunk_prefill_partition(0, 32, 0) == -2
+    assert lib.kda_chunk_prefill_partition(1, 0, 0) == -2
+    assert kda.prefill_partition(1, 96) == "split" and kda.prefill_partition(4, 64) == "fused"
 
 
 def test_workspace_size_formula():

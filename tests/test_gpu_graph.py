@@ -1,6 +1,7 @@
 """The library under HIP graph capture: kda_decode (the page's -1 rows are
 "graph padding", so the decode is meant to be captured) and
-kda_chunk_prefill with a caller-owned workspace are captured once, then
+kda_chunk_prefill with a caller-owned workspace (in both of the forms it
+picks between: split at a few units, fused at 256) are captured once, then
 replayed on new inputs copied into the captured buffers; every replay must
 equal a direct call on the same inputs bit for bit.  Eager work and host
 synchronisations run between the replays.
@@ -51,10 +52,11 @@ def test_decode_graph_replay(gpu_lib):
         say(f"decode graph replay {r}: identical to the direct call")
 
 
-def test_prefill_graph_replay(gpu_lib):
+@pytest.mark.parametrize("B,T,H,HV", [(1, 300, 2, 4), (4, 300, 16, 64)], ids=["split", "fused"])
+def test_prefill_graph_replay(gpu_lib, B, T, H, HV):
     kda = gpu_lib
     dev = "cuda"
-    B, T, H, HV = 1, 300, 2, 4
+    assert kda.prefill_partition(B, HV) == ("split" if B * HV < 192 else "fused")
     first = synth.prefill_basic(50, B, T, H, HV, init="normal0.1")
     names = ("q", "k", "v", "g", "beta", "initial_state")
     static = {n: getattr(first, n).to(dev) for n in names}

@@ -60,7 +60,7 @@ def _check(kda, inp, pad=0):
     assert torch.equal(pool[torch.from_numpy(others).cuda()], before[torch.from_numpy(others).cuda()])
 
 
-@pytest.mark.parametrize("B", [1, 8, 32, 256])
+@pytest.mark.parametrize("B", [1, 4, 8, 32, 256])
 def test_packed_decode_workload(gpu_lib, B):
     _check(gpu_lib, synth.packed_decode_config(B))
 
@@ -102,3 +102,28 @@ def test_packed_equals_split_decode_at_closed_form_point(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
     assert torch.equal(pool_a.view(torch.int16), pool_b.view(torch.int16))
+
+
+def test_packed_decode_batch_invariant(gpu_lib):
+    """As for kda_decode: the small-batch and the large-batch kernel give the
+    same bits, so rows of a 256-row batch decoded alone or in 5-, 6-, 31-
+    and 32-row batches equal the full batch's rows."""
+    inp = synth.packed_decode_config(256, row_pad=24)
+    dev = "cuda"
+    H, K = inp.H, 128
+    qkv = inp.mixed_qkv.to(dev)[:, : 3 * H * K]
+    a = [t.to(dev) for t in (inp.raw_gate, inp.raw_beta)]
+    A_log, dt_bias = inp.A_log.to(dev), inp.dt_bias.to(dev)
+    idx = inp.state_indices.to(dev)
+    pool_full = inp.pool.to(dev)
+    o_full = gpu_lib.packed_decode(qkv, *a, A_log, dt_bias, pool_full, idx)
+    torch.cuda.synchronize()
+    for lo, hi in ((0, 31), (31, 63), (200, 201), (10, 15), (20, 26)):
+        say(f"packed decode rows {lo}..{hi - 1} alone (B={hi - lo})")
+        pool = inp.pool.to(dev)
+        o = gpu_lib.packed_decode(qkv[lo:hi], *(t[lo:hi] for t in a), A_log, dt_bias, pool, idx[lo:hi])
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_full[lo:hi].view(torch.int16)), f"rows {lo}..{hi}: o differs"
+        act = idx[lo:hi][idx[lo:hi] >= 0].long()
+        assert torch.equal(pool[act].view(torch.int16), pool_full[act].view(torch.int16)), \
+            f"rows {lo}..{hi}: state differs"

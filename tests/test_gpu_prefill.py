@@ -157,21 +157,27 @@ def test_state_near_domain_bound(gpu_lib):
 
 
 def test_many_windows_varlen(gpu_lib):
-    """512 value heads make the allocation-free entry point's slot windows
-    (64 MiB) one slot long, so sequences span many windows (the state
+    """A workspace of one chunk slot per value head makes the split form's
+    windows one slot long, so sequences span many windows (the state
     crossing them through final_state) and empty and one-token sequences
     sit inside later windows; compared in full against the oracle, and
-    bitwise against the single-window call."""
+    bitwise against the single-window split call, the allocation-free call
+    and the automatic call (both fused here: 7 x 512 units)."""
     lens = [100, 0, 1, 64, 200, 0, 37]
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
     inp = synth.prefill_basic(97, 1, int(cu[-1]), 256, 512, init="normal0.1", cu_seqlens=cu,
                               name="varlen_512heads")
     dev = "cuda"
     a = [t.to(dev) for t in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.initial_state, inp.cu_seqlens)]
-    o, s = gpu_lib.chunk_prefill_noalloc(*a)
-    o1, s1 = gpu_lib.chunk_prefill(*a)
+    one_slot = torch.empty(512 * gpu_lib.PREFILL_SLOT_BYTES, dtype=torch.uint8, device=dev)
+    o, s = gpu_lib.chunk_prefill_split(*a, workspace=one_slot)
+    runs = {"split, one window": gpu_lib.chunk_prefill_split(*a),
+            "allocation-free": gpu_lib.chunk_prefill_noalloc(*a),
+            "automatic": gpu_lib.chunk_prefill(*a)}
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o1.view(torch.int16)) and torch.equal(s, s1)
+    assert gpu_lib.prefill_partition(1, 512, len(lens)) == "fused"
+    for what, (o1, s1) in runs.items():
+        assert torch.equal(o.view(torch.int16), o1.view(torch.int16)) and torch.equal(s, s1), what
     o_ref, s_ref = _ref(inp)
     eo = check_o(o, o_ref, inp.name)
     es = check_state(s, s_ref, inp.name)

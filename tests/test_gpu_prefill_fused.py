@@ -1,13 +1,15 @@
-"""kda_chunk_prefill_fused (the fused partition) on the GPU.
+"""The two prefill partitions on the GPU: kda_chunk_prefill_fused,
+kda_chunk_prefill_split and kda_chunk_prefill, which picks one of them.
 
 Both partitions run the same per-chunk arithmetic with the same operand
 precisions and the same MFMA accumulation orders; the split form only
 passes the chunk-local matrices through the workspace, which stores exactly
 the values the fused form reads from LDS.  So the fused results must equal
-the split results bit for bit, which is checked on every workload shape the
-split form is tested on (the split form itself is checked against the
-oracle in test_gpu_prefill.py); a few cases are also compared with the
-oracle directly.
+the split results bit for bit, and the automatic entry point must equal
+both, which is checked on every workload shape the prefill is tested on
+(kda_chunk_prefill itself is checked against the oracle in
+test_gpu_prefill.py); a few cases are also compared with the oracle
+directly.
 """
 
 import numpy as np
@@ -28,19 +30,18 @@ def _args(inp):
     return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), s0, cu)
 
 
-def _both(kda, inp):
-    say(f"fused vs split {inp.name} shape={inp.shape}")
-    a = _args(inp)
-    of, sf = kda.chunk_prefill_fused(*a)
-    os_, ss = kda.chunk_prefill(*a)
-    torch.cuda.synchronize()
-    return of, sf, os_, ss
-
-
 def _bitwise(kda, inp):
-    of, sf, os_, ss = _both(kda, inp)
-    assert torch.equal(of.view(torch.int16), os_.view(torch.int16)), f"{inp.name}: o differs"
-    assert torch.equal(sf, ss), f"{inp.name}: final state differs"
+    a = _args(inp)
+    N = inp.cu_seqlens.numel() - 1 if inp.cu_seqlens is not None else 0
+    say(f"fused vs split vs automatic ({kda.prefill_partition(inp.q.shape[0], inp.v.shape[2], N)}) "
+        f"{inp.name} shape={inp.shape}")
+    of, sf = kda.chunk_prefill_fused(*a)
+    os_, ss = kda.chunk_prefill_split(*a)
+    oa, sa = kda.chunk_prefill(*a)
+    torch.cuda.synchronize()
+    for what, (o, s) in (("split", (os_, ss)), ("automatic", (oa, sa))):
+        assert torch.equal(of.view(torch.int16), o.view(torch.int16)), f"{inp.name}: o differs ({what})"
+        assert torch.equal(sf, s), f"{inp.name}: final state differs ({what})"
     return of, sf
 
 
@@ -113,3 +114,20 @@ def test_fused_many_units_varlen(gpu_lib):
     """The packed 16-sequence GQA batch (512 units, more than the compute
     units), fused == split bitwise."""
     _bitwise(gpu_lib, synth.config3())
+
+
+def test_partition_choice_on_device(gpu_lib):
+    """On MI355X (256 compute units) the automatic entry point runs the
+    split form at the 96-unit workload and the fused form from 192 units."""
+    kda = gpu_lib
+    assert kda.prefill_partition(1, 96) == "split"
+    assert kda.prefill_partition(1, 191) == "split"
+    assert kda.prefill_partition(1, 192) == "fused"
+    assert kda.prefill_partition(1, 32, 16) == "fused"
+    assert kda.prefill_partition(16, 64) == "fused"
+
+
+def test_fused_crossover_shapes(gpu_lib):
+    """Either side of the crossover (191 and 192 units), all three equal."""
+    _bitwise(gpu_lib, synth.prefill_basic(95, 1, 130, 1, 191, init="normal0.1", name="units191"))
+    _bitwise(gpu_lib, synth.prefill_basic(96, 1, 130, 1, 192, init="normal0.1", name="units192"))
