@@ -188,7 +188,10 @@ __global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict
     const float kd = (s_red[0][0][c] + s_red[0][1][c]) + (s_red[0][2][c] + s_red[0][3][c]);
     rr[j] = s_v[c] - kd;
   }
-  // S' = S_decay + beta k r^T, stored rounded to bf16 in place.
+  // S' = S_decay + beta k r^T, stored rounded to bf16 in place, with the
+  // nontemporal hint (the slot is not read again by this step; measured 2.5%
+  // faster at B = 256 after a prefill, where the same hint on the loads was
+  // slower).
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float bk = bt * s_k[kr + 16 * i];
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict
     out.y = kda::pack_bf16(fmaf(bk, rr[2], sd[i][2]), fmaf(bk, rr[3], sd[i][3]));
     out.z = kda::pack_bf16(fmaf(bk, rr[4], sd[i][4]), fmaf(bk, rr[5], sd[i][5]));
     out.w = kda::pack_bf16(fmaf(bk, rr[6], sd[i][6]), fmaf(bk, rr[7], sd[i][7]));
-    slot[(kr + 16 * i) * (V / 8) + cg] = out;
+    kda::store_nt(&slot[(kr + 16 * i) * (V / 8) + cg], out);
   }
   // o = K^-1/2 q^T S' = K^-1/2 (q^T S_decay + beta (q.k) r), from the unrounded S'.
   if (kr == 0) {

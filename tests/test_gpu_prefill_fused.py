@@ -131,3 +131,21 @@ def test_fused_crossover_shapes(gpu_lib):
     """Either side of the crossover (191 and 192 units), all three equal."""
     _bitwise(gpu_lib, synth.prefill_basic(95, 1, 130, 1, 191, init="normal0.1", name="units191"))
     _bitwise(gpu_lib, synth.prefill_basic(96, 1, 130, 1, 192, init="normal0.1", name="units192"))
+
+
+def test_fused_longest_first_order_ties_and_empties(gpu_lib):
+    """Packed sequences are taken longest first (ties by index); lengths with
+    equal chunk counts, empty and one-token sequences, 9 x 24 = 216 units."""
+    lens = [64, 130, 0, 1, 129, 65, 64, 200, 0]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    _bitwise(gpu_lib, synth.prefill_basic(97, 1, int(cu[-1]), 8, 24, init="normal0.1", cu_seqlens=cu,
+                                          name="varlen_ties"))
+
+
+def test_fused_more_sequences_than_threads(gpu_lib):
+    """600 packed sequences (more than the 512 a workgroup ranks): index order."""
+    rng = np.random.default_rng(98)
+    lens = rng.integers(0, 40, size=600)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    _bitwise(gpu_lib, synth.prefill_basic(98, 1, int(cu[-1]), 1, 1, init="normal0.1", cu_seqlens=cu,
+                                          name="varlen_600"))
