@@ -39,16 +39,18 @@ struct SplitInputs {
     const int hq = hv / (HV / H);
     return (key ? k : q) + (int64_t(b) * H + hq) * (K / 8);
   }
-  __device__ float decay(int b, int hv, int HV, int j) const {
-    return expf(g[(int64_t(b) * HV + hv) * K + j]);
-  }
-  __device__ float value(int b, int hv, int HV, int j) const {
-    return kda::bf16f(v[(int64_t(b) * HV + hv) * V + j]);
-  }
+  // The decay of channel j: loaded (decay_load), then formed (decay_of).
+  struct DecayIn {
+    float g;
+  };
+  __device__ DecayIn decay_load(int b, int hv, int HV, int j) const { return {g[(int64_t(b) * HV + hv) * K + j]}; }
+  __device__ float decay_of(const DecayIn& d) const { return expf(d.g); }
+  __device__ uint16_t value_load(int b, int hv, int HV, int j) const { return v[(int64_t(b) * HV + hv) * V + j]; }
   __device__ uint4 value8(int b, int hv, int HV, int j0) const {
     return *reinterpret_cast<const uint4*>(v + (int64_t(b) * HV + hv) * V + j0);
   }
-  __device__ float beta_of(int b, int hv, int HV) const { return kda::bf16f(beta[int64_t(b) * HV + hv]); }
+  __device__ uint16_t beta_load(int b, int hv, int HV) const { return beta[int64_t(b) * HV + hv]; }
+  __device__ float beta_of(uint16_t raw) const { return kda::bf16f(raw); }
 };
 
 // Page "flashinfer.kda_decode.packed_kda_decode": one packed bf16 row per
@@ -69,21 +71,55 @@ struct PackedInputs {
   __device__ const uint4* qk_row(int b, int hv, int HV, bool key) const {
     return reinterpret_cast<const uint4*>(qkv + int64_t(b) * row_stride + (key ? HV * K : 0) + hv * K);
   }
-  __device__ float decay(int b, int hv, int HV, int j) const {
-    const float x = kda::bf16f(raw_gate[(int64_t(b) * HV + hv) * K + j]) + dt_bias[hv * K + j];
-    const float z = expf(A_log[hv]) * x;
+  struct DecayIn {
+    uint16_t raw;
+    float bias, alog;
+  };
+  __device__ DecayIn decay_load(int b, int hv, int HV, int j) const {
+    return {raw_gate[(int64_t(b) * HV + hv) * K + j], dt_bias[hv * K + j], A_log[hv]};
+  }
+  __device__ float decay_of(const DecayIn& d) const {
+    const float x = kda::bf16f(d.raw) + d.bias;
+    const float z = expf(d.alog) * x;
     return expf(kLowerBound / (1.0f + expf(-z)));
   }
-  __device__ float value(int b, int hv, int HV, int j) const {
-    return kda::bf16f(qkv[int64_t(b) * row_stride + 2 * HV * K + hv * V + j]);
+  __device__ uint16_t value_load(int b, int hv, int HV, int j) const {
+    return qkv[int64_t(b) * row_stride + 2 * HV * K + hv * V + j];
   }
   __device__ uint4 value8(int b, int hv, int HV, int j0) const {
     return *reinterpret_cast<const uint4*>(qkv + int64_t(b) * row_stride + 2 * HV * K + hv * V + j0);
   }
-  __device__ float beta_of(int b, int hv, int HV) const {
-    return 1.0f / (1.0f + expf(-kda::bf16f(raw_beta[int64_t(b) * HV + hv])));
-  }
+  __device__ uint16_t beta_load(int b, int hv, int HV) const { return raw_beta[int64_t(b) * HV + hv]; }
+  __device__ float beta_of(uint16_t raw) const { return 1.0f / (1.0f + expf(-kda::bf16f(raw))); }
 };
+
+// An empty asm that claims to change its operand: nothing that reads the
+// value can move above it, and the load that produced it must be complete
+// there.  Used to hold a wave's per-row inputs until its state loads are
+// issued.
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint16_t& x) {
+  uint32_t y = x;
+  pin(y);
+  x = uint16_t(y);
+}
+__device__ __forceinline__ void pin(float& x) {
+  uint32_t y = __builtin_bit_cast(uint32_t, x);
+  pin(y);
+  x = __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ void pin(uint4& x) {
+  pin(x.x);
+  pin(x.y);
+  pin(x.z);
+  pin(x.w);
+}
+__device__ __forceinline__ void pin(SplitInputs::DecayIn& d) { pin(d.g); }
+__device__ __forceinline__ void pin(PackedInputs::DecayIn& d) {
+  pin(d.raw);
+  pin(d.bias);
+  pin(d.alog);
+}
 
 template <class In>
 __global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict__ pool, int64_t slot_stride,
@@ -106,17 +142,34 @@ __global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict
     return;
   }
 
+  // The per-row inputs are loaded before the state: the vector-memory counter
+  // completes in order, so waiting for them leaves the 32 KB of state in
+  // flight while the norm and the decay are formed (measured 3% faster, and
+  // 8% for the packed inputs, whose decay takes three exponentials).  Every
+  // wave issues all of them at the same addresses (the copies hit in the
+  // caches) and pins them after its state loads, so that neither the loads
+  // nor their uses move into the per-wave branches, where a masked-off path
+  // would wait for them.
+  const int l64 = t & 63;
+  uint4 xl = *(in.qk_row(b, hv, HV, l64 >= 16) + (l64 & 15));   // lanes 0-15 q, 16-31 k
+  typename In::DecayIn d0 = in.decay_load(b, hv, HV, l64);
+  typename In::DecayIn d1 = in.decay_load(b, hv, HV, l64 + 64);
+  uint16_t vr0 = in.value_load(b, hv, HV, l64);
+  uint16_t vr1 = in.value_load(b, hv, HV, l64 + 64);
+  const uint16_t braw = in.beta_load(b, hv, HV);
+
   uint4* slot = reinterpret_cast<uint4*>(pool + idx * slot_stride + int64_t(hv) * K * V);
   uint4 sv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sv[i] = slot[(kr + 16 * i) * (V / 8) + cg];
+  pin(xl);
+  pin(d0);
+  pin(d1);
+  pin(vr0);
+  pin(vr1);
 
   if (wave == 0) {
-    // Lanes 0-15 hold the q row, 16-31 the k row; the loads are unconditional
-    // (a load inside a branch would be waited for inside it).
     const int lane = t;
-    const uint4* src = in.qk_row(b, hv, HV, lane >= 16) + (lane & 15);
-    const uint4 xl = *src;
     const uint4 x = lane < 32 ? xl : make_uint4(0u, 0u, 0u, 0u);
     uint4 y = kda::l2norm_row16(x);
     float* dst = lane < 16 ? s_q : s_k;
@@ -130,15 +183,13 @@ __global__ __launch_bounds__(256) void decode_kernel(In in, uint16_t* __restrict
       }
     }
   } else if (wave == 1) {
-    const int j = t - 64;
-    s_eg[j] = in.decay(b, hv, HV, j);
-    s_eg[j + 64] = in.decay(b, hv, HV, j + 64);
+    s_eg[l64] = in.decay_of(d0);
+    s_eg[l64 + 64] = in.decay_of(d1);
   } else if (wave == 2) {
-    const int j = t - 128;
-    s_v[j] = in.value(b, hv, HV, j);
-    s_v[j + 64] = in.value(b, hv, HV, j + 64);
+    s_v[l64] = kda::bf16f(vr0);
+    s_v[l64 + 64] = kda::bf16f(vr1);
   }
-  const float bt = in.beta_of(b, hv, HV);
+  const float bt = in.beta_of(braw);
   __syncthreads();
 
   float sd[8][8];
@@ -281,18 +332,27 @@ __global__ __launch_bounds__(64) void decode_quarter_kernel(In in, uint16_t* __r
     return;
   }
 
+  // Per-row inputs first, then the state, as in decode_kernel.  q^ (lanes
+  // 0-15) and k^ (lanes 16-31), 8 elements per lane; lanes 32-63 normalise a
+  // zero row alongside.
+  uint4 xl = *(in.qk_row(b, hv, HV, (lane & 16) != 0) + (lane & 15));
+  uint4 vv = in.value8(b, hv, HV, c0);
+  typename In::DecayIn d0 = in.decay_load(b, hv, HV, lane);
+  typename In::DecayIn d1 = in.decay_load(b, hv, HV, lane + 64);
+  const uint16_t braw = in.beta_load(b, hv, HV);
+
   uint4* slot = reinterpret_cast<uint4*>(pool + idx * slot_stride + int64_t(hv) * K * V);
   uint4 sv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sv[i] = slot[((rg + 16 * i) * V + c0) / 8];
+  pin(xl);
+  pin(vv);
+  pin(d0);
+  pin(d1);
 
-  // q^ (lanes 0-15) and k^ (lanes 16-31), 8 elements per lane; the loads
-  // are unconditional and lanes 32-63 normalise a zero row alongside.
-  const uint4 xl = *(in.qk_row(b, hv, HV, (lane & 16) != 0) + (lane & 15));
   const uint4 x = lane < 32 ? xl : make_uint4(0u, 0u, 0u, 0u);
-  const uint4 vv = in.value8(b, hv, HV, c0);
-  const float e0 = in.decay(b, hv, HV, lane), e1 = in.decay(b, hv, HV, lane + 64);
-  const float bt = in.beta_of(b, hv, HV);
+  const float e0 = in.decay_of(d0), e1 = in.decay_of(d1);
+  const float bt = in.beta_of(braw);
   const uint4 y = kda::l2norm_row16(x);
   if (lane < 32) {
     float* dst = s_x[lane < 16 ? 0 : 1] + (lane & 15) * 8;
