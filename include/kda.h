@@ -140,8 +140,10 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *                  as many chunk slots as it holds, so
  *                  kda_chunk_prefill_workspace_size(...) bytes (one window)
  *                  is the fastest and a smaller workspace trades speed for
- *                  memory; bytes beyond that size are not used.  Its
- *                  contents on entry do not matter and are overwritten.
+ *                  memory; bytes beyond that size are not used.  When
+ *                  kda_chunk_prefill_partition reports the fused form, the
+ *                  workspace is checked but not touched, so the minimum
+ *                  suffices.  Its contents on entry do not matter.
  *                  Calls that share a workspace must not overlap.
  * Sizes: B, T, H, HV >= 1 (T == 0 is accepted, may pass NULL token tensors,
  * and only writes final_state), HV % H == 0, K == V == 128.  q, k, v, g,

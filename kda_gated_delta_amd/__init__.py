@@ -207,7 +207,11 @@ def _prefill_with_workspace(entry, q, k, v, g, beta, initial_state, cu_seqlens, 
     dev, (B, T, H, HV, K, V), nseq_arg, out, final_state = _prefill_args(
         q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     if workspace is None:
-        workspace = torch.empty(max(workspace_size(B, T, H, HV, nseq_arg, K, V), 16), dtype=torch.uint8, device=dev)
+        if entry == "kda_chunk_prefill" and prefill_partition(B, HV, nseq_arg) == "fused":
+            need = HV * PREFILL_SLOT_BYTES     # checked, never touched by the fused form
+        else:
+            need = workspace_size(B, T, H, HV, nseq_arg, K, V)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
     code = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(initial_state), _ptr(cu_seqlens), nseq_arg,
@@ -222,10 +226,12 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     """KDA prefill.  q, k [B,T,H,K] bf16; v [B,T,HV,V] bf16; g [B,T,HV,K]
     fp32; beta [B,T,HV] bf16; initial_state [N,HV,K,V] fp32 or None;
     cu_seqlens int32 [N+1] (with B == 1) or None; workspace: a uint8 GPU
-    tensor, or None to allocate workspace_size(...) bytes (the fastest
-    size; any size from HV * PREFILL_SLOT_BYTES up is accepted, the split
-    form then running in more windows).  The library picks the split or the
-    fused form (prefill_partition); both give the same result bit for bit.
+    tensor, or None to allocate one (workspace_size(...) bytes, the fastest
+    size for the split form; any size from HV * PREFILL_SLOT_BYTES up is
+    accepted, the split form then running in more windows).  The library
+    picks the split or the fused form (prefill_partition); both give the same
+    result bit for bit.  The fused form does not touch the workspace, so for
+    it only the minimum is allocated.
     Returns (o, final_state)."""
     return _prefill_with_workspace("kda_chunk_prefill", q, k, v, g, beta, initial_state, cu_seqlens,
                                    out, final_state, workspace)
