@@ -111,3 +111,41 @@ def test_decode_batch_invariant(gpu_lib):
         act = idx[lo:hi][idx[lo:hi] >= 0].long()
         assert torch.equal(pool[act].view(torch.int16), pool_full[act].view(torch.int16)), \
             f"rows {lo}..{hi}: state differs"
+
+
+def test_decode_max_batch(gpu_lib):
+    """The largest batch kda_decode accepts (B = 65535, the launch grid's
+    limit), one head, a 2 GiB pool generated on the device: 256 sampled rows
+    against the oracle, their inactive rows zero, and every slot no row
+    addresses left untouched."""
+    B, N = 65535, 65535 + 17
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(30)
+    q = torch.randn(B, 1, 128, generator=gen).to(torch.bfloat16)
+    k = torch.randn(B, 1, 128, generator=gen).to(torch.bfloat16)
+    v = torch.randn(B, 1, 128, generator=gen).to(torch.bfloat16)
+    g = torch.nn.functional.logsigmoid(torch.randn(B, 1, 128, generator=gen) + 3.0)
+    beta = torch.sigmoid(torch.randn(B, 1, generator=gen)).to(torch.bfloat16)
+    idx = torch.randperm(N, generator=gen)[:B].to(torch.int32)
+    idx[torch.arange(B) % 8 == 7] = -1
+    dgen = torch.Generator(device=dev).manual_seed(31)
+    pool = (0.1 * torch.randn(N, 1, 128, 128, generator=dgen, device=dev)).to(torch.bfloat16)
+    rows = torch.randperm(B, generator=gen)[:256].sort().values
+    used = torch.zeros(N, dtype=torch.bool)
+    used[idx[idx >= 0].long()] = True
+    free_slots = torch.nonzero(~used).flatten().to(dev)
+    act = [int(r) for r in rows if idx[r] >= 0]
+    before_rows = pool[idx[act].long().to(dev)].float().cpu().numpy()
+    before_free = pool[free_slots].clone()
+    say(f"decode B={B}: {len(act)} sampled active rows, {free_slots.numel()} unaddressed slots")
+    o = gpu_lib.decode(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev), pool, idx.to(dev))
+    torch.cuda.synchronize()
+    sub = lambda t: t[rows].float().numpy()
+    remap = np.array([act.index(int(r)) if idx[r] >= 0 else -1 for r in rows], np.int32)
+    o_ref, new_ref = oracle.decode_step(sub(q), sub(k), sub(v), sub(g), sub(beta), before_rows, remap)
+    check_o(o[rows.to(dev), 0], o_ref, "decode max batch")
+    og = o[rows.to(dev), 0].float().cpu().numpy()
+    assert np.all(og[remap < 0] == 0), "inactive rows not zero"
+    got = pool[idx[act].long().to(dev)].float().cpu().numpy()
+    assert np.all(np.abs(got - new_ref) <= np.abs(new_ref) * 2.0 ** -7 + 1e-6 * np.abs(new_ref).max())
+    assert torch.equal(pool[free_slots], before_free), "an unaddressed slot changed"

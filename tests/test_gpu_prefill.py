@@ -330,3 +330,16 @@ def test_fused_normalisation_bit_exact(gpu_lib):
             bad_k += np.count_nonzero(kgt.view(np.float16) != want_k)
     say(f"fused normalisation: q mismatches {bad_q}, k mismatches {bad_k} of {T * H * 128} each")
     assert bad_q == 0 and bad_k == 0
+
+
+def test_long_sequence_full(gpu_lib):
+    """One 131,072-token sequence (2,048 chunks per head), H=HV=8, with an
+    initial state: every output and final state against the oracle."""
+    inp = synth.prefill_basic(99, 1, 131072, 8, 8, init="normal0.1", name="t131072")
+    say(f"prefill {inp.name} shape={inp.shape}")
+    o, s = _gpu(gpu_lib, inp)
+    a = synth.to_numpy(inp)
+    o_ref, s_ref = recurrent_parallel(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"])
+    eo = check_o(o, o_ref, inp.name)
+    es = check_state(s, s_ref, inp.name)
+    say(f"  o_err={eo:.2e} state_err={es:.2e}")
