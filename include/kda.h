@@ -146,8 +146,8 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *                  suffices.  Its contents on entry do not matter.
  *                  Calls that share a workspace must not overlap.
  * Sizes: B, T, H, HV >= 1 (T == 0 is accepted, may pass NULL token tensors,
- * and only writes final_state), HV % H == 0, K == V == 128.  q, k, v, g,
- * beta, o and the workspace must not alias.
+ * and only writes final_state), HV <= 65535, HV % H == 0, K == V == 128.
+ * q, k, v, g, beta, o and the workspace must not alias.
  */
 #define KDA_PREFILL_SLOT_BYTES 66048
 int kda_chunk_prefill(const void* q, const void* k, const void* v,
@@ -179,7 +179,7 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v,
  * kda_chunk_prefill_noalloc) runs for these sizes on the current device:
  * KDA_PARTITION_SPLIT or KDA_PARTITION_FUSED (num_seqs as for
  * kda_chunk_prefill_workspace_size).  Returns -KDA_ERR_SHAPE for B or
- * HV < 1.  Host query; enqueues nothing.  When the runtime reports no
+ * HV < 1 or HV > 65535.  Host query; enqueues nothing.  When the runtime reports no
  * current device it answers for 256 compute units (MI355X).
  */
 #define KDA_PARTITION_SPLIT 0

@@ -1827,7 +1827,8 @@ extern "C" int kda_chunk_backward(const void* q, const void* k, const void* v, c
                                   const void* d_out, const float* d_final_state, void* dq, void* dk, void* dv,
                                   float* dg, void* dbeta, float* d_initial_state, int32_t grad_dtype,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
+  // HV <= 65535: value heads are a launch-grid dimension.
+  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV > 65535 || HV % H != 0) return KDA_ERR_SHAPE;
   if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
   if (grad_dtype != KDA_GRAD_FLOAT32 && grad_dtype != KDA_GRAD_INPUT_DTYPE) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;

@@ -1472,7 +1472,8 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
             const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
             int32_t T, int32_t H, int32_t HV, int32_t Kd, int32_t Vd, void* o, float* final_state,
             Params& p) {
-  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
+  // HV <= 65535 keeps the kernels' 32-bit offsets within a chunk in range.
+  if (B < 1 || T < 0 || H < 1 || HV < 1 || HV > 65535 || HV % H != 0) return KDA_ERR_SHAPE;
   if (!final_state || (T > 0 && (!q || !k || !v || !g || !beta || !o))) return KDA_ERR_NULL;
   if (Kd != KD || Vd != KD) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens && (B != 1 || num_seqs < 1)) return KDA_ERR_SHAPE;
@@ -1554,7 +1555,7 @@ extern "C" int kda_chunk_prefill(const void* q, const void* k, const void* v, co
 }
 
 extern "C" int kda_chunk_prefill_partition(int32_t B, int32_t HV, int32_t num_seqs) {
-  if (B < 1 || HV < 1) return -KDA_ERR_SHAPE;
+  if (B < 1 || HV < 1 || HV > 65535) return -KDA_ERR_SHAPE;
   const int64_t nseq = num_seqs > 0 ? num_seqs : B;
   return use_fused(nseq * HV) ? KDA_PARTITION_FUSED : KDA_PARTITION_SPLIT;
 }

@@ -95,6 +95,9 @@ def test_prefill_metadata_errors(entry):
     # whatever the unit count (so the errors do not depend on the partition)
     assert kda.PREFILL_SLOT_BYTES == 66048
     assert _prefill(lib, H=2, HV=4, wsb=4 * 66048 - 16) == 5
+    # value heads are bounded (32-bit offsets within a chunk)
+    assert _prefill(lib, H=1, HV=65536) == 2
+    assert _prefill(lib, H=65536, HV=65536) == 2
     assert _prefill(lib, B=64, H=64, HV=64, wsb=64 * 66048 - 16) == 5
 
 
@@ -111,6 +114,7 @@ def test_partition_query():
     assert lib.kda_chunk_prefill_partition(1, 32, 5) == 0
     assert lib.kda_chunk_prefill_partition(0, 32, 0) == -2
     assert lib.kda_chunk_prefill_partition(1, 0, 0) == -2
+    assert lib.kda_chunk_prefill_partition(1, 65536, 0) == -2
     assert kda.prefill_partition(1, 96) == "split" and kda.prefill_partition(4, 64) == "fused"
 
 
@@ -208,6 +212,7 @@ def test_fused_prefill_metadata_errors():
     assert call(B=0) == 2
     assert call(K=64) == 3
     assert call(cu=FAKE, n=2, B=2) == 2
+    assert call(H=1, HV=65536) == 2
     assert call(v=MISALIGNED) == 4
 
 
@@ -237,6 +242,7 @@ def test_backward_metadata_errors():
     assert _backward(lib, wsb=1000) == 5
     assert _backward(lib, gd=2) == 3                        # unknown gradient dtype
     assert _backward(lib, gd=-1) == 3
+    assert _backward(lib, H=1, HV=65536) == 2          # value heads are a grid dimension
 
 
 def test_backward_workspace_size_formula():
