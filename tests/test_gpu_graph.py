@@ -81,3 +81,69 @@ def test_prefill_graph_replay(gpu_lib, B, T, H, HV):
         assert torch.equal(_bits(out), _bits(ref_o)), f"replay {r}: o differs"
         assert torch.equal(fin, ref_s), f"replay {r}: final state differs"
         say(f"prefill graph replay {r}: identical to the direct call")
+
+
+@pytest.mark.parametrize("B,T,H,HV", [(1, 700, 2, 4), (4, 300, 16, 64)], ids=["split", "fused"])
+def test_prefill_noalloc_graph_replay(gpu_lib, B, T, H, HV):
+    """The allocation-free prefill (its workspace a static device array, so
+    nothing is allocated inside the capture), captured once and replayed on
+    new inputs: every replay equals a direct call bit for bit."""
+    kda = gpu_lib
+    dev = "cuda"
+    first = synth.prefill_basic(60, B, T, H, HV, init="normal0.1")
+    names = ("q", "k", "v", "g", "beta", "initial_state")
+    static = {n: getattr(first, n).to(dev) for n in names}
+    out = torch.empty((B, T, HV, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, HV, 128, 128), dtype=torch.float32, device=dev)
+    kda.chunk_prefill_noalloc(*(static[n] for n in names), out=out, final_state=fin)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.chunk_prefill_noalloc(*(static[n] for n in names), out=out, final_state=fin)
+    torch.cuda.synchronize()
+    for r in range(4):
+        nxt = synth.prefill_basic(61 + r, B, T, H, HV, init="normal0.1")
+        for n in names:
+            static[n].copy_(getattr(nxt, n).to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_s = kda.chunk_prefill_split(*(static[n] for n in names))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_o)), f"replay {r}: o differs"
+        assert torch.equal(fin, ref_s), f"replay {r}: final state differs"
+        say(f"noalloc prefill graph replay {r} ({kda.prefill_partition(B, HV)} form): identical to the direct call")
+
+
+def test_packed_decode_graph_replay(gpu_lib):
+    kda = gpu_lib
+    dev = "cuda"
+    B = 32
+    base = synth.packed_decode_config(B, N=64, row_pad=8, seed=42)
+    H = base.H
+    names = ("mixed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias", "state_indices")
+    static = {n: getattr(base, n).to(dev) for n in names}
+    pool0 = base.pool.to(dev)
+    pool = pool0.clone()
+    out = torch.empty((B, 1, H, 128), dtype=torch.bfloat16, device=dev)
+    qkv = lambda d: d["mixed_qkv"][:, : 3 * H * 128]
+    call = lambda d, p, **kw: kda.packed_decode(qkv(d), d["raw_gate"], d["raw_beta"], d["A_log"], d["dt_bias"], p,
+                                                d["state_indices"], **kw)
+    call(static, pool, out=out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, pool, out=out)
+    torch.cuda.synchronize()
+    for r in range(4):
+        nxt = synth.packed_decode_config(B, N=64, row_pad=8, seed=43 + r)
+        for n in names:
+            static[n].copy_(getattr(nxt, n).to(dev))
+        pool.copy_(pool0)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_pool = pool0.clone()
+        ref_out = call(static, ref_pool)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_out)), f"replay {r}: o differs"
+        assert torch.equal(_bits(pool), _bits(ref_pool)), f"replay {r}: pool differs"
+        say(f"packed decode graph replay {r}: identical to the direct call")
