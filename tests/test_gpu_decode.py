@@ -149,3 +149,10 @@ def test_decode_max_batch(gpu_lib):
     got = pool[idx[act].long().to(dev)].float().cpu().numpy()
     assert np.all(np.abs(got - new_ref) <= np.abs(new_ref) * 2.0 ** -7 + 1e-6 * np.abs(new_ref).max())
     assert torch.equal(pool[free_slots], before_free), "an unaddressed slot changed"
+
+
+@pytest.mark.parametrize("B,H,HV", [(3, 1, 12), (50, 4, 20), (2, 5, 5)], ids=["group12", "group5", "odd"])
+def test_decode_head_layouts(gpu_lib, B, H, HV):
+    """GQA groups and odd head counts on both decode kernels (B=3 and B=2
+    take the column-quarter kernel, B=50 the row kernel)."""
+    _check(gpu_lib, synth.decode_config(B, N=3 * B + 5, H=H, HV=HV, seed=50 + HV))

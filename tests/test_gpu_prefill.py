@@ -343,3 +343,18 @@ def test_long_sequence_full(gpu_lib):
     eo = check_o(o, o_ref, inp.name)
     es = check_state(s, s_ref, inp.name)
     say(f"  o_err={eo:.2e} state_err={es:.2e}")
+
+
+@pytest.mark.parametrize("B,T,H,HV", [(1, 200, 1, 64), (1, 130, 2, 200), (3, 77, 7, 21)],
+                         ids=["group64-split", "group100-fused", "odd-heads"])
+def test_large_gqa_groups_full(gpu_lib, B, T, H, HV):
+    """Large GQA groups (up to 100 value heads per Q/K head) and odd head
+    counts, on both partitions: every output and state against the oracle."""
+    inp = synth.prefill_basic(100 + HV, B, T, H, HV, init="normal0.1", name=f"gqa_h{H}_hv{HV}")
+    say(f"prefill {inp.name} shape={inp.shape} ({gpu_lib.prefill_partition(B, HV)} form)")
+    o, s = _gpu(gpu_lib, inp)
+    a = synth.to_numpy(inp)
+    o_ref, s_ref = recurrent_parallel(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"])
+    eo = check_o(o, o_ref, inp.name)
+    es = check_state(s, s_ref, inp.name)
+    say(f"  o_err={eo:.2e} state_err={es:.2e}")
