@@ -403,8 +403,8 @@ def measured_ceilings(torch, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=8192)
     ap.add_argument("--H", type=int, default=96)
     ap.add_argument("--decode-B", type=int, default=256)
