@@ -750,11 +750,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
             const int ch0 = 32 * s + 8 * gq;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+              // On a diagonal block j == i, so the two factors' exponents are
+              // G_i - G_ref and its negation.
               const float4 gi = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
-              const float4 gj = *reinterpret_cast<const float4*>(sG + j * GS + ch0 + 4 * h);
               const float4 gr = *reinterpret_cast<const float4*>(sG + ref * GS + ch0 + 4 * h);
-              emax = fmaxf(emax, fmaxf(fmaxf(gi.x - gr.x, gi.y - gr.y), fmaxf(gi.z - gr.z, gi.w - gr.w)));
-              emax = fmaxf(emax, fmaxf(fmaxf(gr.x - gj.x, gr.y - gj.y), fmaxf(gr.z - gj.z, gr.w - gj.w)));
+              emax = fmaxf(emax, fmaxf(fmaxf(fabsf(gi.x - gr.x), fabsf(gi.y - gr.y)),
+                                       fmaxf(fabsf(gi.z - gr.z), fabsf(gi.w - gr.w))));
             }
           }
         }
