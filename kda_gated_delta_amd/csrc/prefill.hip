@@ -83,6 +83,7 @@
 // same logical piece of sixteen consecutive rows hit distinct LDS banks once
 // the slot is copied verbatim into LDS.
 #include <atomic>
+#include <mutex>
 
 #include "kda_device.h"
 #include "kda_host.h"
@@ -169,9 +170,9 @@ constexpr int SLOT_U4 = WS_SLOT / 16;                     // 16-byte pieces per 
 constexpr int SLOT_BLOCKS = (WS_SLOT + 1023) / 1024;      // 1 KB load blocks per slot
 constexpr int BLOCKS_PER_WAVE = (SLOT_BLOCKS + NWI - 1) / NWI;
 constexpr int BUF_BYTES = SLOT_BLOCKS * 1024;
-constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [4 waves][64 tokens][16 columns]
-constexpr int INTER_LDS = OFF_V + NWI * C * 16 * 2;
-static_assert(INTER_LDS <= 160 * 1024, "LDS budget");
+constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [4 waves][64 tokens][CW columns]
+constexpr int inter_lds(int cw) { return OFF_V + NWI * C * cw * 2; }
+static_assert(inter_lds(32) <= 160 * 1024, "LDS budget");
 static_assert(2 * VT == KD, "two workgroups cover the state columns");
 
 struct Params {
@@ -188,6 +189,15 @@ struct Params {
   int64_t nslots;          // slots per value head
   int64_t w0, w1;          // slot window [w0, w1) of this launch (split form)
   int64_t wslots;          // workspace slots per value head (the window capacity)
+  int64_t i_lo, i_hi;      // chunk-parallel kernel: this launch's item ids [i_lo, i_hi) of the window
+  // Overlapped split schedule (one window): ready flags, one int per item of
+  // the window, for the items from sync_lo on.  The chunk-parallel launch
+  // that runs first clears them (flag_mode 1), the one that runs beside the
+  // carry (intra_kernel<false, true>) sets each after its slot is stored,
+  // and the carry waits for them.  Null flags: no overlap.
+  int* flags;
+  int64_t sync_lo;
+  int flag_mode;
   int T, H, HV, N;
 };
 
@@ -389,8 +399,14 @@ constexpr int WAIT_ALL = 0x0000;   // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)
 // Word 3 of a raw (untyped) buffer resource on gfx9-family chips: 32-bit
 // data format, no swizzle.
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// Cache-policy operand of the buffer and LDS-direct memory builtins: bit 1
+// nontemporal, bit 4 device scope (coherent across the XCDs' L2 caches).
+constexpr int AUX_NT_DEV = 2 | 16;
+constexpr int AUX_DEV = 16;
 typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 constexpr int WAIT_VM4 = 0x0F74;   // s_waitcnt vmcnt(4): low vmcnt bits 3:0, high bits 15:14 zero
+constexpr int WAIT_VM8 = 0x0F78;   // s_waitcnt vmcnt(8)
+constexpr int WAIT_VM9 = 0x0F79;   // s_waitcnt vmcnt(9)
 constexpr int WAIT_VM0 = 0x0F70;   // s_waitcnt vmcnt(0) only
 
 // Direct load of this wave's v tile (64 tokens x 16 columns from column c0,
@@ -462,7 +478,7 @@ __device__ __forceinline__ int longest_first_seq(const Params& p, int w, int* sc
   return s;
 }
 
-template <bool kFused>
+template <bool kFused, bool kPublish = false>
 __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
@@ -504,7 +520,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     items = (unit_len + C - 1) / C;
     stride = 1;
   } else {
-    items = int(p.w1 - p.w0) * p.HV;
+    items = int(min(p.i_hi, (p.w1 - p.w0) * p.HV));
     stride = gridDim.x;
   }
   struct Item {
@@ -569,7 +585,22 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     }
   };
 
-  Item first = find(kFused ? 0 : int(blockIdx.x));
+  if constexpr (!kFused) {
+    // Overlapped schedule, first launch: clear the flags of the items the
+    // second launch will set (the carry starts only after this launch ends).
+    if (p.flag_mode == 1) {
+      const int64_t n_items = (p.w1 - p.w0) * p.HV;
+      for (int64_t i = p.sync_lo + int64_t(blockIdx.x) * NT + tid; i < n_items; i += int64_t(gridDim.x) * NT)
+        p.flags[i] = 0;
+    }
+  }
+  // Overlapped schedule: the item whose slot stores are in flight, and the
+  // release of its flag (a device-scope store, which the carry polls).
+  int pend = -1;
+  auto publish = [&](int id) __attribute__((always_inline)) {
+    __hip_atomic_store(p.flags + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  Item first = find(kFused ? 0 : int(p.i_lo) + int(blockIdx.x));
   if (first.id >= items) {
     write_final_state();   // fused form, empty sequence: the state passes through
     return;
@@ -872,6 +903,16 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 
     // ---------------------------------------------------------- phase 3: solve
     if (nxt.id < items) load_raw_g(R, p, nxt.trow, nxt.nvalid, nxt.hv, tid);
+    // Overlapped schedule: the previous item's 9 slot stores precede this
+    // item's 9 prefetch loads (none after the last item) in the in-order
+    // completion counter, so this wait completes exactly those stores; its
+    // flag is set after the barrier below, once every thread has waited.
+    if constexpr (kPublish) {
+      if (pend >= 0) {
+        if (nxt.id < items) __builtin_amdgcn_s_waitcnt(WAIT_VM9);
+        else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+      }
+    }
     // Fused form: this chunk's v tile for the wave's 16 state columns, for
     // the carry at the end of the item.
     if constexpr (kFused) load_v_lds(sVt, p, cur.trow, cur.nvalid, cur.hv, 16 * wave, lane);
@@ -932,6 +973,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       }
     }
     lds_barrier();
+    if constexpr (kPublish) {
+      if (pend >= 0 && tid == 0) publish(pend);
+    }
     // Off-diagonal blocks of T on fp32 MFMA (16x16x4), through the inverse
     // of the two 32x32 diagonal halves Z0 = [[T00, 0], [T10, T11]] and
     // Z1 = [[T22, 0], [T32, T33]]:
@@ -1091,6 +1135,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // slot, v and o traffic measured slower.
     {
       unsigned char* dst = p.ws + (int64_t(cur.hv) * p.wslots + (cur.slot - p.w0)) * WS_SLOT;
+      // kPublish: device-scope stores, since the carry reads the slot while
+      // this kernel runs, maybe from another XCD, once its stores are
+      // complete (kernel boundaries publish the other launches' slots).
+      const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, WS_SLOT, BUF_RSRC_WORD3);
 #pragma unroll
       for (int k = 0; k < (SLOT_U4 + NT - 1) / NT; ++k) {
         const int u = min(tid + k * NT, SLOT_U4 - 1);
@@ -1112,8 +1160,15 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         } else {
           src = reinterpret_cast<const unsigned char*>(sGam) + (b - WS_GAM);
         }
-        kda::store_nt(reinterpret_cast<uint4*>(dst + b), *reinterpret_cast<const uint4*>(src));
+        const uint4 val = *reinterpret_cast<const uint4*>(src);
+        if constexpr (kPublish) {
+          const u32x4_t w = {val.x, val.y, val.z, val.w};
+          __builtin_amdgcn_raw_buffer_store_b128(w, srsrc, b, 0, AUX_NT_DEV);
+        } else {
+          kda::store_nt(reinterpret_cast<uint4*>(dst + b), val);
+        }
       }
+      pend = cur.id;
     }
     } else {
       carry(cur);
@@ -1138,6 +1193,11 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     nxt = find(cur.id + stride);
     chunk(cur, nxt, false);
   }
+  if constexpr (kPublish) {   // the last item's flag, once its stores are complete
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    lds_barrier();
+    if (tid == 0) publish(pend);
+  }
   write_final_state();
 }
 
@@ -1147,6 +1207,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 // of the slot re-read its last piece into the buffer's padding, and a wave
 // with fewer blocks repeats the last block (same bytes to the same place), so
 // every wave issues the same number of loads.
+template <int AUX = 0>
 __device__ __forceinline__ void load_slot_part(unsigned char* buf, const unsigned char* slot, int wave, int lane,
                                                int j0, int j1) {
 #pragma unroll
@@ -1154,7 +1215,18 @@ __device__ __forceinline__ void load_slot_part(unsigned char* buf, const unsigne
     const int blk = min(wave + NWI * j, SLOT_BLOCKS - 1);
     const int u = min(blk * 64 + lane, SLOT_U4 - 1);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(slot + u * 16),
-                                     (lds_void*)(buf + blk * 1024), 16, 0, 0);
+                                     (lds_void*)(buf + blk * 1024), 16, 0, AUX);
+  }
+}
+
+// Overlapped schedule: wait until the chunk-parallel kernel running beside
+// the carry has flagged a slot as stored.  The poll is bounded (about 0.1 s
+// of sleeps) so that a workgroup always ends.
+__device__ __forceinline__ void wait_ready(const int* flag) {
+  for (int it = 0; it < (1 << 21); ++it) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+      return;
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
@@ -1170,8 +1242,16 @@ constexpr int PF1 = 6, PF2 = 12;
 
 // One workgroup per CU (its LDS footprint), so one wave per SIMD: telling the
 // compiler lets it schedule for latency with the full register file.
+//
+// CW = state columns per wave: 16 (two workgroups per unit, 64 columns each)
+// or 32 (one workgroup per unit; each wave runs its two 16-column tiles
+// through the same operand reads, so a slot is staged once per unit and each
+// operand read serves twice the columns, at twice the matrix work per wave).
+// A column's arithmetic is the same in both.
+template <int CW>
 __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) void inter_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NCT = CW / 16;                   // 16-column tiles per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1179,12 +1259,19 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  // Workgroups 16g + j and 16g + 8 + j (j < 8) are the two column halves of
-  // unit 8g + j: with workgroups dealt round-robin over the 8 XCDs, both
-  // halves of a unit run on one XCD and share its L2 for the slot reads.
-  const int grp = blockIdx.x >> 4, within = blockIdx.x & 15;
-  const int half = within >> 3;
-  const int unit = 8 * grp + (within & 7);
+  // CW = 16: workgroups 16g + j and 16g + 8 + j (j < 8) are the two column
+  // halves of unit 8g + j: with workgroups dealt round-robin over the 8
+  // XCDs, both halves of a unit run on one XCD and share its L2 for the slot
+  // reads.  CW = 32: workgroup u is unit u.
+  int unit, half;
+  if constexpr (NCT == 1) {
+    const int grp = blockIdx.x >> 4, within = blockIdx.x & 15;
+    half = within >> 3;
+    unit = 8 * grp + (within & 7);
+  } else {
+    half = 0;
+    unit = blockIdx.x;
+  }
   if (unit >= p.N * p.HV) return;
   const int n = unit / p.HV;
   const int hv = unit - n * p.HV;
@@ -1204,31 +1291,59 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto slot_of = [&](int c) {
     return p.ws + (int64_t(hv) * p.wslots + (base + c - p.w0)) * WS_SLOT;
   };
-  unsigned char* sv = smem + OFF_V + wave * (C * 16 * 2);
-  const int c0 = half * VT + wave * 16;          // first state column of this wave
+  // Overlapped schedule (32-column form): the slots of items from sync_lo on
+  // are being stored while this kernel runs; each is read only after its
+  // ready flag is seen, with device-scope loads.
+  constexpr int SAUX = NCT == 2 ? AUX_DEV : 0;
+  const int* flag_base = (NCT == 2 && p.flags) ? p.flags + ((base - p.w0) * p.HV + hv) : nullptr;
+  auto flagged = [&](int c) {
+    return NCT == 2 && flag_base != nullptr && (base + c - p.w0) * p.HV + hv >= p.sync_lo;
+  };
+  unsigned char* sv = smem + OFF_V + wave * (C * CW * 2);   // NCT v tiles of 2 KB
+  const int c0 = half * VT + wave * CW;          // first state column of this wave
 
-  const int col = c0 + l16;                      // this lane's state column
-  f32x4 S[8];                                    // rows 16rt + 4gq + r of column `col`
+  f32x4 S[NCT][8];                               // rows 16rt + 4gq + r of column c0 + 16t + l16
   const float* s_in = c_lo > 0 ? p.sfin : p.s0;
-  if (s_in) {   // one branch around all 32 loads, so they are in flight together
+  if (s_in) {   // one branch around all the loads, so they are in flight together
     const float* s0 = s_in + (int64_t(n) * p.HV + hv) * KD * KD;
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int t = 0; t < NCT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[rt][r] = s0[(16 * rt + 4 * gq + r) * KD + col];
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[t][rt][r] = s0[(16 * rt + 4 * gq + r) * KD + c0 + 16 * t + l16];
   } else {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NCT; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) S[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // rdy: the next chunk's slot is known to be stored.
+  int rdy = 1;
   if (c_lo < c_hi) {
-    load_slot_part(smem, slot_of(c_lo), wave, lane, 0, BLOCKS_PER_WAVE);
-    load_v_lds(sv, p, tok0 + int64_t(c_lo) * C, min(C, len - c_lo * C), hv, c0, lane);
+    if (flagged(c_lo)) wait_ready(flag_base + int64_t(c_lo) * p.HV);
+    rdy = flagged(c_lo + 1) ? 0 : 1;
+    load_slot_part<SAUX>(smem, slot_of(c_lo), wave, lane, 0, BLOCKS_PER_WAVE);
+#pragma unroll
+    for (int t = 0; t < NCT; ++t)
+      load_v_lds(sv + t * 2048, p, tok0 + int64_t(c_lo) * C, min(C, len - c_lo * C), hv, c0 + 16 * t, lane);
   }
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);
   lds_barrier();
 
   for (int c = c_lo; c < c_hi; ++c) {
+    // The flag of the chunk after next, polled a chunk ahead of its use.  The
+    // load is unconditional (an input word stands in where no flag is
+    // needed) so that the wait for it stays counted exactly and implied by
+    // the one at the end of the chunk.
+    bool need2 = false;
+    int fl2 = 1;
+    if constexpr (NCT == 2) {
+      need2 = c + 2 < c_hi && flagged(c + 2);
+      const int* fa = need2 ? flag_base + int64_t(c + 2) * p.HV : reinterpret_cast<const int*>(p.v);
+      fl2 = __hip_atomic_load(fa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int nvalid = min(C, len - c * C);
     const int64_t trow = tok0 + int64_t(c) * C;
     const unsigned char* cur = smem + ((c - c_lo) & 1) * BUF_BYTES;
@@ -1249,13 +1364,17 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Rows past the chunk's end hold copies of its last row (finite) and
     // need no masking: their beta is zero, so their columns of A are exact
     // zeros.
-    f16x8 Vv[2];
-    read_v_operand(sv, l16, gq, Vv);
+    f16x8 Vv[NCT][2];
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) read_v_operand(sv + t * 2048, l16, gq, Vv[t]);
     // This wave's v slot is free once its reads are done: fetch the next
     // chunk's, then the first part of the next slot.
     __builtin_amdgcn_s_waitcnt(WAIT_LDS);
-    load_v_lds(sv, p, tok0 + int64_t(cn) * C, min(C, len - cn * C), hv, c0, lane);
-    load_slot_part(nbuf, nslot, wave, lane, 0, PF1);
+    if (!rdy && cn != c) wait_ready(flag_base + int64_t(cn) * p.HV);
+#pragma unroll
+    for (int t = 0; t < NCT; ++t)
+      load_v_lds(sv + t * 2048, p, tok0 + int64_t(cn) * C, min(C, len - cn * C), hv, c0 + 16 * t, lane);
+    load_slot_part<SAUX>(nbuf, nslot, wave, lane, 0, PF1);
 
     // Contraction orders: for products with S the channel index of k-slot
     // (gq, e) is 32s + 4gq + e (e < 4) or 32s + 16 + 4gq + (e - 4), which is
@@ -1277,37 +1396,45 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int mt = 0; mt < 4; ++mt) oW[4 * s + mt] = swz_read(sW, 16 * mt + l16, 256, 4 * s + gq);
     // S as the fp16 operand of the products with S; then, in the same pass
     // over the accumulators, the decay e^{G_last} S of the state update.
-    f16x8 Sh[4];
+    f16x8 Sh[NCT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int t = 0; t < NCT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Sh[s][r] = (_Float16)S[2 * s][r];
-        Sh[s][4 + r] = (_Float16)S[2 * s + 1][r];
-      }
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Sh[t][s][r] = (_Float16)S[t][2 * s][r];
+          Sh[t][s][4 + r] = (_Float16)S[t][2 * s + 1][r];
+        }
     {
       f32x4 gam[8];
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) gam[rt] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * gq);
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+      for (int t = 0; t < NCT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt][r] *= gam[rt][r];
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[t][rt][r] *= gam[rt][r];
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // U = A v, then Vnew = U + (-W) S; the four token tiles are independent
+    // U = A v, then Vnew = U + (-W) S; the token tiles are independent
     // accumulation chains.
-    f32x4 Vn[4];
+    f32x4 Vn[NCT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Vn[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NCT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Vn[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0, i = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s)
-        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oA[i++], Vv[s], Vn[mt], 0, 0, 0);
+      for (int s = 0; s <= (mt >> 1); ++s, ++i)
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+          Vn[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oA[i], Vv[t][s], Vn[t][mt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_slot_part(nbuf, nslot, wave, lane, PF1, PF2);
+    load_slot_part<SAUX>(nbuf, nslot, wave, lane, PF1, PF2);
     f16x8 oQ[16];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1318,9 +1445,11 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        Vn[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oW[4 * s + mt], Sh[s], Vn[mt], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+          Vn[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oW[4 * s + mt], Sh[t][s], Vn[t][mt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_slot_part(nbuf, nslot, wave, lane, PF2, BLOCKS_PER_WAVE);
+    load_slot_part<SAUX>(nbuf, nslot, wave, lane, PF2, BLOCKS_PER_WAVE);
     f16x8 oQK[6];
 #pragma unroll
     for (int mt = 0, i = 0; mt < 4; ++mt)
@@ -1330,22 +1459,28 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // O^T = S^T Qg^T + Vnew^T Aqk^T: the same operands as O = Qg S + Aqk Vnew
     // with their roles swapped, so each lane ends up holding four adjacent
     // columns of one token and writes them with one 8-byte store.
-    f32x4 Ot[4];
+    f32x4 Ot[NCT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NCT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Ot[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Sh[s], oQ[4 * s + mt], Ot[mt], 0, 0, 0);
-    f16x8 Vh[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+        for (int t = 0; t < NCT; ++t)
+          Ot[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Sh[t][s], oQ[4 * s + mt], Ot[t][mt], 0, 0, 0);
+    f16x8 Vh[NCT][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Vh[s][r] = (_Float16)Vn[2 * s][r];
-        Vh[s][4 + r] = (_Float16)Vn[2 * s + 1][r];
-      }
+    for (int t = 0; t < NCT; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Vh[t][s][r] = (_Float16)Vn[t][2 * s][r];
+          Vh[t][s][4 + r] = (_Float16)Vn[t][2 * s + 1][r];
+        }
     __builtin_amdgcn_sched_barrier(0);
     f16x8 oK[16];
 #pragma unroll
@@ -1356,39 +1491,48 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int mt = 0, i = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s)
-        Ot[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vh[s], oQK[i++], Ot[mt], 0, 0, 0);
-    // S = (e^{G_last} S) + Kg^T Vnew; eight independent row tiles.
+      for (int s = 0; s <= (mt >> 1); ++s, ++i)
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+          Ot[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vh[t][s], oQK[i], Ot[t][mt], 0, 0, 0);
+    // S = (e^{G_last} S) + Kg^T Vnew; eight independent row tiles per column tile.
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oK[8 * s + rt], Vh[s], S[rt], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+          S[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oK[8 * s + rt], Vh[t][s], S[t][rt], 0, 0, 0);
     // Buffer stores against a range of exactly the chunk's valid rows: the
     // hardware drops the rows past the end, with no branch.
     {
       const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
           p.o + (trow * p.HV + hv) * KD, 0, nvalid * p.HV * KD * 2, BUF_RSRC_WORD3);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int t = 16 * mt + l16;
-        const u32x2_t w = {pack_bf16(Ot[mt][0], Ot[mt][1]), pack_bf16(Ot[mt][2], Ot[mt][3])};
-        __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, (t * p.HV * KD + c0 + 4 * gq) * 2, 0, 0);
-      }
+      for (int t = 0; t < NCT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int tk = 16 * mt + l16;
+          const u32x2_t w = {pack_bf16(Ot[t][mt][0], Ot[t][mt][1]), pack_bf16(Ot[t][mt][2], Ot[t][mt][3])};
+          __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, (tk * p.HV * KD + c0 + 16 * t + 4 * gq) * 2, 0, 0);
+        }
     }
-    // The next chunk's slot and v tile must have landed before anyone reads
-    // them.  They were issued before this chunk's 4 o stores, and exactly
-    // those 4 stores follow them, so waiting until at most 4 memory
+    // The next chunk's slot and v tiles must have landed before anyone reads
+    // them.  They were issued before this chunk's 4 NCT o stores, and exactly
+    // those stores follow them, so waiting until at most that many memory
     // operations remain covers the loads without waiting for the stores.
-    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
+    __builtin_amdgcn_s_waitcnt(NCT == 1 ? WAIT_VM4 : WAIT_VM8);
+    if constexpr (NCT == 2) rdy = need2 ? __builtin_amdgcn_readfirstlane(fl2) : 1;
     lds_barrier();
   }
 
   float* sf = p.sfin + (int64_t(n) * p.HV + hv) * KD * KD;
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+  for (int t = 0; t < NCT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + c0 + 16 * t + l16] = S[t][rt][r];
 }
 
 // Raise a kernel's dynamic-LDS limit, once per device (the attribute is a
@@ -1408,6 +1552,10 @@ int set_lds(Kern kern, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
 }
 
 int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq + 1; }
+
+// Ready flags of the overlapped schedule: one int per (value head, slot),
+// after the slots, in 256-byte units.
+size_t flag_bytes(int64_t nslots, int64_t HV) { return (size_t(nslots * HV) * 4 + 255) & ~size_t(255); }
 
 using kda::device_cus;
 
@@ -1432,12 +1580,120 @@ int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
   return w < nslots ? w : nslots;
 }
 
+// Overlapped split schedule.  The sequential schedule runs the
+// chunk-parallel kernel on every CU, then the carry on two workgroups per
+// unit; the carry walks its chunks one after another and leaves most of its
+// CUs' arithmetic idle.  Here the chunk kernel runs in two launches over the
+// chunk rows (all value heads of a chunk slot), [0, rs) on every CU, then
+// [rs, rows) on the CUs that the carry, started as soon as the first launch
+// ends, leaves free: one workgroup per unit with 32 state columns per wave
+// (inter_kernel<32>), on a second stream, waiting for each slot of the second
+// launch to be flagged.  rs is chosen so that the second launch and the carry
+// end together: with t_item the chunk kernel's time per item per CU and
+// t_step the carry's time per chunk while both run,
+//   (rows - rs) * HV * t_item / keep = rows * t_step,   keep = CUs - units.
+// t_step / t_item = 0.36 is the ratio whose split row timed fastest on
+// MI355X at B=1, H=HV=96, T=8192 (52 of 130 rows; 48 to 56 rows within
+// 3 us of each other, 60 rows 25 us slower).
+#ifndef KDA_OVERLAP_RATIO
+#define KDA_OVERLAP_RATIO 0.36
+#endif
+
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex m;   // one call's fork-join sequence at a time
+};
+
+// The calling device's second stream and its two events, made on first use
+// and kept for the life of the process (null if the runtime refuses).
+SideStream* side_stream() {
+  static std::atomic<SideStream*> side[kMaxDevices];
+  static std::mutex make;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream* s = side[dev].load(std::memory_order_acquire);
+  if (s) return s;
+  std::lock_guard<std::mutex> lock(make);
+  s = side[dev].load(std::memory_order_acquire);
+  if (s) return s;
+  s = new SideStream;
+  if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&s->join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;   // the partial object is leaked once; calls fall back to the sequential schedule
+  }
+  side[dev].store(s, std::memory_order_release);
+  return s;
+}
+
+// Split row of the overlapped schedule, or 0 where it does not apply: one
+// sequence, one workspace window with room for the flags, 48 to CUs - 32
+// value heads and at least 48 chunk rows.  Measured on MI355X at T = 8192
+// against the sequential schedule: 16 and 32 value heads 33% and 7% slower
+// (the 32-column carry is slower than the two-workgroup one and little
+// chunk work is left to overlap), 48 to 191 value heads 5% to 18% faster;
+// at 96 value heads, 34 rows 3% slower and 66 rows 6% faster.
+int64_t overlap_rows(const Params& p) {
+  const int64_t units = int64_t(p.N) * p.HV;
+  const int64_t cus = device_cus();
+  const int64_t rows = p.nslots;
+  if (!p.flags || p.N != 1 || p.wslots < rows || units < 48 || units > cus - 32 || rows < 48) return 0;
+  const double keep = double(cus - units);
+  int64_t rs = int64_t(double(rows) * (1.0 - KDA_OVERLAP_RATIO * keep / double(units)));
+  if (rs < 1) rs = 1;
+  if (rs > rows - 1) rs = rows - 1;
+  return rs;
+}
+
+int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side) {
+  static std::atomic<bool> intra_set[kMaxDevices], pub_set[kMaxDevices], inter_set[kMaxDevices];
+  if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&intra_kernel<false, true>, INTRA_LDS, pub_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&inter_kernel<32>, inter_lds(32), inter_set) != KDA_OK) return KDA_ERR_HIP;
+  const int64_t units = int64_t(p.N) * p.HV;
+  const int64_t cus = device_cus();
+  const int64_t items = p.nslots * p.HV;
+  p.w0 = 0;
+  p.w1 = p.nslots;
+  p.sync_lo = rs * p.HV;
+  Params first = p;
+  first.i_lo = 0;
+  first.i_hi = p.sync_lo;
+  first.flag_mode = 1;
+  Params second = p;
+  second.i_lo = p.sync_lo;
+  second.i_hi = items;
+  second.flag_mode = 0;
+  const int64_t b1 = first.i_hi < cus ? first.i_hi : cus;
+  const int64_t b2 = (items - p.sync_lo) < (cus - units) ? (items - p.sync_lo) : (cus - units);
+  std::lock_guard<std::mutex> lock(side->m);
+  hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(b1)), dim3(NT), INTRA_LDS, stream, first);
+  int st = launch_status();
+  if (st != KDA_OK) return st;
+  if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+    return KDA_ERR_HIP;
+  hipLaunchKernelGGL(inter_kernel<32>, dim3(unsigned(units)), dim3(NTI), inter_lds(32), side->stream, second);
+  st = launch_status();
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL((intra_kernel<false, true>), dim3(unsigned(b2)), dim3(NT), INTRA_LDS, stream, second);
+  st = launch_status();
+  if (st != KDA_OK) return st;
+  if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 // Launch the split form over windows of p.wslots slots (p.ws holds
-// p.wslots slots per value head).
+// p.wslots slots per value head), overlapped where that applies.
 int launch(Params p, hipStream_t stream) {
+  if (const int64_t rs = overlap_rows(p)) {
+    if (SideStream* side = side_stream()) return launch_overlapped(p, rs, stream, side);
+  }
   static std::atomic<bool> intra_set[kMaxDevices], inter_set[kMaxDevices];
   if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
-  if (set_lds(&inter_kernel, INTER_LDS, inter_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&inter_kernel<16>, inter_lds(16), inter_set) != KDA_OK) return KDA_ERR_HIP;
   if (p.wslots < 1) return KDA_ERR_WORKSPACE;
   if (p.wslots * p.HV > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
   const int64_t units = int64_t(p.N) * p.HV;
@@ -1447,11 +1703,15 @@ int launch(Params p, hipStream_t stream) {
     p.w0 = w0;
     p.w1 = w0 + p.wslots < p.nslots ? w0 + p.wslots : p.nslots;
     const int64_t items = (p.w1 - p.w0) * p.HV;
+    p.i_lo = 0;
+    p.i_hi = items;
+    p.flags = nullptr;
+    p.flag_mode = 0;
     const int64_t intra_blocks = items < device_cus() ? items : device_cus();
     hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
     int st = launch_status();
     if (st != KDA_OK) return st;
-    hipLaunchKernelGGL(inter_kernel, dim3(unsigned(inter_blocks)), dim3(NTI), INTER_LDS, stream, p);
+    hipLaunchKernelGGL(inter_kernel<16>, dim3(unsigned(inter_blocks)), dim3(NTI), inter_lds(16), stream, p);
     st = launch_status();
     if (st != KDA_OK) return st;
   }
@@ -1496,6 +1756,11 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
   p.w0 = 0;
   p.w1 = p.nslots;
   p.wslots = p.nslots;
+  p.i_lo = 0;
+  p.i_hi = 0;
+  p.flags = nullptr;
+  p.sync_lo = 0;
+  p.flag_mode = 0;
   p.T = T;
   p.H = H;
   p.HV = HV;
@@ -1510,8 +1775,10 @@ extern "C" size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t
   (void)H;
   if (B < 1 || T < 0 || HV < 1 || Kd != KD || Vd != KD) return 0;
   const int64_t nseq = num_seqs > 0 ? num_seqs : B;
-  const int64_t w = window_slots(slots_per_head(int64_t(B) * T, nseq), HV, kWindowBytes);
-  return size_t((w > 0 ? w : 1) * HV) * WS_SLOT;
+  const int64_t nslots = slots_per_head(int64_t(B) * T, nseq);
+  const int64_t w = window_slots(nslots, HV, kWindowBytes);
+  const size_t slots = size_t((w > 0 ? w : 1) * HV) * WS_SLOT;
+  return w == nslots ? slots + flag_bytes(nslots, HV) : slots;
 }
 
 // The partition kda_chunk_prefill runs.  The fused form walks each
@@ -1535,8 +1802,14 @@ int take_workspace(Params& p, int32_t B, int32_t T, int32_t H, int32_t HV, int32
   const size_t per = size_t(HV) * WS_SLOT;
   if (workspace_bytes < per) return KDA_ERR_WORKSPACE;
   const size_t full = kda_chunk_prefill_workspace_size(B, T, H, HV, Kd, Vd, p.N);
+  const int64_t w = window_slots(p.nslots, HV, kWindowBytes);
+  const size_t slots = size_t(w > 0 ? w : 1) * per;
   p.ws = static_cast<unsigned char*>(workspace);
-  p.wslots = int64_t((workspace_bytes < full ? workspace_bytes : full) / per);
+  p.wslots = int64_t((workspace_bytes < slots ? workspace_bytes : slots) / per);
+  // The flags follow the slots when one window holds every slot and the
+  // workspace has room for them (what the size query returns).
+  p.flags = (p.wslots == p.nslots && full > slots && workspace_bytes >= full)
+                ? reinterpret_cast<int*>(p.ws + slots) : nullptr;
   return KDA_OK;
 }
 

@@ -1,0 +1,166 @@
+"""The split prefill's overlapped schedule against its sequential schedule.
+
+With one sequence, 48 to CUs - 32 value heads, at least 48 chunk slots per
+head and a workspace with room for the ready flags (the size
+kda_chunk_prefill_workspace_size returns), kda_chunk_prefill_split runs the
+chunk-parallel kernel in two launches and the carry (one workgroup per unit,
+32 state columns per wave) on a second stream beside the second launch,
+waiting for each of its slots to be flagged.  The arithmetic of every
+column is the one the sequential schedule performs, so both schedules (and
+the fused form) must agree bit for bit; a workspace without the flag room
+forces the sequential schedule on the same inputs.  That the overlapped
+schedule ran is read back from the flags it leaves set in the workspace.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_o, check_state, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def _args(inp):
+    dev = "cuda"
+    s0 = None if inp.initial_state is None else inp.initial_state.to(dev)
+    return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), s0, None)
+
+
+def _flag_bytes(nslots, HV):
+    return (nslots * HV * 4 + 255) // 256 * 256
+
+
+def _run(kda, args, B, T, H, HV, overlapped):
+    """kda_chunk_prefill_split with the full workspace (overlapped) or the
+    slots alone (sequential, one window); returns o, final state and the
+    flag region (None for the sequential run)."""
+    need = kda.workspace_size(B, T, H, HV)
+    nslots = (B * T) // 64 + B + 1
+    fb = _flag_bytes(nslots, HV)
+    assert need == nslots * HV * kda.PREFILL_SLOT_BYTES + fb
+    ws = torch.zeros(need if overlapped else need - fb, dtype=torch.uint8, device="cuda")
+    o, s = kda.chunk_prefill_split(*args, workspace=ws)
+    torch.cuda.synchronize()
+    return o, s, (ws[need - fb:].view(torch.int32) if overlapped else None)
+
+
+def _compare(kda, inp, name):
+    B, T, H = inp.q.shape[:3]
+    HV = inp.v.shape[2]
+    a = _args(inp)
+    oo, so, flags = _run(kda, a, B, T, H, HV, True)
+    os_, ss, _ = _run(kda, a, B, T, H, HV, False)
+    set_flags = int((flags != 0).sum())
+    assert set_flags > 0, f"{name}: the overlapped schedule did not run"
+    assert torch.equal(_bits(oo), _bits(os_)), f"{name}: o differs between the schedules"
+    assert torch.equal(so, ss), f"{name}: final state differs between the schedules"
+    say(f"overlapped == sequential bitwise, {name} (B={B} T={T} H={H} HV={HV}; {set_flags} slots flagged)")
+    return oo, so
+
+
+def test_overlap_bench_workload(gpu_lib):
+    """The bench workload (B=1, H=HV=96, T=8192): both schedules, the fused
+    form and the automatic entry point agree bit for bit."""
+    kda = gpu_lib
+    inp = synth.config2()
+    oo, so = _compare(kda, inp, "B=1 H=HV=96 T=8192")
+    of, sf = kda.chunk_prefill_fused(*_args(inp))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oo), _bits(of)) and torch.equal(so, sf), "fused form differs"
+    # the automatic entry point with its default workspace takes the same path
+    oa, sa = kda.chunk_prefill(*_args(inp))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oo), _bits(oa)) and torch.equal(so, sa), "automatic entry point differs"
+
+
+def test_overlap_ragged_gqa_against_oracle(gpu_lib):
+    """48 value heads over 24 Q/K heads, a ragged last chunk and an initial
+    state; sampled heads against the fp64 oracle."""
+    kda = gpu_lib
+    inp = synth.prefill_basic(120, 1, 3085, 24, 48, init="normal0.1", name="ragged_gqa48")
+    oo, so = _compare(kda, inp, "ragged GQA")
+    a = synth.to_numpy(inp)
+    for hv in (0, 17, 47):
+        hq = hv // 2
+        o_ref, s_ref = oracle.recurrent(a["q"][:, :, hq:hq + 1], a["k"][:, :, hq:hq + 1], a["v"][:, :, hv:hv + 1],
+                                        a["g"][:, :, hv:hv + 1], a["beta"][:, :, hv:hv + 1],
+                                        a["initial_state"][:, hv:hv + 1], None)
+        e_o = check_o(oo[:, :, hv:hv + 1], o_ref, f"head {hv}")
+        e_s = check_state(so[:, hv:hv + 1], s_ref, f"head {hv}")
+        say(f"  value head {hv}: o_err={e_o:.2e} state_err={e_s:.2e}")
+
+
+def test_overlap_smallest_qualifying_shape(gpu_lib):
+    """48 value heads and 48 chunk slots (the fewest heads and rows the
+    schedule takes), no initial state; and the most heads it takes on 256
+    compute units (224)."""
+    _compare(gpu_lib, synth.prefill_basic(121, 1, 2944, 48, 48, init="none", name="min48"), "smallest")
+    _compare(gpu_lib, synth.prefill_basic(122, 1, 3072, 32, 224, init="normal0.1", name="max224"), "most heads")
+
+
+@pytest.mark.parametrize("T,H,HV", [(2943, 48, 48), (2944, 47, 47), (2944, 75, 225)],
+                         ids=["47rows", "47heads", "225heads"])
+def test_overlap_boundaries_run_sequential(gpu_lib, T, H, HV):
+    """Just outside the schedule's range (47 chunk rows, 47 or 225 value
+    heads on 256 compute units) the split form runs sequentially even with
+    the flag room: the flags stay untouched."""
+    kda = gpu_lib
+    inp = synth.prefill_basic(123, 1, T, H, HV, init="none")
+    oo, so, flags = _run(kda, _args(inp), 1, T, H, HV, True)
+    assert int((flags != 0).sum()) == 0, "the overlapped schedule ran outside its range"
+
+
+def test_overlap_repeated_calls_one_workspace(gpu_lib):
+    """Three calls in a row on one workspace: each call clears the flags it
+    waits for, so a previous call's flags never release a slot early."""
+    kda = gpu_lib
+    B, T, H, HV = 1, 4096, 64, 64
+    need = kda.workspace_size(B, T, H, HV)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for r in range(3):
+        inp = synth.prefill_basic(130 + r, B, T, H, HV, init="normal0.1", name=f"rep{r}")
+        a = _args(inp)
+        o, s = kda.chunk_prefill_split(*a, workspace=ws)
+        ro, rs, _ = _run(kda, a, B, T, H, HV, False)
+        assert torch.equal(_bits(o), _bits(ro)) and torch.equal(s, rs), f"call {r} differs"
+        say(f"call {r} on a reused workspace: identical to the sequential schedule")
+
+
+def test_overlap_graph_replay(gpu_lib):
+    """The overlapped schedule captured in a HIP graph (its second stream
+    forks from and joins the captured stream), replayed on new inputs with
+    eager work between the replays; every replay equals a direct call."""
+    kda = gpu_lib
+    dev = "cuda"
+    B, T, H, HV = 1, 3085, 24, 48
+    names = ("q", "k", "v", "g", "beta", "initial_state")
+    first = synth.prefill_basic(140, B, T, H, HV, init="normal0.1")
+    static = {n: getattr(first, n).to(dev) for n in names}
+    need = kda.workspace_size(B, T, H, HV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, HV, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, HV, 128, 128), dtype=torch.float32, device=dev)
+    call = lambda d, **kw: kda.chunk_prefill_split(*(d[n] for n in names), **kw)
+    call(static, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        nxt = synth.prefill_basic(141 + r, B, T, H, HV, init="normal0.1")
+        for n in names:
+            static[n].copy_(getattr(nxt, n).to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_s, _ = _run(kda, tuple(static[n] for n in names) + (None,), B, T, H, HV, False)
+        assert torch.equal(_bits(out), _bits(ref_o)), f"replay {r}: o differs"
+        assert torch.equal(fin, ref_s), f"replay {r}: final state differs"
+        say(f"overlapped prefill graph replay {r}: identical to the sequential schedule")
