@@ -10,9 +10,12 @@ decode runs cache-cold.
 
 Prints one JSON line:
   value        prefill tokens/s (T / mean prefill call time by HIP events)
-  roofline     the prefill entry point -- its two kernels, intra_kernel then
-               inter_kernel, timed together by HIP events on the launch
-               stream -- against the HBM roofline: algorithmic bytes per
+  roofline     the prefill entry point -- on this workload the split form's
+               overlapped schedule: the chunk kernel in two launches and the
+               carry beside the second, on the library's second stream,
+               joined back into the launch stream; the call timed by HIP
+               events on the launch stream -- against the HBM roofline:
+               algorithmic bytes per
                call / mean call time.  traffic is the measured HBM bytes per
                call from the committed rocprofv3 counter summary when that
                was taken on the current kernel source, else null
@@ -29,7 +32,8 @@ Prints one JSON line:
                with a prefill before every launch, so they too meet the
                caches the way they would in serving
   prefill_partitions  mean call time of the split and the fused prefill
-               partitions on this workload, on the 16-sequence varlen GQA
+               partitions (on this workload also the split form's
+               sequential schedule) on this workload, on the 16-sequence varlen GQA
                batch (512 units) and on B=16 H=HV=64 T=2048 (1024 units),
                with the one kda_chunk_prefill picks ("auto")
   backward     the prefill's backward on this workload (float32 ALU roofline)
@@ -128,10 +132,20 @@ def source_hash(name):
 KTRACE_PATH = os.path.join(ROOT, "profiles", "kernel_trace_h96_t8192.json")
 
 
+def flag_room(B, T, HV, nseq=0):
+    """Bytes of ready flags at the end of the prefill's full workspace (see
+    kda_chunk_prefill_workspace_size in include/kda.h)."""
+    nslots = (B * T) // C + (nseq or B) + 1
+    return (nslots * HV * 4 + 255) // 256 * 256
+
+
 def kernel_trace_summary(stats_csv, out_path):
-    """Average device durations per kernel from a rocprofv3 --kernel-trace
-    --stats run of `bench.py --only-steps` (run_kernel_stats.csv), recorded
-    with the hashes of the kernel sources they were measured on."""
+    """Device durations from a rocprofv3 --kernel-trace --stats run of
+    `bench.py --only-steps` (run_kernel_stats.csv and, beside it,
+    run_kernel_trace.csv), recorded with the hashes of the kernel sources
+    they were measured on: each kernel's average, and the prefill call's
+    device span (first kernel start to last kernel end; its kernels overlap
+    in the overlapped split schedule, so their durations do not add up)."""
     import csv
     rec = {"workload": "prefill B=1 H=HV=96 T=8192 then decode B=256 H=HV=12, back-to-back steps",
            "source": "rocprofv3 --kernel-trace --stats (kernel start to end on the device)",
@@ -140,9 +154,25 @@ def kernel_trace_summary(stats_csv, out_path):
     with open(stats_csv) as f:
         for row in csv.DictReader(f):
             name = row["Name"]
-            for key in ("intra_kernel", "inter_kernel", "decode_kernel"):
-                if key in name and ("decode" not in key or "SplitInputs" in name):
-                    rec["kernels_us"][key] = float(row["AverageNs"]) / 1e3
+            m = re.search(r"(intra_kernel|inter_kernel|decode_kernel)(<[^(]*>)?", name)
+            if m and ("decode" not in m.group(1) or "SplitInputs" in name):
+                key = m.group(1) + (m.group(2) or "").replace("(anonymous namespace)::", "")
+                rec["kernels_us"][key] = float(row["AverageNs"]) / 1e3
+    trace_csv = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    spans = []
+    with open(trace_csv) as f:
+        rows = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(f)))
+    call = None
+    for t0, t1, name in rows:
+        if "intra_kernel" in name or "inter_kernel" in name:
+            call = [t0, t1] if call is None else [min(call[0], t0), max(call[1], t1)]
+        elif call is not None:             # the decode (or anything else) ends the prefill call
+            spans.append((call[1] - call[0]) / 1e3)
+            call = None
+    if call is not None:
+        spans.append((call[1] - call[0]) / 1e3)
+    rec["prefill_call_span_us"] = sum(spans) / len(spans) if spans else None
+    rec["prefill_calls"] = len(spans)
     with open(out_path, "w") as fo:
         json.dump(rec, fo, indent=1)
         fo.write("\n")
@@ -270,11 +300,9 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
                 sums.setdefault(name, []).append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in sums.items()}
 
-    def pick(d, key):
-        vals = [v for k, v in d.items() if key in k]
-        if not vals:
-            raise SystemExit(f"no {key} dispatches in the counter file")
-        return vals[0]
+    def short(name):
+        m = re.search(r"(intra_kernel|inter_kernel)(<[^(]*>)?", name)
+        return m.group(1) + (m.group(2) or "") if m else None
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
@@ -290,12 +318,20 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
         "write_scale": w_scale,
         "kernels": {},
     }
+    # Every prefill kernel is dispatched once per call (the chunk kernel's
+    # two launches of the overlapped schedule are two instantiations), so a
+    # call's traffic is the sum of the per-dispatch averages.
     total = 0.0
-    for key in ("intra_kernel", "inter_kernel"):
-        fb = pick(f, key) / f_scale * 1024.0
-        wb = pick(w, key) / w_scale * 1024.0
+    for name in f:
+        key = short(name)
+        if key is None or name not in w:
+            continue
+        fb = f[name] / f_scale * 1024.0
+        wb = w[name] / w_scale * 1024.0
         rec["kernels"][key] = {"fetch_bytes": fb, "write_bytes": wb}
         total += fb + wb
+    if not rec["kernels"]:
+        raise SystemExit("no prefill dispatches in the counter files")
     rec["hbm_bytes_per_launch"] = total
     with open(out_path, "w") as fo:
         json.dump(rec, fo, indent=1)
@@ -547,7 +583,7 @@ def main():
             "parallelism": "single-gpu",
         },
         "roofline": {
-            "kernel": "kda_chunk_prefill (intra_kernel + inter_kernel)",
+            "kernel": "kda_chunk_prefill (intra_kernel x2 + inter_kernel<32>, overlapped)",
             "bound": "hbm",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
@@ -590,12 +626,13 @@ def main():
     kt = kernel_trace_from_profiles()
     if kt:
         ku = kt["kernels_us"]
-        for key, names, nbytes in (("prefill", ("intra_kernel", "inter_kernel"), pbytes),
-                                   ("decode", ("decode_kernel",), dbytes)):
-            us = sum(ku.get(n, 0.0) for n in names)
-            result[key]["device_trace_us"] = {"us_per_call": us, "kernels": {n: ku.get(n) for n in names},
+        for key, us, nbytes in (("prefill", kt.get("prefill_call_span_us"), pbytes),
+                                ("decode", ku.get("decode_kernel"), dbytes)):
+            kern = {n: v for n, v in ku.items() if (n.startswith("decode") == (key == "decode"))}
+            result[key]["device_trace_us"] = {"us_per_call": us, "kernels": kern,
                                               "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None,
-                                              "source": "profiles/kernel_trace_h96_t8192.json (" + kt["source"] + ")"}
+                                              "source": "profiles/kernel_trace_h96_t8192.json (" + kt["source"] +
+                                                        ("; the prefill call's device span" if key == "prefill" else "") + ")"}
     else:
         result["prefill"]["device_trace_us"] = result["decode"]["device_trace_us"] = None
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -713,6 +750,11 @@ def main():
         "auto": kda.prefill_partition(B, HV),
         "split_us": mean_us(lambda: kda.chunk_prefill_split(q, k, v, g, beta, s0, None, out=o, final_state=sf,
                                                             workspace=ws), n_part),
+        # the same split form without room for the ready flags: the
+        # sequential schedule (chunk kernel, then the two-workgroup carry)
+        "split_sequential_us": mean_us(lambda: kda.chunk_prefill_split(
+            q, k, v, g, beta, s0, None, out=o, final_state=sf,
+            workspace=ws[:kda.workspace_size(B, T, H, HV) - flag_room(B, T, HV)]), n_part),
         "fused_us": mean_us(lambda: kda.chunk_prefill_fused(q, k, v, g, beta, s0, None, out=o, final_state=sf),
                             n_part),
     }

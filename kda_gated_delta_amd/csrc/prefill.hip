@@ -28,16 +28,26 @@
 //   and the chunk's W, Qg, Kg^T, Aqk, A and exp(G_last) are written to the
 //   workspace (66 KB per chunk and head, fp16 except exp(G_last)).
 //
-// inter_kernel -- two 256-thread workgroups per (sequence, value head), one
-//   per half of the state's 128 columns (the columns evolve independently:
-//   column v of S only ever meets column v of the values), placed on the
-//   same XCD so the second read of each chunk's workspace slot hits L2.
-//   Wave w of a half owns 16 columns and keeps that 128x16 slice of S in
-//   registers as float32 for the whole sequence.  Chunk slots stream through
-//   two LDS buffers (the next chunk is loaded while the current one is
-//   computed).  Per chunk, on MFMA: U = A v and Vnew = U - W S accumulate in
-//   float32 (U is never rounded), O^T = S^T Qg^T + Vnew^T Aqk^T, and
+// inter_kernel<16> -- two 256-thread workgroups per (sequence, value head),
+//   one per half of the state's 128 columns (the columns evolve
+//   independently: column v of S only ever meets column v of the values),
+//   placed on the same XCD so the second read of each chunk's workspace slot
+//   hits L2.  Wave w of a half owns 16 columns and keeps that 128x16 slice of
+//   S in registers as float32 for the whole sequence.  Chunk slots stream
+//   through two LDS buffers (the next chunk is loaded while the current one
+//   is computed).  Per chunk, on MFMA: U = A v and Vnew = U - W S accumulate
+//   in float32 (U is never rounded), O^T = S^T Qg^T + Vnew^T Aqk^T, and
 //   S = exp(G_last) S + Kg^T Vnew.
+// inter_kernel<32> -- the same carry with one workgroup per unit, each wave
+//   owning 32 columns (two 16-column tiles through the same operand reads).
+//
+// Two schedules of the split form.  Sequential: the chunk kernel over every
+// item, then inter_kernel<16>.  Overlapped (one sequence, 48 to CUs - 32
+// value heads, a workspace with room for ready flags): the chunk kernel
+// runs over the first rs chunk rows on every CU, then over the rest on the
+// CUs that inter_kernel<32>, started on a second stream, leaves free; the
+// carry polls a ready flag per slot of that second launch.  Both schedules
+// give the same results bit for bit.
 //
 // Fused partition (export kda_chunk_prefill_fused): intra_kernel<true>, one
 //   workgroup per (sequence, value head), runs steps 1-4 for that unit's
