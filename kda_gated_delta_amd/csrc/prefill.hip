@@ -1465,6 +1465,14 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int mt = 0, i = 0; mt < 4; ++mt)
 #pragma unroll
       for (int s = 0; s <= (mt >> 1); ++s) oQK[i++] = swz_read(sAqk, 16 * mt + l16, 128, 4 * s + gq);
+    // Kg^T for the state update, read here so that its LDS latency hides
+    // behind the O products (measured 1% faster in the overlapped schedule,
+    // neutral in the sequential one).
+    f16x8 oK[16];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) oK[8 * s + rt] = swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq);
     __builtin_amdgcn_sched_barrier(0);
     // O^T = S^T Qg^T + Vnew^T Aqk^T: the same operands as O = Qg S + Aqk Vnew
     // with their roles swapped, so each lane ends up holding four adjacent
@@ -1491,12 +1499,6 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           Vh[t][s][r] = (_Float16)Vn[t][2 * s][r];
           Vh[t][s][4 + r] = (_Float16)Vn[t][2 * s + 1][r];
         }
-    __builtin_amdgcn_sched_barrier(0);
-    f16x8 oK[16];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt) oK[8 * s + rt] = swz_read(sKgT, 16 * rt + l16, 128, 4 * s + gq);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0, i = 0; mt < 4; ++mt)
