@@ -1618,14 +1618,23 @@ struct SideStream {
 };
 
 // The calling device's second stream and its two events, made on first use
-// and kept for the life of the process (null if the runtime refuses).
-SideStream* side_stream() {
+// and kept for the life of the process (null if the runtime refuses).  They
+// are not made while `stream` is being captured into a graph (making a
+// stream there can invalidate the capture): such a call runs the sequential
+// schedule, and calls after one uncaptured overlapped call capture the
+// overlap.
+SideStream* side_stream(hipStream_t stream) {
   static std::atomic<SideStream*> side[kMaxDevices];
   static std::mutex make;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   SideStream* s = side[dev].load(std::memory_order_acquire);
   if (s) return s;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
   std::lock_guard<std::mutex> lock(make);
   s = side[dev].load(std::memory_order_acquire);
   if (s) return s;
@@ -1701,7 +1710,7 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
 // p.wslots slots per value head), overlapped where that applies.
 int launch(Params p, hipStream_t stream) {
   if (const int64_t rs = overlap_rows(p)) {
-    if (SideStream* side = side_stream()) return launch_overlapped(p, rs, stream, side);
+    if (SideStream* side = side_stream(stream)) return launch_overlapped(p, rs, stream, side);
   }
   static std::atomic<bool> intra_set[kMaxDevices], inter_set[kMaxDevices];
   if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;

@@ -164,3 +164,49 @@ def test_overlap_graph_replay(gpu_lib):
         assert torch.equal(_bits(out), _bits(ref_o)), f"replay {r}: o differs"
         assert torch.equal(fin, ref_s), f"replay {r}: final state differs"
         say(f"overlapped prefill graph replay {r}: identical to the sequential schedule")
+
+
+_FIRST_CALL_CAPTURED = r'''
+import sys, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+import kda_gated_delta_amd as kda, synth
+dev = "cuda"
+B, T, H, HV = 1, 3085, 24, 48
+names = ("q", "k", "v", "g", "beta", "initial_state")
+static = {n: getattr(synth.prefill_basic(150, B, T, H, HV, init="normal0.1"), n).to(dev) for n in names}
+need = kda.workspace_size(B, T, H, HV)
+ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+out = torch.empty((B, T, HV, 128), dtype=torch.bfloat16, device=dev)
+fin = torch.empty((B, HV, 128, 128), dtype=torch.float32, device=dev)
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):
+    kda.chunk_prefill_split(*(static[n] for n in names), out=out, final_state=fin, workspace=ws)
+torch.cuda.synchronize()
+nslots = T // 64 + 2
+fb = (nslots * HV * 4 + 255) // 256 * 256
+ws[need - fb:].zero_()
+graph.replay()
+torch.cuda.synchronize()
+captured_flags = int((ws[need - fb:].view(torch.int32) != 0).sum())
+ref_o, ref_s = kda.chunk_prefill_split(*(static[n] for n in names))
+torch.cuda.synchronize()
+same = torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(fin, ref_s)
+print(f"RESULT captured_flags={captured_flags} same={same}", flush=True)
+'''
+
+
+def test_overlap_first_call_under_capture():
+    """In a fresh process whose first overlapped-size call is captured into a
+    graph, the library makes no stream during the capture: the captured call
+    runs the sequential schedule (its replay leaves the flags untouched) and
+    equals a direct call made afterwards (which runs overlapped)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], capture_output=True, text=True,
+                       timeout=300)
+    line = [l for l in r.stdout.splitlines() if l.startswith("RESULT")]
+    assert r.returncode == 0 and line, f"subprocess failed: {r.stdout[-2000:]} {r.stderr[-2000:]}"
+    say(line[0])
+    assert line[0] == "RESULT captured_flags=0 same=True"
