@@ -124,9 +124,11 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  * split form overlaps its two kernels: the chunk kernel covers the first
  * chunk slots on every compute unit, then the rest beside the carry, which
  * runs on a second stream of the library's own (one per device, made on
- * the first such call and kept; it joins the caller's stream before the
- * call's work ends, also under HIP graph capture) and waits for each slot
- * it reads to be flagged as stored.  Otherwise the kernels run one after
+ * the first such call that is not under graph capture, and kept; it forks
+ * from and joins the caller's stream, which must belong to the current
+ * device, so the call's work stays ordered on that stream, also under HIP
+ * graph capture; a call captured before any uncaptured one runs
+ * sequentially) and waits for each slot it reads to be flagged as stored.  Otherwise the kernels run one after
  * the other.  Both schedules give the same results bit for bit; measured on
  * MI355X at T = 8192 the overlap takes 0.82-0.95 of the time.
  *
