@@ -118,11 +118,12 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  * 192 units up and 1.7-2x at 96 units.  The workspace is checked either
  * way, so the errors a call returns do not depend on the device.
  *
- * Split-form schedule.  With one sequence (N == 1), 48 to CUs - 32 value
- * heads, at least 48 chunk slots per head and the whole workspace
+ * Split-form schedule.  With sequences of equal length (cu_seqlens NULL,
+ * or a single packed sequence), 48 to CUs - 32 (sequence, value head)
+ * units, at least 48 chunks per sequence and the whole workspace
  * kda_chunk_prefill_workspace_size returns (slots plus ready flags), the
  * split form overlaps its two kernels: the chunk kernel covers the first
- * chunk slots on every compute unit, then the rest beside the carry, which
+ * chunks of every unit on every compute unit, then the rest beside the carry, which
  * runs on a second stream of the library's own (one per device, made on
  * the first such call that is not under graph capture, and kept; it forks
  * from and joins the caller's stream, which must belong to the current

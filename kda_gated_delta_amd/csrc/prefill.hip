@@ -42,12 +42,12 @@
 //   owning 32 columns (two 16-column tiles through the same operand reads).
 //
 // Two schedules of the split form.  Sequential: the chunk kernel over every
-// item, then inter_kernel<16>.  Overlapped (one sequence, 48 to CUs - 32
-// value heads, a workspace with room for ready flags): the chunk kernel
-// runs over the first rs chunk rows on every CU, then over the rest on the
-// CUs that inter_kernel<32>, started on a second stream, leaves free; the
-// carry polls a ready flag per slot of that second launch.  Both schedules
-// give the same results bit for bit.
+// item, then inter_kernel<16>.  Overlapped (equal-length sequences, 48 to
+// CUs - 32 units, a workspace with room for ready flags): the chunk kernel
+// runs over the first rs chunk rows (a row: one chunk of every unit) on
+// every CU, then over the rest on the CUs that inter_kernel<32>, started on
+// a second stream, leaves free; the carry polls a ready flag per slot of
+// that second launch.  Both schedules give the same results bit for bit.
 //
 // Fused partition (export kda_chunk_prefill_fused): intra_kernel<true>, one
 //   workgroup per (sequence, value head), runs steps 1-4 for that unit's
@@ -200,14 +200,19 @@ struct Params {
   int64_t w0, w1;          // slot window [w0, w1) of this launch (split form)
   int64_t wslots;          // workspace slots per value head (the window capacity)
   int64_t i_lo, i_hi;      // chunk-parallel kernel: this launch's item ids [i_lo, i_hi) of the window
-  // Overlapped split schedule (one window): ready flags, one int per item of
-  // the window, for the items from sync_lo on.  The chunk-parallel launch
-  // that runs first clears them (flag_mode 1), the one that runs beside the
-  // carry (intra_kernel<false, true>) sets each after its slot is stored,
-  // and the carry waits for them.  Null flags: no overlap.
+  // Overlapped split schedule (one window): ready flags, one int per (slot,
+  // value head) of the window.  The chunk-parallel launch that runs first
+  // clears them (flag_mode 1), the one that runs beside the carry
+  // (intra_kernel<false, true>) sets each after its slot is stored, and the
+  // carry waits for those of chunks sync_row and later.  Null flags: no
+  // overlap.  cmajor: the chunk kernel's item i is chunk i / (N HV) of
+  // sequence (i / HV) % N, value head i % HV (every sequence has T tokens),
+  // so that a range of items covers whole chunk rows of all units; else
+  // item i is slot i / HV of the window, value head i % HV.
   int* flags;
-  int64_t sync_lo;
+  int sync_row;
   int flag_mode;
+  int cmajor;
   int T, H, HV, N;
 };
 
@@ -548,6 +553,20 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       it.hq = unit_hv / (p.HV / p.H);
       return it;
     }
+    if (p.cmajor) {
+      if (i < items) {
+        const int units = p.N * p.HV;
+        const int c = i / units;
+        const int n = (i - c * units) / p.HV;
+        it.hv = i - c * units - n * p.HV;
+        it.trow = int64_t(n) * p.T + int64_t(c) * C;
+        it.nvalid = min(C, p.T - c * C);
+        it.slot = int(slot_base(p, n)) + c;
+        it.hq = it.hv / (p.HV / p.H);
+      }
+      it.id = i;
+      return it;
+    }
     for (; i < items; i += stride) {
       const int s = int(p.w0) + i / p.HV;
       int c;
@@ -599,13 +618,13 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // Overlapped schedule, first launch: clear the flags of the items the
     // second launch will set (the carry starts only after this launch ends).
     if (p.flag_mode == 1) {
-      const int64_t n_items = (p.w1 - p.w0) * p.HV;
-      for (int64_t i = p.sync_lo + int64_t(blockIdx.x) * NT + tid; i < n_items; i += int64_t(gridDim.x) * NT)
-        p.flags[i] = 0;
+      const int64_t n_flags = (p.w1 - p.w0) * p.HV;
+      for (int64_t i = int64_t(blockIdx.x) * NT + tid; i < n_flags; i += int64_t(gridDim.x) * NT) p.flags[i] = 0;
     }
   }
-  // Overlapped schedule: the item whose slot stores are in flight, and the
-  // release of its flag (a device-scope store, which the carry polls).
+  // Overlapped schedule: the flag index (slot, value head) of the item whose
+  // slot stores are in flight, and the release of its flag (a device-scope
+  // store, which the carry polls).
   int pend = -1;
   auto publish = [&](int id) __attribute__((always_inline)) {
     __hip_atomic_store(p.flags + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1178,7 +1197,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
           kda::store_nt(reinterpret_cast<uint4*>(dst + b), val);
         }
       }
-      pend = cur.id;
+      pend = (cur.slot - int(p.w0)) * p.HV + cur.hv;
     }
     } else {
       carry(cur);
@@ -1301,13 +1320,13 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto slot_of = [&](int c) {
     return p.ws + (int64_t(hv) * p.wslots + (base + c - p.w0)) * WS_SLOT;
   };
-  // Overlapped schedule (32-column form): the slots of items from sync_lo on
-  // are being stored while this kernel runs; each is read only after its
-  // ready flag is seen, with device-scope loads.
+  // Overlapped schedule (32-column form): the slots of chunks sync_row and
+  // later are being stored while this kernel runs; each is read only after
+  // its ready flag is seen, with device-scope loads.
   constexpr int SAUX = NCT == 2 ? AUX_DEV : 0;
   const int* flag_base = (NCT == 2 && p.flags) ? p.flags + ((base - p.w0) * p.HV + hv) : nullptr;
   auto flagged = [&](int c) {
-    return NCT == 2 && flag_base != nullptr && (base + c - p.w0) * p.HV + hv >= p.sync_lo;
+    return NCT == 2 && flag_base != nullptr && c >= p.sync_row;
   };
   unsigned char* sv = smem + OFF_V + wave * (C * CW * 2);   // NCT v tiles of 2 KB
   const int c0 = half * VT + wave * CW;          // first state column of this wave
@@ -1649,18 +1668,28 @@ SideStream* side_stream(hipStream_t stream) {
   return s;
 }
 
-// Split row of the overlapped schedule, or 0 where it does not apply: one
-// sequence, one workspace window with room for the flags, 48 to CUs - 32
-// value heads and at least 48 chunk rows.  Measured on MI355X at T = 8192
-// against the sequential schedule: 16 and 32 value heads 33% and 7% slower
-// (the 32-column carry is slower than the two-workgroup one and little
-// chunk work is left to overlap), 48 to 191 value heads 5% to 18% faster;
-// at 96 value heads, 34 rows 3% slower and 66 rows 6% faster.
+// Chunk rows of the overlapped schedule: with every sequence T tokens long
+// (no cu_seqlens) a row is chunk c of all N sequences (the chunk kernel
+// enumerates its items chunk-major); with cu_seqlens and one sequence a row
+// is one slot of the window.  Rows of the other packed inputs are not
+// formed, so they run sequentially.
+int64_t overlap_row_count(const Params& p) {
+  if (!p.cu) return (int64_t(p.T) + C - 1) / C;
+  return p.N == 1 ? p.nslots : 0;
+}
+
+// Split row of the overlapped schedule, or 0 where it does not apply: rows
+// as above, one workspace window with room for the flags, 48 to CUs - 32
+// (sequence, value head) units and at least 48 chunk rows.  Measured on
+// MI355X at T = 8192 against the sequential schedule: 16 and 32 value heads
+// 33% and 7% slower (the 32-column carry is slower than the two-workgroup
+// one and little chunk work is left to overlap), 48 to 191 value heads 5% to
+// 18% faster; at 96 value heads, 34 rows 3% slower and 66 rows 6% faster.
 int64_t overlap_rows(const Params& p) {
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
-  const int64_t rows = p.nslots;
-  if (!p.flags || p.N != 1 || p.wslots < rows || units < 48 || units > cus - 32 || rows < 48) return 0;
+  const int64_t rows = overlap_row_count(p);
+  if (!p.flags || p.wslots < p.nslots || rows < 48 || units < 48 || units > cus - 32) return 0;
   const double keep = double(cus - units);
   int64_t rs = int64_t(double(rows) * (1.0 - KDA_OVERLAP_RATIO * keep / double(units)));
   if (rs < 1) rs = 1;
@@ -1675,20 +1704,22 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   if (set_lds(&inter_kernel<32>, inter_lds(32), inter_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
-  const int64_t items = p.nslots * p.HV;
+  p.cmajor = p.cu ? 0 : 1;
+  const int64_t per_row = p.cmajor ? units : p.HV;
+  const int64_t items = overlap_row_count(p) * per_row;
   p.w0 = 0;
   p.w1 = p.nslots;
-  p.sync_lo = rs * p.HV;
+  p.sync_row = int(rs);
   Params first = p;
   first.i_lo = 0;
-  first.i_hi = p.sync_lo;
+  first.i_hi = rs * per_row;
   first.flag_mode = 1;
   Params second = p;
-  second.i_lo = p.sync_lo;
+  second.i_lo = rs * per_row;
   second.i_hi = items;
   second.flag_mode = 0;
   const int64_t b1 = first.i_hi < cus ? first.i_hi : cus;
-  const int64_t b2 = (items - p.sync_lo) < (cus - units) ? (items - p.sync_lo) : (cus - units);
+  const int64_t b2 = (items - second.i_lo) < (cus - units) ? (items - second.i_lo) : (cus - units);
   std::lock_guard<std::mutex> lock(side->m);
   hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(b1)), dim3(NT), INTRA_LDS, stream, first);
   int st = launch_status();
@@ -1728,6 +1759,7 @@ int launch(Params p, hipStream_t stream) {
     p.i_hi = items;
     p.flags = nullptr;
     p.flag_mode = 0;
+    p.cmajor = 0;
     const int64_t intra_blocks = items < device_cus() ? items : device_cus();
     hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
     int st = launch_status();
@@ -1780,8 +1812,9 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
   p.i_lo = 0;
   p.i_hi = 0;
   p.flags = nullptr;
-  p.sync_lo = 0;
+  p.sync_row = 0;
   p.flag_mode = 0;
+  p.cmajor = 0;
   p.T = T;
   p.H = H;
   p.HV = HV;

@@ -1,7 +1,8 @@
 """The split prefill's overlapped schedule against its sequential schedule.
 
-With one sequence, 48 to CUs - 32 value heads, at least 48 chunk slots per
-head and a workspace with room for the ready flags (the size
+With sequences of equal length (no cu_seqlens; or one packed sequence), 48
+to CUs - 32 (sequence, value head) units, at least 48 chunk rows and a
+workspace with room for the ready flags (the size
 kda_chunk_prefill_workspace_size returns), kda_chunk_prefill_split runs the
 chunk-parallel kernel in two launches and the carry (one workgroup per unit,
 32 state columns per wave) on a second stream beside the second launch,
@@ -98,23 +99,64 @@ def test_overlap_ragged_gqa_against_oracle(gpu_lib):
 
 
 def test_overlap_smallest_qualifying_shape(gpu_lib):
-    """48 value heads and 48 chunk slots (the fewest heads and rows the
-    schedule takes), no initial state; and the most heads it takes on 256
+    """48 value heads and 48 chunk rows (the fewest units and rows the
+    schedule takes), no initial state; and the most units it takes on 256
     compute units (224)."""
-    _compare(gpu_lib, synth.prefill_basic(121, 1, 2944, 48, 48, init="none", name="min48"), "smallest")
+    _compare(gpu_lib, synth.prefill_basic(121, 1, 3072, 48, 48, init="none", name="min48"), "smallest")
     _compare(gpu_lib, synth.prefill_basic(122, 1, 3072, 32, 224, init="normal0.1", name="max224"), "most heads")
 
 
-@pytest.mark.parametrize("T,H,HV", [(2943, 48, 48), (2944, 47, 47), (2944, 75, 225)],
+@pytest.mark.parametrize("T,H,HV", [(3008, 48, 48), (3072, 47, 47), (3072, 75, 225)],
                          ids=["47rows", "47heads", "225heads"])
 def test_overlap_boundaries_run_sequential(gpu_lib, T, H, HV):
-    """Just outside the schedule's range (47 chunk rows, 47 or 225 value
-    heads on 256 compute units) the split form runs sequentially even with
-    the flag room: the flags stay untouched."""
+    """Just outside the schedule's range (47 chunk rows, 47 or 225 units on
+    256 compute units) the split form runs sequentially even with the flag
+    room: the flags stay untouched."""
     kda = gpu_lib
     inp = synth.prefill_basic(123, 1, T, H, HV, init="none")
     oo, so, flags = _run(kda, _args(inp), 1, T, H, HV, True)
     assert int((flags != 0).sum()) == 0, "the overlapped schedule ran outside its range"
+
+
+def test_overlap_several_sequences(gpu_lib):
+    """Several equal-length sequences: the chunk kernel takes its items
+    chunk-major across the sequences, the carry waits by chunk row.  Two
+    sequences of 48 heads with a ragged tail and an initial state (sampled
+    heads of the second sequence against the oracle), and three sequences
+    of 32 value heads over 16 Q/K heads."""
+    kda = gpu_lib
+    inp = synth.prefill_basic(124, 2, 3100, 48, 48, init="normal0.1", name="b2_h48")
+    oo, so = _compare(kda, inp, "two sequences")
+    a = synth.to_numpy(inp)
+    for hv in (5, 40):
+        o_ref, s_ref = oracle.recurrent(a["q"][1:2, :, hv:hv + 1], a["k"][1:2, :, hv:hv + 1],
+                                        a["v"][1:2, :, hv:hv + 1], a["g"][1:2, :, hv:hv + 1],
+                                        a["beta"][1:2, :, hv:hv + 1], a["initial_state"][1:2, hv:hv + 1], None)
+        e_o = check_o(oo[1:2, :, hv:hv + 1], o_ref, f"sequence 1 head {hv}")
+        e_s = check_state(so[1:2, hv:hv + 1], s_ref, f"sequence 1 head {hv}")
+        say(f"  sequence 1, value head {hv}: o_err={e_o:.2e} state_err={e_s:.2e}")
+    _compare(kda, synth.prefill_basic(125, 3, 4096, 16, 32, init="normal0.1", name="b3_gqa"), "three sequences")
+
+
+def test_overlap_packed_sequences_run_sequential(gpu_lib):
+    """Two packed sequences (cu_seqlens) take the sequential schedule: their
+    chunk rows are not formed, and the flags stay untouched."""
+    kda = gpu_lib
+    lens = [3100, 3300]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    T = int(cu[-1])
+    inp = synth.prefill_basic(126, 1, T, 48, 48, init="normal0.1", cu_seqlens=cu, name="packed2")
+    a = _args(inp)[:6] + (cu.cuda(),)
+    need = kda.workspace_size(1, T, 48, 48, 2)
+    nslots = T // 64 + 2 + 1
+    fb = _flag_bytes(nslots, 48)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    o, s = kda.chunk_prefill_split(*a, workspace=ws)
+    torch.cuda.synchronize()
+    assert int((ws[need - fb:].view(torch.int32) != 0).sum()) == 0
+    of, sf = kda.chunk_prefill_fused(*a)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(of)) and torch.equal(s, sf)
 
 
 def test_overlap_repeated_calls_one_workspace(gpu_lib):
