@@ -133,10 +133,11 @@ KTRACE_PATH = os.path.join(ROOT, "profiles", "kernel_trace_h96_t8192.json")
 
 
 def flag_room(B, T, HV, nseq=0):
-    """Bytes of ready flags at the end of the prefill's full workspace (see
-    kda_chunk_prefill_workspace_size in include/kda.h)."""
+    """Bytes of ready flags and unit status words at the end of the
+    prefill's full workspace (see kda_chunk_prefill_workspace_size in
+    include/kda.h)."""
     nslots = (B * T) // C + (nseq or B) + 1
-    return (nslots * HV * 4 + 255) // 256 * 256
+    return ((nslots + (nseq or B)) * HV * 4 + 255) // 256 * 256
 
 
 def kernel_trace_summary(stats_csv, out_path):

@@ -129,7 +129,12 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  * from and joins the caller's stream, which must belong to the current
  * device, so the call's work stays ordered on that stream, also under HIP
  * graph capture; a call captured before any uncaptured one runs
- * sequentially) and waits for each slot it reads to be flagged as stored.  Otherwise the kernels run one after
+ * sequentially) and waits for each slot it reads to be flagged as stored.
+ * If the runtime runs the carry before the chunk launch it waits for (a
+ * runtime that serialises kernels, for example), the carry gives up after
+ * a bounded wait (about 1 ms) and a sequential carry launched after the
+ * join redoes those units, so the results do not depend on the two running
+ * at once.  Otherwise the kernels run one after
  * the other.  Both schedules give the same results bit for bit; measured on
  * MI355X at T = 8192 the overlap takes 0.82-0.95 of the time.
  *
@@ -211,11 +216,23 @@ int kda_chunk_prefill_partition(int32_t B, int32_t HV, int32_t num_seqs);
  * one window of min(floor(B*T/64) + N + 1, floor(2^31 / (HV * 66048)))
  * slots (about 1 KB per token and value head, at most about 2 GiB): the
  * prefill runs window by window over the slots and reuses the workspace.
- * When one window holds every slot, 4 bytes per slot and value head follow
- * for the overlapped schedule's ready flags, rounded up to 256 bytes.
+ * When one window holds every slot, the overlapped schedule's ready flags
+ * and unit status words follow: 4 bytes per (slot + sequence) and value
+ * head, rounded up to 256 bytes.
  */
 size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t HV,
                                         int32_t K, int32_t V, int32_t num_seqs);
+
+/*
+ * kda_prefill_overlap_wait_limit -- testing hook for the overlapped split
+ * schedule: the number of polls (about 55 ns each) its carry makes for one
+ * ready flag before it gives up and leaves the unit to the sequential carry
+ * after the join (default 16384, about 0.9 ms).  0 makes every wait give up
+ * at once, which forces that path; a negative value restores the default.
+ * Applies to calls enqueued afterwards; returns the previous value.  Not
+ * needed in normal use.
+ */
+int32_t kda_prefill_overlap_wait_limit(int32_t polls);
 
 /*
  * kda_chunk_prefill_noalloc -- kda_chunk_prefill for callers that cannot

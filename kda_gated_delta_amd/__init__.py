@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 EXPORTS = ("kda_status_string", "kda_build_id", "kda_qk_l2norm", "kda_chunk_prefill", "kda_chunk_prefill_split",
            "kda_chunk_prefill_fused", "kda_chunk_prefill_noalloc", "kda_chunk_prefill_partition",
-           "kda_chunk_prefill_workspace_size", "kda_decode", "kda_packed_decode",
+           "kda_chunk_prefill_workspace_size", "kda_prefill_overlap_wait_limit", "kda_decode", "kda_packed_decode",
            "kda_state_to_pool", "kda_chunk_backward", "kda_chunk_backward_workspace_size")
 
 _lib = None
@@ -74,6 +74,8 @@ def load():
                                               _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.kda_prefill_overlap_wait_limit.restype = _i32
+    lib.kda_prefill_overlap_wait_limit.argtypes = [_i32]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                _i32, _i32, _i32, _i32, _i32, _vp, _vp]
@@ -188,6 +190,14 @@ def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     _need(final_state, "final_state", torch.float32, 4, dev)
     nseq_arg = N if cu_seqlens is not None else 0
     return dev, (B, T, H, HV, K, V), nseq_arg, out, final_state
+
+
+def prefill_overlap_wait_limit(polls):
+    """Testing hook (kda_prefill_overlap_wait_limit): polls the overlapped
+    schedule's carry makes for one ready flag before it leaves the unit to
+    the sequential carry; 0 forces that path, negative restores the default.
+    Returns the previous value."""
+    return int(load().kda_prefill_overlap_wait_limit(int(polls)))
 
 
 PREFILL_SLOT_BYTES = 66048   # kda.h KDA_PREFILL_SLOT_BYTES: the smallest workspace is HV of these

@@ -181,7 +181,8 @@ constexpr int SLOT_BLOCKS = (WS_SLOT + 1023) / 1024;      // 1 KB load blocks pe
 constexpr int BLOCKS_PER_WAVE = (SLOT_BLOCKS + NWI - 1) / NWI;
 constexpr int BUF_BYTES = SLOT_BLOCKS * 1024;
 constexpr int OFF_V = 2 * BUF_BYTES;                      // bf16 [4 waves][64 tokens][CW columns]
-constexpr int inter_lds(int cw) { return OFF_V + NWI * C * cw * 2; }
+constexpr int off_abort(int cw) { return OFF_V + NWI * C * cw * 2; }   // 4 ints: a wave gave up waiting
+constexpr int inter_lds(int cw) { return off_abort(cw) + 16; }
 static_assert(inter_lds(32) <= 160 * 1024, "LDS budget");
 static_assert(2 * VT == KD, "two workgroups cover the state columns");
 
@@ -213,6 +214,12 @@ struct Params {
   int sync_row;
   int flag_mode;
   int cmajor;
+  // Overlapped schedule: one word per unit after the flags, set when the
+  // unit's 32-column carry gave up waiting (its slots were not stored in
+  // time, e.g. when the runtime ran the carry before the chunk launch); the
+  // sequential carry launched after the join redoes exactly those units.
+  int* status;
+  int wait_limit;          // polls (about 55 ns each) before a carry gives up on a flag
   int T, H, HV, N;
 };
 
@@ -617,8 +624,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   if constexpr (!kFused) {
     // Overlapped schedule, first launch: clear the flags of the items the
     // second launch will set (the carry starts only after this launch ends).
-    if (p.flag_mode == 1) {
-      const int64_t n_flags = (p.w1 - p.w0) * p.HV;
+    if (p.flag_mode == 1) {   // the flags, then the unit status words after them
+      const int64_t n_flags = (p.w1 - p.w0) * p.HV + int64_t(p.N) * p.HV;
       for (int64_t i = int64_t(blockIdx.x) * NT + tid; i < n_flags; i += int64_t(gridDim.x) * NT) p.flags[i] = 0;
     }
   }
@@ -1249,14 +1256,15 @@ __device__ __forceinline__ void load_slot_part(unsigned char* buf, const unsigne
 }
 
 // Overlapped schedule: wait until the chunk-parallel kernel running beside
-// the carry has flagged a slot as stored.  The poll is bounded (about 0.1 s
-// of sleeps) so that a workgroup always ends.
-__device__ __forceinline__ void wait_ready(const int* flag) {
-  for (int it = 0; it < (1 << 21); ++it) {
+// the carry has flagged a slot as stored.  The poll is bounded (`limit`
+// polls); false if it gave up.
+__device__ __forceinline__ bool wait_ready(const int* flag, int limit) {
+  for (int it = 0; it < limit; ++it) {
     if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
-      return;
+      return true;
     __builtin_amdgcn_s_sleep(2);
   }
+  return false;
 }
 
 // 16-byte operand read of logical piece `piece` of swizzled row `row`.
@@ -1302,6 +1310,9 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unit = blockIdx.x;
   }
   if (unit >= p.N * p.HV) return;
+  // Overlapped schedule's repair launch: only units whose 32-column carry
+  // gave up are redone.
+  if (NCT == 1 && p.status && p.status[unit] == 0) return;
   const int n = unit / p.HV;
   const int hv = unit - n * p.HV;
   int64_t tok0;
@@ -1348,10 +1359,25 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int rt = 0; rt < 8; ++rt) S[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // rdy: the next chunk's slot is known to be stored.
+  // rdy: the next chunk's slot is known to be stored.  A wave that gives up
+  // waiting (gave) waits no more and records it in its own word of abort_w
+  // (set only from 0 to 1); after the last barrier every wave reads the same
+  // verdict.  Data read after giving up may be stale: the unit's outputs are
+  // then redone by the repair launch, and it writes no final state.
   int rdy = 1;
+  bool gave = false;
+  int* abort_w = reinterpret_cast<int*>(smem + off_abort(CW));
+  if constexpr (NCT == 2) {
+    if (lane == 0) abort_w[wave] = 0;
+  }
+  auto wait_for = [&](int c) __attribute__((always_inline)) {
+    if (!gave && !wait_ready(flag_base + int64_t(c) * p.HV, p.wait_limit)) {
+      gave = true;
+      if (lane == 0) abort_w[wave] = 1;
+    }
+  };
   if (c_lo < c_hi) {
-    if (flagged(c_lo)) wait_ready(flag_base + int64_t(c_lo) * p.HV);
+    if (flagged(c_lo)) wait_for(c_lo);
     rdy = flagged(c_lo + 1) ? 0 : 1;
     load_slot_part<SAUX>(smem, slot_of(c_lo), wave, lane, 0, BLOCKS_PER_WAVE);
 #pragma unroll
@@ -1399,7 +1425,7 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // This wave's v slot is free once its reads are done: fetch the next
     // chunk's, then the first part of the next slot.
     __builtin_amdgcn_s_waitcnt(WAIT_LDS);
-    if (!rdy && cn != c) wait_ready(flag_base + int64_t(cn) * p.HV);
+    if (!rdy && cn != c) wait_for(cn);
 #pragma unroll
     for (int t = 0; t < NCT; ++t)
       load_v_lds(sv + t * 2048, p, tok0 + int64_t(cn) * C, min(C, len - cn * C), hv, c0 + 16 * t, lane);
@@ -1556,6 +1582,16 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (NCT == 2) rdy = need2 ? __builtin_amdgcn_readfirstlane(fl2) : 1;
     lds_barrier();
   }
+  // A unit whose carry gave up waiting leaves its outputs to the repair
+  // launch: no final state (so an initial state stored in the same place
+  // is still intact there), and its status word set.
+  if constexpr (NCT == 2) {
+    const int4 a = *reinterpret_cast<const int4*>(abort_w);
+    if ((a.x | a.y | a.z | a.w) != 0) {
+      if (tid == 0) __hip_atomic_store(p.status + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
 
   float* sf = p.sfin + (int64_t(n) * p.HV + hv) * KD * KD;
 #pragma unroll
@@ -1585,8 +1621,18 @@ int set_lds(Kern kern, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
 int64_t slots_per_head(int64_t tokens, int64_t nseq) { return tokens / C + nseq + 1; }
 
 // Ready flags of the overlapped schedule: one int per (value head, slot),
-// after the slots, in 256-byte units.
-size_t flag_bytes(int64_t nslots, int64_t HV) { return (size_t(nslots * HV) * 4 + 255) & ~size_t(255); }
+// after the slots, then one status int per (sequence, value head) unit, in
+// 256-byte units.
+size_t flag_bytes(int64_t nslots, int64_t HV, int64_t nseq) {
+  return (size_t((nslots + nseq) * HV) * 4 + 255) & ~size_t(255);
+}
+
+// Polls a 32-column carry makes for one flag before it gives up (about
+// 0.9 ms, against waits of tens of us in normal running; a unit that gives
+// up is redone by the sequential carry after the join).  Settable for tests
+// (kda_prefill_overlap_wait_limit).
+constexpr int kWaitLimit = 1 << 14;
+std::atomic<int> g_wait_limit{kWaitLimit};
 
 using kda::device_cus;
 
@@ -1698,10 +1744,12 @@ int64_t overlap_rows(const Params& p) {
 }
 
 int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side) {
-  static std::atomic<bool> intra_set[kMaxDevices], pub_set[kMaxDevices], inter_set[kMaxDevices];
+  static std::atomic<bool> intra_set[kMaxDevices], pub_set[kMaxDevices], inter_set[kMaxDevices],
+      rep_set[kMaxDevices];
   if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&intra_kernel<false, true>, INTRA_LDS, pub_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<32>, inter_lds(32), inter_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&inter_kernel<16>, inter_lds(16), rep_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
   p.cmajor = p.cu ? 0 : 1;
@@ -1710,6 +1758,8 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   p.w0 = 0;
   p.w1 = p.nslots;
   p.sync_row = int(rs);
+  p.status = p.flags + p.nslots * p.HV;
+  p.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   Params first = p;
   first.i_lo = 0;
   first.i_hi = rs * per_row;
@@ -1718,8 +1768,15 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   second.i_lo = rs * per_row;
   second.i_hi = items;
   second.flag_mode = 0;
+  Params repair = p;      // the sequential carry, for the units that gave up
+  repair.flags = nullptr;
+  repair.cmajor = 0;
   const int64_t b1 = first.i_hi < cus ? first.i_hi : cus;
   const int64_t b2 = (items - second.i_lo) < (cus - units) ? (items - second.i_lo) : (cus - units);
+  // (A runtime that runs the carry before the second chunk launch, for
+  // example one that serialises kernels, makes every carry give up after
+  // its bounded wait; the repair launch then redoes all units.  Enqueueing
+  // the chunk launch first would avoid that but measured 3.7 us slower.)
   std::lock_guard<std::mutex> lock(side->m);
   hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(b1)), dim3(NT), INTRA_LDS, stream, first);
   int st = launch_status();
@@ -1734,7 +1791,9 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   if (st != KDA_OK) return st;
   if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
     return KDA_ERR_HIP;
-  return KDA_OK;
+  hipLaunchKernelGGL(inter_kernel<16>, dim3(unsigned(16 * ((units + 7) / 8))), dim3(NTI), inter_lds(16), stream,
+                     repair);
+  return launch_status();
 }
 
 // Launch the split form over windows of p.wslots slots (p.ws holds
@@ -1758,6 +1817,7 @@ int launch(Params p, hipStream_t stream) {
     p.i_lo = 0;
     p.i_hi = items;
     p.flags = nullptr;
+    p.status = nullptr;
     p.flag_mode = 0;
     p.cmajor = 0;
     const int64_t intra_blocks = items < device_cus() ? items : device_cus();
@@ -1815,6 +1875,8 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
   p.sync_row = 0;
   p.flag_mode = 0;
   p.cmajor = 0;
+  p.status = nullptr;
+  p.wait_limit = 0;
   p.T = T;
   p.H = H;
   p.HV = HV;
@@ -1832,7 +1894,7 @@ extern "C" size_t kda_chunk_prefill_workspace_size(int32_t B, int32_t T, int32_t
   const int64_t nslots = slots_per_head(int64_t(B) * T, nseq);
   const int64_t w = window_slots(nslots, HV, kWindowBytes);
   const size_t slots = size_t((w > 0 ? w : 1) * HV) * WS_SLOT;
-  return w == nslots ? slots + flag_bytes(nslots, HV) : slots;
+  return w == nslots ? slots + flag_bytes(nslots, HV, nseq) : slots;
 }
 
 // The partition kda_chunk_prefill runs.  The fused form walks each
@@ -1956,4 +2018,10 @@ extern "C" int kda_chunk_prefill_fused(const void* q, const void* k, const void*
                          final_state, p);
   if (st != KDA_OK) return st;
   return launch_fused(p, as_stream(stream));
+}
+
+extern "C" int32_t kda_prefill_overlap_wait_limit(int32_t polls) {
+  const int previous = g_wait_limit.load();
+  g_wait_limit.store(polls < 0 ? kWaitLimit : polls);
+  return previous;
 }

@@ -124,12 +124,12 @@ def test_workspace_size_formula():
     # one window of chunk slots per value head: the window holds
     # min(floor(B*T/64) + N + 1, floor(2 GiB / (HV * slot))) slots; when it
     # holds them all, 4 bytes per slot and value head of ready flags follow
-    # (rounded up to 256 bytes)
+    # and one status word per (sequence, value head) (rounded up to 256 bytes)
     flags = lambda n: (n * 4 + 255) // 256 * 256
-    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) == 130 * 96 * slot + flags(130 * 96)
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 96, 96, 128, 128, 0) == 130 * 96 * slot + flags(131 * 96)
     assert lib.kda_chunk_prefill_workspace_size(1, 65536, 96, 96, 128, 128, 0) == (2**31 // (96 * slot)) * 96 * slot
-    assert lib.kda_chunk_prefill_workspace_size(2, 1000, 8, 8, 128, 128, 0) == 34 * 8 * slot + flags(34 * 8)
-    assert lib.kda_chunk_prefill_workspace_size(1, 500, 2, 4, 128, 128, 5) == 13 * 4 * slot + flags(13 * 4)
+    assert lib.kda_chunk_prefill_workspace_size(2, 1000, 8, 8, 128, 128, 0) == 34 * 8 * slot + flags(36 * 8)
+    assert lib.kda_chunk_prefill_workspace_size(1, 500, 2, 4, 128, 128, 5) == 13 * 4 * slot + flags(18 * 4)
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 1, 1, 64, 128, 0) == 0
 
 

@@ -34,8 +34,9 @@ def _args(inp):
     return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), s0, None)
 
 
-def _flag_bytes(nslots, HV):
-    return (nslots * HV * 4 + 255) // 256 * 256
+def _flag_bytes(nslots, HV, nseq=1):
+    # ready flags per (slot, value head), then a status word per unit
+    return ((nslots + nseq) * HV * 4 + 255) // 256 * 256
 
 
 def _run(kda, args, B, T, H, HV, overlapped):
@@ -44,7 +45,7 @@ def _run(kda, args, B, T, H, HV, overlapped):
     flag region (None for the sequential run)."""
     need = kda.workspace_size(B, T, H, HV)
     nslots = (B * T) // 64 + B + 1
-    fb = _flag_bytes(nslots, HV)
+    fb = _flag_bytes(nslots, HV, B)
     assert need == nslots * HV * kda.PREFILL_SLOT_BYTES + fb
     ws = torch.zeros(need if overlapped else need - fb, dtype=torch.uint8, device="cuda")
     o, s = kda.chunk_prefill_split(*args, workspace=ws)
@@ -149,7 +150,7 @@ def test_overlap_packed_sequences_run_sequential(gpu_lib):
     a = _args(inp)[:6] + (cu.cuda(),)
     need = kda.workspace_size(1, T, 48, 48, 2)
     nslots = T // 64 + 2 + 1
-    fb = _flag_bytes(nslots, 48)
+    fb = _flag_bytes(nslots, 48, 2)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     o, s = kda.chunk_prefill_split(*a, workspace=ws)
     torch.cuda.synchronize()
@@ -225,7 +226,7 @@ with torch.cuda.graph(graph):
     kda.chunk_prefill_split(*(static[n] for n in names), out=out, final_state=fin, workspace=ws)
 torch.cuda.synchronize()
 nslots = T // 64 + 2
-fb = (nslots * HV * 4 + 255) // 256 * 256
+fb = ((nslots + 1) * HV * 4 + 255) // 256 * 256
 ws[need - fb:].zero_()
 graph.replay()
 torch.cuda.synchronize()
@@ -252,3 +253,71 @@ def test_overlap_first_call_under_capture():
     assert r.returncode == 0 and line, f"subprocess failed: {r.stdout[-2000:]} {r.stderr[-2000:]}"
     say(line[0])
     assert line[0] == "RESULT captured_flags=0 same=True"
+
+
+def test_overlap_carry_gives_up_and_is_repaired(gpu_lib):
+    """With the carry's wait limit at 0, every wait for a flag that is not
+    yet set gives up at once: the unit marks its status word, writes no
+    final state, and the sequential carry launched after the join redoes it.
+    The results still equal the sequential schedule's bit for bit.  (One
+    split row here, so each unit waits on its second chunk almost at once.)"""
+    kda = gpu_lib
+    B, T, H, HV = 2, 3100, 12, 24
+    inp = synth.prefill_basic(127, B, T, H, HV, init="normal0.1", name="give_up")
+    a = _args(inp)
+    prev = kda.prefill_overlap_wait_limit(0)
+    try:
+        oo, so, flags = _run(kda, a, B, T, H, HV, True)
+    finally:
+        kda.prefill_overlap_wait_limit(-1)
+    assert prev > 0
+    nslots = (B * T) // 64 + B + 1
+    gave_up = int((flags[nslots * HV:nslots * HV + B * HV] != 0).sum())
+    os_, ss, _ = _run(kda, a, B, T, H, HV, False)
+    assert torch.equal(_bits(oo), _bits(os_)) and torch.equal(so, ss), "repaired results differ"
+    say(f"{gave_up} of {B * HV} units gave up waiting and were redone; results bitwise equal")
+    assert gave_up > 0
+
+
+_SERIALISED = r'''
+import sys, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+import kda_gated_delta_amd as kda, synth
+dev = "cuda"
+B, T, H, HV = 1, 3085, 24, 48
+inp = synth.prefill_basic(151, B, T, H, HV, init="normal0.1")
+a = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.initial_state)] + [None]
+need = kda.workspace_size(B, T, H, HV)
+nslots = T // 64 + 2
+fb = ((nslots + 1) * HV * 4 + 255) // 256 * 256
+ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+o, s = kda.chunk_prefill_split(*a, workspace=ws)
+torch.cuda.synchronize()
+flags = ws[need - fb:].view(torch.int32)
+ran = int((flags[:nslots * HV] != 0).sum())
+gave_up = int((flags[nslots * HV:nslots * HV + HV] != 0).sum())
+ws2 = torch.zeros(need - fb, dtype=torch.uint8, device=dev)
+ro, rs = kda.chunk_prefill_split(*a, workspace=ws2)
+torch.cuda.synchronize()
+same = torch.equal(o.view(torch.int16), ro.view(torch.int16)) and torch.equal(s, rs)
+print(f"RESULT overlapped={ran > 0} same={same} gave_up={gave_up}", flush=True)
+'''
+
+
+def test_overlap_under_serialised_kernels():
+    """In a process where the runtime runs every kernel to completion before
+    the next (AMD_SERIALIZE_KERNEL=3), the carry runs before the chunk launch
+    whose slots it waits for: every unit gives up after its bounded wait and
+    the sequential carry after the join redoes it, so the results still equal
+    the sequential schedule's bit for bit."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, AMD_SERIALIZE_KERNEL="3")
+    r = subprocess.run([sys.executable, "-c", _SERIALISED, root], capture_output=True, text=True, timeout=300,
+                       env=env)
+    line = [l for l in r.stdout.splitlines() if l.startswith("RESULT")]
+    assert r.returncode == 0 and line, f"subprocess failed: {r.stdout[-2000:]} {r.stderr[-2000:]}"
+    say(line[0])
+    assert line[0].startswith("RESULT overlapped=True same=True")
