@@ -43,11 +43,11 @@
 //
 // Two schedules of the split form.  Sequential: the chunk kernel over every
 // item, then inter_kernel<16>.  Overlapped (equal-length sequences, 48 to
-// CUs - 32 units, a workspace with room for ready flags): the chunk kernel
-// runs over the first rs chunk rows (a row: one chunk of every unit) on
-// every CU, then over the rest on the CUs that inter_kernel<32>, started on
-// a second stream, leaves free; the carry polls a ready flag per slot of
-// that second launch.  Both schedules give the same results bit for bit.
+// CUs - 32 units, a workspace with room for ready flags): one chunk-kernel
+// launch runs the first rs chunk rows (a row: one chunk of every unit) on
+// every CU and the rest on the CUs - units workgroups that stay, while
+// inter_kernel<32>, on a second stream, takes the CUs of those that leave
+// and polls a ready flag per slot.  Both give the same results bit for bit.
 //
 // Fused partition (export kda_chunk_prefill_fused): intra_kernel<true>, one
 //   workgroup per (sequence, value head), runs steps 1-4 for that unit's
@@ -200,24 +200,25 @@ struct Params {
   int64_t nslots;          // slots per value head
   int64_t w0, w1;          // slot window [w0, w1) of this launch (split form)
   int64_t wslots;          // workspace slots per value head (the window capacity)
-  int64_t i_lo, i_hi;      // chunk-parallel kernel: this launch's item ids [i_lo, i_hi) of the window
   // Overlapped split schedule (one window): ready flags, one int per (slot,
-  // value head) of the window.  The chunk-parallel launch that runs first
-  // clears them (flag_mode 1), the one that runs beside the carry
-  // (intra_kernel<false, true>) sets each after its slot is stored, and the
-  // carry waits for those of chunks sync_row and later.  Null flags: no
-  // overlap.  cmajor: the chunk kernel's item i is chunk i / (N HV) of
-  // sequence (i / HV) % N, value head i % HV (every sequence has T tokens),
-  // so that a range of items covers whole chunk rows of all units; else
-  // item i is slot i / HV of the window, value head i % HV.
+  // value head) of the window, cleared by a small kernel before the chunk
+  // kernel (intra_kernel<false, true>) sets each once its slot is stored;
+  // the 32-column carry waits for them.  Null flags: sequential schedule.
+  // cmajor: the chunk kernel's item i is chunk i / (N HV) of sequence
+  // (i / HV) % N, value head i % HV (every sequence has T tokens), so that
+  // items run in chunk rows of all units; else item i is slot i / HV of the
+  // window, value head i % HV.  phase2_wgs > 0: the chunk kernel's items
+  // below phase2_lo are spread over the whole grid, the rest over its first
+  // phase2_wgs workgroups only, so the others leave early and the carry
+  // takes their CUs.
   int* flags;
-  int sync_row;
-  int flag_mode;
   int cmajor;
-  // Overlapped schedule: one word per unit after the flags, set when the
-  // unit's 32-column carry gave up waiting (its slots were not stored in
-  // time, e.g. when the runtime ran the carry before the chunk launch); the
-  // sequential carry launched after the join redoes exactly those units.
+  int64_t phase2_lo;
+  int phase2_wgs;
+  // One word per unit after the flags, set when the unit's 32-column carry
+  // gave up waiting (its slots were not stored in time, e.g. when the
+  // runtime ran the carry before the chunk kernel); the sequential carry
+  // launched after the join redoes exactly those units.
   int* status;
   int wait_limit;          // polls (about 55 ns each) before a carry gives up on a flag
   int T, H, HV, N;
@@ -542,12 +543,23 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     items = (unit_len + C - 1) / C;
     stride = 1;
   } else {
-    items = int(min(p.i_hi, (p.w1 - p.w0) * p.HV));
+    items = p.cmajor ? ((p.T + C - 1) / C) * p.N * p.HV : int(p.w1 - p.w0) * p.HV;
     stride = gridDim.x;
   }
   struct Item {
     int64_t trow;
     int id, slot, hv, hq, nvalid;
+  };
+  // Next item id of this workgroup (see phase2_wgs).
+  auto next_of = [&](int id) __attribute__((always_inline)) {
+    if (kFused || p.phase2_wgs == 0) return id + stride;
+    const int p1 = int(p.phase2_lo);
+    if (id < p1) {
+      const int n = id + stride;
+      if (n < p1) return n;
+      return int(blockIdx.x) < p.phase2_wgs ? p1 + int(blockIdx.x) : items;
+    }
+    return id + p.phase2_wgs;
   };
   auto find = [&](int i) {
     Item it;
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       it.id = i;
       return it;
     }
-    for (; i < items; i += stride) {
+    for (; i < items; i = next_of(i)) {
       const int s = int(p.w0) + i / p.HV;
       int c;
       const int n = slot_owner(p, s, c);
@@ -621,14 +633,6 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     }
   };
 
-  if constexpr (!kFused) {
-    // Overlapped schedule, first launch: clear the flags of the items the
-    // second launch will set (the carry starts only after this launch ends).
-    if (p.flag_mode == 1) {   // the flags, then the unit status words after them
-      const int64_t n_flags = (p.w1 - p.w0) * p.HV + int64_t(p.N) * p.HV;
-      for (int64_t i = int64_t(blockIdx.x) * NT + tid; i < n_flags; i += int64_t(gridDim.x) * NT) p.flags[i] = 0;
-    }
-  }
   // Overlapped schedule: the flag index (slot, value head) of the item whose
   // slot stores are in flight, and the release of its flag (a device-scope
   // store, which the carry polls).
@@ -636,7 +640,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   auto publish = [&](int id) __attribute__((always_inline)) {
     __hip_atomic_store(p.flags + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  Item first = find(kFused ? 0 : int(p.i_lo) + int(blockIdx.x));
+  int first_id = kFused ? 0 : int(blockIdx.x);
+  if (!kFused && p.phase2_wgs > 0 && first_id >= int(p.phase2_lo))
+    first_id = int(blockIdx.x) < p.phase2_wgs ? int(p.phase2_lo) + int(blockIdx.x) : items;
+  Item first = find(first_id);
   if (first.id >= items) {
     write_final_state();   // fused form, empty sequence: the state passes through
     return;
@@ -1222,11 +1229,11 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   // first item is peeled off the loop so that the loop is entered in that
   // same state; with a plain loop the entry path (loads only) would make the
   // compiler's wait at the loop head conservative and drain the stores too.
-  Item nxt = find(first.id + stride);
+  Item nxt = find(next_of(first.id));
   chunk(first, nxt, true);
   while (nxt.id < items) {
     const Item cur = nxt;
-    nxt = find(cur.id + stride);
+    nxt = find(next_of(cur.id));
     chunk(cur, nxt, false);
   }
   if constexpr (kPublish) {   // the last item's flag, once its stores are complete
@@ -1331,13 +1338,14 @@ __global__ __launch_bounds__(NTI) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto slot_of = [&](int c) {
     return p.ws + (int64_t(hv) * p.wslots + (base + c - p.w0)) * WS_SLOT;
   };
-  // Overlapped schedule (32-column form): the slots of chunks sync_row and
-  // later are being stored while this kernel runs; each is read only after
-  // its ready flag is seen, with device-scope loads.
+  // Overlapped schedule (32-column form): the slots are being stored while
+  // this kernel runs; each is read only after its ready flag is seen, with
+  // device-scope loads.
   constexpr int SAUX = NCT == 2 ? AUX_DEV : 0;
   const int* flag_base = (NCT == 2 && p.flags) ? p.flags + ((base - p.w0) * p.HV + hv) : nullptr;
   auto flagged = [&](int c) {
-    return NCT == 2 && flag_base != nullptr && c >= p.sync_row;
+    (void)c;
+    return NCT == 2 && flag_base != nullptr;
   };
   unsigned char* sv = smem + OFF_V + wave * (C * CW * 2);   // NCT v tiles of 2 KB
   const int c0 = half * VT + wave * CW;          // first state column of this wave
@@ -1660,20 +1668,22 @@ int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
 // Overlapped split schedule.  The sequential schedule runs the
 // chunk-parallel kernel on every CU, then the carry on two workgroups per
 // unit; the carry walks its chunks one after another and leaves most of its
-// CUs' arithmetic idle.  Here the chunk kernel runs in two launches over the
-// chunk rows (all value heads of a chunk slot), [0, rs) on every CU, then
-// [rs, rows) on the CUs that the carry, started as soon as the first launch
-// ends, leaves free: one workgroup per unit with 32 state columns per wave
-// (inter_kernel<32>), on a second stream, waiting for each slot of the second
-// launch to be flagged.  rs is chosen so that the second launch and the carry
-// end together: with t_item the chunk kernel's time per item per CU and
-// t_step the carry's time per chunk while both run,
-//   (rows - rs) * HV * t_item / keep = rows * t_step,   keep = CUs - units.
-// t_step / t_item = 0.36 is the ratio whose split row timed fastest on
-// MI355X at B=1, H=HV=96, T=8192 (52 of 130 rows; 48 to 56 rows within
-// 3 us of each other, 60 rows 25 us slower).
+// CUs' arithmetic idle.  Here one chunk-kernel launch covers the chunk rows
+// [0, rs) (a row: one chunk of every unit) on every CU, then its first
+// keep = CUs - units workgroups go on to [rs, rows) while the others leave,
+// and the carry -- one workgroup per unit with 32 state columns per wave
+// (inter_kernel<32>), on a second stream -- takes their CUs, waiting for
+// each slot to be flagged.  rs is chosen so that the chunk kernel and the
+// carry end together: with t_item the chunk kernel's time per item per CU
+// and t_step the carry's time per chunk while both run,
+//   (rows - rs) * units * t_item / keep = rows * t_step.
+// t_step / t_item = 0.345 is the ratio whose split row timed fastest on
+// MI355X at B=1, H=HV=96, T=8192 (54 of 128 rows; 45 rows 13 us and 57
+// rows 2 us slower).  An earlier form in two chunk launches, the carry
+// started at the first one's end, measured 11 us slower (the launch
+// boundary's gaps and the first launch's tail).
 #ifndef KDA_OVERLAP_RATIO
-#define KDA_OVERLAP_RATIO 0.36
+#define KDA_OVERLAP_RATIO 0.345
 #endif
 
 struct SideStream {
@@ -1743,50 +1753,49 @@ int64_t overlap_rows(const Params& p) {
   return rs;
 }
 
+// Clears the overlapped schedule's flags and status words.
+__global__ void clear_flags_kernel(int* f, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) f[i] = 0;
+}
+
 int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side) {
-  static std::atomic<bool> intra_set[kMaxDevices], pub_set[kMaxDevices], inter_set[kMaxDevices],
-      rep_set[kMaxDevices];
-  if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
+  static std::atomic<bool> pub_set[kMaxDevices], inter_set[kMaxDevices], rep_set[kMaxDevices];
   if (set_lds(&intra_kernel<false, true>, INTRA_LDS, pub_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<32>, inter_lds(32), inter_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<16>, inter_lds(16), rep_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
-  p.cmajor = p.cu ? 0 : 1;
-  const int64_t per_row = p.cmajor ? units : p.HV;
-  const int64_t items = overlap_row_count(p) * per_row;
   p.w0 = 0;
   p.w1 = p.nslots;
-  p.sync_row = int(rs);
+  p.cmajor = p.cu ? 0 : 1;
   p.status = p.flags + p.nslots * p.HV;
   p.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
-  Params first = p;
-  first.i_lo = 0;
-  first.i_hi = rs * per_row;
-  first.flag_mode = 1;
-  Params second = p;
-  second.i_lo = rs * per_row;
-  second.i_hi = items;
-  second.flag_mode = 0;
+  // The chunk kernel: items of the first rs rows over every CU, the rest over
+  // the CUs - units workgroups that stay; the carry takes the CUs of those
+  // that leave.
+  Params chunks = p;
+  chunks.phase2_lo = rs * (p.cmajor ? units : p.HV);
+  chunks.phase2_wgs = int(cus - units);
   Params repair = p;      // the sequential carry, for the units that gave up
   repair.flags = nullptr;
   repair.cmajor = 0;
-  const int64_t b1 = first.i_hi < cus ? first.i_hi : cus;
-  const int64_t b2 = (items - second.i_lo) < (cus - units) ? (items - second.i_lo) : (cus - units);
-  // (A runtime that runs the carry before the second chunk launch, for
-  // example one that serialises kernels, makes every carry give up after
-  // its bounded wait; the repair launch then redoes all units.  Enqueueing
-  // the chunk launch first would avoid that but measured 3.7 us slower.)
+  const int64_t nclear = p.nslots * p.HV + units;
   std::lock_guard<std::mutex> lock(side->m);
-  hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(b1)), dim3(NT), INTRA_LDS, stream, first);
+  hipLaunchKernelGGL(clear_flags_kernel, dim3(unsigned((nclear + 1023) / 1024)), dim3(1024), 0, stream, p.flags,
+                     nclear);
   int st = launch_status();
   if (st != KDA_OK) return st;
-  if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
-    return KDA_ERR_HIP;
-  hipLaunchKernelGGL(inter_kernel<32>, dim3(unsigned(units)), dim3(NTI), inter_lds(32), side->stream, second);
+  if (hipEventRecord(side->fork, stream) != hipSuccess) return KDA_ERR_HIP;
+  hipLaunchKernelGGL((intra_kernel<false, true>), dim3(unsigned(cus)), dim3(NT), INTRA_LDS, stream, chunks);
   st = launch_status();
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL((intra_kernel<false, true>), dim3(unsigned(b2)), dim3(NT), INTRA_LDS, stream, second);
+  // The carry is enqueued after the chunk kernel and waits only for the
+  // flags' clearing, so its workgroups get the CUs the chunk kernel leaves.
+  // (A runtime that runs the two one after the other runs the carry either
+  // after the chunk kernel, where it never waits, or before it, where every
+  // unit gives up after its bounded wait and the repair launch redoes it.)
+  if (hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return KDA_ERR_HIP;
+  hipLaunchKernelGGL(inter_kernel<32>, dim3(unsigned(units)), dim3(NTI), inter_lds(32), side->stream, p);
   st = launch_status();
   if (st != KDA_OK) return st;
   if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
@@ -1814,12 +1823,10 @@ int launch(Params p, hipStream_t stream) {
     p.w0 = w0;
     p.w1 = w0 + p.wslots < p.nslots ? w0 + p.wslots : p.nslots;
     const int64_t items = (p.w1 - p.w0) * p.HV;
-    p.i_lo = 0;
-    p.i_hi = items;
     p.flags = nullptr;
     p.status = nullptr;
-    p.flag_mode = 0;
     p.cmajor = 0;
+    p.phase2_wgs = 0;
     const int64_t intra_blocks = items < device_cus() ? items : device_cus();
     hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
     int st = launch_status();
@@ -1869,12 +1876,10 @@ int prepare(const void* q, const void* k, const void* v, const float* g, const v
   p.w0 = 0;
   p.w1 = p.nslots;
   p.wslots = p.nslots;
-  p.i_lo = 0;
-  p.i_hi = 0;
   p.flags = nullptr;
-  p.sync_row = 0;
-  p.flag_mode = 0;
   p.cmajor = 0;
+  p.phase2_lo = 0;
+  p.phase2_wgs = 0;
   p.status = nullptr;
   p.wait_limit = 0;
   p.T = T;
