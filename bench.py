@@ -155,7 +155,7 @@ def kernel_trace_summary(stats_csv, out_path):
     with open(stats_csv) as f:
         for row in csv.DictReader(f):
             name = row["Name"]
-            m = re.search(r"(intra_kernel|inter_kernel|decode_kernel)(<[^(]*>)?", name)
+            m = re.search(r"(intra_kernel|inter_kernel|clear_flags_kernel|decode_kernel)(<[^(]*>)?", name)
             if m and ("decode" not in m.group(1) or "SplitInputs" in name):
                 key = m.group(1) + (m.group(2) or "").replace("(anonymous namespace)::", "")
                 rec["kernels_us"][key] = float(row["AverageNs"]) / 1e3
@@ -165,7 +165,7 @@ def kernel_trace_summary(stats_csv, out_path):
         rows = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(f)))
     call = None
     for t0, t1, name in rows:
-        if "intra_kernel" in name or "inter_kernel" in name:
+        if "intra_kernel" in name or "inter_kernel" in name or "clear_flags_kernel" in name:
             call = [t0, t1] if call is None else [min(call[0], t0), max(call[1], t1)]
         elif call is not None:             # the decode (or anything else) ends the prefill call
             spans.append((call[1] - call[0]) / 1e3)
@@ -302,7 +302,7 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
         return {k: sum(v) / len(v) for k, v in sums.items()}
 
     def short(name):
-        m = re.search(r"(intra_kernel|inter_kernel)(<[^(]*>)?", name)
+        m = re.search(r"(intra_kernel|inter_kernel|clear_flags_kernel)(<[^(]*>)?", name)
         return m.group(1) + (m.group(2) or "") if m else None
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -319,13 +319,13 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
         "write_scale": w_scale,
         "kernels": {},
     }
-    # Every prefill kernel is dispatched once per call (the chunk kernel's
-    # two launches of the overlapped schedule are two instantiations), so a
-    # call's traffic is the sum of the per-dispatch averages.  Counter runs
-    # serialise the kernels, so the overlapped schedule's carry
-    # (inter_kernel<32>) gives up waiting there and its repair launch
-    # (inter_kernel<16>) redoes every unit, which a normal call does not:
-    # the repair is left out when the 32-column carry is present.
+    # Every prefill kernel is dispatched once per call, so a call's traffic
+    # is the sum of the per-dispatch averages.  The overlapped schedule's
+    # repair launch (inter_kernel<16> beside inter_kernel<32>) redoes only
+    # units whose carry gave up waiting, which a normal call has none of; a
+    # counter run serialises the kernels, and should its carry run before
+    # the chunk kernel there, the repair would redo every unit: it is left
+    # out when the 32-column carry is present.
     overlapped = any(short(n) == "inter_kernel<32>" for n in f)
     total = 0.0
     for name in f:
@@ -589,7 +589,7 @@ def main():
             "parallelism": "single-gpu",
         },
         "roofline": {
-            "kernel": "kda_chunk_prefill (intra_kernel x2 + inter_kernel<32>, overlapped)",
+            "kernel": "kda_chunk_prefill (intra_kernel<false, true> beside inter_kernel<32>, overlapped)",
             "bound": "hbm",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,

@@ -45,7 +45,7 @@
 // item, then inter_kernel<16>.  Overlapped (equal-length sequences, 48 to
 // CUs - 32 units, a workspace with room for ready flags): one chunk-kernel
 // launch runs the first rs chunk rows (a row: one chunk of every unit) on
-// every CU and the rest on the CUs - units workgroups that stay, while
+// every CU and the rest on the workgroups that stay, while
 // inter_kernel<32>, on a second stream, takes the CUs of those that leave
 // and polls a ready flag per slot.  Both give the same results bit for bit.
 //
@@ -550,14 +550,17 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     int64_t trow;
     int id, slot, hv, hq, nvalid;
   };
-  // Next item id of this workgroup (see phase2_wgs).
+  // Next item id of this workgroup.  Overlapped schedule: items below
+  // phase2_lo over the whole grid, the rest over its first phase2_wgs
+  // workgroups (w2 >= 0); the others leave.
+  const int w2 = int(blockIdx.x) < p.phase2_wgs ? int(blockIdx.x) : -1;
   auto next_of = [&](int id) __attribute__((always_inline)) {
     if (kFused || p.phase2_wgs == 0) return id + stride;
     const int p1 = int(p.phase2_lo);
     if (id < p1) {
       const int n = id + stride;
       if (n < p1) return n;
-      return int(blockIdx.x) < p.phase2_wgs ? p1 + int(blockIdx.x) : items;
+      return w2 >= 0 ? p1 + w2 : items;
     }
     return id + p.phase2_wgs;
   };
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   };
   int first_id = kFused ? 0 : int(blockIdx.x);
   if (!kFused && p.phase2_wgs > 0 && first_id >= int(p.phase2_lo))
-    first_id = int(blockIdx.x) < p.phase2_wgs ? int(p.phase2_lo) + int(blockIdx.x) : items;
+    first_id = w2 >= 0 ? int(p.phase2_lo) + w2 : items;
   Item first = find(first_id);
   if (first.id >= items) {
     write_final_state();   // fused form, empty sequence: the state passes through
@@ -1669,13 +1672,13 @@ int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
 // chunk-parallel kernel on every CU, then the carry on two workgroups per
 // unit; the carry walks its chunks one after another and leaves most of its
 // CUs' arithmetic idle.  Here one chunk-kernel launch covers the chunk rows
-// [0, rs) (a row: one chunk of every unit) on every CU, then its first
-// keep = CUs - units workgroups go on to [rs, rows) while the others leave,
-// and the carry -- one workgroup per unit with 32 state columns per wave
-// (inter_kernel<32>), on a second stream -- takes their CUs, waiting for
-// each slot to be flagged.  rs is chosen so that the chunk kernel and the
-// carry end together: with t_item the chunk kernel's time per item per CU
-// and t_step the carry's time per chunk while both run,
+// [0, rs) (a row: one chunk of every unit) on every CU, then its first keep
+// workgroups (about CUs - units, see overlap_keep) go on to [rs, rows) while
+// the others leave, and the carry -- one workgroup per unit with 32 state
+// columns per wave (inter_kernel<32>), on a second stream -- takes their
+// CUs, waiting for each slot to be flagged.  rs is chosen so that the
+// chunk kernel and the carry end together: with t_item the chunk kernel's
+// time per item per CU and t_step the carry's time per chunk while both run,
 //   (rows - rs) * units * t_item / keep = rows * t_step.
 // t_step / t_item = 0.345 is the ratio whose split row timed fastest on
 // MI355X at B=1, H=HV=96, T=8192 (54 of 128 rows; 45 rows 13 us and 57
@@ -1734,19 +1737,32 @@ int64_t overlap_row_count(const Params& p) {
   return p.N == 1 ? p.nslots : 0;
 }
 
+// Workgroups of the overlapped chunk kernel that stay after the split row.
+// The others leave and the carry's workgroups take their CUs; their count is
+// rounded up to a multiple of 32 (8 XCDs x 4 shader engines) so that every
+// shader engine frees at least as many CUs as the carry places on it,
+// however the dispatcher spreads the two launches over them.  Freeing
+// exactly `units` CUs, 48, 176 and 191 units measured 23-42% slower at
+// T = 8192 (708 against 499 us at 48): a few carry workgroups found no free
+// CU where they were placed and waited for the chunk kernel's end.  Letting
+// the first workgroups leave instead of the last measured 8 us slower at 96
+// units.
+int64_t overlap_keep(int64_t units, int64_t cus) { return cus - (units + 31) / 32 * 32; }
+
 // Split row of the overlapped schedule, or 0 where it does not apply: rows
 // as above, one workspace window with room for the flags, 48 to CUs - 32
 // (sequence, value head) units and at least 48 chunk rows.  Measured on
 // MI355X at T = 8192 against the sequential schedule: 16 and 32 value heads
 // 33% and 7% slower (the 32-column carry is slower than the two-workgroup
 // one and little chunk work is left to overlap), 48 to 191 value heads 5% to
-// 18% faster; at 96 value heads, 34 rows 3% slower and 66 rows 6% faster.
+// 17% faster; at 96 value heads, 64 rows 4% faster (and 34 rows 3% slower,
+// measured with the chunk kernel in two launches).
 int64_t overlap_rows(const Params& p) {
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
   const int64_t rows = overlap_row_count(p);
   if (!p.flags || p.wslots < p.nslots || rows < 48 || units < 48 || units > cus - 32) return 0;
-  const double keep = double(cus - units);
+  const double keep = double(overlap_keep(units, cus));
   int64_t rs = int64_t(double(rows) * (1.0 - KDA_OVERLAP_RATIO * keep / double(units)));
   if (rs < 1) rs = 1;
   if (rs > rows - 1) rs = rows - 1;
@@ -1771,11 +1787,10 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   p.status = p.flags + p.nslots * p.HV;
   p.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   // The chunk kernel: items of the first rs rows over every CU, the rest over
-  // the CUs - units workgroups that stay; the carry takes the CUs of those
-  // that leave.
+  // the workgroups that stay; the carry takes the CUs of those that leave.
   Params chunks = p;
   chunks.phase2_lo = rs * (p.cmajor ? units : p.HV);
-  chunks.phase2_wgs = int(cus - units);
+  chunks.phase2_wgs = int(overlap_keep(units, cus));
   Params repair = p;      // the sequential carry, for the units that gave up
   repair.flags = nullptr;
   repair.cmajor = 0;

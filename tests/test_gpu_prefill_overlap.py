@@ -59,8 +59,13 @@ def _compare(kda, inp, name):
     a = _args(inp)
     oo, so, flags = _run(kda, a, B, T, H, HV, True)
     os_, ss, _ = _run(kda, a, B, T, H, HV, False)
-    set_flags = int((flags != 0).sum())
+    nslots = (B * T) // 64 + B + 1
+    set_flags = int((flags[:nslots * HV] != 0).sum())
+    gave_up = int((flags[nslots * HV:nslots * HV + B * HV] != 0).sum())
     assert set_flags > 0, f"{name}: the overlapped schedule did not run"
+    # one flag per (chunk, value head) of every sequence, each set once its slot is stored
+    assert set_flags == B * ((T + 63) // 64) * HV, f"{name}: {set_flags} slots flagged"
+    assert gave_up == 0, f"{name}: {gave_up} units gave up waiting"
     assert torch.equal(_bits(oo), _bits(os_)), f"{name}: o differs between the schedules"
     assert torch.equal(so, ss), f"{name}: final state differs between the schedules"
     say(f"overlapped == sequential bitwise, {name} (B={B} T={T} H={H} HV={HV}; {set_flags} slots flagged)")
@@ -101,10 +106,12 @@ def test_overlap_ragged_gqa_against_oracle(gpu_lib):
 
 def test_overlap_smallest_qualifying_shape(gpu_lib):
     """48 value heads and 48 chunk rows (the fewest units and rows the
-    schedule takes), no initial state; and the most units it takes on 256
-    compute units (224)."""
+    schedule takes), no initial state; the most units it takes on 256
+    compute units (224); and 191 units, whose leaving workgroups are
+    rounded up to 192."""
     _compare(gpu_lib, synth.prefill_basic(121, 1, 3072, 48, 48, init="none", name="min48"), "smallest")
     _compare(gpu_lib, synth.prefill_basic(122, 1, 3072, 32, 224, init="normal0.1", name="max224"), "most heads")
+    _compare(gpu_lib, synth.prefill_basic(126, 1, 3072, 191, 191, init="normal0.1", name="u191"), "191 units")
 
 
 @pytest.mark.parametrize("T,H,HV", [(3008, 48, 48), (3072, 47, 47), (3072, 75, 225)],
