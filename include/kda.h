@@ -120,7 +120,8 @@ int kda_qk_l2norm(const void* x, void* y, int64_t rows, int32_t K, void* stream)
  *
  * Split-form schedule.  With sequences of equal length (cu_seqlens NULL,
  * or a single packed sequence), 48 to CUs - 32 (sequence, value head)
- * units, at least 48 chunks per sequence and the whole workspace
+ * units, at least 48 chunks per sequence (24 when twice the units exceed
+ * the compute units) and the whole workspace
  * kda_chunk_prefill_workspace_size returns (slots plus ready flags), the
  * split form overlaps its two kernels: the chunk kernel covers the first
  * chunks of every unit on every compute unit, then the rest beside the carry, which

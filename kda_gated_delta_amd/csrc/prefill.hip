@@ -1751,17 +1751,20 @@ int64_t overlap_keep(int64_t units, int64_t cus) { return cus - (units + 31) / 3
 
 // Split row of the overlapped schedule, or 0 where it does not apply: rows
 // as above, one workspace window with room for the flags, 48 to CUs - 32
-// (sequence, value head) units and at least 48 chunk rows.  Measured on
-// MI355X at T = 8192 against the sequential schedule: 16 and 32 value heads
-// 33% and 7% slower (the 32-column carry is slower than the two-workgroup
-// one and little chunk work is left to overlap), 48 to 191 value heads 5% to
-// 17% faster; at 96 value heads, 64 rows 4% faster (and 34 rows 3% slower,
-// measured with the chunk kernel in two launches).
+// (sequence, value head) units, and at least 48 chunk rows, or at least 24
+// where the sequential carry's two workgroups per unit exceed the CUs.
+// Measured on MI355X at T = 8192 against the sequential schedule: 16 and 32
+// value heads 33% and 7% slower (the 32-column carry is slower than the
+// two-workgroup one and little chunk work is left to overlap), 48 to 191
+// value heads 5% to 17% faster; at 96 value heads, 40 rows 1% and 64 rows
+// 4% faster, 32 rows 2% slower (64 units 6%, 128 units 2%, 48 units 21%
+// slower); with 136 to 191 units, 24 to 40 rows 3% to 14% faster.
 int64_t overlap_rows(const Params& p) {
   const int64_t units = int64_t(p.N) * p.HV;
   const int64_t cus = device_cus();
   const int64_t rows = overlap_row_count(p);
-  if (!p.flags || p.wslots < p.nslots || rows < 48 || units < 48 || units > cus - 32) return 0;
+  if (!p.flags || p.wslots < p.nslots || units < 48 || units > cus - 32) return 0;
+  if (rows < 48 && !(rows >= 24 && 2 * units > cus)) return 0;
   const double keep = double(overlap_keep(units, cus));
   int64_t rs = int64_t(double(rows) * (1.0 - KDA_OVERLAP_RATIO * keep / double(units)));
   if (rs < 1) rs = 1;

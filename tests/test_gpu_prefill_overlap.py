@@ -1,12 +1,14 @@
 """The split prefill's overlapped schedule against its sequential schedule.
 
 With sequences of equal length (no cu_seqlens; or one packed sequence), 48
-to CUs - 32 (sequence, value head) units, at least 48 chunk rows and a
-workspace with room for the ready flags (the size
-kda_chunk_prefill_workspace_size returns), kda_chunk_prefill_split runs the
-chunk-parallel kernel in two launches and the carry (one workgroup per unit,
-32 state columns per wave) on a second stream beside the second launch,
-waiting for each of its slots to be flagged.  The arithmetic of every
+to CUs - 32 (sequence, value head) units, at least 48 chunk rows (24 when
+twice the units exceed the compute units) and a workspace with room for the
+ready flags (the size kda_chunk_prefill_workspace_size returns),
+kda_chunk_prefill_split runs the chunk-parallel kernel over the first chunk
+rows on every compute unit and over the rest on the workgroups that stay,
+while the carry (one workgroup per unit, 32 state columns per wave) runs on
+a second stream on the compute units of those that leave, waiting for each
+of its slots to be flagged.  The arithmetic of every
 column is the one the sequential schedule performs, so both schedules (and
 the fused form) must agree bit for bit; a workspace without the flag room
 forces the sequential schedule on the same inputs.  That the overlapped
@@ -107,19 +109,23 @@ def test_overlap_ragged_gqa_against_oracle(gpu_lib):
 def test_overlap_smallest_qualifying_shape(gpu_lib):
     """48 value heads and 48 chunk rows (the fewest units and rows the
     schedule takes), no initial state; the most units it takes on 256
-    compute units (224); and 191 units, whose leaving workgroups are
-    rounded up to 192."""
+    compute units (224); 191 units, whose leaving workgroups are rounded up
+    to 192; and 24 chunk rows with 160 units (twice the units above the
+    compute units)."""
     _compare(gpu_lib, synth.prefill_basic(121, 1, 3072, 48, 48, init="none", name="min48"), "smallest")
     _compare(gpu_lib, synth.prefill_basic(122, 1, 3072, 32, 224, init="normal0.1", name="max224"), "most heads")
     _compare(gpu_lib, synth.prefill_basic(126, 1, 3072, 191, 191, init="normal0.1", name="u191"), "191 units")
+    _compare(gpu_lib, synth.prefill_basic(127, 1, 1536, 80, 160, init="normal0.1", name="r24u160"), "24 rows")
 
 
-@pytest.mark.parametrize("T,H,HV", [(3008, 48, 48), (3072, 47, 47), (3072, 75, 225)],
-                         ids=["47rows", "47heads", "225heads"])
+@pytest.mark.parametrize("T,H,HV", [(3008, 48, 48), (3072, 47, 47), (3072, 75, 225), (1472, 160, 160),
+                                    (1536, 128, 128)],
+                         ids=["47rows", "47heads", "225heads", "23rows160heads", "24rows128heads"])
 def test_overlap_boundaries_run_sequential(gpu_lib, T, H, HV):
     """Just outside the schedule's range (47 chunk rows, 47 or 225 units on
-    256 compute units) the split form runs sequentially even with the flag
-    room: the flags stay untouched."""
+    256 compute units; 23 rows with 160 units; 24 rows with 128 units, whose
+    sequential carry fits the compute units) the split form runs
+    sequentially even with the flag room: the flags stay untouched."""
     kda = gpu_lib
     inp = synth.prefill_basic(123, 1, T, H, HV, init="none")
     oo, so, flags = _run(kda, _args(inp), 1, T, H, HV, True)
