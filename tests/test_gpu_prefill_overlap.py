@@ -173,6 +173,46 @@ def test_overlap_packed_sequences_run_sequential(gpu_lib):
     assert torch.equal(_bits(o), _bits(of)) and torch.equal(s, sf)
 
 
+def test_overlap_single_packed_sequence(gpu_lib):
+    """One packed sequence (cu_seqlens holding a single sequence) keeps the
+    slot order as its chunk rows: 1,580 tokens (25 chunks, the last ragged,
+    26 slot rows) with 160 value heads over 80 Q/K heads takes the
+    overlapped schedule (24 rows suffice with twice the units above the
+    compute units).  Bitwise equal to the sequential schedule and to the
+    fused form, every chunk flagged, no unit gave up; one head against the
+    oracle."""
+    kda = gpu_lib
+    T, H, HV = 1580, 80, 160
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    inp = synth.prefill_basic(128, 1, T, H, HV, init="normal0.1", cu_seqlens=cu, name="packed1_u160")
+    a = _args(inp)[:6] + (cu.cuda(),)
+    need = kda.workspace_size(1, T, H, HV, 1)
+    nslots = T // 64 + 2
+    fb = _flag_bytes(nslots, HV, 1)
+    assert need == nslots * HV * kda.PREFILL_SLOT_BYTES + fb
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    oo, so = kda.chunk_prefill_split(*a, workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws[need - fb:].view(torch.int32)
+    assert int((flags[:nslots * HV] != 0).sum()) == ((T + 63) // 64) * HV, "the overlapped schedule did not run"
+    assert int((flags[nslots * HV:nslots * HV + HV] != 0).sum()) == 0, "a unit gave up waiting"
+    ws2 = torch.zeros(need - fb, dtype=torch.uint8, device="cuda")
+    os_, ss = kda.chunk_prefill_split(*a, workspace=ws2)
+    of, sf = kda.chunk_prefill_fused(*a)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oo), _bits(os_)) and torch.equal(so, ss), "overlapped differs from sequential"
+    assert torch.equal(_bits(oo), _bits(of)) and torch.equal(so, sf), "overlapped differs from the fused form"
+    x = synth.to_numpy(inp)
+    hv = 131
+    hq = hv // (HV // H)
+    o_ref, s_ref = oracle.recurrent(x["q"][:, :, hq:hq + 1], x["k"][:, :, hq:hq + 1], x["v"][:, :, hv:hv + 1],
+                                    x["g"][:, :, hv:hv + 1], x["beta"][:, :, hv:hv + 1],
+                                    x["initial_state"][:, hv:hv + 1], x["cu_seqlens"])
+    e_o = check_o(oo[:, :, hv:hv + 1], o_ref, f"value head {hv}")
+    e_s = check_state(so[:, hv:hv + 1], s_ref, f"value head {hv}")
+    say(f"single packed sequence, value head {hv}: o_err={e_o:.2e} state_err={e_s:.2e}")
+
+
 def test_overlap_repeated_calls_one_workspace(gpu_lib):
     """Three calls in a row on one workspace: each call clears the flags it
     waits for, so a previous call's flags never release a slot early."""
