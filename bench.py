@@ -11,12 +11,11 @@ decode runs cache-cold.
 Prints one JSON line:
   value        prefill tokens/s (T / mean prefill call time by HIP events)
   roofline     the prefill entry point -- on this workload the split form's
-               overlapped schedule: the chunk kernel in two launches and the
-               carry beside the second, on the library's second stream,
-               joined back into the launch stream; the call timed by HIP
-               events on the launch stream -- against the HBM roofline:
-               algorithmic bytes per
-               call / mean call time.  traffic is the measured HBM bytes per
+               overlapped schedule: one chunk-kernel launch, the carry
+               beside its later rows on the library's second stream, joined
+               back into the launch stream; the call timed by HIP events on
+               the launch stream -- against the HBM roofline: algorithmic
+               bytes per call / mean call time.  traffic is the measured HBM bytes per
                call from the committed rocprofv3 counter summary when that
                was taken on the current kernel source, else null
   prefill, decode  event statistics (mean, p10, median, p90), the device

@@ -1682,7 +1682,9 @@ int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
 //   (rows - rs) * units * t_item / keep = rows * t_step.
 // t_step / t_item = 0.345 is the ratio whose split row timed fastest on
 // MI355X at B=1, H=HV=96, T=8192 (54 of 128 rows; 45 rows 13 us and 57
-// rows 2 us slower).  An earlier form in two chunk launches, the carry
+// rows 2 us slower), and against 0.30 and 0.40 it was fastest or within
+// 1 us from 48 to 191 units and at T = 4096 and 16384.  An earlier form in
+// two chunk launches, the carry
 // started at the first one's end, measured 11 us slower (the launch
 // boundary's gaps and the first launch's tail).
 #ifndef KDA_OVERLAP_RATIO
@@ -1741,7 +1743,7 @@ int64_t overlap_row_count(const Params& p) {
 // The others leave and the carry's workgroups take their CUs; their count is
 // rounded up to a multiple of 32 (8 XCDs x 4 shader engines) so that every
 // shader engine frees at least as many CUs as the carry places on it,
-// however the dispatcher spreads the two launches over them.  Freeing
+// however the dispatcher spreads the two kernels over them.  Freeing
 // exactly `units` CUs, 48, 176 and 191 units measured 23-42% slower at
 // T = 8192 (708 against 499 us at 48): a few carry workgroups found no free
 // CU where they were placed and waited for the chunk kernel's end.  Letting
