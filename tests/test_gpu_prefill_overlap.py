@@ -374,3 +374,76 @@ def test_overlap_under_serialised_kernels():
     assert r.returncode == 0 and line, f"subprocess failed: {r.stdout[-2000:]} {r.stderr[-2000:]}"
     say(line[0])
     assert line[0].startswith("RESULT overlapped=True same=True")
+
+
+def _overlap_expected(units, rows, cus):
+    """The schedule's range: 48 to CUs - 32 units and at least 48 chunk rows,
+    or at least 24 where twice the units exceed the compute units."""
+    if units < 48 or units > cus - 32:
+        return False
+    return rows >= 48 or (rows >= 24 and 2 * units > cus)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_overlap_random_shapes(gpu_lib, seed):
+    """Seeded random shapes around the overlapped schedule's range: several
+    equal-length sequences or one packed sequence, GQA groups, ragged tails,
+    initial state present or absent.  The schedule runs exactly where its
+    rule says (every chunk flagged, no unit gave up; otherwise the flags stay
+    untouched); the split form's two schedules and the fused form agree bit
+    for bit; two random heads against the oracle."""
+    kda = gpu_lib
+    rng = np.random.default_rng(7000 + seed)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    group = int(rng.choice([1, 2, 4]))
+    units_target = int(rng.integers(40, 233))
+    packed = bool(rng.random() < 0.3)
+    B = 1 if packed else int(rng.choice([1, 1, 2, 3]))
+    HV = max(group, (units_target // B) // group * group)
+    H = HV // group
+    T = int(rng.integers(1400, 3300))
+    init = str(rng.choice(["none", "normal0.1"]))
+    if packed:
+        cu = torch.tensor([0, T], dtype=torch.int32)
+        inp = synth.prefill_basic(7100 + seed, 1, T, H, HV, init=init, cu_seqlens=cu, name=f"ovl_rand{seed}_packed")
+        a = _args(inp)[:6] + (cu.cuda(),)
+        nseq, nslots, rows = 1, T // 64 + 2, T // 64 + 2
+    else:
+        inp = synth.prefill_basic(7100 + seed, B, T, H, HV, init=init, name=f"ovl_rand{seed}")
+        a = _args(inp)
+        nseq, nslots, rows = B, (B * T) // 64 + B + 1, (T + 63) // 64
+    units = nseq * HV
+    expect = _overlap_expected(units, rows, cus)
+    say(f"random overlap case {inp.name}: B={B} T={T} H={H} HV={HV} units={units} rows={rows} "
+        f"packed={packed} init={init} overlapped={expect}")
+    need = kda.workspace_size(B, T, H, HV, nseq if packed else 0)
+    fb = _flag_bytes(nslots, HV, nseq)
+    assert need == nslots * HV * kda.PREFILL_SLOT_BYTES + fb
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    oo, so = kda.chunk_prefill_split(*a, workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws[need - fb:].view(torch.int32)
+    set_flags = int((flags[:nslots * HV] != 0).sum())
+    gave_up = int((flags[nslots * HV:nslots * HV + units] != 0).sum())
+    if expect:
+        assert set_flags == nseq * ((T + 63) // 64) * HV, f"{inp.name}: {set_flags} slots flagged"
+        assert gave_up == 0, f"{inp.name}: {gave_up} units gave up waiting"
+    else:
+        assert set_flags == 0 and gave_up == 0, f"{inp.name}: the overlapped schedule ran outside its range"
+    ws2 = torch.zeros(need - fb, dtype=torch.uint8, device="cuda")
+    os_, ss = kda.chunk_prefill_split(*a, workspace=ws2)
+    of, sf = kda.chunk_prefill_fused(*a)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oo), _bits(os_)) and torch.equal(so, ss), f"{inp.name}: schedules differ"
+    assert torch.equal(_bits(oo), _bits(of)) and torch.equal(so, sf), f"{inp.name}: fused form differs"
+    x = synth.to_numpy(inp)
+    for hv in sorted(set(int(h) for h in rng.integers(0, HV, size=2))):
+        hq = hv // group
+        n = int(rng.integers(0, B))
+        s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, hv:hv + 1]
+        o_ref, s_ref = oracle.recurrent(x["q"][n:n + 1, :, hq:hq + 1], x["k"][n:n + 1, :, hq:hq + 1],
+                                        x["v"][n:n + 1, :, hv:hv + 1], x["g"][n:n + 1, :, hv:hv + 1],
+                                        x["beta"][n:n + 1, :, hv:hv + 1], s0, x["cu_seqlens"])
+        e_o = check_o(oo[n:n + 1, :, hv:hv + 1], o_ref, f"{inp.name} sequence {n} head {hv}")
+        e_s = check_state(so[n:n + 1, hv:hv + 1], s_ref, f"{inp.name} sequence {n} head {hv}")
+        say(f"  sequence {n}, value head {hv}: o_err={e_o:.2e} state_err={e_s:.2e}")
