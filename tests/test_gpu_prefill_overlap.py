@@ -359,10 +359,11 @@ print(f"RESULT overlapped={ran > 0} same={same} gave_up={gave_up}", flush=True)
 
 def test_overlap_under_serialised_kernels():
     """In a process where the runtime runs every kernel to completion before
-    the next (AMD_SERIALIZE_KERNEL=3), the carry runs before the chunk launch
-    whose slots it waits for: every unit gives up after its bounded wait and
-    the sequential carry after the join redoes it, so the results still equal
-    the sequential schedule's bit for bit."""
+    the next (AMD_SERIALIZE_KERNEL=3) the two kernels cannot overlap: the
+    carry runs either after the chunk kernel (it finds every slot flagged;
+    the order this runtime takes) or before it (every unit gives up after
+    its bounded wait and the sequential carry after the join redoes it).
+    Either way the results equal the sequential schedule's bit for bit."""
     import os
     import subprocess
     import sys
