@@ -142,7 +142,7 @@ constexpr int LS = 68;           // fp32 [64][64] arrays
 constexpr int AS = 72;           // 16-bit [*][64] arrays
 
 // intra_kernel LDS map (bytes).  Regions are reused across phases:
-//   U1   : fp32 L and T (phases 2-3), then fp16 -W and E^T (phase 4)
+//   U1   : fp32 L and T (phases 2-3), then fp16 -W (and, fused form, E^T) (phase 4)
 //   AREG : fp32 scan totals (phase 1), fp16 A (phases 3-4)
 constexpr int OFF_Q = 0;                                  // fp16 q^, then fp16 Qg  [64][QS]
 constexpr int OFF_K = OFF_Q + C * QS * 2;                 // fp16 k^                [64][QS]
@@ -165,6 +165,13 @@ static_assert(INTRA_LDS <= 160 * 1024, "LDS budget");
 constexpr int OFF_VT = INTRA_LDS;
 constexpr int FUSED_LDS = OFF_VT + NW * C * 16 * 2;
 static_assert(FUSED_LDS <= 160 * 1024, "LDS budget (fused)");
+// The split form instead forms E^T during the solve, while U1 still holds
+// T, in a region of its own past the shared map, beside the solve's Y
+// blocks (which the fused form keeps in the Kg^T region).
+constexpr int OFF_ETS = INTRA_LDS;                        // fp16 (e^G k)^T         [128][AS]
+constexpr int OFF_YS = OFF_ETS + KD * AS * 2;             // fp32 Y20, Y21          [2][16][16]
+constexpr int SPLIT_LDS = OFF_YS + 2 * 256 * 4;
+static_assert(SPLIT_LDS <= 160 * 1024, "LDS budget (split)");
 static_assert(C * AS * 2 >= 16 * KD * 4, "scan totals fit in the A region");
 static_assert(KD * AS * 2 >= 2 * 4 * 512 * 4, "phase 2 partial sums fit in the Kg^T region");
 
@@ -510,7 +517,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   float* sL = reinterpret_cast<float*>(smem + OFF_L);
   float* sT = reinterpret_cast<float*>(smem + OFF_T);
   uint16_t* sW = reinterpret_cast<uint16_t*>(smem + OFF_W);
-  uint16_t* sET = reinterpret_cast<uint16_t*>(smem + OFF_ET);
+  uint16_t* sET = reinterpret_cast<uint16_t*>(smem + (kFused ? OFF_ET : OFF_ETS));
   uint16_t* sAqk = reinterpret_cast<uint16_t*>(smem + OFF_AQK);
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem + OFF_A);
   float* sScr = reinterpret_cast<float*>(smem + OFF_A);
@@ -634,6 +641,50 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sf[(16 * rt + 4 * gq + r) * KD + col] = S[rt][r];
     }
+  };
+
+  // E^T = (e^G k)^T and Kg^T = (k e^{G_last - G})^T into LDS, and Qg of this
+  // thread's entries into `qg` (stored by store_qg once no thread reads q^
+  // any more).  Thread t handles channels c2, c2+1 (c2 = 2*(t%64)) for
+  // tokens 8*(t/64)..+7.
+  auto form_egk = [&](uint32_t (&qg_pk)[8]) __attribute__((always_inline)) {
+    const int c2 = 2 * (tid & 63);
+    const int j0 = 8 * (tid >> 6);
+    const float2 glast = *reinterpret_cast<const float2*>(sG + (C - 1) * GS + c2);
+    float ev0[8], ev1[8], kv0[8], kv1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int jj = j0 + e;
+      const float2 gj = *reinterpret_cast<const float2*>(sG + jj * GS + c2);
+      const uint32_t kk = *reinterpret_cast<const uint32_t*>(sK + jj * QS + c2);
+      const uint32_t qq = *reinterpret_cast<const uint32_t*>(sQ + jj * QS + c2);
+      const float eg0 = ex2(gj.x), eg1 = ex2(gj.y);
+      const float k0 = f16lo(kk), k1 = f16hi(kk);
+      ev0[e] = k0 * eg0;
+      ev1[e] = k1 * eg1;
+      kv0[e] = k0 * ex2(glast.x - gj.x);
+      kv1[e] = k1 * ex2(glast.y - gj.y);
+      qg_pk[e] = pack_f16(SCALE * f16lo(qq) * eg0, SCALE * f16hi(qq) * eg1);
+    }
+    *reinterpret_cast<uint4*>(sET + c2 * AS + j0) =
+        make_uint4(pack_f16(ev0[0], ev0[1]), pack_f16(ev0[2], ev0[3]), pack_f16(ev0[4], ev0[5]), pack_f16(ev0[6], ev0[7]));
+    *reinterpret_cast<uint4*>(sET + (c2 + 1) * AS + j0) =
+        make_uint4(pack_f16(ev1[0], ev1[1]), pack_f16(ev1[2], ev1[3]), pack_f16(ev1[4], ev1[5]), pack_f16(ev1[6], ev1[7]));
+    // Kg^T in the permuted token layout: tokens j0..j0+3 and j0+4..j0+7 each
+    // land as one contiguous 8-byte group.
+    const int pj0 = perm32(j0), pj4 = perm32(j0 + 4);
+    *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj0) = make_uint2(pack_f16(kv0[0], kv0[1]), pack_f16(kv0[2], kv0[3]));
+    *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj4) = make_uint2(pack_f16(kv0[4], kv0[5]), pack_f16(kv0[6], kv0[7]));
+    *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj0) = make_uint2(pack_f16(kv1[0], kv1[1]), pack_f16(kv1[2], kv1[3]));
+    *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj4) = make_uint2(pack_f16(kv1[4], kv1[5]), pack_f16(kv1[6], kv1[7]));
+  };
+  // Qg over q^ in the permuted channel layout; c2 and c2 + 1 stay adjacent
+  // there.
+  auto store_qg = [&](const uint32_t (&qg_pk)[8]) __attribute__((always_inline)) {
+    const int pc = perm32(2 * (tid & 63));
+    const int j0 = 8 * (tid >> 6);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sQ + (j0 + e) * QS + pc) = qg_pk[e];
   };
 
   // Overlapped schedule: the flag index (slot, value head) of the item whose
@@ -1022,6 +1073,13 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     if constexpr (kPublish) {
       if (pend >= 0 && tid == 0) publish(pend);
     }
+    // Split form: E^T (in its own region), Kg^T (in its region, whose phase-2
+    // partial sums were consumed above) and Qg (in registers) are formed
+    // here, so that their vector work runs beside the MFMA chains of the
+    // off-diagonal steps below; Qg is stored over q^ after the first step's
+    // barrier, when no thread reads q^ any more.
+    uint32_t qg_pk[8];
+    if constexpr (!kFused) form_egk(qg_pk);
     // Off-diagonal blocks of T on fp32 MFMA (16x16x4), through the inverse
     // of the two 32x32 diagonal halves Z0 = [[T00, 0], [T10, T11]] and
     // Z1 = [[T22, 0], [T32, T33]]:
@@ -1032,8 +1090,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     // products whose right operand is an accumulator (which holds exactly
     // those entries) and 4s + gq when both operands come from LDS.
     {
-      float* sY20 = sPart;          // Y20 and Y21, 16x16 row-major (the
-      float* sY21 = sPart + 256;    // partial sums were consumed above)
+      // Y20 and Y21, 16x16 row-major (fused form: where the partial sums,
+      // consumed above, were).
+      float* sY20 = kFused ? sPart : reinterpret_cast<float*>(smem + OFF_YS);
+      float* sY21 = sY20 + 256;
       // acc += L_IM T_MJ, both from LDS.
       auto lt = [&](f32x4 acc, int I, int M, int J) __attribute__((always_inline)) {
 #pragma unroll
@@ -1075,6 +1135,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       else if (wave == 4) Y = lt(z, 2, 0, 0);
       else if (wave == 5) Y = lt(z, 3, 0, 0);
       lds_barrier();
+      if constexpr (!kFused) store_qg(qg_pk);
       // Step 2: the T10 terms of Y20, Y30.
       if (wave == 4) { Y = lt(Y, 2, 1, 0); put_y(Y, sY20); }
       else if (wave == 5) Y = lt(Y, 3, 1, 0);
@@ -1106,48 +1167,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
     lds_barrier();
 
     // ---------------------------------------------------------- phase 4: E, Kg, Qg, W
-    // Thread t handles channels c2, c2+1 (c2 = 2*(t%64)) for tokens
-    // 8*(t/64)..+7.
-    uint32_t qg_pk[8];   // Qg of this thread's entries, stored after the barrier
-    {
-      const int c2 = 2 * (tid & 63);
-      const int j0 = 8 * (tid >> 6);
-      const float2 glast = *reinterpret_cast<const float2*>(sG + (C - 1) * GS + c2);
-      float ev0[8], ev1[8], kv0[8], kv1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = j0 + e;
-        const float2 gj = *reinterpret_cast<const float2*>(sG + jj * GS + c2);
-        const uint32_t kk = *reinterpret_cast<const uint32_t*>(sK + jj * QS + c2);
-        const uint32_t qq = *reinterpret_cast<const uint32_t*>(sQ + jj * QS + c2);
-        const float eg0 = ex2(gj.x), eg1 = ex2(gj.y);
-        const float k0 = f16lo(kk), k1 = f16hi(kk);
-        ev0[e] = k0 * eg0;
-        ev1[e] = k1 * eg1;
-        kv0[e] = k0 * ex2(glast.x - gj.x);
-        kv1[e] = k1 * ex2(glast.y - gj.y);
-        qg_pk[e] = pack_f16(SCALE * f16lo(qq) * eg0, SCALE * f16hi(qq) * eg1);
-      }
-      *reinterpret_cast<uint4*>(sET + c2 * AS + j0) =
-          make_uint4(pack_f16(ev0[0], ev0[1]), pack_f16(ev0[2], ev0[3]), pack_f16(ev0[4], ev0[5]), pack_f16(ev0[6], ev0[7]));
-      *reinterpret_cast<uint4*>(sET + (c2 + 1) * AS + j0) =
-          make_uint4(pack_f16(ev1[0], ev1[1]), pack_f16(ev1[2], ev1[3]), pack_f16(ev1[4], ev1[5]), pack_f16(ev1[6], ev1[7]));
-      // Kg^T in the permuted token layout: tokens j0..j0+3 and j0+4..j0+7 each
-      // land as one contiguous 8-byte group.
-      const int pj0 = perm32(j0), pj4 = perm32(j0 + 4);
-      *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj0) = make_uint2(pack_f16(kv0[0], kv0[1]), pack_f16(kv0[2], kv0[3]));
-      *reinterpret_cast<uint2*>(sKgT + c2 * AS + pj4) = make_uint2(pack_f16(kv0[4], kv0[5]), pack_f16(kv0[6], kv0[7]));
-      *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj0) = make_uint2(pack_f16(kv1[0], kv1[1]), pack_f16(kv1[2], kv1[3]));
-      *reinterpret_cast<uint2*>(sKgT + (c2 + 1) * AS + pj4) = make_uint2(pack_f16(kv1[4], kv1[5]), pack_f16(kv1[6], kv1[7]));
-    }
-    lds_barrier();
-    // Qg (over q^, now no longer read) in the permuted channel layout; c2 and
-    // c2 + 1 stay adjacent there.
-    {
-      const int pc = perm32(2 * (tid & 63));
-      const int j0 = 8 * (tid >> 6);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sQ + (j0 + e) * QS + pc) = qg_pk[e];
+    // (Split form: E^T, Kg^T and Qg were formed during the solve.)
+    if constexpr (kFused) {
+      uint32_t qg_fused[8];
+      form_egk(qg_fused);
+      lds_barrier();
+      store_qg(qg_fused);
     }
     // W = A (e^G k): 4 x 8 output tiles, 4 per wave; A is lower triangular.
     // Computed as W^T = E^T A^T (the same two operand reads, roles swapped),
@@ -1781,7 +1806,7 @@ __global__ void clear_flags_kernel(int* f, int64_t n) {
 
 int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side) {
   static std::atomic<bool> pub_set[kMaxDevices], inter_set[kMaxDevices], rep_set[kMaxDevices];
-  if (set_lds(&intra_kernel<false, true>, INTRA_LDS, pub_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&intra_kernel<false, true>, SPLIT_LDS, pub_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<32>, inter_lds(32), inter_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<16>, inter_lds(16), rep_set) != KDA_OK) return KDA_ERR_HIP;
   const int64_t units = int64_t(p.N) * p.HV;
@@ -1806,7 +1831,7 @@ int launch_overlapped(Params p, int64_t rs, hipStream_t stream, SideStream* side
   int st = launch_status();
   if (st != KDA_OK) return st;
   if (hipEventRecord(side->fork, stream) != hipSuccess) return KDA_ERR_HIP;
-  hipLaunchKernelGGL((intra_kernel<false, true>), dim3(unsigned(cus)), dim3(NT), INTRA_LDS, stream, chunks);
+  hipLaunchKernelGGL((intra_kernel<false, true>), dim3(unsigned(cus)), dim3(NT), SPLIT_LDS, stream, chunks);
   st = launch_status();
   if (st != KDA_OK) return st;
   // The carry is enqueued after the chunk kernel and waits only for the
@@ -1832,7 +1857,7 @@ int launch(Params p, hipStream_t stream) {
     if (SideStream* side = side_stream(stream)) return launch_overlapped(p, rs, stream, side);
   }
   static std::atomic<bool> intra_set[kMaxDevices], inter_set[kMaxDevices];
-  if (set_lds(&intra_kernel<false>, INTRA_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
+  if (set_lds(&intra_kernel<false>, SPLIT_LDS, intra_set) != KDA_OK) return KDA_ERR_HIP;
   if (set_lds(&inter_kernel<16>, inter_lds(16), inter_set) != KDA_OK) return KDA_ERR_HIP;
   if (p.wslots < 1) return KDA_ERR_WORKSPACE;
   if (p.wslots * p.HV > 0x7fffffff - 0x10000) return KDA_ERR_SHAPE;   // 32-bit item ids in the intra kernel
@@ -1848,7 +1873,7 @@ int launch(Params p, hipStream_t stream) {
     p.cmajor = 0;
     p.phase2_wgs = 0;
     const int64_t intra_blocks = items < device_cus() ? items : device_cus();
-    hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), INTRA_LDS, stream, p);
+    hipLaunchKernelGGL(intra_kernel<false>, dim3(unsigned(intra_blocks)), dim3(NT), SPLIT_LDS, stream, p);
     int st = launch_status();
     if (st != KDA_OK) return st;
     hipLaunchKernelGGL(inter_kernel<16>, dim3(unsigned(inter_blocks)), dim3(NTI), inter_lds(16), stream, p);
