@@ -559,8 +559,15 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
   };
   // Next item id of this workgroup.  Overlapped schedule: items below
   // phase2_lo over the whole grid, the rest over its first phase2_wgs
-  // workgroups (w2 >= 0); the others leave.
-  const int w2 = int(blockIdx.x) < p.phase2_wgs ? int(blockIdx.x) : -1;
+  // workgroups (w2 >= 0, their order there); the others leave.  Below
+  // phase2_lo the first (phase2_lo mod grid) workgroups take one item more;
+  // the order is rotated so that the next ones take the rest's short last
+  // round, and the workgroups that stay end within one item of each other.
+  int w2 = -1;
+  if (!kFused && int(blockIdx.x) < p.phase2_wgs) {
+    const int extra1 = int(p.phase2_lo % int64_t(gridDim.x)) % p.phase2_wgs;
+    w2 = (int(blockIdx.x) + p.phase2_wgs - extra1) % p.phase2_wgs;
+  }
   auto next_of = [&](int id) __attribute__((always_inline)) {
     if (kFused || p.phase2_wgs == 0) return id + stride;
     const int p1 = int(p.phase2_lo);
@@ -1705,15 +1712,17 @@ int64_t window_slots(int64_t nslots, int64_t HV, int64_t bytes) {
 // chunk kernel and the carry end together: with t_item the chunk kernel's
 // time per item per CU and t_step the carry's time per chunk while both run,
 //   (rows - rs) * units * t_item / keep = rows * t_step.
-// t_step / t_item = 0.345 is the ratio whose split row timed fastest on
-// MI355X at B=1, H=HV=96, T=8192 (54 of 128 rows; 45 rows 13 us and 57
-// rows 2 us slower), and against 0.30 and 0.40 it was fastest or within
-// 1 us from 48 to 191 units and at T = 4096 and 16384.  An earlier form in
-// two chunk launches, the carry
+// t_step / t_item = 0.357 is the ratio whose split row timed fastest on
+// MI355X at B=1, H=HV=96, T=8192, each ratio in a process of its own (51
+// of 128 rows: 717.3-718.1 us; 49 rows 718.0-719.7, 54 rows 721.2-722.7,
+// 57 rows 729.2-730.6); against 0.345 it ties from 128 to 191 units, is
+// 4-5 us faster at 96 units over 128 rows (one or two sequences) and 2 us
+// slower over 64 rows, and 0.30 and 0.40 are slower still.  An earlier form
+// in two chunk launches, the carry
 // started at the first one's end, measured 11 us slower (the launch
 // boundary's gaps and the first launch's tail).
 #ifndef KDA_OVERLAP_RATIO
-#define KDA_OVERLAP_RATIO 0.345
+#define KDA_OVERLAP_RATIO 0.357
 #endif
 
 struct SideStream {
