@@ -436,7 +436,6 @@ constexpr int AUX_DEV = 16;
 typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 constexpr int WAIT_VM4 = 0x0F74;   // s_waitcnt vmcnt(4): low vmcnt bits 3:0, high bits 15:14 zero
 constexpr int WAIT_VM8 = 0x0F78;   // s_waitcnt vmcnt(8)
-constexpr int WAIT_VM9 = 0x0F79;   // s_waitcnt vmcnt(9)
 constexpr int WAIT_VM0 = 0x0F70;   // s_waitcnt vmcnt(0) only
 
 // Direct load of this wave's v tile (64 tokens x 16 columns from column c0,
@@ -1003,20 +1002,24 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         }
       }
     }
-    lds_barrier();
-
-    // ---------------------------------------------------------- phase 3: solve
-    if (nxt.id < items) load_raw_g(R, p, nxt.trow, nxt.nvalid, nxt.hv, tid);
     // Overlapped schedule: the previous item's 9 slot stores precede this
-    // item's 9 prefetch loads (none after the last item) in the in-order
-    // completion counter, so this wait completes exactly those stores; its
-    // flag is set after the barrier below, once every thread has waited.
+    // item's 4 q/k prefetch loads (none after the last item) in the in-order
+    // completion counter, so this wait completes exactly those stores (issued
+    // an item's first two phases ago); their flag is set after the barrier
+    // below, once every thread has waited.
     if constexpr (kPublish) {
       if (pend >= 0) {
-        if (nxt.id < items) __builtin_amdgcn_s_waitcnt(WAIT_VM9);
+        if (nxt.id < items) __builtin_amdgcn_s_waitcnt(WAIT_VM4);
         else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
       }
     }
+    lds_barrier();
+    if constexpr (kPublish) {
+      if (pend >= 0 && tid == 0) publish(pend);
+    }
+
+    // ---------------------------------------------------------- phase 3: solve
+    if (nxt.id < items) load_raw_g(R, p, nxt.trow, nxt.nvalid, nxt.hv, tid);
     // Fused form: this chunk's v tile for the wave's 16 state columns, for
     // the carry at the end of the item.
     if constexpr (kFused) load_v_lds(sVt, p, cur.trow, cur.nvalid, cur.hv, 16 * wave, lane);
@@ -1077,9 +1080,6 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
       }
     }
     lds_barrier();
-    if constexpr (kPublish) {
-      if (pend >= 0 && tid == 0) publish(pend);
-    }
     // Split form: E^T (in its own region), Kg^T (in its region, whose phase-2
     // partial sums were consumed above) and Qg (in registers) are formed
     // here, so that their vector work runs beside the MFMA chains of the
