@@ -24,7 +24,8 @@
 //     3. T = (I+L)^-1 by blocked forward substitution in float32 (diagonal
 //        blocks by substitution, off-diagonal blocks on fp32 MFMA), then
 //        A = T diag(beta);
-//     4. E = exp(G) k, Kg, Qg, exp(G_last) and W = A E;
+//     4. E = exp(G) k, Kg, Qg, exp(G_last) and W = A E (the split form
+//        forms E, Kg and Qg during 3, beside the off-diagonal MFMA steps);
 //   and the chunk's W, Qg, Kg^T, Aqk, A and exp(G_last) are written to the
 //   workspace (66 KB per chunk and head, fp16 except exp(G_last)).
 //
