@@ -80,8 +80,7 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 constexpr int R_QN = 0;                     // [C][K] q^ as bf16 (two per float slot)
 constexpr int R_KN = R_QN + C * KD / 2;     // [C][K] k^ as bf16
 constexpr int R_G = R_KN + C * KD / 2;      // [C][K] G log2(e), G the inclusive prefix of g
-constexpr int R_E = R_G + C * KD;           // [C][K] exp(G) k^
-constexpr int R_W = R_E + C * KD;           // [C][K] A E
+constexpr int R_W = R_G + C * KD;           // [C][K] A E (E = exp(G) k^ is formed where it is needed)
 constexpr int R_U = R_W + C * KD;           // [C][V] A v
 constexpr int R_QG = R_U + C * KD;          // [C][K] K^-1/2 q^ exp(G)
 constexpr int R_KG = R_QG + C * KD;         // [C][K] k^ exp(G_last - G)
@@ -628,7 +627,6 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BParams p) {
       }
       st4(rec + R_QG + i * KD + d0, qg);
       st4(rec + R_KG + i * KD + d0, kg);
-      st4(rec + R_E + i * KD + d0, ev);
       st4(sQ + i * KP + d0, ev);
     }
 #pragma unroll
@@ -1376,13 +1374,16 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
   tri_store(sDA, LQ, da, wave, lg, l16, tid);
   kda::lds_barrier();
   {
-    // G, E and this tile's own dG and dk^ partials, issued before the products.
-    v4f xg[4], xe[4], xdg[4], xdk[4];
+    // G, k^ (for E = exp(G) k^, formed here as the recompute kernel forms
+    // it) and this tile's own dG and dk^ partials, issued before the
+    // products.
+    v4f xg[4], xdg[4], xdk[4];
+    uint2 xk[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = i0 + r;
       xg[r] = ldg4(rec + R_G + j * KD + d0);
-      xe[r] = ldg4(rec + R_E + j * KD + d0);
+      xk[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(rec + R_KN) + j * KD + d0);
       xdg[r] = ldg4(gdG + j * KD + d0);
       xdk[r] = pdk[r];
     }
@@ -1398,10 +1399,12 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
       const int j = i0 + r;
       if (j < nv) put4(p.dv, ((t0 + j) * p.HV + hv) * KD + d0, av[r], p.obf);
       float vg[4], vk[4];
+      const float kf[4] = {kda::bf16lo(xk[r].x), kda::bf16hi(xk[r].x), kda::bf16lo(xk[r].y), kda::bf16hi(xk[r].y)};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        vg[cc] = fmaf(ae[r][cc], xe[r][cc], xdg[r][cc]);
-        vk[cc] = fmaf(ae[r][cc], ex2(xg[r][cc]), xdk[r][cc]);
+        const float eg = ex2(xg[r][cc]);
+        vg[cc] = fmaf(ae[r][cc], eg * kf[cc], xdg[r][cc]);
+        vk[cc] = fmaf(ae[r][cc], eg, xdk[r][cc]);
       }
       st4(gdG + j * KD + d0, vg);
       pdk[r] = j < nv ? v4f{vk[0], vk[1], vk[2], vk[3]} : v4f{0.f, 0.f, 0.f, 0.f};
