@@ -1224,14 +1224,17 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     }
     kda::lds_barrier();
   }
-  // The epilogue's global operands (G, Qg, Kg rows of this thread's tile,
-  // G_last, gamma), issued now so that they arrive during the round trips.
-  v4f egv[4], eqg[4], ekg[4];
+  // The epilogue's global operands (G, q^ and k^ rows of this thread's
+  // tile, G_last, gamma), issued now so that they arrive during the round
+  // trips.  Qg and Kg are formed from them as the recompute kernel forms
+  // them, sharing the epilogue's exponentials, rather than read back.
+  v4f egv[4];
+  uint2 eqn[4], ekn[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     egv[r] = ldg4(rec + R_G + (i0 + r) * KD + d0);
-    eqg[r] = ldg4(rec + R_QG + (i0 + r) * KD + d0);
-    ekg[r] = ldg4(rec + R_KG + (i0 + r) * KD + d0);
+    eqn[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(rec + R_QN) + (i0 + r) * KD + d0);
+    ekn[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(rec + R_KN) + (i0 + r) * KD + d0);
   }
   const v4f egl = ldg4(rec + R_G + (C - 1) * KD + d0);
   const v4f egm = rb == 0 ? ldg4(rec + R_GAM + d0) : v4f{0.f, 0.f, 0.f, 0.f};
@@ -1279,12 +1282,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(BParams p) {
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r;
       float vq[4], vk[4], vg[4];
+      const float qn[4] = {kda::bf16lo(eqn[r].x), kda::bf16hi(eqn[r].x), kda::bf16lo(eqn[r].y), kda::bf16hi(eqn[r].y)};
+      const float kn[4] = {kda::bf16lo(ekn[r].x), kda::bf16hi(ekn[r].x), kda::bf16lo(ekn[r].y), kda::bf16hi(ekn[r].y)};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        vq[cc] = kScale * aq[r][cc] * ex2(egv[r][cc]);
-        vg[cc] = aq[r][cc] * eqg[r][cc] - akg[r][cc] * ekg[r][cc];
-        vk[cc] = akg[r][cc] * ex2(egl[cc] - egv[r][cc]);
-        dglp[cc] = fmaf(akg[r][cc], ekg[r][cc], dglp[cc]);
+        const float eg = ex2(egv[r][cc]);
+        const float el = ex2(egl[cc] - egv[r][cc]);
+        const float qg = kScale * qn[cc] * eg;
+        const float kg = kn[cc] * el;
+        vq[cc] = kScale * aq[r][cc] * eg;
+        vg[cc] = aq[r][cc] * qg - akg[r][cc] * kg;
+        vk[cc] = akg[r][cc] * el;
+        dglp[cc] = fmaf(akg[r][cc], kg, dglp[cc]);
       }
       st4(gdG + i * KD + d0, vg);
       pdk[r] = i < nv ? v4f{vk[0], vk[1], vk[2], vk[3]} : v4f{0.f, 0.f, 0.f, 0.f};
