@@ -877,33 +877,17 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
         const int i = 16 * I + l16;     // operand row (A side)
         const int j = 16 * J + l16;     // operand row (B side)
         // Largest split-factor exponent of this lane's entries (<= 0 below the
-        // diagonal, so only diagonal blocks need the check).
+        // diagonal, so only diagonal blocks need the check).  In the split
+        // form a diagonal block forms all four k-steps' factors and fp16
+        // operands first, taking the exponents' largest magnitude on the way
+        // (on a diagonal block j == i, so the two factors' exponents are
+        // G_i - G_ref and its negation), and runs the products once the range
+        // is known.
         float emax = 0.f;
-        if (J == I) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int ch0 = 32 * s + 8 * gq;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              // On a diagonal block j == i, so the two factors' exponents are
-              // G_i - G_ref and its negation.
-              const float4 gi = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
-              const float4 gr = *reinterpret_cast<const float4*>(sG + ref * GS + ch0 + 4 * h);
-              emax = fmaxf(emax, fmaxf(fmaxf(fabsf(gi.x - gr.x), fabsf(gi.y - gr.y)),
-                                       fmaxf(fabsf(gi.z - gr.z), fabsf(gi.w - gr.w))));
-            }
-          }
-        }
         f32x4 accL = {0.f, 0.f, 0.f, 0.f};
         f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
-        const bool wide = __any(emax > F16_EXP2);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        auto factors = [&](int s, f32x8& fr, f32x8& fc, float* em) __attribute__((always_inline)) {
           const int ch0 = 32 * s + 8 * gq;
-          const f16x8 ki = *reinterpret_cast<const f16x8*>(sK + i * QS + ch0);
-          const f16x8 qi = *reinterpret_cast<const f16x8*>(sQ + i * QS + ch0);
-          const f16x8 kj = *reinterpret_cast<const f16x8*>(sK + j * QS + ch0);
-          f32x8 fr, fc;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const float4 gi4 = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
@@ -914,27 +898,84 @@ __global__ __launch_bounds__(NT) void intra_kernel(Params p) {
             const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              fr[4 * h + e] = ex2(gi[e] - gr[e]);
+              const float d = gi[e] - gr[e];
+              if (em) *em = fmaxf(*em, fabsf(d));
+              fr[4 * h + e] = ex2(d);
               fc[4 * h + e] = ex2(gr[e] - gj[e]);
             }
           }
-          if (!wide) {
-            // Split factors rounded to fp16, products in packed fp16.
+        };
+        bool wide = false;
+        if constexpr (kFused) {
+          // (The fused form, whose carry state holds more registers, keeps a
+          // separate pass over the exponents: folded in, it spills.)
+          if (J == I) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int ch0 = 32 * s + 8 * gq;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const float4 gi = *reinterpret_cast<const float4*>(sG + i * GS + ch0 + 4 * h);
+                const float4 gr = *reinterpret_cast<const float4*>(sG + ref * GS + ch0 + 4 * h);
+                emax = fmaxf(emax, fmaxf(fmaxf(fabsf(gi.x - gr.x), fabsf(gi.y - gr.y)),
+                                         fmaxf(fabsf(gi.z - gr.z), fabsf(gi.w - gr.w))));
+              }
+            }
+          }
+          wide = __any(emax > F16_EXP2);
+        }
+        if (!kFused && J == I) {
+          f16x8 aL[4], aQ[4], bK[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int ch0 = 32 * s + 8 * gq;
+            const f16x8 ki = *reinterpret_cast<const f16x8*>(sK + i * QS + ch0);
+            const f16x8 qi = *reinterpret_cast<const f16x8*>(sQ + i * QS + ch0);
+            const f16x8 kj = *reinterpret_cast<const f16x8*>(sK + j * QS + ch0);
+            f32x8 fr, fc;
+            factors(s, fr, fc, &emax);
             const f16x8 frh = __builtin_convertvector(fr, f16x8);
             const f16x8 fch = __builtin_convertvector(fc, f16x8);
-            accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ki * frh, kj * fch, accL, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(qi * frh, kj * fch, accQ, 0, 0, 0);
-          } else {
-            // Steep decay inside a diagonal block: bf16 operands keep the range.
-            bf16x8 a, b, c;
+            aL[s] = ki * frh;
+            aQ[s] = qi * frh;
+            bK[s] = kj * fch;
+          }
+          wide = __any(emax > F16_EXP2);
+          if (!wide) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              a[e] = (__bf16)((float)ki[e] * fr[e]);
-              b[e] = (__bf16)((float)qi[e] * fr[e]);
-              c[e] = (__bf16)((float)kj[e] * fc[e]);
+            for (int s = 0; s < 4; ++s) {
+              accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(aL[s], bK[s], accL, 0, 0, 0);
+              accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ[s], bK[s], accQ, 0, 0, 0);
             }
-            accL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c, accL, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, c, accQ, 0, 0, 0);
+          }
+        }
+        if (kFused || J != I || wide) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int ch0 = 32 * s + 8 * gq;
+            const f16x8 ki = *reinterpret_cast<const f16x8*>(sK + i * QS + ch0);
+            const f16x8 qi = *reinterpret_cast<const f16x8*>(sQ + i * QS + ch0);
+            const f16x8 kj = *reinterpret_cast<const f16x8*>(sK + j * QS + ch0);
+            f32x8 fr, fc;
+            factors(s, fr, fc, nullptr);
+            if (!wide) {
+              // Split factors rounded to fp16, products in packed fp16.
+              const f16x8 frh = __builtin_convertvector(fr, f16x8);
+              const f16x8 fch = __builtin_convertvector(fc, f16x8);
+              accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ki * frh, kj * fch, accL, 0, 0, 0);
+              accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(qi * frh, kj * fch, accQ, 0, 0, 0);
+            } else {
+              // Steep decay inside a diagonal block: bf16 operands keep the range.
+              bf16x8 a, b, c;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                a[e] = (__bf16)((float)ki[e] * fr[e]);
+                b[e] = (__bf16)((float)qi[e] * fr[e]);
+                c[e] = (__bf16)((float)kj[e] * fc[e]);
+              }
+              accL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c, accL, 0, 0, 0);
+              accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, c, accQ, 0, 0, 0);
+            }
           }
         }
         const int jc = 16 * J + l16;    // result column
